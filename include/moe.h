@@ -1,0 +1,197 @@
+/*
+ * moe.h -- C ABI of a dropless Mixture-of-Experts layer forward for AMD MI355X (gfx950).
+ *
+ * The operation is the four-stage MoE forward described on the summary page of
+ * "Scalable Training of Mixture-of-Experts Models with Megatron Core" (section
+ * "Method", first paragraph): a router (learned linear projection, optionally in
+ * FP32, then softmax or sigmoid scores and top-k selection), a dispatcher that
+ * permutes tokens so each expert's rows are contiguous, all local experts in one
+ * grouped GEMM, and a combine step; an optional shared expert sees every token.
+ * "Sync-free execution for dropless MoE" (same page, "Method", second paragraph)
+ * and "CUDA-Graph-friendly sync-free execution" (same page, "TL;DR") fix the
+ * execution model: nothing here reads device data back to the host.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers to row-major, densely packed arrays, owned
+ *    by the caller; the library allocates no memory and keeps no per-call state.
+ *    Pointers must be 16-byte aligned.  Inputs and outputs must not alias.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream),
+ *    never synchronise, never copy to the host, and are HIP-graph capturable.
+ *  - Arguments are validated on the host before anything is launched; a failed check
+ *    returns MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED / MOE_ERR_WORKSPACE and
+ *    launches nothing.  A launch failure returns MOE_ERR_HIP.  Faults inside kernels
+ *    surface at the caller's next synchronisation.
+ *  - Integer outputs (expert ids, counts, offsets, permutation) are deterministic:
+ *    the same inputs give the same bits on every run.  No floating-point atomics are
+ *    used anywhere, so floating outputs are run-to-run deterministic as well.
+ *  - Limits: 1 <= k <= min(E, 16); E <= 512; T*k < 2^31.
+ *  - Readings fixed where the pages are silent: selection ranks the fp32 logit plus
+ *    the optional routing bias (one fp32 add); gates use the unbiased logit; ties break
+ *    to the lower expert index; slots are ordered by key descending; inside an expert
+ *    rows follow increasing token index; the first expert matrix's 2F columns are
+ *    [gate | up] and h = SiLU(gate) * up; the shared expert has gate 1.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_TOPK 16
+#define MOE_MAX_EXPERTS 512
+
+typedef void* moe_stream_t; /* a hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, size out of range, inconsistent sizes     */
+  MOE_ERR_UNSUPPORTED = 2, /* valid request this build does not implement            */
+  MOE_ERR_WORKSPACE = 3,   /* workspace pointer missing or smaller than required     */
+  MOE_ERR_HIP = 4          /* a HIP launch failed (hipGetLastError after the launch) */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_FP8_E4M3 = 2 /* OCP E4M3 without infinities ("e4m3fn"), max 448 */
+} moe_dtype;
+
+typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
+
+/* ---------------------------------------------------------------------------------------
+ * Route (summary page, "Method", first paragraph: the router).
+ *   x        [T, H]   x_dt = MOE_F32 or MOE_BF16
+ *   w_router [H, E]   fp32
+ *   bias     [E] fp32 or NULL: added to the logit (one fp32 add) for SELECTION only
+ *   logits   [T, E] fp32 out, or NULL (not written).  When written, these are exactly the
+ *            fp32 values the selection used.
+ *   topk_ids [T, k] int32 out: the k largest keys per token, slots by key descending,
+ *            ties to the lower expert index.
+ *   topk_gates [T, k] fp32 out: softmax over all E of the logits, or sigmoid of the
+ *            logit, taken at the selected experts; divided by their sum if norm_topk != 0.
+ *   workspace device scratch of at least moe_route_workspace_size(T, E, logits != NULL) bytes
+ *            (holds the logits when the caller does not ask for them; may be NULL otherwise).
+ * H must be a multiple of 8.
+ * ------------------------------------------------------------------------------------- */
+size_t moe_route_workspace_size(int64_t T, int32_t E, int32_t logits_given);
+moe_status moe_route(const void* x, moe_dtype x_dt, const float* w_router, const float* bias,
+                     int64_t T, int32_t H, int32_t E, int32_t k, moe_score score, int32_t norm_topk,
+                     float* logits, int32_t* topk_ids, float* topk_gates, void* workspace,
+                     size_t workspace_bytes, moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Dispatch (summary page, "Method", first paragraph: tokens permuted so same-expert
+ * tokens are contiguous, as the grouped GEMM requires).
+ *   topk_ids       [T, k] int32, each in [0, E) and distinct within a token (not checked)
+ *   expert_counts  [E] int32 out, or NULL: rows per expert (sum = T*k)
+ *   expert_offsets [E+1] int32 out: exclusive prefix sum of the counts
+ *   row_map        [T, k] int32 out: permuted row of (t, j)
+ *   src_token      [T*k] int32 out: token of permuted row p (inverse of row_map)
+ *   x_perm         [T*k, H] out: x_perm[row_map[t, j]] = x[t].  perm_dt = x_dt copies the
+ *                  bits; perm_dt = MOE_FP8_E4M3 (x_dt = MOE_BF16, H % 128 == 0) quantises
+ *                  each row in 1x128 blocks: scale = amax / 448 (1 for an all-zero block),
+ *                  code = e4m3_rne(clamp(x / scale, +-448)); scales go to
+ *   x_perm_scales  [T*k, H/128] fp32 out (FP8 only, else ignored).
+ *   x_perm may be NULL to build only the maps.
+ *   workspace      device scratch of at least moe_permute_workspace_size(T, E, k) bytes.
+ * ------------------------------------------------------------------------------------- */
+size_t moe_permute_workspace_size(int64_t T, int32_t E, int32_t k);
+moe_status moe_permute(const void* x, moe_dtype x_dt, const int32_t* topk_ids, int64_t T, int32_t H,
+                       int32_t E, int32_t k, void* x_perm, moe_dtype perm_dt, float* x_perm_scales,
+                       int32_t* row_map, int32_t* src_token, int32_t* expert_counts,
+                       int32_t* expert_offsets, void* workspace, size_t workspace_bytes,
+                       moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Compute (summary page, "Method", first paragraph: all local experts in one grouped GEMM;
+ * SwiGLU experts): for every expert e and every row p in [offsets[e], offsets[e+1]):
+ *     u = x_perm[p] . W1[e]          W1 [E, H, 2F]   (columns [0,F) gate, [F,2F) up)
+ *     h = SiLU(u[:F]) * u[F:]        SiLU(z) = z / (1 + exp(-z))
+ *     y_perm[p] = h . W2[e]          W2 [E, F, H]
+ * Per-expert row counts are read from expert_offsets in DEVICE memory only; `rows` is the
+ * host-known bound T*k used to size the launch (offsets[E] <= rows is required).
+ *   dt = MOE_F32:  x_perm, w1, w2 fp32; h fp32; y_perm fp32 (out_dt MOE_F32).
+ *   dt = MOE_BF16: x_perm, w1, w2 bf16; h rounded to bf16; y_perm bf16 or fp32.
+ *   dt = MOE_FP8_E4M3: x_perm e4m3 with x_perm_scales [rows, H/128]; w1/w2 e4m3 with
+ *        w1_scales [E, H/128, 2F/128], w2_scales [E, F/128, H/128] (128x128 blocks); h is
+ *        quantised to e4m3 in 1x128 blocks inside the path; y_perm bf16 or fp32.
+ * Sizes: H and F multiples of 128 (bf16 / fp8) or of 32 (fp32).
+ * workspace: at least moe_grouped_swiglu_workspace_size(rows, F, dt) bytes (holds h).
+ * Rows beyond offsets[E] are not written.
+ * ------------------------------------------------------------------------------------- */
+size_t moe_grouped_swiglu_workspace_size(int64_t rows, int32_t F, moe_dtype dt);
+moe_status moe_grouped_swiglu(const void* x_perm, const float* x_perm_scales, moe_dtype dt,
+                              const int32_t* expert_offsets, int64_t rows, int32_t E, int32_t H,
+                              int32_t F, const void* w1, const float* w1_scales, const void* w2,
+                              const float* w2_scales, void* y_perm, moe_dtype out_dt,
+                              void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Combine (summary page, "Method", first paragraph):
+ *     y[t] = sum_{j<k} topk_gates[t, j] * y_perm[row_map[t, j]]  (+ shared_out[t], gate 1)
+ * accumulated in fp32 over j ascending and rounded once to out_dt.
+ *   y_perm [T*k, H] y_dt (MOE_F32 | MOE_BF16); shared_out [T, H] y_dt or NULL;
+ *   y [T, H] out_dt (MOE_F32 | MOE_BF16).
+ * ------------------------------------------------------------------------------------- */
+moe_status moe_unpermute_combine(const void* y_perm, moe_dtype y_dt, const int32_t* row_map,
+                                 const float* topk_gates, const void* shared_out, int64_t T,
+                                 int32_t H, int32_t k, void* y, moe_dtype out_dt, moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * The whole layer in one call: route -> permute -> grouped SwiGLU -> (shared expert) ->
+ * combine, launched in that order on `stream`.
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t H, E, k, F;
+  int32_t Fs;           /* shared expert hidden size, 0 = no shared expert                */
+  moe_dtype x_dt;       /* activations x and y: MOE_F32 or MOE_BF16                      */
+  moe_dtype w_dt;       /* expert weights: MOE_F32 (x_dt F32), MOE_BF16, MOE_FP8_E4M3    */
+  moe_dtype out_dt;     /* y: MOE_F32 or MOE_BF16                                        */
+  moe_score score;
+  int32_t norm_topk;
+  const float* w_router; /* [H, E] fp32                                                  */
+  const float* bias;     /* [E] selection bias or NULL                                   */
+  const void* w1;        /* [E, H, 2F]                                                   */
+  const void* w2;        /* [E, F, H]                                                    */
+  const void* ws1;       /* [H, 2Fs] or NULL                                             */
+  const void* ws2;       /* [Fs, H] or NULL                                              */
+  const float* w1_scales, *w2_scales, *ws1_scales, *ws2_scales; /* FP8 only, else NULL  */
+} moe_layer;
+
+/* Optional views of the intermediates: every non-NULL pointer receives that stage's
+ * output (shapes as in the stage calls; x_perm / y_perm in the dtypes moe_forward uses:
+ * x_perm in w_dt (e4m3 codes for FP8, with x_perm_scales), y_perm in x_dt).
+ * stage_events: optional hipEvent_t handles recorded on `stream` at the stage boundaries
+ * (0 before route, 1 after route, 2 after permute, 3 after the first grouped GEMM,
+ * 4 after the second, 5 after the shared expert, 6 after combine); NULL entries are skipped. */
+#define MOE_NUM_STAGE_EVENTS 7
+typedef struct {
+  float* logits;
+  int32_t* topk_ids;
+  float* topk_gates;
+  int32_t* expert_counts;
+  int32_t* expert_offsets;
+  int32_t* row_map;
+  int32_t* src_token;
+  void* x_perm;
+  float* x_perm_scales;
+  void* y_perm;
+  void* stage_events[MOE_NUM_STAGE_EVENTS];
+} moe_debug;
+
+size_t moe_workspace_size(const moe_layer* L, int64_t T);
+moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, const moe_debug* dbg,
+                       void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+const char* moe_status_str(moe_status s);
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

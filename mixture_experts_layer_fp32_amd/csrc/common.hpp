@@ -1,0 +1,115 @@
+// common.hpp -- shared device helpers and the internal launcher interface of the MoE library.
+// gfx950 (CDNA4) only: 64-lane wavefronts, MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (inputs here are finite).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// SiLU(z) = z / (1 + e^-z)
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// OCP E4M3 ("e4m3fn") encode of an fp32 value already clamped to [-448, 448]: round to
+// nearest, ties to even, from the format definition (1-4-3 bits, bias 7, subnormals
+// m * 2^-9, largest finite 448).  Works on the bit pattern, no table.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;            // |v| bits
+  // |v| < 2^-6 (fp32 exponent < 121): subnormal range, quantum 2^-9.
+  if (a < (121u << 23)) {
+    // value / 2^-9 rounded to nearest even integer in [0, 8]; 2^-9 scaling is exact.
+    float q = __uint_as_float(a) * 512.0f;
+    float r = __builtin_rintf(q);          // round half to even (default rounding mode)
+    uint32_t m = static_cast<uint32_t>(r); // 0..8; 8 == smallest normal (code 0x08)
+    return m ? (sign | m) : 0u;            // a value that rounds to zero encodes as +0
+  }
+  // normal: keep 3 mantissa bits with round-to-nearest-even on the fp32 pattern
+  uint32_t lsb = (a >> 20) & 1u;
+  uint32_t rounded = a + 0x7FFFFu + lsb;   // round at bit 20
+  uint32_t e = (rounded >> 23) - 120u;     // e4m3 exponent field (fp32 bias 127, e4m3 bias 7)
+  uint32_t m = (rounded >> 20) & 7u;
+  uint32_t code = (e << 3) | m;
+  if (code > 0x7Eu) code = 0x7Eu;          // saturate (clamped input can only round to 448)
+  return sign | code;                      // code >= 8 here, never a signed zero
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t s = (c & 0x80u) << 24;
+  uint32_t e = (c >> 3) & 0xFu;
+  uint32_t m = c & 7u;
+  float mag;
+  if (e == 0) {
+    mag = static_cast<float>(m) * (1.0f / 512.0f);
+  } else {
+    mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  }
+  return __uint_as_float(__float_as_uint(mag) | s);
+}
+
+// Wave-wide reductions (64 lanes) with cross-lane shuffles.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------------ launcher interface
+// Every launcher enqueues on `stream` and returns hipGetLastError() of its launches.
+// dtype codes follow moe.h: 0 = fp32, 1 = bf16, 2 = fp8 e4m3.
+
+hipError_t launch_route(const void* x, int x_dt, const float* w_router, const float* bias, int64_t T,
+                        int H, int E, int k, int score, int norm, float* logits, int32_t* ids,
+                        float* gates, float* logits_scratch, hipStream_t stream);
+size_t route_scratch_bytes(int64_t T, int E);
+
+size_t permute_scratch_bytes(int64_t T, int E, int k);
+hipError_t launch_permute(const void* x, int x_dt, const int32_t* ids, int64_t T, int H, int E, int k,
+                          void* x_perm, int perm_dt, float* x_perm_scales, int32_t* row_map,
+                          int32_t* src_token, int32_t* counts, int32_t* offsets, void* scratch,
+                          hipStream_t stream);
+
+size_t grouped_swiglu_scratch_bytes(int64_t rows, int F, int dt);
+// offsets == nullptr means one expert owning rows [0, rows) (the shared expert).
+hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int dt,
+                                 const int32_t* offsets, int64_t rows, int E, int H, int F,
+                                 const void* w1, const float* w1_scales, const void* w2,
+                                 const float* w2_scales, void* y_perm, int out_dt, void* scratch,
+                                 hipStream_t stream, hipEvent_t between = nullptr);
+
+hipError_t launch_combine(const void* y_perm, int y_dt, const int32_t* row_map, const float* gates,
+                          const void* shared_out, int64_t T, int H, int k, void* y, int out_dt,
+                          hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,428 @@
+// gemm.hip -- Compute stage: every local SwiGLU expert in one grouped GEMM launch per matrix.
+//
+// "Scalable Training of Mixture-of-Experts Models with Megatron Core", summary page, "Method",
+// first paragraph: the experts run as one grouped GEMM over the permuted rows, so all local
+// experts execute in a single call.  Per expert e and row p of e:
+//     u = x_perm[p] . W1[e]   (W1 [E, H, 2F], columns [0, F) gate, [F, 2F) up)
+//     h = SiLU(gate) * up     (fused into the first GEMM's epilogue)
+//     y_perm[p] = h . W2[e]   (W2 [E, F, H])
+//
+// Sync-free ragged scheduling: the per-expert row counts live only in device memory
+// (expert_offsets).  The host launches a grid sized by the bound
+//     sum_e ceil(M_e / BM) <= floor((rows + E * (BM - 1)) / BM)
+// and every workgroup rebuilds the per-expert m-tile prefix from the offsets in LDS, maps its
+// (XCD-remapped) linear id to (expert, m-tile, n-tile), and exits if it has none.
+//
+// bf16 kernel (gfx950): 256 threads = 4 waves in a 2 x 2 grid, tile BM x 256 x 64, MFMA
+// v_mfma_f32_32x32x16_bf16.  Both LDS tiles are stored K-contiguous (row-major A as loaded;
+// the N-contiguous weight tile transposed in registers, 8 x 8 bf16 per thread, before the LDS
+// store), with a 16-byte-chunk XOR swizzle so the 16-byte fragment reads and the transposed
+// stores avoid bank conflicts.  Double-buffered LDS, one barrier per K step, next K tile
+// prefetched into registers during the MFMAs.  In SwiGLU mode a tile's 256 columns are 128
+// gate columns and the matching 128 up columns, placed so a lane holds gate and up of the
+// same (row, column) in the same accumulator slot.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBK = 64;   // K per LDS stage (bf16)
+constexpr int kBN = 256;  // N per tile (SwiGLU: 128 gate + 128 up)
+constexpr int kMaxExpertsLds = 520;  // >= E + 1 for E <= 512
+
+// 16-byte chunk index swizzle of row/column n of a K-contiguous LDS tile (8 chunks per row).
+__device__ __forceinline__ int swz(int n) { return (n ^ (n >> 3)) & 7; }
+__device__ __forceinline__ int lds_off(int n, int kc) { return n * (kBK * 2) + ((kc ^ swz(n)) << 4); }
+
+// Per-workgroup tile lookup built from the device-resident expert offsets.
+struct TileMap {
+  int expert, mt, nt;
+  int64_t row0, row_end;  // this tile's first row and the expert's end row
+};
+
+// Returns false if this workgroup has no tile.  `s_pref` is LDS of >= E+1 ints.
+template <int BM>
+__device__ bool map_tile(const int32_t* offsets, int64_t rows, int E, int NT, int* s_pref, TileMap& tm) {
+  const int tid = threadIdx.x;
+  if (offsets == nullptr) {  // one dense expert over rows [0, rows)
+    const int mtiles = static_cast<int>(ceil_div(rows, BM));
+    const int total = mtiles * NT;
+    const int per = (total + 7) / 8;
+    const int w = blockIdx.x;
+    if (w >= 8 * per) return false;
+    const int L = (w % 8) * per + w / 8;
+    if (L >= total) return false;
+    tm.expert = 0;
+    tm.nt = L / mtiles;
+    tm.mt = L % mtiles;
+    tm.row0 = static_cast<int64_t>(tm.mt) * BM;
+    tm.row_end = rows;
+    return true;
+  }
+  // m-tiles per expert, exclusive prefix in s_pref[0..E]
+  for (int e = tid; e < E; e += kThreads) {
+    int c = offsets[e + 1] - offsets[e];
+    s_pref[e + 1] = (c + BM - 1) / BM;
+  }
+  if (tid == 0) s_pref[0] = 0;
+  __syncthreads();
+  if (tid < kWave) {  // one wave scans E <= 512 entries in chunks of 64
+    int carry = 0;
+    for (int base = 1; base <= E; base += kWave) {
+      int i = base + tid;
+      int v = i <= E ? s_pref[i] : 0;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        int u = __shfl_up(v, o, kWave);
+        if (tid >= o) v += u;
+      }
+      if (i <= E) s_pref[i] = v + carry;
+      carry += __shfl(v, kWave - 1, kWave);
+    }
+  }
+  __syncthreads();
+  const int total = s_pref[E] * NT;
+  const int per = (total + 7) / 8;
+  const int w = blockIdx.x;
+  if (w >= 8 * per) return false;
+  const int L = (w % 8) * per + w / 8;  // consecutive L of one XCD share weights / rows
+  if (L >= total) return false;
+  // expert whose tile range [s_pref[e]*NT, s_pref[e+1]*NT) holds L (binary search in LDS)
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (s_pref[mid] * NT <= L) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int me = s_pref[e + 1] - s_pref[e];
+  const int idx = L - s_pref[e] * NT;
+  tm.expert = e;
+  tm.nt = idx / me;  // n-major inside an expert: the m-tiles of one weight tile are adjacent
+  tm.mt = idx % me;
+  tm.row0 = static_cast<int64_t>(offsets[e]) + static_cast<int64_t>(tm.mt) * BM;
+  tm.row_end = offsets[e + 1];
+  return true;
+}
+
+// ------------------------------------------------------------------------------ bf16 path
+// A: [rows, K] bf16 row-major (x_perm or h).  B: per expert [K, ldb] bf16, N-contiguous.
+// SWIGLU: out h [rows, F] (F = ldb / 2), tile n covers gate cols n*128.. and up cols F + n*128..
+// else:   out [rows, ldb], tile n covers cols n*256..
+template <int BM, bool SWIGLU, bool OUT_F32>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const int32_t* __restrict__ offsets,
+    int64_t rows, int E, int K, int ldb, int NT, void* __restrict__ out) {
+  constexpr int FM = BM / 64;        // 32x32 blocks per wave along M (2 waves along M)
+  constexpr int FN = kBN / 64;       // 32x32 blocks per wave along N (2 waves along N) = 4
+  constexpr int A_BYTES = BM * kBK * 2;
+  constexpr int B_BYTES = kBN * kBK * 2;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_LOADS = BM * 8 / kThreads;  // 16-byte loads per thread per K tile
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int s_pref[kMaxExpertsLds];
+
+  TileMap tm;
+  if (!map_tile<BM>(offsets, rows, E, NT, s_pref, tm)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int wm = wave / 2, wn = wave % 2;
+
+  const bf16_t* Bexp = B + static_cast<int64_t>(tm.expert) * K * ldb;
+
+  // ---- global load assignment
+  // A: load p covers tile row (tid + p*256) / 8, chunk (tid % 8)
+  const int a_chunk = tid % 8;
+  const bf16_t* a_src[A_LOADS];
+  bool a_live[A_LOADS];
+#pragma unroll
+  for (int p = 0; p < A_LOADS; ++p) {
+    int r = (tid + p * kThreads) / 8;
+    int64_t grow = tm.row0 + r;
+    a_live[p] = grow < tm.row_end;
+    a_src[p] = A + (a_live[p] ? grow : 0) * K + a_chunk * 8;
+  }
+  // B: thread owns an 8 (k) x 8 (n) block: n-block nb = tid % 32, k-block kb = tid / 32
+  const int nb = tid % 32, kb = tid / 32;
+  int64_t b_col;
+  if (SWIGLU) {
+    const int F = ldb / 2;
+    int c = nb * 8;  // local col 0..255
+    b_col = (c < 128) ? static_cast<int64_t>(tm.nt) * 128 + c : F + static_cast<int64_t>(tm.nt) * 128 + (c - 128);
+  } else {
+    b_col = static_cast<int64_t>(tm.nt) * kBN + nb * 8;
+  }
+  const bool b_live = b_col < ldb;  // ldb % 8 == 0: an 8-column group is wholly in or out
+  const bf16_t* b_src = Bexp + static_cast<int64_t>(kb * 8) * ldb + (b_live ? b_col : 0);
+
+  uint4 a_reg[A_LOADS];
+  uint4 b_reg[8];
+
+  auto load_global = [&](int kt) {
+    const int64_t koff = static_cast<int64_t>(kt) * kBK;
+#pragma unroll
+    for (int p = 0; p < A_LOADS; ++p)
+      a_reg[p] = a_live[p] ? *reinterpret_cast<const uint4*>(a_src[p] + koff) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      b_reg[r] = b_live ? *reinterpret_cast<const uint4*>(b_src + (koff + r) * ldb) : make_uint4(0, 0, 0, 0);
+  };
+
+  auto store_lds = [&](int stage) {
+    char* sa = smem + stage * STAGE;
+    char* sb = sa + A_BYTES;
+#pragma unroll
+    for (int p = 0; p < A_LOADS; ++p) {
+      int r = (tid + p * kThreads) / 8;
+      *reinterpret_cast<uint4*>(sa + lds_off(r, a_chunk)) = a_reg[p];
+    }
+    // transpose the 8x8 block: column c gets k-pairs (2q, 2q+1) in dword q
+    uint32_t in[8][4];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      in[r][0] = b_reg[r].x; in[r][1] = b_reg[r].y; in[r][2] = b_reg[r].z; in[r][3] = b_reg[r].w;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t lo = in[2 * q][c / 2], hi = in[2 * q + 1][c / 2];
+        o[q] = (c % 2 == 0) ? ((lo & 0xFFFFu) | (hi << 16)) : ((lo >> 16) | (hi & 0xFFFF0000u));
+      }
+      *reinterpret_cast<uint4*>(sb + lds_off(nb * 8 + c, kb)) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // fragment rows / columns of this lane inside the tile
+  int a_row[FM], b_colt[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) a_row[i] = wm * (BM / 2) + i * 32 + lane % 32;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    if (SWIGLU)
+      b_colt[j] = (j < FN / 2) ? wn * 64 + j * 32 + lane % 32 : 128 + wn * 64 + (j - FN / 2) * 32 + lane % 32;
+    else
+      b_colt[j] = wn * 128 + j * 32 + lane % 32;
+  }
+  const int khalf = lane / 32;
+
+  const int nk = K / kBK;
+  load_global(0);
+  store_lds(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_global(kt + 1);
+    const char* sa = smem + cur * STAGE;
+    const char* sb = sa + A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      bf16x8_t af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + lds_off(a_row[i], ks * 2 + khalf));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + lds_off(b_colt[j], ks * 2 + khalf));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_lds(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue.  32x32 accumulator layout: slot r of lane l is
+  //      row (r / 4) * 8 + (l / 32) * 4 + (r % 4), column l % 32.
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row_t = wm * (BM / 2) + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
+      const int64_t grow = tm.row0 + row_t;
+      if (grow >= tm.row_end) continue;
+      if (SWIGLU) {
+        const int F = ldb / 2;
+#pragma unroll
+        for (int j = 0; j < FN / 2; ++j) {
+          const float g = acc[i][j][r], u = acc[i][j + FN / 2][r];
+          const float h = silu(g) * u;
+          const int64_t col = static_cast<int64_t>(tm.nt) * 128 + wn * 64 + j * 32 + lane % 32;
+          if (OUT_F32)
+            static_cast<float*>(out)[grow * F + col] = h;
+          else
+            static_cast<bf16_t*>(out)[grow * F + col] = f32_to_bf16(h);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t col = static_cast<int64_t>(tm.nt) * kBN + wn * 128 + j * 32 + lane % 32;
+          if (col >= ldb) continue;
+          if (OUT_F32)
+            static_cast<float*>(out)[grow * ldb + col] = acc[i][j][r];
+          else
+            static_cast<bf16_t*>(out)[grow * ldb + col] = f32_to_bf16(acc[i][j][r]);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------ fp32 path
+// v_mfma_f32_32x32x2_f32: lane l holds A[l % 32][k = l / 32] and B[k = l / 32][l % 32].
+// Tile 64 x 64 (SwiGLU: 32 gate + 32 matching up columns), K step 16, 4 waves in 2 x 2.
+constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(const float* __restrict__ A,
+                                                           const float* __restrict__ B,
+                                                           const int32_t* __restrict__ offsets,
+                                                           int64_t rows, int E, int K, int ldb, int NT,
+                                                           float* __restrict__ out) {
+  __shared__ float sa[kF32BM][kF32BK + 1];
+  __shared__ float sb[kF32BK][kF32BN + 4];
+  __shared__ int s_pref[kMaxExpertsLds];
+  TileMap tm;
+  if (!map_tile<kF32BM>(offsets, rows, E, NT, s_pref, tm)) return;
+
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wm = wave / 2, wn = wave % 2;
+  const float* Bexp = B + static_cast<int64_t>(tm.expert) * K * ldb;
+  const int F = ldb / 2;
+
+  f32x16_t acc = {};
+  for (int k0 = 0; k0 < K; k0 += kF32BK) {
+    for (int i = tid; i < kF32BM * kF32BK; i += kThreads) {
+      int r = i / kF32BK, kk = i % kF32BK;
+      int64_t grow = tm.row0 + r;
+      sa[r][kk] = grow < tm.row_end ? A[grow * K + k0 + kk] : 0.0f;
+    }
+    for (int i = tid; i < kF32BK * kF32BN; i += kThreads) {
+      int kk = i / kF32BN, c = i % kF32BN;
+      int64_t col;
+      if (SWIGLU)
+        col = (c < 32) ? static_cast<int64_t>(tm.nt) * 32 + c : F + static_cast<int64_t>(tm.nt) * 32 + (c - 32);
+      else
+        col = static_cast<int64_t>(tm.nt) * kF32BN + c;
+      sb[kk][c] = col < ldb ? Bexp[static_cast<int64_t>(k0 + kk) * ldb + col] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kF32BK; ks += 2) {
+      float a = sa[wm * 32 + lane % 32][ks + lane / 32];
+      float b = sb[ks + lane / 32][wn * 32 + lane % 32];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // SwiGLU: waves wn = 0 (gate) and wn = 1 (up) hold matching columns; exchange through LDS.
+  if (SWIGLU) {
+    __shared__ float s_up[2][16][kWave];
+    if (wn == 1)
+      for (int r = 0; r < 16; ++r) s_up[wm][r][lane] = acc[r];
+    __syncthreads();
+    if (wn == 0) {
+      for (int r = 0; r < 16; ++r) {
+        const int64_t grow = tm.row0 + wm * 32 + (r / 4) * 8 + (lane / 32) * 4 + (r % 4);
+        if (grow >= tm.row_end) continue;
+        const float h = silu(acc[r]) * s_up[wm][r][lane];
+        out[grow * F + static_cast<int64_t>(tm.nt) * 32 + lane % 32] = h;
+      }
+    }
+  } else {
+    for (int r = 0; r < 16; ++r) {
+      const int64_t grow = tm.row0 + wm * 32 + (r / 4) * 8 + (lane / 32) * 4 + (r % 4);
+      const int64_t col = static_cast<int64_t>(tm.nt) * kF32BN + wn * 32 + lane % 32;
+      if (grow >= tm.row_end || col >= ldb) continue;
+      out[grow * ldb + col] = acc[r];
+    }
+  }
+}
+
+template <int BM>
+int64_t max_tiles(int64_t rows, int E, bool dense) {
+  return dense ? ceil_div(rows, BM) : (rows + static_cast<int64_t>(E) * (BM - 1)) / BM;
+}
+
+unsigned grid_for(int64_t mtiles, int NT) {
+  int64_t g = mtiles * NT;
+  return static_cast<unsigned>(ceil_div(g, 8) * 8);
+}
+
+template <int BM, bool SWIGLU, bool OUT_F32>
+hipError_t launch_bf16(const bf16_t* A, const bf16_t* B, const int32_t* offsets, int64_t rows, int E,
+                       int K, int ldb, int NT, void* out, hipStream_t stream) {
+  constexpr int smem = 2 * (BM * kBK * 2 + kBN * kBK * 2);
+  auto kern = gemm_bf16_kernel<BM, SWIGLU, OUT_F32>;
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  if (err != hipSuccess) return err;
+  const unsigned grid = grid_for(max_tiles<BM>(rows, E, offsets == nullptr), NT);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), smem, stream, A, B, offsets, rows, E, K, ldb, NT,
+                     out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t grouped_swiglu_scratch_bytes(int64_t rows, int F, int dt) {
+  if (dt == 0) return static_cast<size_t>(rows) * F * 4;
+  if (dt == 1) return static_cast<size_t>(rows) * F * 2;
+  // fp8: codes + 1x128 scales
+  size_t a = (static_cast<size_t>(rows) * F + 255) & ~static_cast<size_t>(255);
+  return a + static_cast<size_t>(rows) * (F / 128) * 4;
+}
+
+hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int dt,
+                                 const int32_t* offsets, int64_t rows, int E, int H, int F,
+                                 const void* w1, const float* w1_scales, const void* w2,
+                                 const float* w2_scales, void* y_perm, int out_dt, void* scratch,
+                                 hipStream_t stream, hipEvent_t between) {
+  (void)x_scales; (void)w1_scales; (void)w2_scales;
+  if (dt == 0) {
+    float* h = static_cast<float*>(scratch);
+    const int nt1 = F / 32, nt2 = static_cast<int>(ceil_div(H, kF32BN));
+    const unsigned g1 = grid_for(max_tiles<kF32BM>(rows, E, offsets == nullptr), nt1);
+    hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(g1), dim3(kThreads), 0, stream,
+                       static_cast<const float*>(x_perm), static_cast<const float*>(w1), offsets, rows, E,
+                       H, 2 * F, nt1, h);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (between && (err = hipEventRecord(between, stream)) != hipSuccess) return err;
+    const unsigned g2 = grid_for(max_tiles<kF32BM>(rows, E, offsets == nullptr), nt2);
+    hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(g2), dim3(kThreads), 0, stream, h,
+                       static_cast<const float*>(w2), offsets, rows, E, F, H, nt2,
+                       static_cast<float*>(y_perm));
+    return hipGetLastError();
+  }
+  if (dt == 1) {
+    bf16_t* h = static_cast<bf16_t*>(scratch);
+    hipError_t err = launch_bf16<128, true, false>(static_cast<const bf16_t*>(x_perm),
+                                                   static_cast<const bf16_t*>(w1), offsets, rows, E, H,
+                                                   2 * F, F / 128, h, stream);
+    if (err != hipSuccess) return err;
+    if (between && (err = hipEventRecord(between, stream)) != hipSuccess) return err;
+    if (out_dt == 0)
+      return launch_bf16<128, false, true>(h, static_cast<const bf16_t*>(w2), offsets, rows, E, F, H,
+                                           static_cast<int>(ceil_div(H, kBN)), y_perm, stream);
+    return launch_bf16<128, false, false>(h, static_cast<const bf16_t*>(w2), offsets, rows, E, F, H,
+                                          static_cast<int>(ceil_div(H, kBN)), y_perm, stream);
+  }
+  return hipErrorNotSupported;
+}
+
+}  // namespace moe

@@ -1,0 +1,223 @@
+// permute.hip -- Dispatch stage: expert histogram, prefix sum and stable scatter.
+//
+// The dispatcher permutes tokens so that rows routed to the same expert are contiguous,
+// which the grouped GEMM needs ("Scalable Training of Mixture-of-Experts Models with
+// Megatron Core", summary page, "Method", first paragraph).  Rows of one expert follow
+// increasing token index, so the permutation is a pure function of the expert ids.
+//
+// Three kernels, no host round trip:
+//  1. perm_count: per block of 256 tokens, an LDS bitmap per expert (one bit per token,
+//     set with 64-bit LDS atomic OR, which is order-independent).  A (t, j) pair's rank
+//     inside its expert and block is the popcount of the bits below t; the block's count
+//     for expert e is the popcount of e's bitmap.
+//  2. perm_scan: one workgroup scans the [E][B] count table in expert-major order, giving
+//     each (expert, block) its first permuted row, expert_offsets and expert_counts.
+//  3. perm_scatter: one wavefront per token resolves its k rows, writes row_map/src_token,
+//     reads the token's row once (16 B per lane) and writes it to its k permuted rows,
+//     optionally quantising bf16 -> e4m3 in 1x128 blocks on the way.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kBT = 256;           // tokens per count block (= threads)
+constexpr int kScanThreads = 1024;
+constexpr int kMaxE = 512;
+
+__global__ __launch_bounds__(kBT) void perm_count_kernel(const int32_t* __restrict__ ids, int64_t T,
+                                                         int E, int k, int nblk,
+                                                         int32_t* __restrict__ blk_counts,
+                                                         int32_t* __restrict__ local_rank) {
+  __shared__ unsigned long long bm[kMaxE][kBT / 64];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * (kBT / 64); i += kBT) bm[i / (kBT / 64)][i % (kBT / 64)] = 0ull;
+  __syncthreads();
+  const int b = blockIdx.x;
+  const int64_t t = static_cast<int64_t>(b) * kBT + tid;
+  const int w = tid / 64;
+  const unsigned long long bit = 1ull << (tid % 64);
+  if (t < T) {
+    for (int j = 0; j < k; ++j) atomicOr(&bm[ids[t * k + j]][w], bit);
+  }
+  __syncthreads();
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      int e = ids[t * k + j];
+      int r = __popcll(bm[e][w] & (bit - 1ull));
+      for (int ww = 0; ww < w; ++ww) r += __popcll(bm[e][ww]);
+      local_rank[t * k + j] = r;
+    }
+  }
+  for (int e = tid; e < E; e += kBT) {
+    int c = 0;
+#pragma unroll
+    for (int ww = 0; ww < kBT / 64; ++ww) c += __popcll(bm[e][ww]);
+    blk_counts[static_cast<int64_t>(e) * nblk + b] = c;
+  }
+}
+
+// Exclusive scan of blk_counts (length E * nblk, expert-major) in place -> first row of
+// each (expert, block); also expert_offsets [E+1] and (optionally) expert_counts [E].
+__global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(int32_t* __restrict__ base, int E,
+                                                                 int nblk, int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ counts) {
+  __shared__ int32_t part[kScanThreads];
+  const int tid = threadIdx.x;
+  const int64_t n = static_cast<int64_t>(E) * nblk;
+  const int64_t per = ceil_div(n, kScanThreads);
+  const int64_t lo = tid * per;
+  const int64_t hi = lo + per < n ? lo + per : n;
+  int32_t s = 0;
+  for (int64_t i = lo; i < hi; ++i) s += base[i];
+  part[tid] = s;
+  __syncthreads();
+  // Hillis-Steele inclusive scan of the 1024 partial sums
+  for (int o = 1; o < kScanThreads; o <<= 1) {
+    int32_t v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = part[tid] - s;  // exclusive prefix of this thread's chunk
+  for (int64_t i = lo; i < hi; ++i) {
+    int32_t c = base[i];
+    base[i] = run;
+    run += c;
+  }
+  __syncthreads();
+  const int32_t total = part[kScanThreads - 1];
+  for (int e = tid; e <= E; e += kScanThreads) {
+    int32_t o = e < E ? base[static_cast<int64_t>(e) * nblk] : total;
+    offsets[e] = o;
+    if (counts && e < E) {
+      int32_t o1 = e + 1 < E ? base[static_cast<int64_t>(e + 1) * nblk] : total;
+      counts[e] = o1 - o;
+    }
+  }
+}
+
+constexpr int kScatterThreads = 256;
+constexpr int kTokPerBlock = kScatterThreads / kWave;
+
+// Resolve the k permuted rows of token t in lanes 0..k-1 (others: 0) and publish the maps.
+__device__ __forceinline__ int resolve_row(const int32_t* ids, const int32_t* base,
+                                           const int32_t* local_rank, int64_t t, int k, int nblk,
+                                           int lane, int32_t* row_map, int32_t* src_token) {
+  int row = 0;
+  if (lane < k) {
+    int e = ids[t * k + lane];
+    row = base[static_cast<int64_t>(e) * nblk + t / kBT] + local_rank[t * k + lane];
+    row_map[t * k + lane] = row;
+    src_token[row] = static_cast<int32_t>(t);
+  }
+  return row;
+}
+
+// Bit copy: VEC = 16 bytes per lane.
+__global__ __launch_bounds__(kScatterThreads) void perm_scatter_copy_kernel(
+    const uint4* __restrict__ x, const int32_t* __restrict__ ids, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ local_rank, int64_t T, int row_vecs, int k, int nblk,
+    uint4* __restrict__ x_perm, int32_t* __restrict__ row_map, int32_t* __restrict__ src_token) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + threadIdx.x / kWave;
+  if (t >= T) return;
+  int row = resolve_row(ids, base, local_rank, t, k, nblk, lane, row_map, src_token);
+  if (!x_perm) return;
+  const uint4* src = x + t * row_vecs;
+  for (int c = lane; c < row_vecs; c += kWave) {
+    uint4 v = src[c];
+    for (int j = 0; j < k; ++j) {
+      int r = __shfl(row, j, kWave);
+      x_perm[static_cast<int64_t>(r) * row_vecs + c] = v;
+    }
+  }
+}
+
+// bf16 -> e4m3 with one fp32 scale per 1x128 block (16 lanes x 8 values).
+__global__ __launch_bounds__(kScatterThreads) void perm_scatter_fp8_kernel(
+    const uint4* __restrict__ x, const int32_t* __restrict__ ids, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ local_rank, int64_t T, int H, int k, int nblk,
+    uint2* __restrict__ x_perm, float* __restrict__ scales, int32_t* __restrict__ row_map,
+    int32_t* __restrict__ src_token) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + threadIdx.x / kWave;
+  if (t >= T) return;
+  int row = resolve_row(ids, base, local_rank, t, k, nblk, lane, row_map, src_token);
+  if (!x_perm) return;
+  const int row_vecs = H / 8;
+  const int nsb = H / 128;
+  const uint4* src = x + t * row_vecs;
+  for (int c0 = 0; c0 < row_vecs; c0 += kWave) {  // H % 128 == 0: whole 16-lane groups
+    const int c = c0 + lane;
+    const bool live = c < row_vecs;
+    float f[8];
+    float amax = 0.0f;
+    uint4 v = live ? src[c] : make_uint4(0, 0, 0, 0);
+    uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(wv[i] << 16);
+      f[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
+      amax = fmaxf(amax, fmaxf(fabsf(f[2 * i]), fabsf(f[2 * i + 1])));
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;  // correctly rounded fp32 division
+    uint32_t q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float r = f[i] / s;
+      r = fminf(fmaxf(r, -448.0f), 448.0f);
+      q[i] = f32_to_e4m3(r);
+    }
+    uint2 packed = make_uint2(q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
+                              q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24));
+    for (int j = 0; j < k; ++j) {
+      int r = __shfl(row, j, kWave);
+      if (live) {
+        x_perm[static_cast<int64_t>(r) * row_vecs + c] = packed;
+        if ((lane & 15) == 0) scales[static_cast<int64_t>(r) * nsb + c / 16] = s;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+size_t permute_scratch_bytes(int64_t T, int E, int k) {
+  const int64_t nblk = ceil_div(T, kBT);
+  size_t a = static_cast<size_t>(E) * nblk * sizeof(int32_t);
+  a = (a + 255) & ~static_cast<size_t>(255);
+  return a + static_cast<size_t>(T) * k * sizeof(int32_t);
+}
+
+hipError_t launch_permute(const void* x, int x_dt, const int32_t* ids, int64_t T, int H, int E, int k,
+                          void* x_perm, int perm_dt, float* x_perm_scales, int32_t* row_map,
+                          int32_t* src_token, int32_t* counts, int32_t* offsets, void* scratch,
+                          hipStream_t stream) {
+  const int nblk = static_cast<int>(ceil_div(T, kBT));
+  int32_t* blk = static_cast<int32_t*>(scratch);
+  size_t a = static_cast<size_t>(E) * nblk * sizeof(int32_t);
+  a = (a + 255) & ~static_cast<size_t>(255);
+  int32_t* local_rank = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + a);
+
+  hipLaunchKernelGGL(perm_count_kernel, dim3(nblk), dim3(kBT), 0, stream, ids, T, E, k, nblk, blk,
+                     local_rank);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, blk, E, nblk, offsets,
+                     counts);
+  dim3 grid(static_cast<unsigned>(ceil_div(T, kTokPerBlock)));
+  if (perm_dt == 2) {
+    hipLaunchKernelGGL(perm_scatter_fp8_kernel, grid, dim3(kScatterThreads), 0, stream,
+                       static_cast<const uint4*>(x), ids, blk, local_rank, T, H, k, nblk,
+                       static_cast<uint2*>(x_perm), x_perm_scales, row_map, src_token);
+  } else {
+    const int elt = (x_dt == 0) ? 4 : 2;
+    const int row_vecs = H * elt / 16;
+    hipLaunchKernelGGL(perm_scatter_copy_kernel, grid, dim3(kScatterThreads), 0, stream,
+                       static_cast<const uint4*>(x), ids, blk, local_rank, T, row_vecs, k, nblk,
+                       static_cast<uint4*>(x_perm), row_map, src_token);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

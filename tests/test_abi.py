@@ -1,0 +1,141 @@
+"""The C ABI: the library loads, exports every function include/moe.h declares, and rejects bad
+arguments on the host before launching anything (these calls never reach the GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_fp32_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+INVALID, UNSUP, WS = _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_UNSUPPORTED, _lib.MOE_ERR_WORKSPACE
+P = ctypes.c_void_p(16 * 1024)  # a fake, 16-byte aligned "device" address: never dereferenced here
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    names = declared_functions()
+    assert len(names) == 11
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.moe_abi_version() == 1
+    for s in range(5):
+        assert L.moe_status_str(s).startswith(b"MOE_")
+
+
+def _route(L, **over):
+    a = dict(x=P, x_dt=1, w=P, bias=None, T=8, H=64, E=8, k=2, score=0, norm=0, logits=P, ids=P,
+             gates=P, ws=None, wsb=0)
+    a.update(over)
+    return L.moe_route(a["x"], a["x_dt"], a["w"], a["bias"], a["T"], a["H"], a["E"], a["k"], a["score"],
+                       a["norm"], a["logits"], a["ids"], a["gates"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(x=None), INVALID), (dict(ids=None), INVALID), (dict(k=0), INVALID), (dict(k=9), INVALID),
+    (dict(E=513, k=2), INVALID), (dict(E=32, k=17), INVALID), (dict(H=12), INVALID), (dict(T=-1), INVALID),
+    (dict(x_dt=2), INVALID), (dict(score=7), INVALID), (dict(logits=None), WS),
+    (dict(T=2 ** 30, k=2), INVALID)])
+def test_route_rejects(over, code):
+    assert _route(_lib.lib(), **over) == code
+
+
+def test_route_with_no_tokens_is_a_noop():
+    assert _route(_lib.lib(), T=0) == _lib.MOE_OK
+
+
+def test_workspace_sizes():
+    L = _lib.lib()
+    assert L.moe_route_workspace_size(100, 8, 1) == 0
+    assert L.moe_route_workspace_size(100, 8, 0) >= 100 * 8 * 4
+    assert L.moe_permute_workspace_size(1000, 64, 4) >= 1000 * 4 * 4
+    assert L.moe_grouped_swiglu_workspace_size(512, 256, _lib.MOE_BF16) >= 512 * 256 * 2
+    assert L.moe_grouped_swiglu_workspace_size(512, 256, _lib.MOE_F32) >= 512 * 256 * 4
+    assert L.moe_grouped_swiglu_workspace_size(512, 256, _lib.MOE_FP8_E4M3) >= 512 * 256 + 512 * 2 * 4
+
+
+def _permute(L, **over):
+    a = dict(x=P, x_dt=1, ids=P, T=64, H=128, E=8, k=2, xp=P, pdt=1, sc=None, rm=P, src=P, cnt=None,
+             off=P, ws=P, wsb=1 << 20)
+    a.update(over)
+    return L.moe_permute(a["x"], a["x_dt"], a["ids"], a["T"], a["H"], a["E"], a["k"], a["xp"], a["pdt"],
+                         a["sc"], a["rm"], a["src"], a["cnt"], a["off"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(ids=None), INVALID), (dict(off=None), INVALID), (dict(pdt=0), INVALID),
+    (dict(pdt=2), INVALID), (dict(pdt=2, sc=P, H=64), INVALID), (dict(x_dt=0, pdt=2, sc=P), INVALID),
+    (dict(ws=None), WS), (dict(wsb=16), WS), (dict(x=ctypes.c_void_p(16 * 1024 + 4)), INVALID),
+    (dict(T=0), UNSUP)])
+def test_permute_rejects(over, code):
+    assert _permute(_lib.lib(), **over) == code
+
+
+def _gemm(L, **over):
+    a = dict(xp=P, sc=None, dt=1, off=P, rows=128, E=4, H=256, F=256, w1=P, w1s=None, w2=P, w2s=None,
+             y=P, odt=1, ws=P, wsb=1 << 30)
+    a.update(over)
+    return L.moe_grouped_swiglu(a["xp"], a["sc"], a["dt"], a["off"], a["rows"], a["E"], a["H"], a["F"],
+                                a["w1"], a["w1s"], a["w2"], a["w2s"], a["y"], a["odt"], a["ws"], a["wsb"],
+                                None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(off=None), INVALID), (dict(F=192), INVALID), (dict(H=96), INVALID), (dict(dt=0, odt=1), INVALID),
+    (dict(dt=2), INVALID), (dict(dt=2, sc=P, w1s=P, w2s=P, H=192), INVALID), (dict(E=0), INVALID),
+    (dict(E=600), INVALID), (dict(odt=2), INVALID), (dict(wsb=1024), WS), (dict(rows=0), _lib.MOE_OK)])
+def test_grouped_swiglu_rejects(over, code):
+    assert _gemm(_lib.lib(), **over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(k=0), INVALID), (dict(H=12), INVALID), (dict(y=None), INVALID), (dict(ydt=2), INVALID),
+    (dict(shared=ctypes.c_void_p(16 * 1024 + 8)), INVALID), (dict(T=0), _lib.MOE_OK)])
+def test_combine_rejects(over, code):
+    a = dict(yp=P, ydt=1, rm=P, g=P, shared=None, T=16, H=64, k=2, y=P, odt=1)
+    a.update(over)
+    L = _lib.lib()
+    assert L.moe_unpermute_combine(a["yp"], a["ydt"], a["rm"], a["g"], a["shared"], a["T"], a["H"], a["k"],
+                                   a["y"], a["odt"], None) == code
+
+
+def _layer(**over):
+    f = dict(H=256, E=8, k=2, F=256, Fs=0, x_dt=1, w_dt=1, out_dt=1, score=0, norm_topk=0, w_router=16384,
+             bias=None, w1=16384, w2=16384, ws1=None, ws2=None, w1_scales=None, w2_scales=None,
+             ws1_scales=None, ws2_scales=None)
+    f.update(over)
+    return _lib.MoeLayerC(**f)
+
+
+@pytest.mark.parametrize("over", [dict(k=9), dict(w_dt=0), dict(x_dt=2), dict(F=100), dict(Fs=256),
+                                  dict(w_dt=2), dict(w1=None), dict(score=3), dict(Fs=-1)])
+def test_forward_rejects_bad_layers(over):
+    L = _lib.lib()
+    lay = _layer(**over)
+    assert L.moe_workspace_size(ctypes.byref(lay), 64) == 0
+    assert L.moe_forward(ctypes.byref(lay), P, 64, P, None, P, 1 << 30, None) == INVALID
+
+
+def test_forward_workspace_checks():
+    L = _lib.lib()
+    lay = _layer()
+    need = L.moe_workspace_size(ctypes.byref(lay), 64)
+    assert need > 64 * 256 * 2 * 2
+    assert L.moe_forward(ctypes.byref(lay), P, 64, P, None, P, need - 1, None) == WS
+    assert L.moe_forward(ctypes.byref(lay), P, 64, P, None, None, need, None) == WS
+    assert L.moe_forward(ctypes.byref(lay), P, 0, P, None, P, need, None) == _lib.MOE_OK
+    assert L.moe_forward(None, P, 64, P, None, P, need, None) == INVALID
