@@ -74,11 +74,12 @@ typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
  *            ties to the lower expert index.
  *   topk_gates [T, k] fp32 out: softmax over all E of the logits, or sigmoid of the
  *            logit, taken at the selected experts; divided by their sum if norm_topk != 0.
- *   workspace device scratch of at least moe_route_workspace_size(T, E, logits != NULL) bytes
- *            (holds the logits when the caller does not ask for them; may be NULL otherwise).
+ *   workspace device scratch of at least moe_route_workspace_size(T, H, E, logits != NULL)
+ *            bytes (the router weight split into bf16 parts, and the logits when the caller
+ *            does not ask for them).
  * H must be a multiple of 8.
  * ------------------------------------------------------------------------------------- */
-size_t moe_route_workspace_size(int64_t T, int32_t E, int32_t logits_given);
+size_t moe_route_workspace_size(int64_t T, int32_t H, int32_t E, int32_t logits_given);
 moe_status moe_route(const void* x, moe_dtype x_dt, const float* w_router, const float* bias,
                      int64_t T, int32_t H, int32_t E, int32_t k, moe_score score, int32_t norm_topk,
                      float* logits, int32_t* topk_ids, float* topk_gates, void* workspace,

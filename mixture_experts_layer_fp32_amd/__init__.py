@@ -58,8 +58,8 @@ def route(x, w_router, k, score="softmax", norm=False, bias=None, return_logits=
     gates = torch.empty(T, k, dtype=torch.float32, device=dev)
     logits = torch.empty(T, E, dtype=torch.float32, device=dev) if return_logits else None
     L = _lib.lib()
-    wsb = L.moe_route_workspace_size(T, E, int(return_logits))
-    ws = _ws(wsb, dev) if wsb else None
+    wsb = L.moe_route_workspace_size(T, H, E, int(return_logits))
+    ws = _ws(wsb, dev)
     _lib.check("moe_route", L.moe_route(_ptr(x), _DT[x.dtype], _ptr(w_router), _ptr(bias), T, H, E, k,
                                         _SCORE[score], int(norm), _ptr(logits), _ptr(ids), _ptr(gates),
                                         _ptr(ws), wsb, _stream()))

@@ -18,7 +18,7 @@ MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 SIGNATURES = {
     "moe_status_str": ([_i32], _c.c_char_p),
     "moe_abi_version": ([], _i32),
-    "moe_route_workspace_size": ([_i64, _i32, _i32], _sz),
+    "moe_route_workspace_size": ([_i64, _i32, _i32, _i32], _sz),
     "moe_route": ([_vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "moe_permute_workspace_size": ([_i64, _i32, _i32], _sz),
     "moe_permute": ([_vp, _i32, _vp, _i64, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,

@@ -69,9 +69,9 @@ const char* moe_status_str(moe_status s) {
 
 int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
 
-size_t moe_route_workspace_size(int64_t T, int32_t E, int32_t logits_given) {
-  if (T < 0 || E < 1) return 0;
-  return logits_given ? 0 : align_up(moe::route_scratch_bytes(T, E));
+size_t moe_route_workspace_size(int64_t T, int32_t H, int32_t E, int32_t logits_given) {
+  if (T < 0 || E < 1 || H < 1) return 0;
+  return align_up(moe::route_scratch_bytes(T, H, E, logits_given != 0));
 }
 
 moe_status moe_route(const void* x, moe_dtype x_dt, const float* w_router, const float* bias, int64_t T,
@@ -82,11 +82,11 @@ moe_status moe_route(const void* x, moe_dtype x_dt, const float* w_router, const
   if (st != MOE_OK) return st;
   if (!act_dtype_ok(x_dt) || (score != MOE_SOFTMAX && score != MOE_SIGMOID)) return MOE_ERR_INVALID_ARG;
   if (!x || !w_router || !topk_ids || !topk_gates) return MOE_ERR_INVALID_ARG;
-  const size_t need = moe_route_workspace_size(T, E, logits != nullptr);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+  const size_t need = moe_route_workspace_size(T, H, E, logits != nullptr);
+  if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
   if (T == 0) return MOE_OK;
   return from_hip(moe::launch_route(x, x_dt, w_router, bias, T, H, E, k, score, norm_topk ? 1 : 0,
-                                    logits, topk_ids, topk_gates, static_cast<float*>(workspace),
+                                    logits, topk_ids, topk_gates, workspace,
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -162,7 +162,7 @@ moe_status moe_unpermute_combine(const void* y_perm, moe_dtype y_dt, const int32
 namespace {
 
 struct ForwardPlan {
-  void *logits, *ids, *gates, *counts, *offsets, *row_map, *src, *perm_ws, *x_perm, *x_scales, *gemm_ws,
+  void *logits, *route_ws, *ids, *gates, *counts, *offsets, *row_map, *src, *perm_ws, *x_perm, *x_scales, *gemm_ws,
       *y_perm, *sh_x, *sh_scales, *sh_ws, *sh_out;
   size_t bytes;
 };
@@ -199,6 +199,7 @@ ForwardPlan plan(const moe_layer* L, int64_t T, void* ws, const moe_debug* dbg) 
   ForwardPlan p{};
   auto pick = [&](void* user, size_t n) { void* w = c.take(n); return user ? user : w; };
   p.logits = pick(dbg ? dbg->logits : nullptr, T * L->E * 4);
+  p.route_ws = c.take(moe::route_scratch_bytes(T, L->H, L->E, true));
   p.ids = pick(dbg ? dbg->topk_ids : nullptr, R * 4);
   p.gates = pick(dbg ? dbg->topk_gates : nullptr, R * 4);
   p.counts = pick(dbg ? dbg->expert_counts : nullptr, L->E * 4);
@@ -248,7 +249,7 @@ moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, co
   if (e != hipSuccess) return from_hip(e);
   e = moe::launch_route(x, L->x_dt, L->w_router, L->bias, T, L->H, L->E, L->k, L->score,
                                    L->norm_topk ? 1 : 0, static_cast<float*>(p.logits),
-                                   static_cast<int32_t*>(p.ids), static_cast<float*>(p.gates), nullptr, s);
+                                   static_cast<int32_t*>(p.ids), static_cast<float*>(p.gates), p.route_ws, s);
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return from_hip(e);
   e = moe::launch_permute(x, L->x_dt, static_cast<int32_t*>(p.ids), T, L->H, L->E, L->k, p.x_perm,

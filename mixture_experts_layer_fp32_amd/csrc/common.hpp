@@ -14,6 +14,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
@@ -89,10 +90,11 @@ __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a
 // Every launcher enqueues on `stream` and returns hipGetLastError() of its launches.
 // dtype codes follow moe.h: 0 = fp32, 1 = bf16, 2 = fp8 e4m3.
 
+// scratch: logits (when `logits` is null) followed by the split router weight
 hipError_t launch_route(const void* x, int x_dt, const float* w_router, const float* bias, int64_t T,
                         int H, int E, int k, int score, int norm, float* logits, int32_t* ids,
-                        float* gates, float* logits_scratch, hipStream_t stream);
-size_t route_scratch_bytes(int64_t T, int E);
+                        float* gates, void* scratch, hipStream_t stream);
+size_t route_scratch_bytes(int64_t T, int H, int E, bool logits_given);
 
 size_t permute_scratch_bytes(int64_t T, int E, int k);
 hipError_t launch_permute(const void* x, int x_dt, const int32_t* ids, int64_t T, int H, int E, int k,

@@ -109,18 +109,66 @@ __device__ bool map_tile(const int32_t* offsets, int64_t rows, int E, int NT, in
 // A: [rows, K] bf16 row-major (x_perm or h).  B: per expert [K, ldb] bf16, N-contiguous.
 // SWIGLU: out h [rows, F] (F = ldb / 2), tile n covers gate cols n*128.. and up cols F + n*128..
 // else:   out [rows, ldb], tile n covers cols n*256..
+//
+// Tile BM x 256 x 32, 4 waves in a 2 x 2 grid (each wave (BM/2) x 128), a ring of kStages LDS
+// stages.  Both operands go global -> LDS directly (global_load_lds_dwordx4: lane l of an
+// instruction lands at base + 16 l), so no register staging and no VALU work:
+//   A stage: BM rows x 64 B; 16-byte chunk c of row r is stored at c ^ ((r >> 2) & 3).
+//   B stage: 32 k-rows x 512 B, untransposed; chunk c of k-row k is stored at c ^ 4 (k & 3).
+// A fragments (lane l: row l % 32, k 8 (l / 32) .. +8) are one ds_read_b128 each; B fragments
+// are two ds_read_b64_tr_b16 each: within a group of 16 lanes, lane 16g + 4a + b receives
+// 16-bit column b of the 8-byte pieces addressed by lanes 16g + a + 4e (e = 0..3), so source
+// lane s addresses k-row 8 (s / 32) + 4 r + (s % 16) / 4 at column 16 ((s / 16) % 2) + 4 (s % 4)
+// of the fragment and destination lane d collects column d % 32 for 4 consecutive k.
+// Both swizzles spread a wave's 16-byte (A) and 8-byte (B) fragment reads over all banks.
+//
+// Pipeline: loads of tile t are issued kStages - 1 iterations before use; each iteration waits
+// for its own loads of the next tile (s_waitcnt vmcnt), meets the other waves at one barrier,
+// issues the loads of the tile kStages - 1 ahead into the stage freed by the previous tile, and
+// prefetches the next tile's first fragments while the current tile's last MFMAs run.
+// Loads are unconditional: rows past the expert's end re-read its last row and column groups
+// past the matrix edge re-read column 0; those results are never stored.
+constexpr int kBKT = 32;     // K per stage
+constexpr int kStages = 4;   // LDS ring depth
+constexpr int kBRow = kBN * 2;  // bytes per B k-row
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// 16 bytes per lane from global memory straight into LDS at lds_addr + 16 * lane
+// (global_load_lds_dwordx4).  Issued through asm so the compiler does not insert its own
+// conservative vmcnt waits before unrelated LDS reads; completion is tracked explicitly with
+// wait_vmcnt (vmcnt retires loads in issue order, so the compiler's own counts stay safe).
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
+  // an SALU write of M0 needs one wait state before an LDS-DMA load reads it
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt encoding: vmcnt [3:0] + [15:14], expcnt [6:4] (7 = no wait), lgkmcnt [11:8] (15)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <int BM, bool SWIGLU, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const int32_t* __restrict__ offsets,
     int64_t rows, int E, int K, int ldb, int NT, void* __restrict__ out) {
   constexpr int FM = BM / 64;        // 32x32 blocks per wave along M (2 waves along M)
   constexpr int FN = kBN / 64;       // 32x32 blocks per wave along N (2 waves along N) = 4
-  constexpr int A_BYTES = BM * kBK * 2;
-  constexpr int B_BYTES = kBN * kBK * 2;
+  constexpr int A_BYTES = BM * kBKT * 2;
+  constexpr int B_BYTES = kBKT * kBRow;
   constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int A_LOADS = BM * 8 / kThreads;  // 16-byte loads per thread per K tile
+  constexpr int A_ROUNDS = A_BYTES / 1024 / 4;  // 1 KB wave-instructions per wave per stage
+  constexpr int B_ROUNDS = B_BYTES / 1024 / 4;
+  constexpr int LPT = A_ROUNDS + B_ROUNDS;      // loads per thread per stage
 
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
   __shared__ int s_pref[kMaxExpertsLds];
 
   TileMap tm;
@@ -128,74 +176,73 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / 2, wn = wave % 2;
+  lds_void_t* lds = (lds_void_t*)smem;  // address-space cast: generic -> LDS
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
 
-  const bf16_t* Bexp = B + static_cast<int64_t>(tm.expert) * K * ldb;
-
-  // ---- global load assignment
-  // A: load p covers tile row (tid + p*256) / 8, chunk (tid % 8)
-  const int a_chunk = tid % 8;
-  const bf16_t* a_src[A_LOADS];
-  bool a_live[A_LOADS];
+  // ---- global sources of this lane's direct loads
+  // A round p of wave w: tile rows (4p + w) * 16 + lane / 4, stored chunk lane % 4 holding
+  // logical chunk (lane % 4) ^ ((lane >> 4) & 3).
+  const bf16_t* a_src[A_ROUNDS];
 #pragma unroll
-  for (int p = 0; p < A_LOADS; ++p) {
-    int r = (tid + p * kThreads) / 8;
+  for (int p = 0; p < A_ROUNDS; ++p) {
+    int r = (4 * p + wave) * 16 + lane / 4;
     int64_t grow = tm.row0 + r;
-    a_live[p] = grow < tm.row_end;
-    a_src[p] = A + (a_live[p] ? grow : 0) * K + a_chunk * 8;
+    if (grow >= tm.row_end) grow = tm.row_end - 1;
+    a_src[p] = A + grow * K + (((lane % 4) ^ ((lane >> 4) & 3)) * 8);
   }
-  // B: thread owns an 8 (k) x 8 (n) block: n-block nb = tid % 32, k-block kb = tid / 32
-  const int nb = tid % 32, kb = tid / 32;
+  // B round p of wave w: k-row 2 (4p + w) + lane / 32, stored chunk lane % 32 holding logical
+  // chunk (lane % 32) ^ 4 ((2w + lane / 32) & 3).
+  const int b_lchunk = (lane % 32) ^ (4 * ((2 * wave + lane / 32) & 3));
   int64_t b_col;
   if (SWIGLU) {
     const int F = ldb / 2;
-    int c = nb * 8;  // local col 0..255
-    b_col = (c < 128) ? static_cast<int64_t>(tm.nt) * 128 + c : F + static_cast<int64_t>(tm.nt) * 128 + (c - 128);
+    b_col = (b_lchunk < 16) ? static_cast<int64_t>(tm.nt) * 128 + b_lchunk * 8
+                            : F + static_cast<int64_t>(tm.nt) * 128 + (b_lchunk - 16) * 8;
   } else {
-    b_col = static_cast<int64_t>(tm.nt) * kBN + nb * 8;
+    b_col = static_cast<int64_t>(tm.nt) * kBN + b_lchunk * 8;
   }
-  const bool b_live = b_col < ldb;  // ldb % 8 == 0: an 8-column group is wholly in or out
-  const bf16_t* b_src = Bexp + static_cast<int64_t>(kb * 8) * ldb + (b_live ? b_col : 0);
+  if (b_col >= ldb) b_col = 0;  // ldb % 8 == 0: an 8-column group is wholly in or out
+  const bf16_t* b_src = B + static_cast<int64_t>(tm.expert) * K * ldb +
+                        static_cast<int64_t>(2 * wave + lane / 32) * ldb + b_col;
+  const int64_t b_round = static_cast<int64_t>(8) * ldb;  // 8 k-rows per round
 
-  uint4 a_reg[A_LOADS];
-  uint4 b_reg[8];
-
-  auto load_global = [&](int kt) {
-    const int64_t koff = static_cast<int64_t>(kt) * kBK;
+  auto issue_loads = [&](int kt) {
+    const int st = kt % kStages;
+    const uint32_t sbase = lds_base + st * STAGE;
 #pragma unroll
-    for (int p = 0; p < A_LOADS; ++p)
-      a_reg[p] = a_live[p] ? *reinterpret_cast<const uint4*>(a_src[p] + koff) : make_uint4(0, 0, 0, 0);
+    for (int p = 0; p < A_ROUNDS; ++p)
+      lds_dma16(a_src[p] + static_cast<int64_t>(kt) * kBKT, sbase + (4 * p + wave) * 1024);
+    const bf16_t* bs = b_src + static_cast<int64_t>(kt) * kBKT * ldb;
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-      b_reg[r] = b_live ? *reinterpret_cast<const uint4*>(b_src + (koff + r) * ldb) : make_uint4(0, 0, 0, 0);
+    for (int p = 0; p < B_ROUNDS; ++p) lds_dma16(bs + p * b_round, sbase + A_BYTES + (4 * p + wave) * 1024);
   };
 
-  auto store_lds = [&](int stage) {
-    char* sa = smem + stage * STAGE;
-    char* sb = sa + A_BYTES;
+  // ---- fragment addresses (byte offsets inside a stage)
+  uint32_t a_off[FM][2];
 #pragma unroll
-    for (int p = 0; p < A_LOADS; ++p) {
-      int r = (tid + p * kThreads) / 8;
-      *reinterpret_cast<uint4*>(sa + lds_off(r, a_chunk)) = a_reg[p];
-    }
-    // transpose the 8x8 block: column c gets k-pairs (2q, 2q+1) in dword q
-    uint32_t in[8][4];
+  for (int i = 0; i < FM; ++i) {
+    const int r = wm * (BM / 2) + i * 32 + lane % 32;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      in[r][0] = b_reg[r].x; in[r][1] = b_reg[r].y; in[r][2] = b_reg[r].z; in[r][3] = b_reg[r].w;
-    }
+    for (int ks = 0; ks < 2; ++ks) a_off[i][ks] = r * 64 + (((ks * 2 + lane / 32) ^ ((r >> 2) & 3)) << 4);
+  }
+  uint32_t b_off[FN][2];  // [j][r]; add ks * 16 k-rows
+  {
+    const int g = lane / 16, h = lane / 32, a4 = lane % 4, e = (lane % 16) / 4;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      uint32_t o[4];
+    for (int j = 0; j < FN; ++j) {
+      int cb;
+      if (SWIGLU) cb = (j < FN / 2) ? wn * 64 + j * 32 : 128 + wn * 64 + (j - FN / 2) * 32;
+      else cb = wn * 128 + j * 32;
+      const int col = cb + 16 * (g % 2) + 4 * a4;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t lo = in[2 * q][c / 2], hi = in[2 * q + 1][c / 2];
-        o[q] = (c % 2 == 0) ? ((lo & 0xFFFFu) | (hi << 16)) : ((lo >> 16) | (hi & 0xFFFF0000u));
+      for (int r = 0; r < 2; ++r) {
+        const int krow = 8 * h + 4 * r + e;
+        b_off[j][r] = A_BYTES + krow * kBRow + (((col / 8) ^ (4 * e)) << 4) + (col % 8) * 2;
       }
-      *reinterpret_cast<uint4*>(sb + lds_off(nb * 8 + c, kb)) = make_uint4(o[0], o[1], o[2], o[3]);
     }
-  };
+  }
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -205,49 +252,56 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // fragment rows / columns of this lane inside the tile
-  int a_row[FM], b_colt[FN];
+  bf16x8_t af[2][FM], bfr[2][FN];
+  auto read_frags = [&](int kt, int ks, int buf) {
+    const uint32_t sbase = lds_base + (kt % kStages) * STAGE;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) a_row[i] = wm * (BM / 2) + i * 32 + lane % 32;
+    for (int i = 0; i < FM; ++i)
+      af[buf][i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
+          static_cast<uintptr_t>(sbase + a_off[i][ks]));
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    if (SWIGLU)
-      b_colt[j] = (j < FN / 2) ? wn * 64 + j * 32 + lane % 32 : 128 + wn * 64 + (j - FN / 2) * 32 + lane % 32;
-    else
-      b_colt[j] = wn * 128 + j * 32 + lane % 32;
-  }
-  const int khalf = lane / 32;
-
-  const int nk = K / kBK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_global(kt + 1);
-    const char* sa = smem + cur * STAGE;
-    const char* sb = sa + A_BYTES;
+    for (int j = 0; j < FN; ++j) {
+      v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16_t*>(
+          static_cast<uintptr_t>(sbase + b_off[j][0] + ks * 16 * kBRow)));
+      v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16_t*>(
+          static_cast<uintptr_t>(sbase + b_off[j][1] + ks * 16 * kBRow)));
+      typedef short v8i16_t __attribute__((ext_vector_type(8)));
+      v8i16_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      bfr[buf][j] = __builtin_bit_cast(bf16x8_t, both);
+    }
+  };
+  auto mfmas = [&](int buf) {
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8_t af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + lds_off(a_row[i], ks * 2 + khalf));
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + lds_off(b_colt[j], ks * 2 + khalf));
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0);
+  };
+
+  const int nk = K / kBKT;
+  // prologue: tiles 0 .. kStages-2 in flight, tile 0 landed everywhere
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  for (int t = 0; t < kStages - 1; ++t)
+    if (t < nk) issue_loads(t);
+  if (nk >= kStages - 1) wait_vmcnt<(kStages - 2) * LPT>(); else wait_vmcnt<0>();
+  lds_barrier();
+  read_frags(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    read_frags(kt, 1, 1);
+    mfmas(0);
+    if (kt + 1 < nk) {
+      // own loads of tile kt+1 done -> barrier -> everyone's are, and tile kt-1's stage is free
+      if (kt + kStages - 2 < nk) wait_vmcnt<(kStages - 3) * LPT>(); else wait_vmcnt<0>();
+      lds_barrier();
+      if (kt + kStages - 1 < nk) issue_loads(kt + kStages - 1);
+      read_frags(kt + 1, 0, 0);
     }
-    if (kt + 1 < nk) store_lds(cur ^ 1);
-    __syncthreads();
+    mfmas(1);
   }
 
   // ---- epilogue.  32x32 accumulator layout: slot r of lane l is
   //      row (r / 4) * 8 + (l / 32) * 4 + (r % 4), column l % 32.
+  const int khalf = lane / 32;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -366,7 +420,7 @@ unsigned grid_for(int64_t mtiles, int NT) {
 template <int BM, bool SWIGLU, bool OUT_F32>
 hipError_t launch_bf16(const bf16_t* A, const bf16_t* B, const int32_t* offsets, int64_t rows, int E,
                        int K, int ldb, int NT, void* out, hipStream_t stream) {
-  constexpr int smem = 2 * (BM * kBK * 2 + kBN * kBK * 2);
+  constexpr int smem = kStages * (BM * kBKT * 2 + kBKT * kBRow);
   auto kern = gemm_bf16_kernel<BM, SWIGLU, OUT_F32>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
@@ -411,15 +465,15 @@ hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int 
   }
   if (dt == 1) {
     bf16_t* h = static_cast<bf16_t*>(scratch);
-    hipError_t err = launch_bf16<128, true, false>(static_cast<const bf16_t*>(x_perm),
+    hipError_t err = launch_bf16<256, true, false>(static_cast<const bf16_t*>(x_perm),
                                                    static_cast<const bf16_t*>(w1), offsets, rows, E, H,
                                                    2 * F, F / 128, h, stream);
     if (err != hipSuccess) return err;
     if (between && (err = hipEventRecord(between, stream)) != hipSuccess) return err;
     if (out_dt == 0)
-      return launch_bf16<128, false, true>(h, static_cast<const bf16_t*>(w2), offsets, rows, E, F, H,
+      return launch_bf16<256, false, true>(h, static_cast<const bf16_t*>(w2), offsets, rows, E, F, H,
                                            static_cast<int>(ceil_div(H, kBN)), y_perm, stream);
-    return launch_bf16<128, false, false>(h, static_cast<const bf16_t*>(w2), offsets, rows, E, F, H,
+    return launch_bf16<256, false, false>(h, static_cast<const bf16_t*>(w2), offsets, rows, E, F, H,
                                           static_cast<int>(ceil_div(H, kBN)), y_perm, stream);
   }
   return hipErrorNotSupported;

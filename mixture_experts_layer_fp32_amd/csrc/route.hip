@@ -5,10 +5,16 @@
 // Models with Megatron Core", summary page, "Method", first paragraph; the router stays
 // in higher precision per the same page's [§5] key claim).
 //
-// Two kernels:
-//  1. route_logits: logits[T, E] = x[T, H] . W_r[H, E] in fp32 FMA (x widened exactly from
-//     bf16).  A register-tiled skinny GEMM: a workgroup owns BT tokens x BE experts and
-//     walks H in KC-wide chunks staged in LDS; each thread accumulates a TM x TN tile.
+// Kernels:
+//  1. logits, bf16 x (the usual case): W_r is split once per call into three bf16 matrices
+//     W_r = W_hi + W_mid + W_lo (each the bf16 rounding of what the previous ones leave; the
+//     remainder is below 2^-24 |w|), stored K-contiguous per expert.  x is exactly bf16, so
+//     three bf16 MFMAs (v_mfma_f32_16x16x32_bf16, fp32 accumulate, exact products) give the
+//     fp32 projection at MFMA speed: the stage is then bound by streaming x from HBM.
+//     Fragments come straight from global memory in MFMA layout (16 B per lane); the small
+//     split weight stays in L2.
+//  1'. logits, fp32 x: a register-tiled fp32 FMA skinny GEMM (a workgroup owns BT tokens x
+//     BE experts and walks H in KC-wide chunks staged in LDS).
 //  2. route_topk: one wavefront per token.  Lane l holds experts l, l+64, ...; k rounds of a
 //     wave-wide arg-max (larger key wins, equal keys -> lower index) pick the slots in key
 //     order; softmax statistics come from wave reductions over all E logits.
@@ -87,6 +93,97 @@ __global__ __launch_bounds__(kRouteThreads) void route_logits_kernel(
       if (e < E) logits[t * E + e] = acc[i][j];
     }
   }
+}
+
+// W_r [H, E] fp32 -> ws [3][Ep][H] bf16 (Ep = E rounded up to 16, padded experts are 0).
+__global__ __launch_bounds__(kRouteThreads) void route_split_kernel(const float* __restrict__ w, int H,
+                                                                   int E, int Ep,
+                                                                   bf16_t* __restrict__ ws) {
+  const int64_t n = static_cast<int64_t>(Ep) * H;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kRouteThreads + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kRouteThreads) {
+    const int e = static_cast<int>(i / H), h = static_cast<int>(i % H);
+    float v = e < E ? w[static_cast<int64_t>(h) * E + e] : 0.0f;
+    bf16_t p0 = f32_to_bf16(v);
+    float r1 = v - bf16_to_f32(p0);  // exact: v and its bf16 rounding share the leading bits
+    bf16_t p1 = f32_to_bf16(r1);
+    float r2 = r1 - bf16_to_f32(p1);
+    bf16_t p2 = f32_to_bf16(r2);
+    ws[i] = p0;
+    ws[n + i] = p1;
+    ws[2 * n + i] = p2;
+  }
+}
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4v;
+
+// One wave computes 16*TM tokens x 16*TN experts with v_mfma_f32_16x16x32_bf16.
+// Operand layout: lane l holds row (l % 16), k = 8*(l/16) .. +8 of a 32-wide k step (A: token
+// rows of x; B: expert rows of the split weight); accumulator slot r of lane l is token
+// 4*(l/16) + r, expert l % 16.
+template <int TM, int TN>
+__global__ __launch_bounds__(kRouteThreads) void route_logits_mfma_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ ws, float* __restrict__ logits, int64_t T,
+    int H, int E, int Ep) {
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int64_t t0 = (static_cast<int64_t>(blockIdx.x) * (kRouteThreads / kWave) + wave) * (16 * TM);
+  if (t0 >= T) return;
+  const int e0 = blockIdx.y * (16 * TN);
+  const int64_t plane = static_cast<int64_t>(Ep) * H;
+  const int kq = 8 * (lane / 16);
+  const bf16_t* xa[TM];
+  bool live[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    int64_t t = t0 + i * 16 + lane % 16;
+    live[i] = t < T;
+    xa[i] = x + (live[i] ? t : 0) * H + kq;
+  }
+  const bf16_t* wb[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) wb[j] = ws + static_cast<int64_t>(e0 + j * 16 + lane % 16) * H + kq;
+  f32x4v acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < H; k0 += 32) {
+    const bool kin = k0 + kq < H;  // H % 8 == 0: an 8-wide chunk is wholly in or out
+    bf16x8_t a[TM], b[TN][3];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      uint4 v = (live[i] && kin) ? *reinterpret_cast<const uint4*>(xa[i] + k0) : make_uint4(0, 0, 0, 0);
+      a[i] = *reinterpret_cast<bf16x8_t*>(&v);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int s = 0; s < 3; ++s) {
+        uint4 v = kin ? *reinterpret_cast<const uint4*>(wb[j] + s * plane + k0) : make_uint4(0, 0, 0, 0);
+        b[j][s] = *reinterpret_cast<bf16x8_t*>(&v);
+      }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        // smallest parts first
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j][2], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j][1], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j][0], acc[i][j], 0, 0, 0);
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int e = e0 + j * 16 + lane % 16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + i * 16 + 4 * (lane / 16) + r;
+        if (t < T && e < E) logits[t * E + e] = acc[i][j][r];
+      }
+    }
 }
 
 constexpr int kMaxPerLane = 8;  // E <= 512 = 8 x 64 lanes
@@ -195,17 +292,53 @@ hipError_t launch_logits(const XT* x, const float* w, float* logits, int64_t T, 
   return hipGetLastError();
 }
 
+int padded_experts(int E) { return (E + 15) / 16 * 16; }
+
+size_t split_bytes(int H, int E) { return static_cast<size_t>(3) * padded_experts(E) * H * sizeof(bf16_t); }
+
+hipError_t launch_logits_bf16(const bf16_t* x, const float* w, float* logits, int64_t T, int H, int E,
+                              bf16_t* wsplit, hipStream_t stream) {
+  const int Ep = padded_experts(E);
+  const int64_t n = static_cast<int64_t>(Ep) * H;
+  const unsigned gs = static_cast<unsigned>(ceil_div(n, kRouteThreads) < 2048 ? ceil_div(n, kRouteThreads) : 2048);
+  hipLaunchKernelGGL(route_split_kernel, dim3(gs), dim3(kRouteThreads), 0, stream, w, H, E, Ep, wsplit);
+  constexpr int waves = kRouteThreads / kWave;
+  if (Ep <= 16) {
+    dim3 grid(static_cast<unsigned>(ceil_div(T, waves * 16)), 1);
+    hipLaunchKernelGGL((route_logits_mfma_kernel<1, 1>), grid, dim3(kRouteThreads), 0, stream, x, wsplit,
+                       logits, T, H, E, Ep);
+  } else if (Ep % 64 == 0) {
+    dim3 grid(static_cast<unsigned>(ceil_div(T, waves * 32)), static_cast<unsigned>(Ep / 64));
+    hipLaunchKernelGGL((route_logits_mfma_kernel<2, 4>), grid, dim3(kRouteThreads), 0, stream, x, wsplit,
+                       logits, T, H, E, Ep);
+  } else {
+    dim3 grid(static_cast<unsigned>(ceil_div(T, waves * 32)), static_cast<unsigned>(Ep / 16));
+    hipLaunchKernelGGL((route_logits_mfma_kernel<2, 1>), grid, dim3(kRouteThreads), 0, stream, x, wsplit,
+                       logits, T, H, E, Ep);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
-size_t route_scratch_bytes(int64_t T, int E) { return static_cast<size_t>(T) * E * sizeof(float); }
+size_t route_scratch_bytes(int64_t T, int H, int E, bool logits_given) {
+  size_t a = logits_given ? 0 : (static_cast<size_t>(T) * E * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  return a + split_bytes(H, E);
+}
 
 hipError_t launch_route(const void* x, int x_dt, const float* w_router, const float* bias, int64_t T,
                         int H, int E, int k, int score, int norm, float* logits, int32_t* ids,
-                        float* gates, float* logits_scratch, hipStream_t stream) {
-  float* lg = logits ? logits : logits_scratch;
+                        float* gates, void* scratch, hipStream_t stream) {
+  float* lg = logits;
+  char* sp = static_cast<char*>(scratch);
+  if (!lg) {
+    lg = reinterpret_cast<float*>(sp);
+    sp += (static_cast<size_t>(T) * E * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  }
   hipError_t err = (x_dt == 0)
                        ? launch_logits(static_cast<const float*>(x), w_router, lg, T, H, E, stream)
-                       : launch_logits(static_cast<const bf16_t*>(x), w_router, lg, T, H, E, stream);
+                       : launch_logits_bf16(static_cast<const bf16_t*>(x), w_router, lg, T, H, E,
+                                            reinterpret_cast<bf16_t*>(sp), stream);
   if (err != hipSuccess) return err;
   dim3 grid(static_cast<unsigned>(ceil_div(T, kRouteThreads / kWave)));
   hipLaunchKernelGGL(route_topk_kernel, grid, dim3(kRouteThreads), 0, stream, lg, bias, T, E, k, score,

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def _route(L, **over):
     a = dict(x=P, x_dt=1, w=P, bias=None, T=8, H=64, E=8, k=2, score=0, norm=0, logits=P, ids=P,
-             gates=P, ws=None, wsb=0)
+             gates=P, ws=P, wsb=1 << 20)
     a.update(over)
     return L.moe_route(a["x"], a["x_dt"], a["w"], a["bias"], a["T"], a["H"], a["E"], a["k"], a["score"],
                        a["norm"], a["logits"], a["ids"], a["gates"], a["ws"], a["wsb"], None)
@@ -48,7 +48,7 @@ def _route(L, **over):
 @pytest.mark.parametrize("over,code", [
     (dict(x=None), INVALID), (dict(ids=None), INVALID), (dict(k=0), INVALID), (dict(k=9), INVALID),
     (dict(E=513, k=2), INVALID), (dict(E=32, k=17), INVALID), (dict(H=12), INVALID), (dict(T=-1), INVALID),
-    (dict(x_dt=2), INVALID), (dict(score=7), INVALID), (dict(logits=None), WS),
+    (dict(x_dt=2), INVALID), (dict(score=7), INVALID), (dict(ws=None), WS), (dict(logits=None, wsb=1024), WS),
     (dict(T=2 ** 30, k=2), INVALID)])
 def test_route_rejects(over, code):
     assert _route(_lib.lib(), **over) == code
@@ -60,8 +60,8 @@ def test_route_with_no_tokens_is_a_noop():
 
 def test_workspace_sizes():
     L = _lib.lib()
-    assert L.moe_route_workspace_size(100, 8, 1) == 0
-    assert L.moe_route_workspace_size(100, 8, 0) >= 100 * 8 * 4
+    assert L.moe_route_workspace_size(100, 64, 8, 1) >= 3 * 16 * 64 * 2
+    assert L.moe_route_workspace_size(100, 64, 8, 0) >= 100 * 8 * 4 + 3 * 16 * 64 * 2
     assert L.moe_permute_workspace_size(1000, 64, 4) >= 1000 * 4 * 4
     assert L.moe_grouped_swiglu_workspace_size(512, 256, _lib.MOE_BF16) >= 512 * 256 * 2
     assert L.moe_grouped_swiglu_workspace_size(512, 256, _lib.MOE_F32) >= 512 * 256 * 4
