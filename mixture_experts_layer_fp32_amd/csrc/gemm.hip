@@ -26,14 +26,10 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBK = 64;   // K per LDS stage (bf16)
+constexpr int kThreads = 256;  // fp32 path
 constexpr int kBN = 256;  // N per tile (SwiGLU: 128 gate + 128 up)
 constexpr int kMaxExpertsLds = 520;  // >= E + 1 for E <= 512
 
-// 16-byte chunk index swizzle of row/column n of a K-contiguous LDS tile (8 chunks per row).
-__device__ __forceinline__ int swz(int n) { return (n ^ (n >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int n, int kc) { return n * (kBK * 2) + ((kc ^ swz(n)) << 4); }
 
 // Per-workgroup tile lookup built from the device-resident expert offsets.
 struct TileMap {
@@ -61,7 +57,7 @@ __device__ bool map_tile(const int32_t* offsets, int64_t rows, int E, int NT, in
     return true;
   }
   // m-tiles per expert, exclusive prefix in s_pref[0..E]
-  for (int e = tid; e < E; e += kThreads) {
+  for (int e = tid; e < E; e += static_cast<int>(blockDim.x)) {
     int c = offsets[e + 1] - offsets[e];
     s_pref[e + 1] = (c + BM - 1) / BM;
   }
@@ -106,31 +102,36 @@ __device__ bool map_tile(const int32_t* offsets, int64_t rows, int E, int NT, in
 }
 
 // ------------------------------------------------------------------------------ bf16 path
-// A: [rows, K] bf16 row-major (x_perm or h).  B: per expert [K, ldb] bf16, N-contiguous.
-// SWIGLU: out h [rows, F] (F = ldb / 2), tile n covers gate cols n*128.. and up cols F + n*128..
-// else:   out [rows, ldb], tile n covers cols n*256..
+// A: [rows, K] bf16 row-major (x_perm or h).  B: per expert [K, N] bf16 (N-contiguous, the
+// layout the weights arrive in) or, with B_NK, [N, K] (K-contiguous).
+// SWIGLU: out h [rows, F] (F = N / 2), tile n covers gate cols n*128.. and up cols F + n*128..
+// else:   out [rows, N], tile n covers cols n*256..
 //
-// Tile BM x 256 x 32, 4 waves in a 2 x 2 grid (each wave (BM/2) x 128), a ring of kStages LDS
-// stages.  Both operands go global -> LDS directly (global_load_lds_dwordx4: lane l of an
-// instruction lands at base + 16 l), so no register staging and no VALU work:
-//   A stage: BM rows x 64 B; 16-byte chunk c of row r is stored at c ^ ((r >> 2) & 3).
-//   B stage: 32 k-rows x 512 B, untransposed; chunk c of k-row k is stored at c ^ 4 (k & 3).
-// A fragments (lane l: row l % 32, k 8 (l / 32) .. +8) are one ds_read_b128 each; B fragments
-// are two ds_read_b64_tr_b16 each: within a group of 16 lanes, lane 16g + 4a + b receives
-// 16-bit column b of the 8-byte pieces addressed by lanes 16g + a + 4e (e = 0..3), so source
-// lane s addresses k-row 8 (s / 32) + 4 r + (s % 16) / 4 at column 16 ((s / 16) % 2) + 4 (s % 4)
-// of the fragment and destination lane d collects column d % 32 for 4 consecutive k.
-// Both swizzles spread a wave's 16-byte (A) and 8-byte (B) fragment reads over all banks.
+// Tile BM x 256 x 64 per iteration, 512 threads = 8 waves (2 per SIMD) in a 2 (M) x 4 (N) grid,
+// each wave (BM/2) x 64 = FM x 2 blocks of v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
+// Both operands stream global -> LDS directly (global_load_lds_dwordx4: lane l of a
+// wave-instruction lands at base + 16 l), so there is no register staging and no VALU work in
+// the loop.  Two LDS stages per operand (128 KB):
+//   A stage: BM rows x 128 B; 16-byte chunk c of row r is stored at c ^ ((r >> 1) & 7).
+//   B stage, [K, N] weights: 64 k-rows x 512 B, untransposed; chunk c of k-row k at c ^ 4 (k & 3).
+//   B stage, [N, K] weights: like A (256 n-rows x 128 B).
+// A fragments (lane l: row l % 32, k 8 (l / 32) .. +8) are one ds_read_b128 each.  B fragments
+// from [K, N] are two ds_read_b64_tr_b16 each: within a group of 16 lanes, lane 16g + 4a + b
+// receives 16-bit column b of the 8-byte pieces addressed by lanes 16g + a + 4e (e = 0..3), so
+// source lane s addresses k-row 8 (s / 32) + 4 r + (s % 16) / 4 at column 16 ((s / 16) % 2) +
+// 4 (s % 4) of the fragment and destination lane d collects column d % 32 for 4 consecutive k.
+// The swizzles spread every fragment read of a 16-lane group over distinct banks.
 //
-// Pipeline: loads of tile t are issued kStages - 1 iterations before use; each iteration waits
-// for its own loads of the next tile (s_waitcnt vmcnt), meets the other waves at one barrier,
-// issues the loads of the tile kStages - 1 ahead into the stage freed by the previous tile, and
-// prefetches the next tile's first fragments while the current tile's last MFMAs run.
+// Iteration kt (four 16-deep k-steps): MFMAs of k-step s interleave with the LDS reads of the
+// fragments of k-step s + 1.  Before the last k-step the wave waits for its own reads of tile
+// kt and its own loads of tile kt + 1, meets the other waves at the single barrier of the
+// iteration, issues the loads of tile kt + 2 into tile kt's stages, and then runs the last
+// k-step while reading tile kt + 1's first fragments.
 // Loads are unconditional: rows past the expert's end re-read its last row and column groups
 // past the matrix edge re-read column 0; those results are never stored.
-constexpr int kBKT = 32;     // K per stage
-constexpr int kStages = 4;   // LDS ring depth
-constexpr int kBRow = kBN * 2;  // bytes per B k-row
+constexpr int kBKT = 64;        // K per iteration / stage
+constexpr int kGemmThreads = 512;  // 8 waves, two per SIMD
+constexpr int kBRow = kBN * 2;  // bytes per [K, N] B k-row
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
@@ -154,19 +155,38 @@ __device__ __forceinline__ void wait_vmcnt() {
   // gfx9 s_waitcnt encoding: vmcnt [3:0] + [15:14], expcnt [6:4] (7 = no wait), lgkmcnt [11:8] (15)
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14)); }
 
-template <int BM, bool SWIGLU, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
+// Scheduling groups for one k-step: NM MFMAs, each followed by up to RPM of the NR LDS reads.
+template <int Q, int NM, int NR, int RPM>
+__device__ __forceinline__ void sched_mfma_reads() {
+  if constexpr (Q < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    constexpr int left = NR - Q * RPM;
+    constexpr int nr = left < RPM ? left : RPM;
+    if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);  // LDS reads
+    sched_mfma_reads<Q + 1, NM, NR, RPM>();
+  }
+}
+
+// SiLU for the epilogue: z * 1 / (1 + 2^(-z log2 e)) with the hardware exp2 and reciprocal
+// (about 1e-6 relative error, far below the bf16 rounding of h).
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+
+template <int BM, bool SWIGLU, bool OUT_F32, bool B_NK>
+__global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const int32_t* __restrict__ offsets,
     int64_t rows, int E, int K, int ldb, int NT, void* __restrict__ out) {
-  constexpr int FM = BM / 64;        // 32x32 blocks per wave along M (2 waves along M)
-  constexpr int FN = kBN / 64;       // 32x32 blocks per wave along N (2 waves along N) = 4
+  constexpr int NWAVE = kGemmThreads / kWave;  // 8: 2 along M x 4 along N
+  constexpr int FM = BM / 64;                  // 32x32 blocks per wave along M
+  constexpr int FN = 2;                        // 32x32 blocks per wave along N (64 columns)
   constexpr int A_BYTES = BM * kBKT * 2;
-  constexpr int B_BYTES = kBKT * kBRow;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int A_ROUNDS = A_BYTES / 1024 / 4;  // 1 KB wave-instructions per wave per stage
-  constexpr int B_ROUNDS = B_BYTES / 1024 / 4;
-  constexpr int LPT = A_ROUNDS + B_ROUNDS;      // loads per thread per stage
+  constexpr int B_BYTES = kBN * kBKT * 2;
+  constexpr int B_BASE = 2 * A_BYTES;               // byte offset of the two B stages
+  constexpr int A_ROUNDS = A_BYTES / 1024 / NWAVE;  // 1 KB wave-instructions per wave per stage
+  constexpr int B_ROUNDS = B_BYTES / 1024 / NWAVE;
 
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   __shared__ int s_pref[kMaxExpertsLds];
@@ -177,72 +197,105 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wm = wave / 2, wn = wave % 2;
+  const int wm = wave / 4, wn = wave % 4;
   lds_void_t* lds = (lds_void_t*)smem;  // address-space cast: generic -> LDS
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
 
   // ---- global sources of this lane's direct loads
-  // A round p of wave w: tile rows (4p + w) * 16 + lane / 4, stored chunk lane % 4 holding
-  // logical chunk (lane % 4) ^ ((lane >> 4) & 3).
+  // A round p of wave w covers tile rows (8p + w) * 8 + lane / 8 (1 KB = 8 rows x 128 B);
+  // stored chunk lane % 8 holds logical chunk (lane % 8) ^ ((row >> 1) & 7).
   const bf16_t* a_src[A_ROUNDS];
 #pragma unroll
   for (int p = 0; p < A_ROUNDS; ++p) {
-    int r = (4 * p + wave) * 16 + lane / 4;
+    const int r = (NWAVE * p + wave) * 8 + lane / 8;
     int64_t grow = tm.row0 + r;
     if (grow >= tm.row_end) grow = tm.row_end - 1;
-    a_src[p] = A + grow * K + (((lane % 4) ^ ((lane >> 4) & 3)) * 8);
+    a_src[p] = A + grow * K + (((lane % 8) ^ ((r >> 1) & 7)) * 8);
   }
-  // B round p of wave w: k-row 2 (4p + w) + lane / 32, stored chunk lane % 32 holding logical
-  // chunk (lane % 32) ^ 4 ((2w + lane / 32) & 3).
-  const int b_lchunk = (lane % 32) ^ (4 * ((2 * wave + lane / 32) & 3));
-  int64_t b_col;
-  if (SWIGLU) {
-    const int F = ldb / 2;
-    b_col = (b_lchunk < 16) ? static_cast<int64_t>(tm.nt) * 128 + b_lchunk * 8
-                            : F + static_cast<int64_t>(tm.nt) * 128 + (b_lchunk - 16) * 8;
+  // B sources.  [K, N]: round p of wave w covers k-rows 2 (8p + w) + lane / 32 (1 KB = 2 k-rows
+  // x 512 B); stored chunk lane % 32 holds logical chunk (lane % 32) ^ 4 ((2w + lane / 32) & 3).
+  // [N, K]: round p covers n-rows (8p + w) * 8 + lane / 8, swizzled like A.
+  const bf16_t* b_src[B_ROUNDS];
+  int64_t b_kstep;
+  if (!B_NK) {
+    const int b_lchunk = (lane % 32) ^ (4 * ((2 * wave + lane / 32) & 3));
+    int64_t b_col;
+    if (SWIGLU) {
+      const int F = ldb / 2;
+      b_col = (b_lchunk < 16) ? static_cast<int64_t>(tm.nt) * 128 + b_lchunk * 8
+                              : F + static_cast<int64_t>(tm.nt) * 128 + (b_lchunk - 16) * 8;
+    } else {
+      b_col = static_cast<int64_t>(tm.nt) * kBN + b_lchunk * 8;
+    }
+    if (b_col >= ldb) b_col = 0;  // ldb % 8 == 0: an 8-column group is wholly in or out
+    const bf16_t* b0 = B + static_cast<int64_t>(tm.expert) * K * ldb +
+                       static_cast<int64_t>(2 * wave + lane / 32) * ldb + b_col;
+#pragma unroll
+    for (int p = 0; p < B_ROUNDS; ++p) b_src[p] = b0 + static_cast<int64_t>(2 * NWAVE * p) * ldb;
+    b_kstep = static_cast<int64_t>(kBKT) * ldb;
   } else {
-    b_col = static_cast<int64_t>(tm.nt) * kBN + b_lchunk * 8;
+#pragma unroll
+    for (int p = 0; p < B_ROUNDS; ++p) {
+      const int r = (NWAVE * p + wave) * 8 + lane / 8;
+      int64_t n;
+      if (SWIGLU) {
+        const int F = ldb / 2;
+        n = (r < 128) ? static_cast<int64_t>(tm.nt) * 128 + r : F + static_cast<int64_t>(tm.nt) * 128 + (r - 128);
+      } else {
+        n = static_cast<int64_t>(tm.nt) * kBN + r;
+      }
+      if (n >= ldb) n = 0;
+      b_src[p] = B + (static_cast<int64_t>(tm.expert) * ldb + n) * K + (((lane % 8) ^ ((r >> 1) & 7)) * 8);
+    }
+    b_kstep = kBKT;
   }
-  if (b_col >= ldb) b_col = 0;  // ldb % 8 == 0: an 8-column group is wholly in or out
-  const bf16_t* b_src = B + static_cast<int64_t>(tm.expert) * K * ldb +
-                        static_cast<int64_t>(2 * wave + lane / 32) * ldb + b_col;
-  const int64_t b_round = static_cast<int64_t>(8) * ldb;  // 8 k-rows per round
 
   auto issue_loads = [&](int kt) {
-    const int st = kt % kStages;
-    const uint32_t sbase = lds_base + st * STAGE;
+    const uint32_t abase = lds_base + (kt & 1) * A_BYTES;
+    const uint32_t bbase = lds_base + B_BASE + (kt & 1) * B_BYTES;
 #pragma unroll
     for (int p = 0; p < A_ROUNDS; ++p)
-      lds_dma16(a_src[p] + static_cast<int64_t>(kt) * kBKT, sbase + (4 * p + wave) * 1024);
-    const bf16_t* bs = b_src + static_cast<int64_t>(kt) * kBKT * ldb;
+      lds_dma16(a_src[p] + static_cast<int64_t>(kt) * kBKT, abase + (NWAVE * p + wave) * 1024);
 #pragma unroll
-    for (int p = 0; p < B_ROUNDS; ++p) lds_dma16(bs + p * b_round, sbase + A_BYTES + (4 * p + wave) * 1024);
+    for (int p = 0; p < B_ROUNDS; ++p)
+      lds_dma16(b_src[p] + static_cast<int64_t>(kt) * b_kstep, bbase + (NWAVE * p + wave) * 1024);
   };
 
-  // ---- fragment addresses (byte offsets inside a stage)
-  uint32_t a_off[FM][2];
+  // ---- fragment addresses (byte offsets inside a stage; k-step ks adds 32 B (A, [N,K] B) or
+  // 16 k-rows ([K,N] B))
+  uint32_t a_row_off[FM], a_sw[FM];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int r = wm * (BM / 2) + i * 32 + lane % 32;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) a_off[i][ks] = r * 64 + (((ks * 2 + lane / 32) ^ ((r >> 2) & 3)) << 4);
+    a_row_off[i] = r * 128;
+    a_sw[i] = (r >> 1) & 7;
   }
-  uint32_t b_off[FN][2];  // [j][r]; add ks * 16 k-rows
-  {
+  uint32_t b_off[FN][2], b_sw[FN];
+  if (B_NK) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int cb = SWIGLU ? j * 128 + wn * 32 : wn * 64 + j * 32;
+      const int r = cb + lane % 32;
+      b_off[j][0] = r * 128;
+      b_off[j][1] = 0;
+      b_sw[j] = (r >> 1) & 7;
+    }
+  } else {
     const int g = lane / 16, h = lane / 32, a4 = lane % 4, e = (lane % 16) / 4;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      int cb;
-      if (SWIGLU) cb = (j < FN / 2) ? wn * 64 + j * 32 : 128 + wn * 64 + (j - FN / 2) * 32;
-      else cb = wn * 128 + j * 32;
+      // SwiGLU: block 0 = gate columns wn*32.., block 1 = the matching up columns 128 + wn*32..
+      const int cb = SWIGLU ? j * 128 + wn * 32 : wn * 64 + j * 32;
       const int col = cb + 16 * (g % 2) + 4 * a4;
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int krow = 8 * h + 4 * r + e;
-        b_off[j][r] = A_BYTES + krow * kBRow + (((col / 8) ^ (4 * e)) << 4) + (col % 8) * 2;
+        b_off[j][r] = krow * kBRow + (((col / 8) ^ (4 * e)) << 4) + (col % 8) * 2;
       }
+      b_sw[j] = 0;
     }
   }
+  const int khalf = lane / 32;
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -254,20 +307,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 
   bf16x8_t af[2][FM], bfr[2][FN];
   auto read_frags = [&](int kt, int ks, int buf) {
-    const uint32_t sbase = lds_base + (kt % kStages) * STAGE;
+    const uint32_t abase = lds_base + (kt & 1) * A_BYTES;
+    const uint32_t bbase = lds_base + B_BASE + (kt & 1) * B_BYTES;
+    const uint32_t chunk = ks * 2 + khalf;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
       af[buf][i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
-          static_cast<uintptr_t>(sbase + a_off[i][ks]));
+          static_cast<uintptr_t>(abase + a_row_off[i] + ((chunk ^ a_sw[i]) << 4)));
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16_t*>(
-          static_cast<uintptr_t>(sbase + b_off[j][0] + ks * 16 * kBRow)));
-      v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16_t*>(
-          static_cast<uintptr_t>(sbase + b_off[j][1] + ks * 16 * kBRow)));
-      typedef short v8i16_t __attribute__((ext_vector_type(8)));
-      v8i16_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      bfr[buf][j] = __builtin_bit_cast(bf16x8_t, both);
+      if (B_NK) {
+        bfr[buf][j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
+            static_cast<uintptr_t>(bbase + b_off[j][0] + ((chunk ^ b_sw[j]) << 4)));
+      } else {
+        v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16_t*>(
+            static_cast<uintptr_t>(bbase + b_off[j][0] + ks * 16 * kBRow)));
+        v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16_t*>(
+            static_cast<uintptr_t>(bbase + b_off[j][1] + ks * 16 * kBRow)));
+        typedef short v8i16_t __attribute__((ext_vector_type(8)));
+        v8i16_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        bfr[buf][j] = __builtin_bit_cast(bf16x8_t, both);
+      }
     }
   };
   auto mfmas = [&](int buf) {
@@ -277,31 +337,50 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0);
   };
+  // MFMAs of one k-step interleaved with the LDS reads of the next k-step's fragments
+  constexpr int NREADS = FM + (B_NK ? FN : 2 * FN);
+  constexpr int NMFMA = FM * FN;
+  constexpr int RPM = (NREADS + NMFMA - 1) / NMFMA;  // LDS reads per MFMA slot
+  auto interleave = [&]() { sched_mfma_reads<0, NMFMA, NREADS, RPM>(); };
 
   const int nk = K / kBKT;
-  // prologue: tiles 0 .. kStages-2 in flight, tile 0 landed everywhere
-#pragma unroll
-  for (int t = 0; t < kStages - 1; ++t)
-    if (t < nk) issue_loads(t);
-  if (nk >= kStages - 1) wait_vmcnt<(kStages - 2) * LPT>(); else wait_vmcnt<0>();
+  issue_loads(0);
+  if (nk > 1) {
+    issue_loads(1);
+    wait_vmcnt<A_ROUNDS + B_ROUNDS>();  // tile 0 landed (tile 1 may be in flight)
+  } else {
+    wait_vmcnt<0>();
+  }
   lds_barrier();
   read_frags(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    read_frags(kt, 1, 1);
     mfmas(0);
-    if (kt + 1 < nk) {
-      // own loads of tile kt+1 done -> barrier -> everyone's are, and tile kt-1's stage is free
-      if (kt + kStages - 2 < nk) wait_vmcnt<(kStages - 3) * LPT>(); else wait_vmcnt<0>();
-      lds_barrier();
-      if (kt + kStages - 1 < nk) issue_loads(kt + kStages - 1);
-      read_frags(kt + 1, 0, 0);
-    }
+    read_frags(kt, 1, 1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
     mfmas(1);
+    read_frags(kt, 2, 0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0);
+    read_frags(kt, 3, 1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) {
+      wait_lgkm0();       // this wave's reads of tile kt are complete
+      wait_vmcnt<0>();    // this wave's loads of tile kt + 1 have landed
+      lds_barrier();      // ... for every wave: tile kt + 1 readable, tile kt's stages free
+      if (kt + 2 < nk) issue_loads(kt + 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
+    read_frags(kt + 1, 0, 0);  // past the last tile this reads a stale stage (in bounds, unused)
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- epilogue.  32x32 accumulator layout: slot r of lane l is
   //      row (r / 4) * 8 + (l / 32) * 4 + (r % 4), column l % 32.
-  const int khalf = lane / 32;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -311,20 +390,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
       if (grow >= tm.row_end) continue;
       if (SWIGLU) {
         const int F = ldb / 2;
-#pragma unroll
-        for (int j = 0; j < FN / 2; ++j) {
-          const float g = acc[i][j][r], u = acc[i][j + FN / 2][r];
-          const float h = silu(g) * u;
-          const int64_t col = static_cast<int64_t>(tm.nt) * 128 + wn * 64 + j * 32 + lane % 32;
-          if (OUT_F32)
-            static_cast<float*>(out)[grow * F + col] = h;
-          else
-            static_cast<bf16_t*>(out)[grow * F + col] = f32_to_bf16(h);
-        }
+        const float g = acc[i][0][r], u = acc[i][1][r];
+        const float h = silu_fast(g) * u;
+        const int64_t col = static_cast<int64_t>(tm.nt) * 128 + wn * 32 + lane % 32;
+        if (OUT_F32)
+          static_cast<float*>(out)[grow * F + col] = h;
+        else
+          static_cast<bf16_t*>(out)[grow * F + col] = f32_to_bf16(h);
       } else {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int64_t col = static_cast<int64_t>(tm.nt) * kBN + wn * 128 + j * 32 + lane % 32;
+          const int64_t col = static_cast<int64_t>(tm.nt) * kBN + wn * 64 + j * 32 + lane % 32;
           if (col >= ldb) continue;
           if (OUT_F32)
             static_cast<float*>(out)[grow * ldb + col] = acc[i][j][r];
@@ -417,18 +493,34 @@ unsigned grid_for(int64_t mtiles, int NT) {
   return static_cast<unsigned>(ceil_div(g, 8) * 8);
 }
 
-template <int BM, bool SWIGLU, bool OUT_F32>
+template <int BM, bool SWIGLU, bool OUT_F32, bool B_NK = false>
 hipError_t launch_bf16(const bf16_t* A, const bf16_t* B, const int32_t* offsets, int64_t rows, int E,
                        int K, int ldb, int NT, void* out, hipStream_t stream) {
-  constexpr int smem = kStages * (BM * kBKT * 2 + kBKT * kBRow);
-  auto kern = gemm_bf16_kernel<BM, SWIGLU, OUT_F32>;
+  constexpr int smem = 2 * BM * kBKT * 2 + 2 * kBN * kBKT * 2;
+  auto kern = gemm_bf16_kernel<BM, SWIGLU, OUT_F32, B_NK>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (err != hipSuccess) return err;
   const unsigned grid = grid_for(max_tiles<BM>(rows, E, offsets == nullptr), NT);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), smem, stream, A, B, offsets, rows, E, K, ldb, NT,
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), smem, stream, A, B, offsets, rows, E, K, ldb, NT,
                      out);
   return hipGetLastError();
+}
+
+// GEMM1 (+SwiGLU) then GEMM2 with BM-row tiles; `between` (optional) is recorded after GEMM1.
+template <int BM>
+hipError_t launch_bf16_pair(const void* x_perm, const void* w1, const void* w2, const int32_t* offsets,
+                            int64_t rows, int E, int H, int F, void* y_perm, int out_dt, void* scratch,
+                            hipStream_t stream, hipEvent_t between) {
+  bf16_t* h = static_cast<bf16_t*>(scratch);
+  hipError_t err = launch_bf16<BM, true, false>(static_cast<const bf16_t*>(x_perm), static_cast<const bf16_t*>(w1),
+                                                offsets, rows, E, H, 2 * F, F / 128, h, stream);
+  if (err != hipSuccess) return err;
+  if (between && (err = hipEventRecord(between, stream)) != hipSuccess) return err;
+  const int nt2 = static_cast<int>(ceil_div(H, kBN));
+  if (out_dt == 0)
+    return launch_bf16<BM, false, true>(h, static_cast<const bf16_t*>(w2), offsets, rows, E, F, H, nt2, y_perm, stream);
+  return launch_bf16<BM, false, false>(h, static_cast<const bf16_t*>(w2), offsets, rows, E, F, H, nt2, y_perm, stream);
 }
 
 }  // namespace
@@ -464,17 +556,10 @@ hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int 
     return hipGetLastError();
   }
   if (dt == 1) {
-    bf16_t* h = static_cast<bf16_t*>(scratch);
-    hipError_t err = launch_bf16<256, true, false>(static_cast<const bf16_t*>(x_perm),
-                                                   static_cast<const bf16_t*>(w1), offsets, rows, E, H,
-                                                   2 * F, F / 128, h, stream);
-    if (err != hipSuccess) return err;
-    if (between && (err = hipEventRecord(between, stream)) != hipSuccess) return err;
-    if (out_dt == 0)
-      return launch_bf16<256, false, true>(h, static_cast<const bf16_t*>(w2), offsets, rows, E, F, H,
-                                           static_cast<int>(ceil_div(H, kBN)), y_perm, stream);
-    return launch_bf16<256, false, false>(h, static_cast<const bf16_t*>(w2), offsets, rows, E, F, H,
-                                          static_cast<int>(ceil_div(H, kBN)), y_perm, stream);
+    // 256-row tiles when experts average >= 768 rows, else 128-row tiles (less padding)
+    const bool big = offsets == nullptr ? rows >= 768 : rows >= 768 * static_cast<int64_t>(E);
+    return big ? launch_bf16_pair<256>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream, between)
+               : launch_bf16_pair<128>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream, between);
   }
   return hipErrorNotSupported;
 }
