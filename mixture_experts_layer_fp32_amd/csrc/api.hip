@@ -81,10 +81,10 @@ moe_status moe_route(const void* x, moe_dtype x_dt, const float* w_router, const
   moe_status st = check_common(T, H, E, k);
   if (st != MOE_OK) return st;
   if (!act_dtype_ok(x_dt) || (score != MOE_SOFTMAX && score != MOE_SIGMOID)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;  // nothing to do; empty tensors may carry null pointers
   if (!x || !w_router || !topk_ids || !topk_gates) return MOE_ERR_INVALID_ARG;
   const size_t need = moe_route_workspace_size(T, H, E, logits != nullptr);
   if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
-  if (T == 0) return MOE_OK;
   return from_hip(moe::launch_route(x, x_dt, w_router, bias, T, H, E, k, score, norm_topk ? 1 : 0,
                                     logits, topk_ids, topk_gates, workspace,
                                     static_cast<hipStream_t>(stream)));
@@ -133,13 +133,13 @@ moe_status moe_grouped_swiglu(const void* x_perm, const float* x_perm_scales, mo
   if (rows < 0 || rows >= (int64_t{1} << 31) || E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
   moe_status st = check_gemm_shape(dt, H, F);
   if (st != MOE_OK) return st;
-  if (!x_perm || !expert_offsets || !w1 || !w2 || !y_perm) return MOE_ERR_INVALID_ARG;
   if (dt == MOE_F32 && out_dt != MOE_F32) return MOE_ERR_INVALID_ARG;
   if (!act_dtype_ok(out_dt)) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;  // nothing to do; empty tensors may carry null pointers
+  if (!x_perm || !expert_offsets || !w1 || !w2 || !y_perm) return MOE_ERR_INVALID_ARG;
   if (dt == MOE_FP8_E4M3 && (!x_perm_scales || !w1_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
   if (workspace_bytes < moe_grouped_swiglu_workspace_size(rows, F, dt) || !workspace)
     return MOE_ERR_WORKSPACE;
-  if (rows == 0) return MOE_OK;
   return from_hip(moe::launch_grouped_swiglu(x_perm, x_perm_scales, dt, expert_offsets, rows, E, H, F,
                                              w1, w1_scales, w2, w2_scales, y_perm, out_dt, workspace,
                                              static_cast<hipStream_t>(stream)));
@@ -150,10 +150,10 @@ moe_status moe_unpermute_combine(const void* y_perm, moe_dtype y_dt, const int32
                                  int32_t k, void* y, moe_dtype out_dt, moe_stream_t stream) {
   if (T < 0 || H < 8 || H % 8 != 0 || k < 1 || k > MOE_MAX_TOPK) return MOE_ERR_INVALID_ARG;
   if (!act_dtype_ok(y_dt) || !act_dtype_ok(out_dt)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;  // nothing to do; empty tensors may carry null pointers
   if (!y_perm || !row_map || !topk_gates || !y) return MOE_ERR_INVALID_ARG;
   if (!aligned16(y_perm) || !aligned16(y) || (shared_out && !aligned16(shared_out)))
     return MOE_ERR_INVALID_ARG;
-  if (T == 0) return MOE_OK;
   return from_hip(moe::launch_combine(y_perm, y_dt, row_map, topk_gates, shared_out, T, H, k, y, out_dt,
                                       static_cast<hipStream_t>(stream)));
 }
@@ -234,10 +234,10 @@ moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, co
   if (st != MOE_OK) return st;
   st = check_common(T, L->H, L->E, L->k);
   if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;  // nothing to do; empty tensors may carry null pointers
   if (!x || !y || !aligned16(x) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
   const size_t need = plan(L, T, nullptr, nullptr).bytes;
   if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
-  if (T == 0) return MOE_OK;
   ForwardPlan p = plan(L, T, workspace, dbg);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t R = T * L->k;

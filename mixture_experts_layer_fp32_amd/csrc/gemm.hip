@@ -498,9 +498,10 @@ hipError_t launch_bf16(const bf16_t* A, const bf16_t* B, const int32_t* offsets,
                        int K, int ldb, int NT, void* out, hipStream_t stream) {
   constexpr int smem = 2 * BM * kBKT * 2 + 2 * kBN * kBKT * 2;
   auto kern = gemm_bf16_kernel<BM, SWIGLU, OUT_F32, B_NK>;
-  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-  if (err != hipSuccess) return err;
+  // once per instantiation (and never inside a stream capture after the first eager call)
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  if (attr != hipSuccess) return attr;
   const unsigned grid = grid_for(max_tiles<BM>(rows, E, offsets == nullptr), NT);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), smem, stream, A, B, offsets, rows, E, K, ldb, NT,
                      out);

@@ -117,18 +117,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_split_kernel(const float*
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4v;
 
-// One wave computes 16*TM tokens x 16*TN experts with v_mfma_f32_16x16x32_bf16.
-// Operand layout: lane l holds row (l % 16), k = 8*(l/16) .. +8 of a 32-wide k step (A: token
-// rows of x; B: expert rows of the split weight); accumulator slot r of lane l is token
-// 4*(l/16) + r, expert l % 16.
-template <int TM, int TN>
+// A workgroup computes 16*TM tokens x 16*TN experts with v_mfma_f32_16x16x32_bf16; its 4 waves
+// split H four ways (each keeping U k-steps of loads in flight) and their partial sums are
+// added in LDS.  Operand layout: lane l holds row (l % 16), k = 8*(l/16) .. +8 of a 32-wide
+// k-step (A: token rows of x; B: expert rows of the split weight); accumulator slot r of lane l
+// is token 4*(l/16) + r, expert l % 16.
+template <int TM, int TN, int U>
 __global__ __launch_bounds__(kRouteThreads) void route_logits_mfma_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ ws, float* __restrict__ logits, int64_t T,
     int H, int E, int Ep) {
+  constexpr int NW = kRouteThreads / kWave;
+  __shared__ float part[NW][TM][TN][4][kWave];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int64_t t0 = (static_cast<int64_t>(blockIdx.x) * (kRouteThreads / kWave) + wave) * (16 * TM);
-  if (t0 >= T) return;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * (16 * TM);
   const int e0 = blockIdx.y * (16 * TN);
   const int64_t plane = static_cast<int64_t>(Ep) * H;
   const int kq = 8 * (lane / 16);
@@ -148,31 +150,48 @@ __global__ __launch_bounds__(kRouteThreads) void route_logits_mfma_kernel(
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < H; k0 += 32) {
-    const bool kin = k0 + kq < H;  // H % 8 == 0: an 8-wide chunk is wholly in or out
-    bf16x8_t a[TM], b[TN][3];
+  // this wave's share of the 32-wide k-steps
+  const int steps = (H + 31) / 32;
+  const int s0 = wave * steps / NW, s1 = (wave + 1) * steps / NW;
+  for (int sb = s0; sb < s1; sb += U) {
+    bf16x8_t a[U][TM], b[U][TN][3];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      uint4 v = (live[i] && kin) ? *reinterpret_cast<const uint4*>(xa[i] + k0) : make_uint4(0, 0, 0, 0);
-      a[i] = *reinterpret_cast<bf16x8_t*>(&v);
+    for (int u = 0; u < U; ++u) {
+      const int k0 = (sb + u) * 32;
+      const bool kin = (sb + u) < s1 && k0 + kq < H;  // H % 8 == 0: an 8-wide chunk is wholly in or out
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        uint4 v = (live[i] && kin) ? *reinterpret_cast<const uint4*>(xa[i] + k0) : make_uint4(0, 0, 0, 0);
+        a[u][i] = *reinterpret_cast<bf16x8_t*>(&v);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp) {
+          uint4 v = kin ? *reinterpret_cast<const uint4*>(wb[j] + sp * plane + k0) : make_uint4(0, 0, 0, 0);
+          b[u][j][sp] = *reinterpret_cast<bf16x8_t*>(&v);
+        }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          // smallest parts first
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][i], b[u][j][2], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][i], b[u][j][1], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][i], b[u][j][0], acc[i][j], 0, 0, 0);
+        }
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        uint4 v = kin ? *reinterpret_cast<const uint4*>(wb[j] + s * plane + k0) : make_uint4(0, 0, 0, 0);
-        b[j][s] = *reinterpret_cast<bf16x8_t*>(&v);
-      }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        // smallest parts first
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j][2], acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j][1], acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j][0], acc[i][j], 0, 0, 0);
-      }
-  }
+      for (int r = 0; r < 4; ++r) part[wave][i][j][r][lane] = acc[i][j][r];
+  __syncthreads();
+  if (wave != 0) return;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -180,8 +199,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_logits_mfma_kernel(
       const int e = e0 + j * 16 + lane % 16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        float v = part[0][i][j][r][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += part[w][i][j][r][lane];
         const int64_t t = t0 + i * 16 + 4 * (lane / 16) + r;
-        if (t < T && e < E) logits[t * E + e] = acc[i][j][r];
+        if (t < T && e < E) logits[t * E + e] = v;
       }
     }
 }
@@ -302,18 +324,17 @@ hipError_t launch_logits_bf16(const bf16_t* x, const float* w, float* logits, in
   const int64_t n = static_cast<int64_t>(Ep) * H;
   const unsigned gs = static_cast<unsigned>(ceil_div(n, kRouteThreads) < 2048 ? ceil_div(n, kRouteThreads) : 2048);
   hipLaunchKernelGGL(route_split_kernel, dim3(gs), dim3(kRouteThreads), 0, stream, w, H, E, Ep, wsplit);
-  constexpr int waves = kRouteThreads / kWave;
   if (Ep <= 16) {
-    dim3 grid(static_cast<unsigned>(ceil_div(T, waves * 16)), 1);
-    hipLaunchKernelGGL((route_logits_mfma_kernel<1, 1>), grid, dim3(kRouteThreads), 0, stream, x, wsplit,
+    dim3 grid(static_cast<unsigned>(ceil_div(T, 16)), 1);
+    hipLaunchKernelGGL((route_logits_mfma_kernel<1, 1, 4>), grid, dim3(kRouteThreads), 0, stream, x, wsplit,
                        logits, T, H, E, Ep);
   } else if (Ep % 64 == 0) {
-    dim3 grid(static_cast<unsigned>(ceil_div(T, waves * 32)), static_cast<unsigned>(Ep / 64));
-    hipLaunchKernelGGL((route_logits_mfma_kernel<2, 4>), grid, dim3(kRouteThreads), 0, stream, x, wsplit,
+    dim3 grid(static_cast<unsigned>(ceil_div(T, 32)), static_cast<unsigned>(Ep / 64));
+    hipLaunchKernelGGL((route_logits_mfma_kernel<2, 4, 2>), grid, dim3(kRouteThreads), 0, stream, x, wsplit,
                        logits, T, H, E, Ep);
   } else {
-    dim3 grid(static_cast<unsigned>(ceil_div(T, waves * 32)), static_cast<unsigned>(Ep / 16));
-    hipLaunchKernelGGL((route_logits_mfma_kernel<2, 1>), grid, dim3(kRouteThreads), 0, stream, x, wsplit,
+    dim3 grid(static_cast<unsigned>(ceil_div(T, 32)), static_cast<unsigned>(Ep / 16));
+    hipLaunchKernelGGL((route_logits_mfma_kernel<2, 1, 4>), grid, dim3(kRouteThreads), 0, stream, x, wsplit,
                        logits, T, H, E, Ep);
   }
   return hipGetLastError();

@@ -1,0 +1,180 @@
+"""GPU edge cases: tiny and degenerate shapes, forced routings, ties, canaries, graphs."""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+import mixture_experts_layer_fp32_amd as moe_gpu
+from oracle import moe
+from tests.checks import check_permutation, rel_frobenius
+from tests.gpu_oracle import TOL, host, routing_from_logits, weights_of
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run_and_check(cfg, seed=0):
+    d = moe_inputs.make_inputs(cfg, seed=seed, weight_device=DEV, act_device=DEV)
+    layer = moe_gpu.Layer.from_inputs(d, cfg.k, cfg.score, cfg.norm)
+    y, dbg = moe_gpu.forward(d["x"], layer, debug=True)
+    torch.cuda.synchronize()
+    w1 = [weights_of(d["w1"], None, e) for e in range(cfg.E)]
+    w2 = [weights_of(d["w2"], None, e) for e in range(cfg.E)]
+    sw1 = weights_of(d["ws1"], None, None) if cfg.Fs else None
+    sw2 = weights_of(d["ws2"], None, None) if cfg.Fs else None
+    o = moe.forward(host(d["x"]), host(d["w_router"]), lambda e: w1[e], lambda e: w2[e], E=cfg.E, k=cfg.k,
+                    score=cfg.score, norm=cfg.norm, shared_w1=sw1, shared_w2=sw2, logits=host(dbg["logits"]))
+    assert np.array_equal(host(dbg["topk_ids"]), o["ids"])
+    assert np.array_equal(host(dbg["row_map"]), o["row_map"])
+    return rel_frobenius(host(y), o["y"]), d, dbg, y
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 65])
+def test_few_tokens(T):
+    cfg = moe_inputs.CONFIGS["deepseek_v3"].replace(T=T, H=256, E=16, k=4, F=128, Fs=128)
+    err, *_ = _run_and_check(cfg)
+    assert err <= TOL["bf16"]
+
+
+def test_k_equals_E():
+    cfg = moe_inputs.CONFIGS["qwen3_235b"].replace(T=130, H=128, E=6, k=6, F=128)
+    err, d, dbg, _ = _run_and_check(cfg)
+    assert err <= TOL["bf16"]
+    assert (host(dbg["expert_counts"]) == 130).all()
+
+
+def test_fp32_tiny_against_tolerance():
+    err, *_ = _run_and_check(moe_inputs.CONFIGS["tiny_fp32"].replace(T=33))
+    assert err <= TOL["f32"]
+
+
+def test_forced_routing_one_expert_takes_all_and_empty_experts():
+    """Caller-supplied ids (router replay): experts 3 and 5 get every token, the others none."""
+    cfg = moe_inputs.CONFIGS["mixtral_8x7b"].replace(T=777, H=256, E=8, k=2, F=256)
+    d = moe_inputs.make_inputs(cfg, seed=3, weight_device=DEV, act_device=DEV)
+    ids = torch.tensor([[5, 3]], dtype=torch.int32, device=DEV).repeat(cfg.T, 1)
+    p = moe_gpu.permute(d["x"], ids, cfg.E)
+    yp = moe_gpu.grouped_swiglu(p["x_perm"], p["offsets"], d["w1"], d["w2"])
+    torch.cuda.synchronize()
+    cnt = host(p["counts"])
+    assert cnt.tolist() == [0, 0, 0, 777, 0, 777, 0, 0]
+    check_permutation(host(ids), cnt, host(p["offsets"]), host(p["row_map"]), host(p["src_token"]))
+    x = host(d["x"])
+    ref3 = moe.swiglu_expert(x, weights_of(d["w1"], None, 3), weights_of(d["w2"], None, 3))
+    ref5 = moe.swiglu_expert(x, weights_of(d["w1"], None, 5), weights_of(d["w2"], None, 5))
+    got = host(yp)
+    assert rel_frobenius(got[:777], ref3) <= TOL["bf16"]
+    assert rel_frobenius(got[777:], ref5) <= TOL["bf16"]
+
+
+def test_tie_heavy_router_is_bit_exact():
+    """Integer-valued x and W_r in {-1,0,1}/8: logits are exact, so the GPU logits equal the
+    oracle's and the many exact ties must break to the lower expert index in both."""
+    cfg = moe_inputs.CONFIGS["qwen3_235b"].replace(T=1000, H=512)
+    x, w = moe_inputs.tie_heavy_router(cfg)
+    ids, gates, logits = moe_gpu.route(x.to(DEV), w.to(DEV), cfg.k, cfg.score, cfg.norm, return_logits=True)
+    torch.cuda.synchronize()
+    lo = moe.router_logits(host(x), host(w))
+    assert np.array_equal(host(logits), lo)
+    ref = moe.topk_ids(lo, cfg.k)
+    assert np.array_equal(host(ids), ref)
+    ties = sum(len(np.unique(row)) < len(row) for row in lo)
+    assert ties > 900  # the case really is tie-heavy
+
+
+def test_empty_input():
+    cfg = moe_inputs.CONFIGS["mixtral_8x7b"].replace(T=4, H=128, F=128)
+    d = moe_inputs.make_inputs(cfg, seed=0, weight_device=DEV, act_device=DEV)
+    layer = moe_gpu.Layer.from_inputs(d, cfg.k, cfg.score, cfg.norm)
+    y = moe_gpu.forward(d["x"][:0], layer)
+    assert y.shape == (0, 128)
+
+
+def test_guard_bands_untouched():
+    """Every stage output lives inside a larger buffer filled with a sentinel; only the output
+    region may change."""
+    cfg = moe_inputs.CONFIGS["deepseek_v3"].replace(T=301, H=256, E=16, k=4, F=128, Fs=0)
+    d = moe_inputs.make_inputs(cfg, seed=1, weight_device=DEV, act_device=DEV)
+    pad = 4096
+
+    def guarded(shape, dtype):
+        n = int(np.prod(shape))
+        buf = torch.full((n + 2 * pad,), -7, dtype=torch.int32 if dtype == torch.int32 else torch.float32,
+                         device=DEV)
+        view = buf[pad:pad + n].view(*shape)
+        if dtype not in (torch.int32, torch.float32):
+            raise ValueError(dtype)
+        return buf, view
+
+    ids_b, ids = guarded((cfg.T, cfg.k), torch.int32)
+    g_b, gates = guarded((cfg.T, cfg.k), torch.float32)
+    lg_b, logits = guarded((cfg.T, cfg.E), torch.float32)
+    from mixture_experts_layer_fp32_amd import _lib
+    import ctypes
+    L = _lib.lib()
+    wsb = L.moe_route_workspace_size(cfg.T, cfg.H, cfg.E, 1)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    st = L.moe_route(ctypes.c_void_p(d["x"].data_ptr()), 1, ctypes.c_void_p(d["w_router"].data_ptr()), None,
+                     cfg.T, cfg.H, cfg.E, cfg.k, 1, 1, ctypes.c_void_p(logits.data_ptr()),
+                     ctypes.c_void_p(ids.data_ptr()), ctypes.c_void_p(gates.data_ptr()),
+                     ctypes.c_void_p(ws.data_ptr()), wsb, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    for buf in (ids_b, g_b, lg_b):
+        h = buf.cpu()
+        sentinel = torch.full((pad,), -7, dtype=h.dtype)
+        assert torch.equal(h[:pad], sentinel) and torch.equal(h[-pad:], sentinel)
+    p = moe_gpu.permute(d["x"], ids, cfg.E)
+    R = cfg.T * cfg.k
+    xp_b = torch.full((R * cfg.H + 2 * pad,), 12345, dtype=torch.int16, device=DEV)
+    xp = xp_b[pad:pad + R * cfg.H].view(torch.bfloat16).view(R, cfg.H)
+    yp_b = torch.full((R * cfg.H + 2 * pad,), 12345, dtype=torch.int16, device=DEV)
+    yp = yp_b[pad:pad + R * cfg.H].view(torch.bfloat16).view(R, cfg.H)
+    L.moe_permute(ctypes.c_void_p(d["x"].data_ptr()), 1, ctypes.c_void_p(ids.data_ptr()), cfg.T, cfg.H, cfg.E,
+                  cfg.k, ctypes.c_void_p(xp.data_ptr()), 1, None, ctypes.c_void_p(p["row_map"].data_ptr()),
+                  ctypes.c_void_p(p["src_token"].data_ptr()), None, ctypes.c_void_p(p["offsets"].data_ptr()),
+                  ctypes.c_void_p(torch.empty(L.moe_permute_workspace_size(cfg.T, cfg.E, cfg.k), dtype=torch.uint8,
+                                              device=DEV).data_ptr()),
+                  L.moe_permute_workspace_size(cfg.T, cfg.E, cfg.k),
+                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    gws = L.moe_grouped_swiglu_workspace_size(R, cfg.F, 1)
+    gw = torch.empty(gws, dtype=torch.uint8, device=DEV)
+    st = L.moe_grouped_swiglu(ctypes.c_void_p(xp.data_ptr()), None, 1, ctypes.c_void_p(p["offsets"].data_ptr()), R,
+                              cfg.E, cfg.H, cfg.F, ctypes.c_void_p(d["w1"].data_ptr()), None,
+                              ctypes.c_void_p(d["w2"].data_ptr()), None, ctypes.c_void_p(yp.data_ptr()), 1,
+                              ctypes.c_void_p(gw.data_ptr()), gws,
+                              ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    for buf in (xp_b, yp_b):
+        h = buf.cpu()
+        sentinel = torch.full((pad,), 12345, dtype=torch.int16)
+        assert torch.equal(h[:pad], sentinel) and torch.equal(h[-pad:], sentinel)
+    assert not (yp.view(torch.int16) == 12345).all(dim=1).any()  # every row was written
+
+
+def test_hip_graph_capture_and_replay():
+    """The fused forward records into a HIP graph (no sync, no allocation inside) and every
+    replay, with eager work in between, reproduces the eager result bit for bit."""
+    cfg = moe_inputs.CONFIGS["deepseek_v3"].replace(T=512, H=256, E=16, k=4, F=128, Fs=128)
+    d = moe_inputs.make_inputs(cfg, seed=2, weight_device=DEV, act_device=DEV)
+    layer = moe_gpu.Layer.from_inputs(d, cfg.k, cfg.score, cfg.norm)
+    ws = torch.empty(moe_gpu.workspace_size(layer, cfg.T, d["x"].dtype), dtype=torch.uint8, device=DEV)
+    x = d["x"].clone()
+    eager = moe_gpu.forward(x, layer, workspace=ws).clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe_gpu.forward(x, layer, workspace=ws)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        y_g = moe_gpu.forward(x, layer, workspace=ws)
+    for rep in range(3):
+        junk = torch.randn(1000, 1000, device=DEV) @ torch.randn(1000, 1000, device=DEV)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        del junk
