@@ -28,6 +28,25 @@ METRIC = "MoE-layer fwd active TFLOPS + tokens/s at 1 GPU; % of MFMA / HBM peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 STAGES = ["route", "permute", "gemm1_swiglu", "gemm2", "shared_expert", "combine"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_swiglu_mixtral_8x7b_hbm_traffic.txt")
+GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_fp32_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the first grouped GEMM from the committed PMC summary, or None
+    when the kernel source changed since the counters were taken."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if kv.get("gemm_source_sha256") != sha or "traffic_bytes_per_launch" not in kv:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
 
 
 def _hip():
@@ -81,8 +100,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=64)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (for scaling HBM counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -90,6 +111,14 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": 1 << 30, "launches": args.steps}))
+        return
     import moe_inputs
     import mixture_experts_layer_fp32_amd as moe_gpu
     from mixture_experts_layer_fp32_amd import _lib
@@ -166,9 +195,9 @@ def main():
         stages[s] = rec
     g1 = alg["gemm1_swiglu"]
     g1_tflops = g1["flops"] / (avg_ms["gemm1_swiglu"] * 1e-3) / 1e12
-    roofline = {"kernel": "gemm_bf16_kernel<128,swiglu> (grouped GEMM1 + fused SwiGLU)", "bound": "mfma",
+    roofline = {"kernel": "gemm_bf16_kernel<256,swiglu> (grouped GEMM1 + fused SwiGLU)", "bound": "mfma",
                 "achieved": round(g1_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(g1_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(g1_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                 "flops_per_launch": g1["flops"], "avg_launch_us": round(avg_ms["gemm1_swiglu"] * 1e3, 2)}
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
