@@ -264,9 +264,15 @@ moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, co
   if (e == hipSuccess) e = mark(4);
   if (e != hipSuccess) return from_hip(e);
   if (L->Fs > 0) {
-    if (fp8) return MOE_ERR_UNSUPPORTED;  // shared expert input quantisation: not built yet
-    e = moe::launch_grouped_swiglu(x, nullptr, L->w_dt, nullptr, T, 1, L->H, L->Fs, L->ws1, L->ws1_scales,
-                                   L->ws2, L->ws2_scales, p.sh_out, L->x_dt, p.sh_ws, s);
+    const void* sx = x;
+    if (fp8) {  // the shared expert sees every token, quantised like the routed rows
+      e = moe::launch_quant_rows_fp8(x, L->x_dt, T, L->H, static_cast<uint8_t*>(p.sh_x),
+                                     static_cast<float*>(p.sh_scales), s);
+      if (e != hipSuccess) return from_hip(e);
+      sx = p.sh_x;
+    }
+    e = moe::launch_grouped_swiglu(sx, static_cast<float*>(p.sh_scales), L->w_dt, nullptr, T, 1, L->H, L->Fs,
+                                   L->ws1, L->ws1_scales, L->ws2, L->ws2_scales, p.sh_out, L->x_dt, p.sh_ws, s);
     if (e != hipSuccess) return from_hip(e);
   }
   e = mark(5);

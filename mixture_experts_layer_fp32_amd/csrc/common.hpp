@@ -110,6 +110,18 @@ hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int 
                                  const float* w2_scales, void* y_perm, int out_dt, void* scratch,
                                  hipStream_t stream, hipEvent_t between = nullptr);
 
+// FP8 (E4M3) path: x_perm codes + [rows, H/128] scales, weights as codes + 128x128-block scales;
+// the SwiGLU output h is re-quantised to E4M3 in 1x128 blocks in the scratch buffer
+// (fp8_hidden_bytes(rows, F) bytes of codes, then [rows, F/128] fp32 scales).
+size_t fp8_hidden_bytes(int64_t rows, int F);
+hipError_t launch_grouped_swiglu_fp8(const void* x_perm, const float* x_scales, const int32_t* offsets,
+                                     int64_t rows, int E, int H, int F, const void* w1, const float* w1_scales,
+                                     const void* w2, const float* w2_scales, void* y_perm, int out_dt,
+                                     void* scratch, hipStream_t stream, hipEvent_t between);
+// Per-row 1x128 E4M3 quantisation of a dense [T, H] bf16 / fp32 matrix (shared-expert input).
+hipError_t launch_quant_rows_fp8(const void* x, int x_dt, int64_t T, int H, uint8_t* codes, float* scales,
+                                 hipStream_t stream);
+
 hipError_t launch_combine(const void* y_perm, int y_dt, const int32_t* row_map, const float* gates,
                           const void* shared_out, int64_t T, int H, int k, void* y, int out_dt,
                           hipStream_t stream);

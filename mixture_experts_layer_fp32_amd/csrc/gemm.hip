@@ -21,85 +21,15 @@
 // prefetched into registers during the MFMAs.  In SwiGLU mode a tile's 256 columns are 128
 // gate columns and the matching 128 up columns, placed so a lane holds gate and up of the
 // same (row, column) in the same accumulator slot.
-#include "common.hpp"
+#include "gemm_common.hpp"
 
 namespace moe {
 namespace {
 
+using namespace gemm;
+
 constexpr int kThreads = 256;  // fp32 path
-constexpr int kBN = 256;  // N per tile (SwiGLU: 128 gate + 128 up)
-constexpr int kMaxExpertsLds = 520;  // >= E + 1 for E <= 512
 
-
-// Per-workgroup tile lookup built from the device-resident expert offsets.
-struct TileMap {
-  int expert, mt, nt;
-  int64_t row0, row_end;  // this tile's first row and the expert's end row
-};
-
-// Returns false if this workgroup has no tile.  `s_pref` is LDS of >= E+1 ints.
-template <int BM>
-__device__ bool map_tile(const int32_t* offsets, int64_t rows, int E, int NT, int* s_pref, TileMap& tm) {
-  const int tid = threadIdx.x;
-  if (offsets == nullptr) {  // one dense expert over rows [0, rows)
-    const int mtiles = static_cast<int>(ceil_div(rows, BM));
-    const int total = mtiles * NT;
-    const int per = (total + 7) / 8;
-    const int w = blockIdx.x;
-    if (w >= 8 * per) return false;
-    const int L = (w % 8) * per + w / 8;
-    if (L >= total) return false;
-    tm.expert = 0;
-    tm.nt = L / mtiles;
-    tm.mt = L % mtiles;
-    tm.row0 = static_cast<int64_t>(tm.mt) * BM;
-    tm.row_end = rows;
-    return true;
-  }
-  // m-tiles per expert, exclusive prefix in s_pref[0..E]
-  for (int e = tid; e < E; e += static_cast<int>(blockDim.x)) {
-    int c = offsets[e + 1] - offsets[e];
-    s_pref[e + 1] = (c + BM - 1) / BM;
-  }
-  if (tid == 0) s_pref[0] = 0;
-  __syncthreads();
-  if (tid < kWave) {  // one wave scans E <= 512 entries in chunks of 64
-    int carry = 0;
-    for (int base = 1; base <= E; base += kWave) {
-      int i = base + tid;
-      int v = i <= E ? s_pref[i] : 0;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        int u = __shfl_up(v, o, kWave);
-        if (tid >= o) v += u;
-      }
-      if (i <= E) s_pref[i] = v + carry;
-      carry += __shfl(v, kWave - 1, kWave);
-    }
-  }
-  __syncthreads();
-  const int total = s_pref[E] * NT;
-  const int per = (total + 7) / 8;
-  const int w = blockIdx.x;
-  if (w >= 8 * per) return false;
-  const int L = (w % 8) * per + w / 8;  // consecutive L of one XCD share weights / rows
-  if (L >= total) return false;
-  // expert whose tile range [s_pref[e]*NT, s_pref[e+1]*NT) holds L (binary search in LDS)
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (s_pref[mid] * NT <= L) lo = mid; else hi = mid - 1;
-  }
-  const int e = lo;
-  const int me = s_pref[e + 1] - s_pref[e];
-  const int idx = L - s_pref[e] * NT;
-  tm.expert = e;
-  tm.nt = idx / me;  // n-major inside an expert: the m-tiles of one weight tile are adjacent
-  tm.mt = idx % me;
-  tm.row0 = static_cast<int64_t>(offsets[e]) + static_cast<int64_t>(tm.mt) * BM;
-  tm.row_end = offsets[e + 1];
-  return true;
-}
 
 // ------------------------------------------------------------------------------ bf16 path
 // A: [rows, K] bf16 row-major (x_perm or h).  B: per expert [K, N] bf16 (N-contiguous, the
@@ -130,50 +60,7 @@ __device__ bool map_tile(const int32_t* offsets, int64_t rows, int E, int NT, in
 // Loads are unconditional: rows past the expert's end re-read its last row and column groups
 // past the matrix edge re-read column 0; those results are never stored.
 constexpr int kBKT = 64;        // K per iteration / stage
-constexpr int kGemmThreads = 512;  // 8 waves, two per SIMD
 constexpr int kBRow = kBN * 2;  // bytes per [K, N] B k-row
-
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// 16 bytes per lane from global memory straight into LDS at lds_addr + 16 * lane
-// (global_load_lds_dwordx4).  Issued through asm so the compiler does not insert its own
-// conservative vmcnt waits before unrelated LDS reads; completion is tracked explicitly with
-// wait_vmcnt (vmcnt retires loads in issue order, so the compiler's own counts stay safe).
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
-  // an SALU write of M0 needs one wait state before an LDS-DMA load reads it
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr)
-               : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  // gfx9 s_waitcnt encoding: vmcnt [3:0] + [15:14], expcnt [6:4] (7 = no wait), lgkmcnt [11:8] (15)
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14)); }
-
-// Scheduling groups for one k-step: NM MFMAs, each followed by up to RPM of the NR LDS reads.
-template <int Q, int NM, int NR, int RPM>
-__device__ __forceinline__ void sched_mfma_reads() {
-  if constexpr (Q < NM) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    constexpr int left = NR - Q * RPM;
-    constexpr int nr = left < RPM ? left : RPM;
-    if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);  // LDS reads
-    sched_mfma_reads<Q + 1, NM, NR, RPM>();
-  }
-}
-
-// SiLU for the epilogue: z * 1 / (1 + 2^(-z log2 e)) with the hardware exp2 and reciprocal
-// (about 1e-6 relative error, far below the bf16 rounding of h).
-__device__ __forceinline__ float silu_fast(float z) {
-  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
-}
 
 template <int BM, bool SWIGLU, bool OUT_F32, bool B_NK>
 __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
@@ -483,16 +370,6 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(const float* __restr
   }
 }
 
-template <int BM>
-int64_t max_tiles(int64_t rows, int E, bool dense) {
-  return dense ? ceil_div(rows, BM) : (rows + static_cast<int64_t>(E) * (BM - 1)) / BM;
-}
-
-unsigned grid_for(int64_t mtiles, int NT) {
-  int64_t g = mtiles * NT;
-  return static_cast<unsigned>(ceil_div(g, 8) * 8);
-}
-
 template <int BM, bool SWIGLU, bool OUT_F32, bool B_NK = false>
 hipError_t launch_bf16(const bf16_t* A, const bf16_t* B, const int32_t* offsets, int64_t rows, int E,
                        int K, int ldb, int NT, void* out, hipStream_t stream) {
@@ -529,9 +406,8 @@ hipError_t launch_bf16_pair(const void* x_perm, const void* w1, const void* w2, 
 size_t grouped_swiglu_scratch_bytes(int64_t rows, int F, int dt) {
   if (dt == 0) return static_cast<size_t>(rows) * F * 4;
   if (dt == 1) return static_cast<size_t>(rows) * F * 2;
-  // fp8: codes + 1x128 scales
-  size_t a = (static_cast<size_t>(rows) * F + 255) & ~static_cast<size_t>(255);
-  return a + static_cast<size_t>(rows) * (F / 128) * 4;
+  // fp8: h codes + their 1x128 scales
+  return fp8_hidden_bytes(rows, F) + static_cast<size_t>(rows) * (F / 128) * 4;
 }
 
 hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int dt,
@@ -539,7 +415,9 @@ hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int 
                                  const void* w1, const float* w1_scales, const void* w2,
                                  const float* w2_scales, void* y_perm, int out_dt, void* scratch,
                                  hipStream_t stream, hipEvent_t between) {
-  (void)x_scales; (void)w1_scales; (void)w2_scales;
+  if (dt == 2)
+    return launch_grouped_swiglu_fp8(x_perm, x_scales, offsets, rows, E, H, F, w1, w1_scales, w2, w2_scales,
+                                     y_perm, out_dt, scratch, stream, between);
   if (dt == 0) {
     float* h = static_cast<float*>(scratch);
     const int nt1 = F / 32, nt2 = static_cast<int>(ceil_div(H, kF32BN));

@@ -133,6 +133,33 @@ __global__ __launch_bounds__(kScatterThreads) void perm_scatter_copy_kernel(
   }
 }
 
+// 8 bf16 values of a lane -> 8 e4m3 codes, with one fp32 scale per 1x128 block shared by the
+// 16 lanes that hold the block (lanes 16g .. 16g+15 of the wave).  Lanes with live == false
+// contribute zeros to the block maximum.
+__device__ __forceinline__ uint2 quant_e4m3_x8(uint4 v, float& scale) {
+  uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(wv[i] << 16);
+    f[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
+    amax = fmaxf(amax, fmaxf(fabsf(f[2 * i]), fabsf(f[2 * i + 1])));
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;  // correctly rounded fp32 division
+  uint32_t q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float r = f[i] / s;
+    r = fminf(fmaxf(r, -448.0f), 448.0f);
+    q[i] = f32_to_e4m3(r);
+  }
+  scale = s;
+  return make_uint2(q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24), q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24));
+}
+
 // bf16 -> e4m3 with one fp32 scale per 1x128 block (16 lanes x 8 values).
 __global__ __launch_bounds__(kScatterThreads) void perm_scatter_fp8_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ ids, const int32_t* __restrict__ base,
@@ -150,34 +177,35 @@ __global__ __launch_bounds__(kScatterThreads) void perm_scatter_fp8_kernel(
   for (int c0 = 0; c0 < row_vecs; c0 += kWave) {  // H % 128 == 0: whole 16-lane groups
     const int c = c0 + lane;
     const bool live = c < row_vecs;
-    float f[8];
-    float amax = 0.0f;
-    uint4 v = live ? src[c] : make_uint4(0, 0, 0, 0);
-    uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __uint_as_float(wv[i] << 16);
-      f[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
-      amax = fmaxf(amax, fmaxf(fabsf(f[2 * i]), fabsf(f[2 * i + 1])));
-    }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
-    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;  // correctly rounded fp32 division
-    uint32_t q[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float r = f[i] / s;
-      r = fminf(fmaxf(r, -448.0f), 448.0f);
-      q[i] = f32_to_e4m3(r);
-    }
-    uint2 packed = make_uint2(q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
-                              q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24));
+    float s;
+    const uint2 packed = quant_e4m3_x8(live ? src[c] : make_uint4(0, 0, 0, 0), s);
     for (int j = 0; j < k; ++j) {
       int r = __shfl(row, j, kWave);
       if (live) {
         x_perm[static_cast<int64_t>(r) * row_vecs + c] = packed;
         if ((lane & 15) == 0) scales[static_cast<int64_t>(r) * nsb + c / 16] = s;
       }
+    }
+  }
+}
+
+// Dense per-row quantisation (the shared expert's input): one wavefront per row.
+__global__ __launch_bounds__(kScatterThreads) void quant_rows_fp8_kernel(const uint4* __restrict__ x, int64_t T,
+                                                                          int H, uint2* __restrict__ codes,
+                                                                          float* __restrict__ scales) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + threadIdx.x / kWave;
+  if (t >= T) return;
+  const int row_vecs = H / 8;
+  const int nsb = H / 128;
+  for (int c0 = 0; c0 < row_vecs; c0 += kWave) {
+    const int c = c0 + lane;
+    const bool live = c < row_vecs;
+    float s;
+    const uint2 packed = quant_e4m3_x8(live ? x[t * row_vecs + c] : make_uint4(0, 0, 0, 0), s);
+    if (live) {
+      codes[t * row_vecs + c] = packed;
+      if ((lane & 15) == 0) scales[t * nsb + c / 16] = s;
     }
   }
 }
@@ -217,6 +245,16 @@ hipError_t launch_permute(const void* x, int x_dt, const int32_t* ids, int64_t T
                        static_cast<const uint4*>(x), ids, blk, local_rank, T, row_vecs, k, nblk,
                        static_cast<uint4*>(x_perm), row_map, src_token);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_fp8(const void* x, int x_dt, int64_t T, int H, uint8_t* codes, float* scales,
+                                 hipStream_t stream) {
+  if (x_dt != 1 || H % 128 != 0) return hipErrorInvalidValue;
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3(static_cast<unsigned>(ceil_div(T, kTokPerBlock))),
+                     dim3(kScatterThreads), 0, stream, static_cast<const uint4*>(x), T, H,
+                     reinterpret_cast<uint2*>(codes), scales);
   return hipGetLastError();
 }
 

@@ -4,7 +4,8 @@ Per workload (seed 0): router logits vs the float64 oracle on all tokens; expert
 counts, offsets, row_map and src_token from the GPU's own logits (bit-exact, all tokens);
 permuted rows exact (all rows); expert outputs on every row of three sampled experts (the
 busiest, the least busy non-empty one and one drawn at random); combine on all tokens from the
-GPU's own expert outputs; the shared expert on sampled tokens.
+GPU's own expert outputs; the shared expert on sampled tokens.  In FP8 the permuted rows are
+compared as E4M3 codes + 1x128 scales against the oracle's quantiser, bit for bit.
 """
 
 import numpy as np
@@ -13,7 +14,7 @@ import torch
 
 import moe_inputs
 import mixture_experts_layer_fp32_amd as moe_gpu
-from oracle import moe
+from oracle import e4m3, moe
 from tests.checks import check_permutation, rel_frobenius
 from tests.gpu_oracle import TOL, TOL_GATES, TOL_LOGITS, host, routing_from_logits, weights_of
 
@@ -25,7 +26,7 @@ def _tol(cfg):
     return TOL["fp8" if cfg.w_dtype == "fp8" else cfg.act_dtype]
 
 
-@pytest.mark.parametrize("name", ["mixtral_8x7b", "qwen3_235b", "deepseek_v3"])
+@pytest.mark.parametrize("name", ["mixtral_8x7b", "qwen3_235b", "deepseek_v3", "deepseek_v3_fp8_zipf"])
 def test_full_size_layer(name):
     cfg = moe_inputs.CONFIGS[name]
     print(f"[parity-full] {name}: {cfg.description}", flush=True)
@@ -49,8 +50,22 @@ def test_full_size_layer(name):
                      ("src_token", "src_token")):
         assert np.array_equal(host(dbg[key]), r[ref]), key
     check_permutation(r["ids"], r["counts"], r["offsets"], r["row_map"], r["src_token"])
-    xp = host(dbg["x_perm"])
-    assert np.array_equal(xp, x[r["src_token"]])
+    fp8 = cfg.w_dtype == "fp8"
+    if fp8:  # E4M3 codes and 1x128 scales of every permuted row, bit-exact
+        codes, scales = e4m3.quantise_rows_1x128(x)
+        assert np.array_equal(host(dbg["x_perm"]), codes[r["src_token"]])
+        assert np.array_equal(host(dbg["x_perm_scales"]), scales[r["src_token"]])
+        x_hat = e4m3.dequantise_rows_1x128(codes, scales)
+        del codes, scales
+
+        def rows_of(a, b):
+            return x_hat[r["src_token"][a:b]]
+    else:
+        xp = host(dbg["x_perm"])
+        assert np.array_equal(xp, x[r["src_token"]])
+
+        def rows_of(a, b):
+            return xp[a:b]
     # experts: every row of three sampled experts
     cnt, off = r["counts"], r["offsets"]
     nonzero = np.nonzero(cnt)[0]
@@ -60,7 +75,7 @@ def test_full_size_layer(name):
     errs = []
     for e in picks:
         a, b = int(off[e]), int(off[e + 1])
-        ref = moe.swiglu_expert(xp[a:b], weights_of(d["w1"], d["w1_scales"], e), weights_of(d["w2"], d["w2_scales"], e))
+        ref = moe.swiglu_expert(rows_of(a, b), weights_of(d["w1"], d["w1_scales"], e), weights_of(d["w2"], d["w2_scales"], e))
         errs.append(rel_frobenius(host(yp[a:b]), ref))
     print(f"[parity-full] {name}: experts {picks} rows {[int(cnt[e]) for e in picks]} rel_frob {errs}", flush=True)
     assert max(errs) <= _tol(cfg)
@@ -68,10 +83,21 @@ def test_full_size_layer(name):
     shared = None
     if cfg.Fs:
         sel = rng.choice(cfg.T, 64, replace=False)
-        s_ref = moe.swiglu_expert(x[sel], weights_of(d["ws1"], d["ws1_scales"], None),
-                                  weights_of(d["ws2"], d["ws2_scales"], None))
         off1 = torch.tensor([0, cfg.T], dtype=torch.int32, device=DEV)
-        s_gpu = moe_gpu.grouped_swiglu(d["x"], off1, d["ws1"].unsqueeze(0), d["ws2"].unsqueeze(0))
+        if fp8:  # every token on one expert: permute() is the dense 1x128 quantiser
+            xs = e4m3.dequantise_rows_1x128(*e4m3.quantise_rows_1x128(x[sel]))
+            s_ref = moe.swiglu_expert(xs, weights_of(d["ws1"], d["ws1_scales"], None),
+                                      weights_of(d["ws2"], d["ws2_scales"], None))
+            q = moe_gpu.permute(d["x"], torch.zeros(cfg.T, 1, dtype=torch.int32, device=DEV), 1,
+                                perm_dtype=torch.float8_e4m3fn)
+            s_gpu = moe_gpu.grouped_swiglu(q["x_perm"], off1, d["ws1"].unsqueeze(0), d["ws2"].unsqueeze(0),
+                                           x_perm_scales=q["x_perm_scales"],
+                                           w1_scales=d["ws1_scales"].unsqueeze(0),
+                                           w2_scales=d["ws2_scales"].unsqueeze(0))
+        else:
+            s_ref = moe.swiglu_expert(x[sel], weights_of(d["ws1"], d["ws1_scales"], None),
+                                      weights_of(d["ws2"], d["ws2_scales"], None))
+            s_gpu = moe_gpu.grouped_swiglu(d["x"], off1, d["ws1"].unsqueeze(0), d["ws2"].unsqueeze(0))
         torch.cuda.synchronize()
         shared = host(s_gpu)
         assert rel_frobenius(shared[sel], s_ref) <= _tol(cfg)
