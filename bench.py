@@ -1,15 +1,17 @@
 """Benchmark: dropless MoE layer forward on one MI355X.
 
-Workload: the Mixtral-8x7B-shaped layer (T=4096 tokens, H=4096, E=8 experts, top-2 softmax
-router in fp32, SwiGLU F=14336, bf16 activations and weights), synthetic seeded inputs resident
-in HBM.  One step = one full layer forward through the library's fused entry point
-(route -> permute -> grouped SwiGLU GEMMs -> combine).
+Default workload: the Mixtral-8x7B-shaped layer (T=4096 tokens, H=4096, E=8 experts, top-2
+softmax router in fp32, SwiGLU F=14336, bf16 activations and weights), synthetic seeded inputs
+resident in HBM.  One step = one full layer forward through the library's fused entry point
+(route -> permute -> grouped SwiGLU GEMMs -> shared expert -> combine).  ``--workload`` selects
+another of the layer shapes (Qwen3-235B, DeepSeek-V3 in bf16 or with e4m3 experts, the tiny fp32
+layer) for the same measurement.
 
 Prints ONE JSON line: tokens/s over the timed steps, active TFLOP/s, per-stage times from HIP
 events recorded by the library on the compute stream, the roofline of the dominant kernel (the
 first grouped GEMM with the fused SwiGLU epilogue), and the CPU oracle timed on a bounded sample.
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -25,7 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer fwd active TFLOPS + tokens/s at 1 GPU; % of MFMA / HBM peak"
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA by operand type
+PEAK_BF16_TFLOPS = PEAK_TFLOPS["bf16"]
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 STAGES = ["route", "permute", "gemm1_swiglu", "gemm2", "shared_expert", "combine"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_swiglu_mixtral_8x7b_hbm_traffic.txt")
@@ -58,41 +61,76 @@ def _hip():
     return h
 
 
-def algorithmic(cfg):
-    """Useful FLOPs and the bytes each stage must move at the ABI boundary (bf16 = 2 B)."""
+def algorithmic(cfg, active_experts=None):
+    """Useful FLOPs and the bytes each stage must move at the ABI boundary.
+
+    Activations in the config's dtype (bf16 2 B, fp32 4 B); weights and the permuted / hidden
+    rows of the e4m3 path 1 B plus one fp32 scale per 128 values (weights: per 128 x 128 block).
+    Only experts that received rows are streamed (``active_experts``, default all E).
+    """
     T, H, E, k, F, Fs = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
     R = T * k
-    a = 2  # bf16 bytes
+    Ea = E if active_experts is None else active_experts
+    fp8 = cfg.w_dtype == "fp8"
+    a = 4 if cfg.act_dtype == "f32" else 2
+    rowb = (lambda n: n + n // 128 * 4) if fp8 else (lambda n: n * a)   # one row of n values
+    wbytes = (lambda K, N: K * N + (K // 128) * (N // 128) * 4) if fp8 else (lambda K, N: K * N * a)
+    sh = bool(Fs)
     return {
-        "route": dict(flops=2 * T * H * E, bytes=T * H * a + H * E * 4 + R * 8),
-        "permute": dict(flops=0, bytes=T * H * a + R * 4 + R * H * a + R * 8 + (E + 1) * 4),
-        "gemm1_swiglu": dict(flops=4 * R * H * F, bytes=R * H * a + E * H * 2 * F * a + R * F * a),
-        "gemm2": dict(flops=2 * R * F * H, bytes=R * F * a + E * F * H * a + R * H * a),
-        "shared_expert": dict(flops=6 * T * H * Fs, bytes=(T * H * a * 2 + 3 * H * Fs * a) if Fs else 0),
-        "combine": dict(flops=0, bytes=R * H * a + R * 8 + T * H * a),
+        "route": dict(flops=2 * T * H * E, bytes=T * H * a + H * E * 4 + R * 8 + (E * 4 if cfg.zipf_bias else 0)),
+        "permute": dict(flops=0, bytes=T * H * a + R * 4 + R * rowb(H) + R * 8 + (2 * E + 1) * 4),
+        "gemm1_swiglu": dict(flops=4 * R * H * F, bytes=R * rowb(H) + Ea * wbytes(H, 2 * F) + R * rowb(F) + (E + 1) * 4),
+        "gemm2": dict(flops=2 * R * F * H, bytes=R * rowb(F) + Ea * wbytes(F, H) + R * H * a + (E + 1) * 4),
+        "shared_expert": dict(flops=6 * T * H * Fs,
+                              bytes=(T * H * a + (T * rowb(H) * 2 if fp8 else 0) + wbytes(H, 2 * Fs) + wbytes(Fs, H)
+                                     + 2 * T * rowb(Fs) + T * H * a) if sh else 0),
+        "combine": dict(flops=0, bytes=R * H * a + R * 8 + T * H * a + (T * H * a if sh else 0)),
         "active_flops": 2 * T * H * E + 6 * R * H * F + 6 * T * H * Fs,
     }
 
 
 def cpu_baseline(cfg, d, sample_tokens):
-    """The float64 oracle (as it stands) on the first `sample_tokens` tokens of the same layer."""
-    import numpy as np
-    from oracle import moe
+    """The float64 oracle (as it stands) on the first `sample_tokens` tokens of the same layer.
+
+    Expert weights are copied to the host one expert at a time when the oracle asks for them
+    (dequantised by the oracle's own e4m3 decoder for the e4m3 workload); that copy is timed
+    apart and left out of the reported rate.
+    """
+    import torch
+    from oracle import e4m3, moe
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
-    x = d["x"][:sample_tokens].float().cpu().numpy()
+    fp8 = cfg.w_dtype == "fp8"
+    copy_s = [0.0]
+
+    def weight(w, scales):
+        t0 = time.perf_counter()
+        if fp8:
+            out = e4m3.dequantise_blocks_128x128(w.view(torch.uint8).cpu().numpy(), scales.cpu().numpy())
+        else:
+            out = w.float().cpu().numpy()
+        copy_s[0] += time.perf_counter() - t0
+        return out
+
+    x = d["x"][:sample_tokens].float().cpu().numpy()  # bf16 widened exactly
     wr = d["w_router"].cpu().numpy()
-    w1 = [d["w1"][e].float().cpu().numpy() for e in range(cfg.E)]
-    w2 = [d["w2"][e].float().cpu().numpy() for e in range(cfg.E)]
+    bias = None if d["bias"] is None else d["bias"].cpu().numpy()
+    sw1 = sw2 = None
+    if cfg.Fs:
+        sw1 = weight(d["ws1"], d["ws1_scales"])
+        sw2 = weight(d["ws2"], d["ws2_scales"])
+    copy_s[0] = 0.0
     t0 = time.perf_counter()
-    moe.forward(x, wr, lambda e: w1[e], lambda e: w2[e], E=cfg.E, k=cfg.k, score=cfg.score, norm=cfg.norm)
-    dt = time.perf_counter() - t0
+    moe.forward(x, wr, lambda e: weight(d["w1"][e], None if d["w1_scales"] is None else d["w1_scales"][e]),
+                lambda e: weight(d["w2"][e], None if d["w2_scales"] is None else d["w2_scales"][e]),
+                E=cfg.E, k=cfg.k, score=cfg.score, norm=cfg.norm, bias=bias, shared_w1=sw1, shared_w2=sw2, fp8=fp8)
+    dt = time.perf_counter() - t0 - copy_s[0]
     return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {sample_tokens} tokens of the same layer (all {cfg.E} experts' weights widened "
-                      f"to float64 inside the oracle); {dt:.1f} s wall"}
+            "sample": f"first {sample_tokens} tokens of the same layer; float64 oracle {dt:.1f} s wall "
+                      f"(+{copy_s[0]:.1f} s copying the experts it used to the host, not counted)"}
 
 
 def main():
@@ -100,7 +138,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--workload", default="mixtral_8x7b",
+                    help="layer shape: mixtral_8x7b (default), qwen3_235b, deepseek_v3, deepseek_v3_fp8_zipf, tiny_fp32")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=None,
+                    help="tokens in the CPU oracle sample (default: about 10-30 s of oracle work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM counters) and exit")
@@ -123,7 +164,7 @@ def main():
     import mixture_experts_layer_fp32_amd as moe_gpu
     from mixture_experts_layer_fp32_amd import _lib
 
-    cfg = moe_inputs.CONFIGS["mixtral_8x7b"]
+    cfg = moe_inputs.CONFIGS[args.workload]
     dev = "cuda"
     d = moe_inputs.make_inputs(cfg, seed=0, weight_device=dev, act_device=dev)
     layer = moe_gpu.Layer.from_inputs(d, cfg.k, cfg.score, cfg.norm)
@@ -132,7 +173,7 @@ def main():
     L = _lib.lib()
     need = L.moe_workspace_size(ctypes.byref(c_layer), cfg.T)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
-    y = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(cfg.T, cfg.H, dtype=x.dtype, device=dev)
     stream = torch.cuda.current_stream()
     hip = _hip()
     K, W = args.steps, args.warmup
@@ -175,10 +216,21 @@ def main():
         for ev in row:
             hip.hipEventDestroy(ev)
     avg_ms = {s: sum(v) / len(v) for s, v in stage_ms.items()}
-    alg = algorithmic(cfg)
+    counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+    dbg = _lib.MoeDebugC()
+    dbg.expert_counts = counts.data_ptr()
+    _lib.check("moe_forward", L.moe_forward(ctypes.byref(c_layer), ctypes.c_void_p(x.data_ptr()), cfg.T,
+                                            ctypes.c_void_p(y.data_ptr()), ctypes.byref(dbg),
+                                            ctypes.c_void_p(ws.data_ptr()), need,
+                                            ctypes.c_void_p(stream.cuda_stream)))
+    torch.cuda.synchronize()
+    active = int((counts > 0).sum().item())
+    alg = algorithmic(cfg, active)
     ms_per_step = elapsed * 1e3 / K
     tokens_per_s = cfg.T * K / elapsed
     active_tflops = alg["active_flops"] / (ms_per_step * 1e-3) / 1e12
+    mm_dtype = "fp8" if cfg.w_dtype == "fp8" else cfg.act_dtype
+    peak_tf = PEAK_TFLOPS[mm_dtype]
 
     stages = {}
     for s in STAGES:
@@ -188,30 +240,43 @@ def main():
         rec = {"us": round(ms * 1e3, 2), "GB_s": round(alg[s]["bytes"] / (ms * 1e-3) / 1e9, 1)}
         if alg[s]["flops"]:
             rec["TFLOP_s"] = round(alg[s]["flops"] / (ms * 1e-3) / 1e12, 1)
-        if s.startswith("gemm"):
-            rec["frac_mfma_peak"] = round(rec["TFLOP_s"] / PEAK_BF16_TFLOPS, 4)
-        else:
-            rec["frac_hbm_peak"] = round(rec["GB_s"] / PEAK_HBM_GBS, 4)
+        if s.startswith("gemm") or s == "shared_expert":
+            rec["frac_mfma_peak"] = round(rec["TFLOP_s"] / peak_tf, 4)
+        rec["frac_hbm_peak"] = round(rec["GB_s"] / PEAK_HBM_GBS, 4)
         stages[s] = rec
+    # dominant kernel: the first grouped GEMM; its binding roof is the larger of the two ideal times
     g1 = alg["gemm1_swiglu"]
-    g1_tflops = g1["flops"] / (avg_ms["gemm1_swiglu"] * 1e-3) / 1e12
-    roofline = {"kernel": "gemm_bf16_kernel<256,swiglu> (grouped GEMM1 + fused SwiGLU)", "bound": "mfma",
-                "achieved": round(g1_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(g1_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
-                "flops_per_launch": g1["flops"], "avg_launch_us": round(avg_ms["gemm1_swiglu"] * 1e3, 2)}
+    g1_s = avg_ms["gemm1_swiglu"] * 1e-3
+    mfma_bound = g1["flops"] / (peak_tf * 1e12) >= g1["bytes"] / (PEAK_HBM_GBS * 1e9)
+    kernel = {"fp8": "gemm_fp8_kernel<swiglu> (grouped e4m3 GEMM1 + fused SwiGLU + 1x128 re-quantisation)",
+              "bf16": "gemm_bf16_kernel<swiglu> (grouped GEMM1 + fused SwiGLU)",
+              "f32": "gemm_f32_kernel<swiglu> (grouped fp32 GEMM1 + fused SwiGLU)"}[mm_dtype]
+    if mfma_bound:
+        achieved, peak, unit = g1["flops"] / g1_s / 1e12, peak_tf, "TFLOP/s"
+    else:
+        achieved, peak, unit = g1["bytes"] / g1_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    roofline = {"kernel": kernel, "bound": "mfma" if mfma_bound else "hbm", "achieved": round(achieved, 1),
+                "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                "traffic": measured_traffic() if args.workload == "mixtral_8x7b" else None,
+                "flops_per_launch": g1["flops"], "algorithmic_bytes_per_launch": g1["bytes"],
+                "avg_launch_us": round(avg_ms["gemm1_swiglu"] * 1e3, 2)}
+    router = f"fp32 {cfg.score} top-{cfg.k}" + (" renormalised" if cfg.norm else "") + \
+        (" + Zipf(1.2) selection bias" if cfg.zipf_bias else "")
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": mm_dtype, "data": "synthetic",
         "config": {"workload": cfg.description, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "F": cfg.F,
-                   "router": "fp32 softmax top-2", "parallelism": "single GPU"},
+                   "Fs": cfg.Fs, "router": router, "experts_with_rows": active, "parallelism": "single GPU"},
         "active_tflops": round(active_tflops, 1),
-        "frac_bf16_mfma_peak": round(active_tflops / PEAK_BF16_TFLOPS, 4),
+        "frac_mfma_peak": round(active_tflops / peak_tf, 4),
         "stages": stages,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_sample_tokens)
+        default_sample = {"mixtral_8x7b": 1024, "qwen3_235b": 256, "deepseek_v3": 128,
+                          "deepseek_v3_fp8_zipf": 128, "tiny_fp32": 256}
+        out["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_sample_tokens or default_sample[args.workload])
     print(json.dumps(out), flush=True)
 
 

@@ -13,14 +13,12 @@
 // and every workgroup rebuilds the per-expert m-tile prefix from the offsets in LDS, maps its
 // (XCD-remapped) linear id to (expert, m-tile, n-tile), and exits if it has none.
 //
-// bf16 kernel (gfx950): 256 threads = 4 waves in a 2 x 2 grid, tile BM x 256 x 64, MFMA
-// v_mfma_f32_32x32x16_bf16.  Both LDS tiles are stored K-contiguous (row-major A as loaded;
-// the N-contiguous weight tile transposed in registers, 8 x 8 bf16 per thread, before the LDS
-// store), with a 16-byte-chunk XOR swizzle so the 16-byte fragment reads and the transposed
-// stores avoid bank conflicts.  Double-buffered LDS, one barrier per K step, next K tile
-// prefetched into registers during the MFMAs.  In SwiGLU mode a tile's 256 columns are 128
-// gate columns and the matching 128 up columns, placed so a lane holds gate and up of the
-// same (row, column) in the same accumulator slot.
+// bf16 kernel (gfx950): 512 threads = 8 waves, tile BM x 256 x 64, v_mfma_f32_32x32x16_bf16,
+// operands streamed global -> LDS by direct loads into a ring of LDS stages (details at the
+// kernel).  In SwiGLU mode a tile's 256 columns are 128 gate columns and the matching 128 up
+// columns, placed so a lane holds gate and up of the same (row, column) in the same
+// accumulator slot.  fp32 kernel: 64 x 64 tiles on v_mfma_f32_32x32x2_f32.  The e4m3 kernels
+// are in gemm_fp8.hip.
 #include "gemm_common.hpp"
 
 namespace moe {
@@ -33,7 +31,7 @@ constexpr int kThreads = 256;  // fp32 path
 
 // ------------------------------------------------------------------------------ bf16 path
 // A: [rows, K] bf16 row-major (x_perm or h).  B: per expert [K, N] bf16 (N-contiguous, the
-// layout the weights arrive in) or, with B_NK, [N, K] (K-contiguous).
+// layout the weights arrive in).
 // SWIGLU: out h [rows, F] (F = N / 2), tile n covers gate cols n*128.. and up cols F + n*128..
 // else:   out [rows, N], tile n covers cols n*256..
 //
@@ -41,45 +39,63 @@ constexpr int kThreads = 256;  // fp32 path
 // each wave (BM/2) x 64 = FM x 2 blocks of v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
 // Both operands stream global -> LDS directly (global_load_lds_dwordx4: lane l of a
 // wave-instruction lands at base + 16 l), so there is no register staging and no VALU work in
-// the loop.  Two LDS stages per operand (128 KB):
+// the loop.  A ring of NA LDS stages for A and one of NB stages for B:
 //   A stage: BM rows x 128 B; 16-byte chunk c of row r is stored at c ^ ((r >> 1) & 7).
-//   B stage, [K, N] weights: 64 k-rows x 512 B, untransposed; chunk c of k-row k at c ^ 4 (k & 3).
-//   B stage, [N, K] weights: like A (256 n-rows x 128 B).
+//   B stage: 64 k-rows x 512 B, untransposed; chunk c of k-row k at c ^ 4 (k & 3).
+// The weights (B) stream from HBM and get the deeper ring; the activation rows (A) are shared
+// by all N tiles of an expert and mostly hit in L2.
 // A fragments (lane l: row l % 32, k 8 (l / 32) .. +8) are one ds_read_b128 each.  B fragments
-// from [K, N] are two ds_read_b64_tr_b16 each: within a group of 16 lanes, lane 16g + 4a + b
-// receives 16-bit column b of the 8-byte pieces addressed by lanes 16g + a + 4e (e = 0..3), so
-// source lane s addresses k-row 8 (s / 32) + 4 r + (s % 16) / 4 at column 16 ((s / 16) % 2) +
+// are two ds_read_b64_tr_b16 each: within a group of 16 lanes, lane 16g + 4a + b receives
+// 16-bit column b of the 8-byte pieces addressed by lanes 16g + a + 4e (e = 0..3), so source
+// lane s addresses k-row 8 (s / 32) + 4 r + (s % 16) / 4 at column 16 ((s / 16) % 2) +
 // 4 (s % 4) of the fragment and destination lane d collects column d % 32 for 4 consecutive k.
 // The swizzles spread every fragment read of a 16-lane group over distinct banks.
 //
 // Iteration kt (four 16-deep k-steps): MFMAs of k-step s interleave with the LDS reads of the
-// fragments of k-step s + 1.  Before the last k-step the wave waits for its own reads of tile
-// kt and its own loads of tile kt + 1, meets the other waves at the single barrier of the
-// iteration, issues the loads of tile kt + 2 into tile kt's stages, and then runs the last
-// k-step while reading tile kt + 1's first fragments.
+// fragments of k-step s + 1 (read in the order the MFMAs consume them).  Before the last k-step
+// the wave waits for its own reads of tile kt and its own loads of tile kt + 1, meets the other
+// waves at the single barrier of the iteration, issues the loads of A tile kt + NA and B tile
+// kt + NB into the stages tile kt used, and then runs the last k-step while reading tile
+// kt + 1's first fragments.  So A loads have NA - 1 iterations to land and B loads NB - 1.
 // Loads are unconditional: rows past the expert's end re-read its last row and column groups
 // past the matrix edge re-read column 0; those results are never stored.
 constexpr int kBKT = 64;        // K per iteration / stage
 constexpr int kBRow = kBN * 2;  // bytes per [K, N] B k-row
 
-template <int BM, bool SWIGLU, bool OUT_F32, bool B_NK>
-__global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
+template <int BM>
+struct Bf16Rings {
+  static constexpr int NA = BM == 256 ? 2 : 3;  // LDS: 2 x 32 + 3 x 32 KB or 3 x 16 + 3 x 32 KB
+  static constexpr int NB = 3;
+  static constexpr int A_BYTES = BM * kBKT * 2;
+  static constexpr int B_BYTES = kBN * kBKT * 2;
+  static constexpr int SMEM = NA * A_BYTES + NB * B_BYTES;
+};
+
+template <int BM, int WM, bool SWIGLU, bool OUT_F32, int S>
+__global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const int32_t* __restrict__ offsets,
-    int64_t rows, int E, int K, int ldb, int NT, void* __restrict__ out) {
-  constexpr int NWAVE = kGemmThreads / kWave;  // 8: 2 along M x 4 along N
-  constexpr int FM = BM / 64;                  // 32x32 blocks per wave along M
+    int64_t rows, int E, int K, int ldb, int NT, void* __restrict__ out, int ncu) {
+  using R = Bf16Rings<BM>;
+  constexpr int NA = R::NA, NB = R::NB;
+  constexpr int NWAVE = 4 * WM;                // WM along M x 4 along N
+  constexpr int WROWS = BM / WM;               // rows per wave
+  constexpr int FM = WROWS / 32;               // 32x32 blocks per wave along M
   constexpr int FN = 2;                        // 32x32 blocks per wave along N (64 columns)
-  constexpr int A_BYTES = BM * kBKT * 2;
-  constexpr int B_BYTES = kBN * kBKT * 2;
-  constexpr int B_BASE = 2 * A_BYTES;               // byte offset of the two B stages
+  constexpr int A_BYTES = R::A_BYTES;
+  constexpr int B_BYTES = R::B_BYTES;
+  constexpr int B_RING = NA * A_BYTES;              // byte offset of the B ring
   constexpr int A_ROUNDS = A_BYTES / 1024 / NWAVE;  // 1 KB wave-instructions per wave per stage
   constexpr int B_ROUNDS = B_BYTES / 1024 / NWAVE;
+  constexpr int RPT = A_ROUNDS + B_ROUNDS;
+  static_assert(NA >= 2 && NB >= NA, "ring depths");
+  static_assert(kMaxExpertsLds * 4 <= B_BYTES, "tile-map prefix fits in the first B stage");
 
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  __shared__ int s_pref[kMaxExpertsLds];
-
+  // The per-expert m-tile prefix of the tile map lives in the first B stage until the first loads.
   TileMap tm;
-  if (!map_tile<BM>(offsets, rows, E, NT, s_pref, tm)) return;
+  if (!map_tile<BM>(offsets, rows, E, NT, reinterpret_cast<int*>(smem + B_RING), tm, ncu, S)) return;
+  __syncthreads();
+  const int nk = K / kBKT;
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -99,12 +115,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
     if (grow >= tm.row_end) grow = tm.row_end - 1;
     a_src[p] = A + grow * K + (((lane % 8) ^ ((r >> 1) & 7)) * 8);
   }
-  // B sources.  [K, N]: round p of wave w covers k-rows 2 (8p + w) + lane / 32 (1 KB = 2 k-rows
-  // x 512 B); stored chunk lane % 32 holds logical chunk (lane % 32) ^ 4 ((2w + lane / 32) & 3).
-  // [N, K]: round p covers n-rows (8p + w) * 8 + lane / 8, swizzled like A.
-  const bf16_t* b_src[B_ROUNDS];
-  int64_t b_kstep;
-  if (!B_NK) {
+  // B round p of wave w covers k-rows 2 (8p + w) + lane / 32 (1 KB = 2 k-rows x 512 B); stored
+  // chunk lane % 32 holds logical chunk (lane % 32) ^ 4 ((2w + lane / 32) & 3).
+  const bf16_t* b_src;
+  {
     const int b_lchunk = (lane % 32) ^ (4 * ((2 * wave + lane / 32) & 3));
     int64_t b_col;
     if (SWIGLU) {
@@ -115,59 +129,49 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
       b_col = static_cast<int64_t>(tm.nt) * kBN + b_lchunk * 8;
     }
     if (b_col >= ldb) b_col = 0;  // ldb % 8 == 0: an 8-column group is wholly in or out
-    const bf16_t* b0 = B + static_cast<int64_t>(tm.expert) * K * ldb +
-                       static_cast<int64_t>(2 * wave + lane / 32) * ldb + b_col;
-#pragma unroll
-    for (int p = 0; p < B_ROUNDS; ++p) b_src[p] = b0 + static_cast<int64_t>(2 * NWAVE * p) * ldb;
-    b_kstep = static_cast<int64_t>(kBKT) * ldb;
-  } else {
-#pragma unroll
-    for (int p = 0; p < B_ROUNDS; ++p) {
-      const int r = (NWAVE * p + wave) * 8 + lane / 8;
-      int64_t n;
-      if (SWIGLU) {
-        const int F = ldb / 2;
-        n = (r < 128) ? static_cast<int64_t>(tm.nt) * 128 + r : F + static_cast<int64_t>(tm.nt) * 128 + (r - 128);
-      } else {
-        n = static_cast<int64_t>(tm.nt) * kBN + r;
-      }
-      if (n >= ldb) n = 0;
-      b_src[p] = B + (static_cast<int64_t>(tm.expert) * ldb + n) * K + (((lane % 8) ^ ((r >> 1) & 7)) * 8);
-    }
-    b_kstep = kBKT;
+    b_src = B + static_cast<int64_t>(tm.expert) * K * ldb + static_cast<int64_t>(2 * wave + lane / 32) * ldb + b_col;
   }
+  const int64_t b_round = static_cast<int64_t>(2 * NWAVE) * ldb;
+  const int64_t b_kstep = static_cast<int64_t>(kBKT) * ldb;
 
-  auto issue_loads = [&](int kt) {
-    const uint32_t abase = lds_base + (kt & 1) * A_BYTES;
-    const uint32_t bbase = lds_base + B_BASE + (kt & 1) * B_BYTES;
+  auto a_stage = [&](int kt) { return lds_base + static_cast<uint32_t>(kt % NA) * A_BYTES; };
+  auto b_stage = [&](int kt) { return lds_base + B_RING + static_cast<uint32_t>(kt % NB) * B_BYTES; };
+  // Load group j (j >= -NB): A tile j + NA and B tile j + NB, each if it exists.  Group j is
+  // issued at iteration j (the prologue issues groups -NB .. -1).
+  auto issue_group = [&](int j) {
+    const int ta = j + NA, tb = j + NB;
+    if (ta >= 0 && ta < nk) {
+      const uint32_t abase = a_stage(ta);
 #pragma unroll
-    for (int p = 0; p < A_ROUNDS; ++p)
-      lds_dma16(a_src[p] + static_cast<int64_t>(kt) * kBKT, abase + (NWAVE * p + wave) * 1024);
+      for (int p = 0; p < A_ROUNDS; ++p)
+        lds_dma16(a_src[p] + static_cast<int64_t>(ta) * kBKT, abase + (NWAVE * p + wave) * 1024);
+    }
+    if (tb < nk) {
+      const uint32_t bbase = b_stage(tb);
+      const bf16_t* bs = b_src + static_cast<int64_t>(tb) * b_kstep;
 #pragma unroll
-    for (int p = 0; p < B_ROUNDS; ++p)
-      lds_dma16(b_src[p] + static_cast<int64_t>(kt) * b_kstep, bbase + (NWAVE * p + wave) * 1024);
+      for (int p = 0; p < B_ROUNDS; ++p) lds_dma16(bs + p * b_round, bbase + (NWAVE * p + wave) * 1024);
+    }
+  };
+  // Loads issued after both A and B tile t + 1 while groups up to t - 1 are out, when every tile
+  // they name exists (t + NB <= nk): the B part of A tile t + 1's group (when NB > NA, B tile
+  // t + 1 came in an earlier group), then NA - 2 whole groups.  Otherwise wait for all.
+  constexpr int B_AFTER_A = NB > NA ? B_ROUNDS : 0;
+  auto wait_tile_next = [&](int t) {
+    if (t + NB <= nk) wait_vmcnt<B_AFTER_A + (NA - 2) * RPT>();
+    else wait_vmcnt<0>();
   };
 
-  // ---- fragment addresses (byte offsets inside a stage; k-step ks adds 32 B (A, [N,K] B) or
-  // 16 k-rows ([K,N] B))
+  // ---- fragment addresses (byte offsets inside a stage; k-step ks adds 32 B (A) or 16 k-rows (B))
   uint32_t a_row_off[FM], a_sw[FM];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int r = wm * (BM / 2) + i * 32 + lane % 32;
+    const int r = wm * WROWS + i * 32 + lane % 32;
     a_row_off[i] = r * 128;
     a_sw[i] = (r >> 1) & 7;
   }
-  uint32_t b_off[FN][2], b_sw[FN];
-  if (B_NK) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int cb = SWIGLU ? j * 128 + wn * 32 : wn * 64 + j * 32;
-      const int r = cb + lane % 32;
-      b_off[j][0] = r * 128;
-      b_off[j][1] = 0;
-      b_sw[j] = (r >> 1) & 7;
-    }
-  } else {
+  uint32_t b_off[FN][2];
+  {
     const int g = lane / 16, h = lane / 32, a4 = lane % 4, e = (lane % 16) / 4;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -179,7 +183,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
         const int krow = 8 * h + 4 * r + e;
         b_off[j][r] = krow * kBRow + (((col / 8) ^ (4 * e)) << 4) + (col % 8) * 2;
       }
-      b_sw[j] = 0;
     }
   }
   const int khalf = lane / 32;
@@ -192,79 +195,91 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  bf16x8_t af[2][FM], bfr[2][FN];
-  auto read_frags = [&](int kt, int ks, int buf) {
-    const uint32_t abase = lds_base + (kt & 1) * A_BYTES;
-    const uint32_t bbase = lds_base + B_BASE + (kt & 1) * B_BYTES;
-    const uint32_t chunk = ks * 2 + khalf;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
+  // Only the 32-row blocks of this wave that hold rows of the expert are computed: NL of the
+  // wave's FM blocks (a wave-uniform count; the last m-tile of an expert is usually partial).
+  int nl_rows = static_cast<int>((tm.row_end - tm.row0 < BM ? tm.row_end - tm.row0 : BM)) - wm * WROWS;
+  nl_rows = nl_rows < 0 ? 0 : nl_rows;
+  const int nlive = __builtin_amdgcn_readfirstlane(nl_rows >= WROWS ? FM : (nl_rows + 31) / 32);
+
+  auto run = [&](auto nl_c) {
+    constexpr int NL = decltype(nl_c)::value;
+    constexpr int NLA = NL > 0 ? NL : 1;
+    bf16x8_t af[2][NLA], bfr[2][FN];
+    auto read_b = [&](uint32_t bbase, int ks, int buf, int j) {
+      v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<lds_v4i16_t*>(static_cast<uintptr_t>(bbase + b_off[j][0] + ks * 16 * kBRow)));
+      v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<lds_v4i16_t*>(static_cast<uintptr_t>(bbase + b_off[j][1] + ks * 16 * kBRow)));
+      typedef short v8i16_t __attribute__((ext_vector_type(8)));
+      v8i16_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      bfr[buf][j] = __builtin_bit_cast(bf16x8_t, both);
+    };
+    auto read_a = [&](uint32_t abase, int ks, int buf, int i) {
+      const uint32_t chunk = ks * 2 + khalf;
       af[buf][i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
           static_cast<uintptr_t>(abase + a_row_off[i] + ((chunk ^ a_sw[i]) << 4)));
+    };
+    // in the order the MFMAs (i-major) consume them: B0, A0, B1, A1, A2, ...
+    auto read_frags = [&](int kt, int ks, int buf) {
+      if constexpr (NL > 0) {
+        const uint32_t abase = a_stage(kt), bbase = b_stage(kt);
+        read_b(bbase, ks, buf, 0);
+        read_a(abase, ks, buf, 0);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      if (B_NK) {
-        bfr[buf][j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
-            static_cast<uintptr_t>(bbase + b_off[j][0] + ((chunk ^ b_sw[j]) << 4)));
-      } else {
-        v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16_t*>(
-            static_cast<uintptr_t>(bbase + b_off[j][0] + ks * 16 * kBRow)));
-        v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16_t*>(
-            static_cast<uintptr_t>(bbase + b_off[j][1] + ks * 16 * kBRow)));
-        typedef short v8i16_t __attribute__((ext_vector_type(8)));
-        v8i16_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        bfr[buf][j] = __builtin_bit_cast(bf16x8_t, both);
+        for (int j = 1; j < FN; ++j) read_b(bbase, ks, buf, j);
+#pragma unroll
+        for (int i = 1; i < NL; ++i) read_a(abase, ks, buf, i);
       }
-    }
-  };
-  auto mfmas = [&](int buf) {
+    };
+    auto mfmas = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < NL; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0);
-  };
-  // MFMAs of one k-step interleaved with the LDS reads of the next k-step's fragments
-  constexpr int NREADS = FM + (B_NK ? FN : 2 * FN);
-  constexpr int NMFMA = FM * FN;
-  constexpr int RPM = (NREADS + NMFMA - 1) / NMFMA;  // LDS reads per MFMA slot
-  auto interleave = [&]() { sched_mfma_reads<0, NMFMA, NREADS, RPM>(); };
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0);
+    };
+    // MFMAs of one k-step interleaved with the LDS reads of the next k-step's fragments
+    auto interleave = [&]() {
+      if constexpr (NL > 0) {
+        constexpr int NREADS = NL + 2 * FN;
+        constexpr int NMFMA = NL * FN;
+        constexpr int RPM = (NREADS + NMFMA - 1) / NMFMA;  // LDS reads per MFMA slot
+        sched_mfma_reads<0, NMFMA, NREADS, RPM>();
+      }
+    };
 
-  const int nk = K / kBKT;
-  issue_loads(0);
-  if (nk > 1) {
-    issue_loads(1);
-    wait_vmcnt<A_ROUNDS + B_ROUNDS>();  // tile 0 landed (tile 1 may be in flight)
-  } else {
-    wait_vmcnt<0>();
-  }
-  lds_barrier();
-  read_frags(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    mfmas(0);
-    read_frags(kt, 1, 1);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(1);
-    read_frags(kt, 2, 0);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(0);
-    read_frags(kt, 3, 1);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) {
-      wait_lgkm0();       // this wave's reads of tile kt are complete
-      wait_vmcnt<0>();    // this wave's loads of tile kt + 1 have landed
-      lds_barrier();      // ... for every wave: tile kt + 1 readable, tile kt's stages free
-      if (kt + 2 < nk) issue_loads(kt + 2);
+    for (int j = -NB; j < 0; ++j) issue_group(j);
+    // tile 0: groups -NA + 1 .. -1 (and B(NB - NA) when NB > NA) may still be in flight
+    if (NB <= nk) wait_vmcnt<B_AFTER_A + (NA - 1) * RPT>(); else wait_vmcnt<0>();
+    lds_barrier();
+    read_frags(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      mfmas(0);
+      read_frags(kt, 1, 1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(1);
+      read_frags(kt, 2, 0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(0);
+      read_frags(kt, 3, 1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < nk) {
+        wait_lgkm0();        // this wave's reads of tile kt are complete
+        wait_tile_next(kt);  // this wave's loads of A and B tile kt + 1 have landed
+        lds_barrier();       // ... for every wave: tile kt + 1 readable, tile kt's stages free
+        issue_group(kt);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(1);
+      read_frags(kt + 1, 0, 0);  // past the last tile this reads a stale stage (in bounds, unused)
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(1);
-    read_frags(kt + 1, 0, 0);  // past the last tile this reads a stale stage (in bounds, unused)
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  };
+  dispatch_live<FM>(nlive, run);
 
   // ---- epilogue.  32x32 accumulator layout: slot r of lane l is
   //      row (r / 4) * 8 + (l / 32) * 4 + (r % 4), column l % 32.
@@ -272,7 +287,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row_t = wm * (BM / 2) + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
+      const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
       const int64_t grow = tm.row0 + row_t;
       if (grow >= tm.row_end) continue;
       if (SWIGLU) {
@@ -370,19 +385,45 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(const float* __restr
   }
 }
 
-template <int BM, bool SWIGLU, bool OUT_F32, bool B_NK = false>
+// Tail of the second GEMM.  Its tiles are K = F deep (16 times the first GEMM's for Mixtral-like
+// shapes), and when their count leaves the last wave of workgroups mostly empty, each tile of
+// that wave is cut into kBands row bands computed by separate workgroups (the band's dead
+// 32-row blocks skip their MFMAs), so the last wave ends about kBands times sooner.
+constexpr int kBands = 4;
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int BM, bool SWIGLU, bool OUT_F32, int WM = 2, int S = 1>
 hipError_t launch_bf16(const bf16_t* A, const bf16_t* B, const int32_t* offsets, int64_t rows, int E,
-                       int K, int ldb, int NT, void* out, hipStream_t stream) {
-  constexpr int smem = 2 * BM * kBKT * 2 + 2 * kBN * kBKT * 2;
-  auto kern = gemm_bf16_kernel<BM, SWIGLU, OUT_F32, B_NK>;
+                       int K, int ldb, int NT, void* out, hipStream_t stream, int ncu = 0) {
+  constexpr int smem = Bf16Rings<BM>::SMEM;
+  auto kern = gemm_bf16_kernel<BM, WM, SWIGLU, OUT_F32, S>;
   // once per instantiation (and never inside a stream capture after the first eager call)
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (attr != hipSuccess) return attr;
-  const unsigned grid = grid_for(max_tiles<BM>(rows, E, offsets == nullptr), NT);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), smem, stream, A, B, offsets, rows, E, K, ldb, NT,
-                     out);
+  const unsigned grid = grid_for(max_tiles<BM>(rows, E, offsets == nullptr), NT, ncu, S);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256 * WM), smem, stream, A, B, offsets, rows, E, K, ldb, NT, out, ncu);
   return hipGetLastError();
+}
+
+// Second GEMM, with the banded tail when the device's CU count is known.
+template <int BM, bool OUT_F32>
+hipError_t launch_bf16_down(const bf16_t* h, const bf16_t* w2, const int32_t* offsets, int64_t rows, int E, int F,
+                            int H, int nt2, void* y_perm, hipStream_t stream) {
+  const int ncu = device_cus();
+  if (ncu < 2) return launch_bf16<BM, false, OUT_F32>(h, w2, offsets, rows, E, F, H, nt2, y_perm, stream);
+  return launch_bf16<BM, false, OUT_F32, 2, kBands>(h, w2, offsets, rows, E, F, H, nt2, y_perm, stream, ncu);
 }
 
 // GEMM1 (+SwiGLU) then GEMM2 with BM-row tiles; `between` (optional) is recorded after GEMM1.
@@ -397,8 +438,8 @@ hipError_t launch_bf16_pair(const void* x_perm, const void* w1, const void* w2, 
   if (between && (err = hipEventRecord(between, stream)) != hipSuccess) return err;
   const int nt2 = static_cast<int>(ceil_div(H, kBN));
   if (out_dt == 0)
-    return launch_bf16<BM, false, true>(h, static_cast<const bf16_t*>(w2), offsets, rows, E, F, H, nt2, y_perm, stream);
-  return launch_bf16<BM, false, false>(h, static_cast<const bf16_t*>(w2), offsets, rows, E, F, H, nt2, y_perm, stream);
+    return launch_bf16_down<BM, true>(h, static_cast<const bf16_t*>(w2), offsets, rows, E, F, H, nt2, y_perm, stream);
+  return launch_bf16_down<BM, false>(h, static_cast<const bf16_t*>(w2), offsets, rows, E, F, H, nt2, y_perm, stream);
 }
 
 }  // namespace
@@ -435,8 +476,9 @@ hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int 
     return hipGetLastError();
   }
   if (dt == 1) {
-    // 256-row tiles when experts average >= 768 rows, else 128-row tiles (less padding)
-    const bool big = offsets == nullptr ? rows >= 768 : rows >= 768 * static_cast<int64_t>(E);
+    // 256-row tiles when experts average >= 192 rows (the last, partial m-tile of an expert only
+    // computes its live 32-row blocks), else 128-row tiles
+    const bool big = offsets == nullptr ? rows >= 192 : rows >= 192 * static_cast<int64_t>(E);
     return big ? launch_bf16_pair<256>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream, between)
                : launch_bf16_pair<128>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream, between);
   }

@@ -2,6 +2,8 @@
 // tile scheduler and the LDS-DMA / wait-count helpers.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -17,25 +19,11 @@ struct TileMap {
   int64_t row0, row_end;  // this tile's first row and the expert's end row
 };
 
-// Returns false if this workgroup has no tile.  `s_pref` is LDS of >= E+1 ints.
+// Tile count (m-tiles summed over experts, times NT); builds the m-tile prefix in s_pref.
 template <int BM>
-__device__ bool map_tile(const int32_t* offsets, int64_t rows, int E, int NT, int* s_pref, TileMap& tm) {
+__device__ int count_tiles(const int32_t* offsets, int64_t rows, int E, int NT, int* s_pref) {
+  if (offsets == nullptr) return static_cast<int>(ceil_div(rows, BM)) * NT;
   const int tid = threadIdx.x;
-  if (offsets == nullptr) {  // one dense expert over rows [0, rows)
-    const int mtiles = static_cast<int>(ceil_div(rows, BM));
-    const int total = mtiles * NT;
-    const int per = (total + 7) / 8;
-    const int w = blockIdx.x;
-    if (w >= 8 * per) return false;
-    const int L = (w % 8) * per + w / 8;
-    if (L >= total) return false;
-    tm.expert = 0;
-    tm.nt = L / mtiles;
-    tm.mt = L % mtiles;
-    tm.row0 = static_cast<int64_t>(tm.mt) * BM;
-    tm.row_end = rows;
-    return true;
-  }
   // m-tiles per expert, exclusive prefix in s_pref[0..E]
   for (int e = tid; e < E; e += static_cast<int>(blockDim.x)) {
     int c = offsets[e + 1] - offsets[e];
@@ -58,12 +46,30 @@ __device__ bool map_tile(const int32_t* offsets, int64_t rows, int E, int NT, in
     }
   }
   __syncthreads();
-  const int total = s_pref[E] * NT;
-  const int per = (total + 7) / 8;
-  const int w = blockIdx.x;
-  if (w >= 8 * per) return false;
-  const int L = (w % 8) * per + w / 8;  // consecutive L of one XCD share weights / rows
-  if (L >= total) return false;
+  return s_pref[E] * NT;
+}
+
+// Tiles that do not fill the last wave of `ncu` workgroups when run whole (at most `ncu` - 1): with
+// S > 1 each of them is cut into up to S row bands (so the last wave holds several times as many
+// pieces, each with a fraction of the MFMA work).
+__device__ __forceinline__ int whole_tiles(int total, int ncu, int S) {
+  return S > 1 ? total - total % ncu : total;
+}
+
+// Linear tile L -> (expert, m-tile, n-tile); n-major inside an expert so the m-tiles of one
+// weight tile are adjacent.
+template <int BM>
+__device__ void locate_tile(const int32_t* offsets, int64_t rows, int E, int NT, const int* s_pref, int L,
+                            TileMap& tm) {
+  if (offsets == nullptr) {  // one dense expert over rows [0, rows)
+    const int mtiles = static_cast<int>(ceil_div(rows, BM));
+    tm.expert = 0;
+    tm.nt = L / mtiles;
+    tm.mt = L % mtiles;
+    tm.row0 = static_cast<int64_t>(tm.mt) * BM;
+    tm.row_end = rows;
+    return;
+  }
   // expert whose tile range [s_pref[e]*NT, s_pref[e+1]*NT) holds L (binary search in LDS)
   int lo = 0, hi = E - 1;
   while (lo < hi) {
@@ -74,10 +80,49 @@ __device__ bool map_tile(const int32_t* offsets, int64_t rows, int E, int NT, in
   const int me = s_pref[e + 1] - s_pref[e];
   const int idx = L - s_pref[e] * NT;
   tm.expert = e;
-  tm.nt = idx / me;  // n-major inside an expert: the m-tiles of one weight tile are adjacent
+  tm.nt = idx / me;
   tm.mt = idx % me;
   tm.row0 = static_cast<int64_t>(offsets[e]) + static_cast<int64_t>(tm.mt) * BM;
   tm.row_end = offsets[e + 1];
+}
+
+// Returns false if this workgroup has no tile.  `s_pref` is LDS of >= E+1 ints.  Workgroups
+// [0, 8 ceil(W / 8)) take the W whole tiles, XCD-remapped (consecutive tiles on one XCD share
+// weights and rows in its L2); the following ones take the S row bands of each tail tile.
+template <int BM>
+__device__ bool map_tile(const int32_t* offsets, int64_t rows, int E, int NT, int* s_pref, TileMap& tm,
+                         int ncu = 0, int S = 1) {
+  const int total = count_tiles<BM>(offsets, rows, E, NT, s_pref);
+  const int whole = whole_tiles(total, ncu, S);
+  const int per = (whole + 7) / 8;
+  const int w = blockIdx.x;
+  if (w < 8 * per) {
+    const int L = (w % 8) * per + w / 8;
+    if (L >= whole) return false;
+    locate_tile<BM>(offsets, rows, E, NT, s_pref, L, tm);
+    return true;
+  }
+  // Tail: as many bands per tile as still fit one wave (at most S; bands are whole 32-row
+  // blocks).  Pieces P = tile * SB + band are XCD-remapped like the whole tiles, whole tiles'
+  // worth of pieces per XCD, so the bands of one tile (which stream the same weight tile) run on
+  // one XCD.
+  const int tail = total - whole;
+  int SB = ncu / (tail > 0 ? tail : 1);
+  SB = SB < 1 ? 1 : (SB > S ? S : SB);
+  const int band_rows = (BM / SB + 31) / 32 * 32;
+  const int pieces = tail * SB;
+  const int per_t = (tail + 7) / 8 * SB;
+  const int q = w - 8 * per;
+  if (q >= 8 * per_t) return false;
+  const int P = (q % 8) * per_t + q / 8;
+  if (P >= pieces) return false;
+  locate_tile<BM>(offsets, rows, E, NT, s_pref, whole + P / SB, tm);
+  const int64_t tile_end = tm.row0 + BM;
+  tm.row0 += static_cast<int64_t>(P % SB) * band_rows;
+  int64_t band_end = tm.row0 + band_rows;
+  if (band_end > tile_end) band_end = tile_end;
+  if (band_end < tm.row_end) tm.row_end = band_end;
+  if (tm.row0 >= tm.row_end) return false;  // band past the tile's or the expert's last row
   return true;
 }
 
@@ -103,6 +148,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   // gfx9 s_waitcnt encoding: vmcnt [3:0] + [15:14], expcnt [6:4] (7 = no wait), lgkmcnt [11:8] (15)
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// Wait (vmcnt) until at most `tiles` (<= MAXT) tiles of RPT loads each are still in flight.
+template <int RPT, int MAXT>
+__device__ __forceinline__ void wait_tiles(int tiles) {
+  if constexpr (MAXT >= 2) {
+    if (tiles >= 2) { wait_vmcnt<2 * RPT>(); return; }
+  }
+  if constexpr (MAXT >= 1) {
+    if (tiles >= 1) { wait_vmcnt<RPT>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14)); }
 
 // Scheduling groups for one k-step: NM MFMAs, each followed by up to RPM of the NR LDS reads.
@@ -124,13 +181,25 @@ __device__ __forceinline__ float silu_fast(float z) {
 }
 
 
+// Calls f(std::integral_constant<int, n>) for the runtime n in [0, MAXN] (wave-uniform).
+template <int MAXN, typename Fn>
+__device__ __forceinline__ void dispatch_live(int n, Fn&& f) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) { f(std::integral_constant<int, MAXN>{}); return; }
+    dispatch_live<MAXN - 1>(n, f);
+  } else {
+    f(std::integral_constant<int, 0>{});
+  }
+}
+
 template <int BM>
 inline int64_t max_tiles(int64_t rows, int E, bool dense) {
   return dense ? ceil_div(rows, BM) : (rows + static_cast<int64_t>(E) * (BM - 1)) / BM;
 }
 
-inline unsigned grid_for(int64_t mtiles, int NT) {
+inline unsigned grid_for(int64_t mtiles, int NT, int ncu = 0, int S = 1) {
   int64_t g = mtiles * NT;
+  if (S > 1) g += 7 + 7 * S + static_cast<int64_t>(ncu - 1) * (S - 1);  // roundings to 8 + tail bands
   return static_cast<unsigned>(ceil_div(g, 8) * 8);
 }
 

@@ -11,9 +11,11 @@
 // scales.  Per K step the two 64-deep MFMAs of a block accumulate into a temporary, then
 //     acc += tmp * s_a[row] * s_b[block]
 // on the VALU.  Operands stream global -> LDS (global_load_lds_dwordx4; the row scales of the
-// step with global_load_lds_dword), double-buffered:
+// step with global_load_lds_dword) through a ring of three LDS stages, so a tile's loads have
+// two iterations to land:
 //   A stage: 128 rows x 128 B, chunk c of row r at c ^ ((r >> 1) & 7) (as the bf16 kernel);
 //   B stage: 128 k-rows x 256 B (untransposed), chunk c of k-row k at c ^ 2 (k & 7).
+// The weight block scales are wave-uniform and come through the scalar cache.
 // B fragments come from ds_read_b64_tr_b8: within a group of 16 lanes, lane 16g + 8a + b
 // receives byte b of the 8-byte pieces addressed by lanes 16g + a + 2e (e = 0..7), so source
 // lane s addresses k-row 8 q + (s % 16) / 2 (+ 32 (s / 32)) at column 16 ((s / 16) % 2) + 8 (s % 2)
@@ -28,6 +30,10 @@ using namespace gemm;
 constexpr int kF8BM = 128;    // rows per tile
 constexpr int kF8BK = 128;    // K per iteration = one scale block
 constexpr int kF8BRow = kBN;  // bytes per B k-row (256 fp8 columns)
+constexpr int kF8Stages = 3;
+constexpr int kF8Stage = kF8BM * kF8BK + kF8BK * kF8BRow;  // A + B of one K tile
+constexpr int kF8ScaleSlots = kF8Stages + 1;                // row-scale ring, one slot longer
+constexpr int kF8Smem = kF8Stages * kF8Stage + kF8ScaleSlots * kF8BM * 4;
 
 typedef int v2i32_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i32_t lds_v2i32_t;
@@ -49,17 +55,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
   constexpr int BM = kF8BM;
   constexpr int FM = 2, FN = 2;
   constexpr int A_BYTES = BM * kF8BK;           // 16 KB
-  constexpr int AS_BYTES = 1024;                // BM fp32 row scales (512 B), padded
   constexpr int B_BYTES = kF8BK * kF8BRow;      // 32 KB
-  constexpr int STAGE = A_BYTES + AS_BYTES + B_BYTES;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int NS = kF8Stages;
   constexpr int A_ROUNDS = A_BYTES / 1024 / NWAVE;  // 2
   constexpr int B_ROUNDS = B_BYTES / 1024 / NWAVE;  // 4
+  constexpr int RPT = A_ROUNDS + B_ROUNDS;          // loads per wave per tile (+1 on waves 0, 1)
+  static_assert(STAGE == kF8Stage && NS * STAGE + kF8ScaleSlots * BM * 4 == kF8Smem, "LDS layout");
 
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   __shared__ int s_pref[kMaxExpertsLds];
 
   TileMap tm;
   if (!map_tile<BM>(offsets, rows, E, NT, s_pref, tm)) return;
+  const int t_expert = __builtin_amdgcn_readfirstlane(tm.expert);  // uniform: scalar address math
+  const int t_nt = __builtin_amdgcn_readfirstlane(tm.nt);
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -105,24 +115,30 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
   const int nbn = ldb / 128;
   int blk[FN];
   if (SWIGLU) {
-    blk[0] = tm.nt;
-    blk[1] = ldb / 256 + tm.nt;
+    blk[0] = t_nt;
+    blk[1] = ldb / 256 + t_nt;
   } else {
-    const int c0 = tm.nt * 2 + wn / 2;
+    const int c0 = t_nt * 2 + wn / 2;
     blk[0] = blk[1] = c0 < nbn ? c0 : 0;
   }
-  const float* bs_src = B_scales + static_cast<int64_t>(tm.expert) * nkb * nbn;
+  const float* bs_src = B_scales + static_cast<int64_t>(t_expert) * nkb * nbn;
 
+  auto stage_base = [&](int kt) { return lds_base + static_cast<uint32_t>(kt % NS) * STAGE; };
+  // row scales of tile kt live in their own ring slot, which the loads issued at the barrier of
+  // iteration kt (tile kt + NS) do not touch, so they can be read after that barrier
+  auto scale_base = [&](int kt) {
+    return lds_base + NS * STAGE + static_cast<uint32_t>(kt % kF8ScaleSlots) * (BM * 4);
+  };
   auto issue_loads = [&](int kt) {
-    const uint32_t sbase = lds_base + (kt & 1) * STAGE;
+    const uint32_t sbase = stage_base(kt);
 #pragma unroll
     for (int p = 0; p < A_ROUNDS; ++p)
       lds_dma16(a_src[p] + static_cast<int64_t>(kt) * kF8BK, sbase + (NWAVE * p + wave) * 1024);
-    if (wave < 2) lds_dma4(as_src + kt, sbase + A_BYTES + wave * 256);
+    if (wave < 2) lds_dma4(as_src + kt, scale_base(kt) + wave * 256);
     const uint8_t* bs = b_src + static_cast<int64_t>(kt) * kF8BK * ldb;
 #pragma unroll
     for (int p = 0; p < B_ROUNDS; ++p)
-      lds_dma16(bs + p * b_round, sbase + A_BYTES + AS_BYTES + (NWAVE * p + wave) * 1024);
+      lds_dma16(bs + p * b_round, sbase + A_BYTES + (NWAVE * p + wave) * 1024);
   };
 
   // ---- fragment addresses
@@ -153,89 +169,104 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   const f32x16_t zero16 = {};
 
-  i32x8_t af[2][FM], bfr[2][FN];
-  // sub-step s (0, 1) of tile kt: 64 K bytes; A lane l holds k 32 (l / 32) .. +32 of it
-  auto read_frags = [&](int kt, int s, int buf) {
-    const uint32_t sbase = lds_base + (kt & 1) * STAGE;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
+  // Only the 32-row blocks of this wave that hold rows of the expert are computed (wave-uniform).
+  int nl_rows = static_cast<int>((tm.row_end - tm.row0 < BM ? tm.row_end - tm.row0 : BM)) - wm * 64;
+  nl_rows = nl_rows < 0 ? 0 : nl_rows;
+  const int nlive = __builtin_amdgcn_readfirstlane(nl_rows >= 64 ? FM : (nl_rows + 31) / 32);
+
+  const int nk = nkb;
+  auto run = [&](auto nl_c) {
+    constexpr int NL = decltype(nl_c)::value;
+    constexpr int NLA = NL > 0 ? NL : 1;
+    i32x8_t af[2][NLA], bfr[2][FN];
+    auto read_a = [&](uint32_t sbase, int s, int buf, int i) {
       const uint32_t c0 = 4 * s + 2 * khalf;
       u32x4_t lo = *reinterpret_cast<const lds_u32x4_t*>(
           static_cast<uintptr_t>(sbase + a_row_off[i] + ((c0 ^ a_sw[i]) << 4)));
       u32x4_t hi = *reinterpret_cast<const lds_u32x4_t*>(
           static_cast<uintptr_t>(sbase + a_row_off[i] + (((c0 + 1) ^ a_sw[i]) << 4)));
       af[buf][i] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    }
-    const uint32_t bbase = sbase + A_BYTES + AS_BYTES + s * 64 * kF8BRow;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
+    };
+    auto read_b = [&](uint32_t sbase, int s, int buf, int j) {
+      const uint32_t bbase = sbase + A_BYTES + s * 64 * kF8BRow;
       v2i32_t q[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         q[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             reinterpret_cast<lds_v2i32_t*>(static_cast<uintptr_t>(bbase + b_off[j] + r * 8 * kF8BRow)));
       bfr[buf][j] = i32x8_t{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
-    }
-  };
-  auto mfmas = [&](int buf, bool first) {
+    };
+    // sub-step s (0, 1) of tile kt: 64 K bytes; A lane l holds k 32 (l / 32) .. +32 of it.
+    // Read in the order the MFMAs (i-major) consume them: B0, A0, B1, A1.
+    auto read_frags = [&](int kt, int s, int buf) {
+      if constexpr (NL > 0) {
+        const uint32_t sbase = stage_base(kt);
+        read_b(sbase, s, buf, 0);
+        read_a(sbase, s, buf, 0);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+        for (int j = 1; j < FN; ++j) read_b(sbase, s, buf, j);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        tmp[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[buf][i], bfr[buf][j],
-                                                                     first ? zero16 : tmp[i][j], 0, 0, 0, 127, 0, 127);
-  };
-  // row scales of this lane's 16 accumulator rows per block i: 4 runs of 4 consecutive rows
-  f32x4_t sa[FM][4];
-  auto read_row_scales = [&](int kt) {
-    const uint32_t sbase = lds_base + (kt & 1) * STAGE + A_BYTES;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = wm * 64 + i * 32 + q * 8 + khalf * 4;
-        sa[i][q] = *reinterpret_cast<const lds_f32x4_t*>(static_cast<uintptr_t>(sbase + row * 4));
+        for (int i = 1; i < NL; ++i) read_a(sbase, s, buf, i);
       }
-  };
+    };
+    auto mfmas = [&](int buf, bool first) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          tmp[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[buf][i], bfr[buf][j],
+                                                                       first ? zero16 : tmp[i][j], 0, 0, 0, 127, 0, 127);
+    };
+    // row scales of this lane's 16 accumulator rows per block i: 4 runs of 4 consecutive rows
+    f32x4_t sa[NLA][4];
+    auto read_row_scales = [&](int kt) {
+      const uint32_t sbase = scale_base(kt);
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = wm * 64 + i * 32 + q * 8 + khalf * 4;
+          sa[i][q] = *reinterpret_cast<const lds_f32x4_t*>(static_cast<uintptr_t>(sbase + row * 4));
+        }
+    };
 
-  const int nk = nkb;
-  float sb[FN], sb_next[FN];
+    float sb[FN], sb_next[FN];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) sb[j] = bs_src[blk[j]];
-  issue_loads(0);
-  if (nk > 1) {
-    issue_loads(1);
-    if (wave < 2) wait_vmcnt<A_ROUNDS + 1 + B_ROUNDS>(); else wait_vmcnt<A_ROUNDS + B_ROUNDS>();
-  } else {
-    wait_vmcnt<0>();
-  }
-  lds_barrier();
-  read_frags(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int ktn = kt + 1 < nk ? kt + 1 : kt;
+    for (int j = 0; j < FN; ++j) sb[j] = bs_src[blk[j]];
+    const int pro = nk < NS ? nk : NS;  // tiles in flight before the loop
+    for (int t = 0; t < pro; ++t) issue_loads(t);
+    if (wave < 2) wait_tiles<RPT + 1, NS - 1>(pro - 1); else wait_tiles<RPT, NS - 1>(pro - 1);  // tile 0 landed
+    lds_barrier();
+    read_frags(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int ktn = kt + 1 < nk ? kt + 1 : kt;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) sb_next[j] = bs_src[static_cast<int64_t>(ktn) * nbn + blk[j]];
-    mfmas(0, true);
-    read_frags(kt, 1, 1);
-    read_row_scales(kt);
-    if (kt + 1 < nk) {
-      wait_lgkm0();      // this wave's reads of tile kt are complete
-      wait_vmcnt<0>();   // ... and its loads of tile kt + 1 have landed
-      lds_barrier();     // for every wave: tile kt + 1 readable, tile kt's stage free
-      if (kt + 2 < nk) issue_loads(kt + 2);
+      for (int j = 0; j < FN; ++j) sb_next[j] = bs_src[static_cast<int64_t>(ktn) * nbn + blk[j]];
+      mfmas(0, true);
+      read_frags(kt, 1, 1);
+      if (kt + 1 < nk) {
+        wait_lgkm0();  // this wave's reads of tile kt are complete
+        // this wave's loads of tile kt + 1 have landed; tiles kt + 2 .. kt + NS - 1 may be in flight
+        const int later = nk - 2 - kt < NS - 2 ? nk - 2 - kt : NS - 2;
+        if (wave < 2) wait_tiles<RPT + 1, NS - 2>(later); else wait_tiles<RPT, NS - 2>(later);
+        lds_barrier();  // for every wave: tile kt + 1 readable, tile kt's stage free
+        if (kt + NS < nk) issue_loads(kt + NS);
+      }
+      mfmas(1, false);
+      read_frags(kt + 1, 0, 0);  // past the last tile this reads a stale stage (in bounds, unused)
+      read_row_scales(kt);
+      // promote the block: acc += tmp * s_a[row] * s_b[column block]
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(tmp[i][j][r], sa[i][r / 4][r % 4] * sb[j], acc[i][j][r]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) sb[j] = sb_next[j];
     }
-    mfmas(1, false);
-    read_frags(kt + 1, 0, 0);  // past the last tile this reads a stale stage (in bounds, unused)
-    // promote the block: acc += tmp * s_a[row] * s_b[column block]
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(tmp[i][j][r], sa[i][r / 4][r % 4] * sb[j], acc[i][j][r]);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) sb[j] = sb_next[j];
-  }
+  };
+  dispatch_live<FM>(nlive, run);
 
   // ---- epilogue.  32x32 accumulator layout: slot r of lane l is
   //      row (r / 4) * 8 + (l / 32) * 4 + (r % 4), column l % 32.
@@ -308,7 +339,7 @@ template <bool SWIGLU, bool OUT_F32>
 hipError_t launch_fp8(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, const int32_t* offsets,
                       int64_t rows, int E, int K, int ldb, int NT, void* out, float* out_scales,
                       hipStream_t stream) {
-  constexpr int smem = 2 * (kF8BM * kF8BK + 1024 + kF8BK * kF8BRow);
+  constexpr int smem = kF8Smem;
   auto kern = gemm_fp8_kernel<SWIGLU, OUT_F32>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, smem);
