@@ -110,6 +110,11 @@ hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int 
                                  const float* w2_scales, void* y_perm, int out_dt, void* scratch,
                                  hipStream_t stream, hipEvent_t between = nullptr);
 
+// Dense out[rows, N] (fp32) = A[rows, K] . B[K, N] with bf16 A and B (B N-contiguous),
+// K % 64 == 0, N % 8 == 0: the grouped-GEMM kernel with one expert.
+hipError_t launch_dense_gemm_f32out(const void* A, const void* B, int64_t rows, int K, int N, float* out,
+                                    hipStream_t stream);
+
 // FP8 (E4M3) path: x_perm codes + [rows, H/128] scales, weights as codes + 128x128-block scales;
 // the SwiGLU output h is re-quantised to E4M3 in 1x128 blocks in the scratch buffer
 // (fp8_hidden_bytes(rows, F) bytes of codes, then [rows, F/128] fp32 scales).

@@ -451,6 +451,13 @@ size_t grouped_swiglu_scratch_bytes(int64_t rows, int F, int dt) {
   return fp8_hidden_bytes(rows, F) + static_cast<size_t>(rows) * (F / 128) * 4;
 }
 
+hipError_t launch_dense_gemm_f32out(const void* A, const void* B, int64_t rows, int K, int N, float* out,
+                                    hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  return launch_bf16<128, false, true>(static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B), nullptr, rows,
+                                       1, K, N, static_cast<int>(ceil_div(N, kBN)), out, stream);
+}
+
 hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int dt,
                                  const int32_t* offsets, int64_t rows, int E, int H, int F,
                                  const void* w1, const float* w1_scales, const void* w2,

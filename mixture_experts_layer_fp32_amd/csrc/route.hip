@@ -115,6 +115,27 @@ __global__ __launch_bounds__(kRouteThreads) void route_split_kernel(const float*
   }
 }
 
+// The same split, stored [H][3 Ep] (N-contiguous, plane-major columns) for the grouped-GEMM
+// kernel used when there are many experts: column p * Ep + e holds part p of W_r[:, e].
+__global__ __launch_bounds__(kRouteThreads) void route_split_kn_kernel(const float* __restrict__ w, int H, int E,
+                                                                      int Ep, bf16_t* __restrict__ wkn) {
+  const int64_t n = static_cast<int64_t>(Ep) * H;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kRouteThreads + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kRouteThreads) {
+    const int h = static_cast<int>(i / Ep), e = static_cast<int>(i % Ep);
+    float v = e < E ? w[static_cast<int64_t>(h) * E + e] : 0.0f;
+    bf16_t p0 = f32_to_bf16(v);
+    float r1 = v - bf16_to_f32(p0);
+    bf16_t p1 = f32_to_bf16(r1);
+    float r2 = r1 - bf16_to_f32(p1);
+    bf16_t p2 = f32_to_bf16(r2);
+    bf16_t* row = wkn + static_cast<int64_t>(h) * 3 * Ep;
+    row[e] = p0;
+    row[Ep + e] = p1;
+    row[2 * Ep + e] = p2;
+  }
+}
+
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4v;
 
 // A workgroup computes 16*TM tokens x 16*TN experts with v_mfma_f32_16x16x32_bf16; its 4 waves
@@ -215,13 +236,16 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
+// With `parts` (the [T][3 Ep] products of x with the three weight parts) the logit is
+// (lo + mid) + hi, written to `logits`; otherwise the logits are read from `logits`.
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
-    const float* __restrict__ logits, const float* __restrict__ bias, int64_t T, int E, int k,
-    int score, int norm, int32_t* __restrict__ ids, float* __restrict__ gates) {
+    float* __restrict__ logits, const float* __restrict__ parts, int Ep, const float* __restrict__ bias, int64_t T,
+    int E, int k, int score, int norm, int32_t* __restrict__ ids, float* __restrict__ gates) {
   const int lane = threadIdx.x % kWave;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * (kRouteThreads / kWave) + threadIdx.x / kWave;
   if (t >= T) return;  // whole wave exits together
-  const float* lt = logits + t * E;
+  float* lt = logits + t * E;
+  const float* pt = parts ? parts + t * 3 * Ep : nullptr;
 
   float lg[kMaxPerLane], key[kMaxPerLane];
   float lmax = -INFINITY;
@@ -229,7 +253,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   for (int i = 0; i < kMaxPerLane; ++i) {
     int e = lane + i * kWave;
     if (e < E) {
-      lg[i] = lt[e];
+      if (pt) {
+        lg[i] = (pt[2 * Ep + e] + pt[Ep + e]) + pt[e];
+        lt[e] = lg[i];
+      } else {
+        lg[i] = lt[e];
+      }
       key[i] = bias ? lg[i] + bias[e] : lg[i];  // one fp32 add
       lmax = fmaxf(lmax, lg[i]);
     } else {
@@ -318,11 +347,25 @@ int padded_experts(int E) { return (E + 15) / 16 * 16; }
 
 size_t split_bytes(int H, int E) { return static_cast<size_t>(3) * padded_experts(E) * H * sizeof(bf16_t); }
 
-hipError_t launch_logits_bf16(const bf16_t* x, const float* w, float* logits, int64_t T, int H, int E,
-                              bf16_t* wsplit, hipStream_t stream) {
+// Many experts (>= 64): the projection is a dense GEMM x [T, H] . W_split [H, 3 Ep] on the
+// grouped-GEMM kernel (fp32 output, one row band per 128 tokens), summed per expert by top-k.
+bool logits_by_gemm(int H, int E) { return padded_experts(E) >= 64 && H % 64 == 0; }
+
+size_t parts_bytes(int64_t T, int E) {
+  return (static_cast<size_t>(T) * 3 * padded_experts(E) * sizeof(float) + 255) & ~static_cast<size_t>(255);
+}
+
+hipError_t launch_logits_bf16(const bf16_t* x, const float* w, float* logits, float* parts, int64_t T, int H,
+                              int E, bf16_t* wsplit, hipStream_t stream) {
   const int Ep = padded_experts(E);
   const int64_t n = static_cast<int64_t>(Ep) * H;
   const unsigned gs = static_cast<unsigned>(ceil_div(n, kRouteThreads) < 2048 ? ceil_div(n, kRouteThreads) : 2048);
+  if (parts) {
+    hipLaunchKernelGGL(route_split_kn_kernel, dim3(gs), dim3(kRouteThreads), 0, stream, w, H, E, Ep, wsplit);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_dense_gemm_f32out(x, wsplit, T, H, 3 * Ep, parts, stream);
+  }
   hipLaunchKernelGGL(route_split_kernel, dim3(gs), dim3(kRouteThreads), 0, stream, w, H, E, Ep, wsplit);
   if (Ep <= 16) {
     dim3 grid(static_cast<unsigned>(ceil_div(T, 16)), 1);
@@ -344,7 +387,9 @@ hipError_t launch_logits_bf16(const bf16_t* x, const float* w, float* logits, in
 
 size_t route_scratch_bytes(int64_t T, int H, int E, bool logits_given) {
   size_t a = logits_given ? 0 : (static_cast<size_t>(T) * E * sizeof(float) + 255) & ~static_cast<size_t>(255);
-  return a + split_bytes(H, E);
+  a += (split_bytes(H, E) + 255) & ~static_cast<size_t>(255);
+  if (logits_by_gemm(H, E)) a += parts_bytes(T, E);
+  return a;
 }
 
 hipError_t launch_route(const void* x, int x_dt, const float* w_router, const float* bias, int64_t T,
@@ -356,14 +401,17 @@ hipError_t launch_route(const void* x, int x_dt, const float* w_router, const fl
     lg = reinterpret_cast<float*>(sp);
     sp += (static_cast<size_t>(T) * E * sizeof(float) + 255) & ~static_cast<size_t>(255);
   }
+  bf16_t* wsplit = reinterpret_cast<bf16_t*>(sp);
+  sp += (split_bytes(H, E) + 255) & ~static_cast<size_t>(255);
+  float* parts = (x_dt != 0 && logits_by_gemm(H, E)) ? reinterpret_cast<float*>(sp) : nullptr;
   hipError_t err = (x_dt == 0)
                        ? launch_logits(static_cast<const float*>(x), w_router, lg, T, H, E, stream)
-                       : launch_logits_bf16(static_cast<const bf16_t*>(x), w_router, lg, T, H, E,
-                                            reinterpret_cast<bf16_t*>(sp), stream);
+                       : launch_logits_bf16(static_cast<const bf16_t*>(x), w_router, lg, parts, T, H, E, wsplit,
+                                            stream);
   if (err != hipSuccess) return err;
   dim3 grid(static_cast<unsigned>(ceil_div(T, kRouteThreads / kWave)));
-  hipLaunchKernelGGL(route_topk_kernel, grid, dim3(kRouteThreads), 0, stream, lg, bias, T, E, k, score,
-                     norm, ids, gates);
+  hipLaunchKernelGGL(route_topk_kernel, grid, dim3(kRouteThreads), 0, stream, lg, parts, padded_experts(E), bias,
+                     T, E, k, score, norm, ids, gates);
   return hipGetLastError();
 }
 

@@ -32,6 +32,8 @@ SMALL = {
     "deepseek_small": _small("deepseek_v3", T=257, H=512, E=32, k=8, F=256, Fs=384),
     # >= 768 rows per expert: the 256-row GEMM tiles; H not a multiple of 256 (ragged N tile)
     "mixtral_bigtile": _small("mixtral_8x7b", T=1700, H=320, E=3, k=2, F=384),
+    # >= 64 experts: router logits through the dense GEMM kernel (3 x 96 columns: a ragged N tile)
+    "qwen3_e96": _small("qwen3_235b", T=300, H=256, E=96, k=8, F=128),
 }
 
 
