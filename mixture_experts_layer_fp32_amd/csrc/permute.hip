@@ -124,11 +124,24 @@ __global__ __launch_bounds__(kScatterThreads) void perm_scatter_copy_kernel(
   int row = resolve_row(ids, base, local_rank, t, k, nblk, lane, row_map, src_token);
   if (!x_perm) return;
   const uint4* src = x + t * row_vecs;
-  for (int c = lane; c < row_vecs; c += kWave) {
-    uint4 v = src[c];
+  // four 16-byte loads in flight per lane before their k stores each
+  // (loads past the row end re-read its last piece; only in-row pieces are stored)
+  constexpr int U = 4;
+  for (int c0 = lane; c0 < row_vecs; c0 += U * kWave) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave;
+      v[u] = src[c < row_vecs ? c : row_vecs - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)  // keep the loaded values: no re-load inside the store loop
+      asm volatile("" : "+v"(v[u].x), "+v"(v[u].y), "+v"(v[u].z), "+v"(v[u].w));
     for (int j = 0; j < k; ++j) {
-      int r = __shfl(row, j, kWave);
-      x_perm[static_cast<int64_t>(r) * row_vecs + c] = v;
+      uint4* dst = x_perm + static_cast<int64_t>(__shfl(row, j, kWave)) * row_vecs;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (c0 + u * kWave < row_vecs) dst[c0 + u * kWave] = v[u];
     }
   }
 }
@@ -174,16 +187,26 @@ __global__ __launch_bounds__(kScatterThreads) void perm_scatter_fp8_kernel(
   const int row_vecs = H / 8;
   const int nsb = H / 128;
   const uint4* src = x + t * row_vecs;
-  for (int c0 = 0; c0 < row_vecs; c0 += kWave) {  // H % 128 == 0: whole 16-lane groups
-    const int c = c0 + lane;
-    const bool live = c < row_vecs;
-    float s;
-    const uint2 packed = quant_e4m3_x8(live ? src[c] : make_uint4(0, 0, 0, 0), s);
-    for (int j = 0; j < k; ++j) {
-      int r = __shfl(row, j, kWave);
-      if (live) {
-        x_perm[static_cast<int64_t>(r) * row_vecs + c] = packed;
-        if ((lane & 15) == 0) scales[static_cast<int64_t>(r) * nsb + c / 16] = s;
+  // two 16-byte loads in flight per lane; H % 128 == 0: whole 16-lane groups stay together
+  for (int c0 = 0; c0 < row_vecs; c0 += 2 * kWave) {
+    uint4 v[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + u * kWave + lane;
+      v[u] = c < row_vecs ? src[c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + u * kWave + lane;
+      const bool live = c < row_vecs;
+      float s;
+      const uint2 packed = quant_e4m3_x8(v[u], s);
+      for (int j = 0; j < k; ++j) {
+        int r = __shfl(row, j, kWave);
+        if (live) {
+          x_perm[static_cast<int64_t>(r) * row_vecs + c] = packed;
+          if ((lane & 15) == 0) scales[static_cast<int64_t>(r) * nsb + c / 16] = s;
+        }
       }
     }
   }
