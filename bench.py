@@ -32,13 +32,22 @@ PEAK_BF16_TFLOPS = PEAK_TFLOPS["bf16"]
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 STAGES = ["route", "permute", "gemm1_swiglu", "gemm2", "shared_expert", "combine"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_swiglu_mixtral_8x7b_hbm_traffic.txt")
-GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_fp32_amd", "csrc", "gemm.hip")
+# the first grouped GEMM's kernel is built from these files
+GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_fp32_amd", "csrc", f)
+                for f in ("gemm.hip", "gemm_common.hpp", "common.hpp")]
+
+
+def gemm_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic():
     """HBM bytes per launch of the first grouped GEMM from the committed PMC summary, or None
     when the kernel source changed since the counters were taken."""
-    import hashlib
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -46,8 +55,7 @@ def measured_traffic():
         if "=" in line and not line.lstrip().startswith("#"):
             key, val = line.split("=", 1)
             kv[key.strip()] = val.strip()
-    sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
-    if kv.get("gemm_source_sha256") != sha or "traffic_bytes_per_launch" not in kv:
+    if kv.get("gemm_source_sha256") != gemm_source_sha256() or "traffic_bytes_per_launch" not in kv:
         return None
     return float(kv["traffic_bytes_per_launch"])
 
@@ -249,7 +257,8 @@ def main():
     g1_s = avg_ms["gemm1_swiglu"] * 1e-3
     mfma_bound = g1["flops"] / (peak_tf * 1e12) >= g1["bytes"] / (PEAK_HBM_GBS * 1e9)
     kernel = {"fp8": "gemm_fp8_kernel<swiglu> (grouped e4m3 GEMM1 + fused SwiGLU + 1x128 re-quantisation)",
-              "bf16": "gemm_bf16_kernel<swiglu> (grouped GEMM1 + fused SwiGLU)",
+              "bf16": f"gemm_bf16_kernel<{256 if cfg.T * cfg.k >= 192 * cfg.E else 128}, swiglu> "
+                      "(grouped GEMM1 + fused SwiGLU)",
               "f32": "gemm_f32_kernel<swiglu> (grouped fp32 GEMM1 + fused SwiGLU)"}[mm_dtype]
     if mfma_bound:
         achieved, peak, unit = g1["flops"] / g1_s / 1e12, peak_tf, "TFLOP/s"
@@ -274,7 +283,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        default_sample = {"mixtral_8x7b": 1024, "qwen3_235b": 256, "deepseek_v3": 128,
+        default_sample = {"mixtral_8x7b": 4096, "qwen3_235b": 256, "deepseek_v3": 128,
                           "deepseek_v3_fp8_zipf": 128, "tiny_fp32": 256}
         out["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_sample_tokens or default_sample[args.workload])
     print(json.dumps(out), flush=True)

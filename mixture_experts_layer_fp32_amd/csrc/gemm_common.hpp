@@ -56,8 +56,18 @@ __device__ __forceinline__ int whole_tiles(int total, int ncu, int S) {
   return S > 1 ? total - total % ncu : total;
 }
 
+// Rows per m-tile when an expert's M rows are spread evenly over its ceil(M / BM) m-tiles, in
+// whole 32-row blocks (<= BM).  Equal tiles run at equal speed (a tile computes only its live
+// row blocks), so the m-tiles that share a weight tile stay in step and share it through L2.
+// The last tile takes the remainder, which can be empty when rounding up overshoots.
+template <int BM>
+__device__ __forceinline__ int64_t balanced_rows(int64_t M, int mtiles) {
+  const int64_t per = (M + mtiles - 1) / mtiles;
+  return (per + 31) / 32 * 32;
+}
+
 // Linear tile L -> (expert, m-tile, n-tile); n-major inside an expert so the m-tiles of one
-// weight tile are adjacent.
+// weight tile are adjacent.  A tile covers rows [row0, row_end): at most BM of its expert.
 template <int BM>
 __device__ void locate_tile(const int32_t* offsets, int64_t rows, int E, int NT, const int* s_pref, int L,
                             TileMap& tm) {
@@ -66,8 +76,9 @@ __device__ void locate_tile(const int32_t* offsets, int64_t rows, int E, int NT,
     tm.expert = 0;
     tm.nt = L / mtiles;
     tm.mt = L % mtiles;
-    tm.row0 = static_cast<int64_t>(tm.mt) * BM;
-    tm.row_end = rows;
+    const int64_t rpt = balanced_rows<BM>(rows, mtiles);
+    tm.row0 = static_cast<int64_t>(tm.mt) * rpt;
+    tm.row_end = tm.row0 + rpt < rows ? tm.row0 + rpt : rows;
     return;
   }
   // expert whose tile range [s_pref[e]*NT, s_pref[e+1]*NT) holds L (binary search in LDS)
@@ -82,8 +93,9 @@ __device__ void locate_tile(const int32_t* offsets, int64_t rows, int E, int NT,
   tm.expert = e;
   tm.nt = idx / me;
   tm.mt = idx % me;
-  tm.row0 = static_cast<int64_t>(offsets[e]) + static_cast<int64_t>(tm.mt) * BM;
-  tm.row_end = offsets[e + 1];
+  const int64_t rpt = balanced_rows<BM>(offsets[e + 1] - offsets[e], me);
+  tm.row0 = static_cast<int64_t>(offsets[e]) + static_cast<int64_t>(tm.mt) * rpt;
+  tm.row_end = tm.row0 + rpt < offsets[e + 1] ? tm.row0 + rpt : offsets[e + 1];
 }
 
 // Returns false if this workgroup has no tile.  `s_pref` is LDS of >= E+1 ints.  Workgroups
@@ -100,7 +112,7 @@ __device__ bool map_tile(const int32_t* offsets, int64_t rows, int E, int NT, in
     const int L = (w % 8) * per + w / 8;
     if (L >= whole) return false;
     locate_tile<BM>(offsets, rows, E, NT, s_pref, L, tm);
-    return true;
+    return tm.row0 < tm.row_end;  // an even split can leave the last m-tile empty
   }
   // Tail: as many bands per tile as still fit one wave (at most S; bands are whole 32-row
   // blocks).  Pieces P = tile * SB + band are XCD-remapped like the whole tiles, whole tiles'
@@ -117,13 +129,10 @@ __device__ bool map_tile(const int32_t* offsets, int64_t rows, int E, int NT, in
   const int P = (q % 8) * per_t + q / 8;
   if (P >= pieces) return false;
   locate_tile<BM>(offsets, rows, E, NT, s_pref, whole + P / SB, tm);
-  const int64_t tile_end = tm.row0 + BM;
   tm.row0 += static_cast<int64_t>(P % SB) * band_rows;
-  int64_t band_end = tm.row0 + band_rows;
-  if (band_end > tile_end) band_end = tile_end;
+  const int64_t band_end = tm.row0 + band_rows;
   if (band_end < tm.row_end) tm.row_end = band_end;
-  if (tm.row0 >= tm.row_end) return false;  // band past the tile's or the expert's last row
-  return true;
+  return tm.row0 < tm.row_end;  // band past the tile's last row, or an empty tile
 }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
