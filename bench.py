@@ -70,7 +70,7 @@ def _hip():
 
 
 def algorithmic(cfg, active_experts=None):
-    """Useful FLOPs and the bytes each stage must move at the ABI boundary.
+    """Useful FLOPs and the bytes each stage of the fused forward must move (unique HBM bytes).
 
     Activations in the config's dtype (bf16 2 B, fp32 4 B); weights and the permuted / hidden
     rows of the e4m3 path 1 B plus one fp32 scale per 128 values (weights: per 128 x 128 block).
@@ -86,12 +86,15 @@ def algorithmic(cfg, active_experts=None):
     sh = bool(Fs)
     return {
         "route": dict(flops=2 * T * H * E, bytes=T * H * a + H * E * 4 + R * 8 + (E * 4 if cfg.zipf_bias else 0)),
-        "permute": dict(flops=0, bytes=T * H * a + R * 4 + R * rowb(H) + R * 8 + (2 * E + 1) * 4),
-        "gemm1_swiglu": dict(flops=4 * R * H * F, bytes=R * rowb(H) + Ea * wbytes(H, 2 * F) + R * rowb(F) + (E + 1) * 4),
+        # the fused forward writes no permuted copy: dispatch = ids -> maps (+ the e4m3 path's
+        # per-token quantisation of x), and GEMM1 gathers the token rows it needs
+        "permute": dict(flops=0, bytes=R * 4 + R * 8 + (2 * E + 1) * 4 + ((T * H * a + T * rowb(H)) if fp8 else 0)),
+        "gemm1_swiglu": dict(flops=4 * R * H * F,
+                             bytes=T * rowb(H) + R * 4 + Ea * wbytes(H, 2 * F) + R * rowb(F) + (E + 1) * 4),
         "gemm2": dict(flops=2 * R * F * H, bytes=R * rowb(F) + Ea * wbytes(F, H) + R * H * a + (E + 1) * 4),
         "shared_expert": dict(flops=6 * T * H * Fs,
-                              bytes=(T * H * a + (T * rowb(H) * 2 if fp8 else 0) + wbytes(H, 2 * Fs) + wbytes(Fs, H)
-                                     + 2 * T * rowb(Fs) + T * H * a) if sh else 0),
+                              bytes=(T * rowb(H) + wbytes(H, 2 * Fs) + wbytes(Fs, H) + 2 * T * rowb(Fs) + T * H * a)
+                              if sh else 0),
         "combine": dict(flops=0, bytes=R * H * a + R * 8 + T * H * a + (T * H * a if sh else 0)),
         "active_flops": 2 * T * H * E + 6 * R * H * F + 6 * T * H * Fs,
     }

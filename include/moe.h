@@ -121,7 +121,7 @@ moe_status moe_permute(const void* x, moe_dtype x_dt, const int32_t* topk_ids, i
  *   dt = MOE_FP8_E4M3: x_perm e4m3 with x_perm_scales [rows, H/128]; w1/w2 e4m3 with
  *        w1_scales [E, H/128, 2F/128], w2_scales [E, F/128, H/128] (128x128 blocks); h is
  *        quantised to e4m3 in 1x128 blocks inside the path; y_perm bf16 or fp32.
- * Sizes: H and F multiples of 128 (bf16 / fp8) or of 32 (fp32).
+ * Sizes: bf16: H a multiple of 64 and F of 128; e4m3: both multiples of 128; fp32: both of 32.
  * workspace: at least moe_grouped_swiglu_workspace_size(rows, F, dt) bytes (holds h).
  * Rows beyond offsets[E] are not written.
  * ------------------------------------------------------------------------------------- */
@@ -166,7 +166,10 @@ typedef struct {
 
 /* Optional views of the intermediates: every non-NULL pointer receives that stage's
  * output (shapes as in the stage calls; x_perm / y_perm in the dtypes moe_forward uses:
- * x_perm in w_dt (e4m3 codes for FP8, with x_perm_scales), y_perm in x_dt).
+ * x_perm in w_dt (e4m3 codes for FP8, with x_perm_scales, which is then required), y_perm in
+ * x_dt).  moe_forward itself does not materialise x_perm: its first grouped GEMM reads the
+ * token rows of x (for FP8: of x quantised once per token) through src_token; x_perm is
+ * written only when requested here.  All pointers 16-byte aligned.
  * stage_events: optional hipEvent_t handles recorded on `stream` at the stage boundaries
  * (0 before route, 1 after route, 2 after permute, 3 after the first grouped GEMM,
  * 4 after the second, 5 after the shared expert, 6 after combine); NULL entries are skipped. */

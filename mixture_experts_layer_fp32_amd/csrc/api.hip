@@ -162,8 +162,8 @@ moe_status moe_unpermute_combine(const void* y_perm, moe_dtype y_dt, const int32
 namespace {
 
 struct ForwardPlan {
-  void *logits, *route_ws, *ids, *gates, *counts, *offsets, *row_map, *src, *perm_ws, *x_perm, *x_scales, *gemm_ws,
-      *y_perm, *sh_x, *sh_scales, *sh_ws, *sh_out;
+  void *logits, *route_ws, *ids, *gates, *counts, *offsets, *row_map, *src, *perm_ws, *x_perm, *x_scales, *xq,
+      *xq_scales, *gemm_ws, *y_perm, *sh_ws, *sh_out;
   size_t bytes;
 };
 
@@ -191,9 +191,12 @@ moe_status validate_layer(const moe_layer* L) {
   return MOE_OK;
 }
 
+// The first grouped GEMM gathers its rows straight from x (or from x quantised once per token
+// in the e4m3 path) through src_token, so the permuted copy x_perm exists only when the caller
+// asks for it through moe_debug.
 ForwardPlan plan(const moe_layer* L, int64_t T, void* ws, const moe_debug* dbg) {
   const int64_t R = T * L->k;
-  const size_t xe = elt_bytes(L->x_dt), we = elt_bytes(L->w_dt);
+  const size_t xe = elt_bytes(L->x_dt);
   const bool fp8 = L->w_dt == MOE_FP8_E4M3;
   Carve c(ws);
   ForwardPlan p{};
@@ -207,13 +210,14 @@ ForwardPlan plan(const moe_layer* L, int64_t T, void* ws, const moe_debug* dbg) 
   p.row_map = pick(dbg ? dbg->row_map : nullptr, R * 4);
   p.src = pick(dbg ? dbg->src_token : nullptr, R * 4);
   p.perm_ws = c.take(moe::permute_scratch_bytes(T, L->E, L->k));
-  p.x_perm = pick(dbg ? dbg->x_perm : nullptr, R * L->H * we);
-  p.x_scales = fp8 ? pick(dbg ? dbg->x_perm_scales : nullptr, R * (L->H / 128) * 4) : nullptr;
+  // debug-only outputs with no workspace share (the layout must not depend on dbg)
+  p.x_perm = dbg ? dbg->x_perm : nullptr;
+  p.x_scales = (fp8 && p.x_perm) ? dbg->x_perm_scales : nullptr;
+  p.xq = fp8 ? c.take(T * L->H) : nullptr;
+  p.xq_scales = fp8 ? c.take(T * (L->H / 128) * 4) : nullptr;
   p.gemm_ws = c.take(moe::grouped_swiglu_scratch_bytes(R, L->F, L->w_dt));
   p.y_perm = pick(dbg ? dbg->y_perm : nullptr, R * L->H * xe);
   if (L->Fs > 0) {
-    p.sh_x = fp8 ? c.take(T * L->H) : nullptr;
-    p.sh_scales = fp8 ? c.take(T * (L->H / 128) * 4) : nullptr;
     p.sh_ws = c.take(moe::grouped_swiglu_scratch_bytes(T, L->Fs, L->w_dt));
     p.sh_out = c.take(T * L->H * xe);
   }
@@ -236,6 +240,8 @@ moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, co
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;  // nothing to do; empty tensors may carry null pointers
   if (!x || !y || !aligned16(x) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  if (dbg && dbg->x_perm && (!aligned16(dbg->x_perm) || (L->w_dt == MOE_FP8_E4M3 && !dbg->x_perm_scales)))
+    return MOE_ERR_INVALID_ARG;  // e4m3 rows come with their scales
   const size_t need = plan(L, T, nullptr, nullptr).bytes;
   if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
   ForwardPlan p = plan(L, T, workspace, dbg);
@@ -256,22 +262,22 @@ moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, co
                           L->w_dt, static_cast<float*>(p.x_scales), static_cast<int32_t*>(p.row_map),
                           static_cast<int32_t*>(p.src), static_cast<int32_t*>(p.counts),
                           static_cast<int32_t*>(p.offsets), p.perm_ws, s);
+  // the e4m3 path quantises each token once (1x128 blocks); the GEMM gathers its rows
+  const void* a = x;
+  if (e == hipSuccess && fp8) {
+    e = moe::launch_quant_rows_fp8(x, L->x_dt, T, L->H, static_cast<uint8_t*>(p.xq),
+                                   static_cast<float*>(p.xq_scales), s);
+    a = p.xq;
+  }
   if (e == hipSuccess) e = mark(2);
   if (e != hipSuccess) return from_hip(e);
-  e = moe::launch_grouped_swiglu(p.x_perm, static_cast<float*>(p.x_scales), L->w_dt,
-                                 static_cast<int32_t*>(p.offsets), R, L->E, L->H, L->F, L->w1, L->w1_scales,
-                                 L->w2, L->w2_scales, p.y_perm, L->x_dt, p.gemm_ws, s, ev(3));
+  e = moe::launch_grouped_swiglu(a, static_cast<float*>(p.xq_scales), L->w_dt, static_cast<int32_t*>(p.offsets),
+                                 R, L->E, L->H, L->F, L->w1, L->w1_scales, L->w2, L->w2_scales, p.y_perm, L->x_dt,
+                                 p.gemm_ws, s, ev(3), static_cast<int32_t*>(p.src));
   if (e == hipSuccess) e = mark(4);
   if (e != hipSuccess) return from_hip(e);
-  if (L->Fs > 0) {
-    const void* sx = x;
-    if (fp8) {  // the shared expert sees every token, quantised like the routed rows
-      e = moe::launch_quant_rows_fp8(x, L->x_dt, T, L->H, static_cast<uint8_t*>(p.sh_x),
-                                     static_cast<float*>(p.sh_scales), s);
-      if (e != hipSuccess) return from_hip(e);
-      sx = p.sh_x;
-    }
-    e = moe::launch_grouped_swiglu(sx, static_cast<float*>(p.sh_scales), L->w_dt, nullptr, T, 1, L->H, L->Fs,
+  if (L->Fs > 0) {  // every token, unpermuted (quantised like the routed rows in the e4m3 path)
+    e = moe::launch_grouped_swiglu(a, static_cast<float*>(p.xq_scales), L->w_dt, nullptr, T, 1, L->H, L->Fs,
                                    L->ws1, L->ws1_scales, L->ws2, L->ws2_scales, p.sh_out, L->x_dt, p.sh_ws, s);
     if (e != hipSuccess) return from_hip(e);
   }

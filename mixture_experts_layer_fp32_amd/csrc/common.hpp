@@ -103,12 +103,15 @@ hipError_t launch_permute(const void* x, int x_dt, const int32_t* ids, int64_t T
                           hipStream_t stream);
 
 size_t grouped_swiglu_scratch_bytes(int64_t rows, int F, int dt);
-// offsets == nullptr means one expert owning rows [0, rows) (the shared expert).
+// offsets == nullptr means one expert owning rows [0, rows) (the shared expert).  With
+// `gather`, row p of the first GEMM's A operand is row gather[p] of x_perm (and of x_scales):
+// the dispatch permutation fused into the GEMM's loads, so x_perm can be the unpermuted input.
 hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int dt,
                                  const int32_t* offsets, int64_t rows, int E, int H, int F,
                                  const void* w1, const float* w1_scales, const void* w2,
                                  const float* w2_scales, void* y_perm, int out_dt, void* scratch,
-                                 hipStream_t stream, hipEvent_t between = nullptr);
+                                 hipStream_t stream, hipEvent_t between = nullptr,
+                                 const int32_t* gather = nullptr);
 
 // Dense out[rows, N] (fp32) = A[rows, K] . B[K, N] with bf16 A and B (B N-contiguous),
 // K % 64 == 0, N % 8 == 0: the grouped-GEMM kernel with one expert.
@@ -122,7 +125,8 @@ size_t fp8_hidden_bytes(int64_t rows, int F);
 hipError_t launch_grouped_swiglu_fp8(const void* x_perm, const float* x_scales, const int32_t* offsets,
                                      int64_t rows, int E, int H, int F, const void* w1, const float* w1_scales,
                                      const void* w2, const float* w2_scales, void* y_perm, int out_dt,
-                                     void* scratch, hipStream_t stream, hipEvent_t between);
+                                     void* scratch, hipStream_t stream, hipEvent_t between,
+                                     const int32_t* gather);
 // Per-row 1x128 E4M3 quantisation of a dense [T, H] bf16 / fp32 matrix (shared-expert input).
 hipError_t launch_quant_rows_fp8(const void* x, int x_dt, int64_t T, int H, uint8_t* codes, float* scales,
                                  hipStream_t stream);

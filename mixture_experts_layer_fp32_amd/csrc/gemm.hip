@@ -74,7 +74,8 @@ struct Bf16Rings {
 template <int BM, int WM, bool SWIGLU, bool OUT_F32, int S>
 __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const int32_t* __restrict__ offsets,
-    int64_t rows, int E, int K, int ldb, int NT, void* __restrict__ out, int ncu) {
+    int64_t rows, int E, int K, int ldb, int NT, void* __restrict__ out, int ncu,
+    const int32_t* __restrict__ gather) {
   using R = Bf16Rings<BM>;
   constexpr int NA = R::NA, NB = R::NB;
   constexpr int NWAVE = 4 * WM;                // WM along M x 4 along N
@@ -113,6 +114,7 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     const int r = (NWAVE * p + wave) * 8 + lane / 8;
     int64_t grow = tm.row0 + r;
     if (grow >= tm.row_end) grow = tm.row_end - 1;
+    if (gather) grow = gather[grow];  // fused dispatch: row p of the tile is token gather[p]
     a_src[p] = A + grow * K + (((lane % 8) ^ ((r >> 1) & 7)) * 8);
   }
   // B round p of wave w covers k-rows 2 (8p + w) + lane / 32 (1 KB = 2 k-rows x 512 B); stored
@@ -324,7 +326,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(const float* __restr
                                                            const float* __restrict__ B,
                                                            const int32_t* __restrict__ offsets,
                                                            int64_t rows, int E, int K, int ldb, int NT,
-                                                           float* __restrict__ out) {
+                                                           float* __restrict__ out,
+                                                           const int32_t* __restrict__ gather) {
   __shared__ float sa[kF32BM][kF32BK + 1];
   __shared__ float sb[kF32BK][kF32BN + 4];
   __shared__ int s_pref[kMaxExpertsLds];
@@ -341,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(const float* __restr
     for (int i = tid; i < kF32BM * kF32BK; i += kThreads) {
       int r = i / kF32BK, kk = i % kF32BK;
       int64_t grow = tm.row0 + r;
-      sa[r][kk] = grow < tm.row_end ? A[grow * K + k0 + kk] : 0.0f;
+      sa[r][kk] = grow < tm.row_end ? A[(gather ? gather[grow] : grow) * K + k0 + kk] : 0.0f;
     }
     for (int i = tid; i < kF32BK * kF32BN; i += kThreads) {
       int kk = i / kF32BN, c = i % kF32BN;
@@ -405,7 +408,8 @@ int device_cus() {
 
 template <int BM, bool SWIGLU, bool OUT_F32, int WM = 2, int S = 1>
 hipError_t launch_bf16(const bf16_t* A, const bf16_t* B, const int32_t* offsets, int64_t rows, int E,
-                       int K, int ldb, int NT, void* out, hipStream_t stream, int ncu = 0) {
+                       int K, int ldb, int NT, void* out, hipStream_t stream, int ncu = 0,
+                       const int32_t* gather = nullptr) {
   constexpr int smem = Bf16Rings<BM>::SMEM;
   auto kern = gemm_bf16_kernel<BM, WM, SWIGLU, OUT_F32, S>;
   // once per instantiation (and never inside a stream capture after the first eager call)
@@ -413,7 +417,8 @@ hipError_t launch_bf16(const bf16_t* A, const bf16_t* B, const int32_t* offsets,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (attr != hipSuccess) return attr;
   const unsigned grid = grid_for(max_tiles<BM>(rows, E, offsets == nullptr), NT, ncu, S);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256 * WM), smem, stream, A, B, offsets, rows, E, K, ldb, NT, out, ncu);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256 * WM), smem, stream, A, B, offsets, rows, E, K, ldb, NT, out, ncu,
+                     gather);
   return hipGetLastError();
 }
 
@@ -430,10 +435,10 @@ hipError_t launch_bf16_down(const bf16_t* h, const bf16_t* w2, const int32_t* of
 template <int BM>
 hipError_t launch_bf16_pair(const void* x_perm, const void* w1, const void* w2, const int32_t* offsets,
                             int64_t rows, int E, int H, int F, void* y_perm, int out_dt, void* scratch,
-                            hipStream_t stream, hipEvent_t between) {
+                            hipStream_t stream, hipEvent_t between, const int32_t* gather) {
   bf16_t* h = static_cast<bf16_t*>(scratch);
   hipError_t err = launch_bf16<BM, true, false>(static_cast<const bf16_t*>(x_perm), static_cast<const bf16_t*>(w1),
-                                                offsets, rows, E, H, 2 * F, F / 128, h, stream);
+                                                offsets, rows, E, H, 2 * F, F / 128, h, stream, 0, gather);
   if (err != hipSuccess) return err;
   if (between && (err = hipEventRecord(between, stream)) != hipSuccess) return err;
   const int nt2 = static_cast<int>(ceil_div(H, kBN));
@@ -462,32 +467,34 @@ hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int 
                                  const int32_t* offsets, int64_t rows, int E, int H, int F,
                                  const void* w1, const float* w1_scales, const void* w2,
                                  const float* w2_scales, void* y_perm, int out_dt, void* scratch,
-                                 hipStream_t stream, hipEvent_t between) {
+                                 hipStream_t stream, hipEvent_t between, const int32_t* gather) {
   if (dt == 2)
     return launch_grouped_swiglu_fp8(x_perm, x_scales, offsets, rows, E, H, F, w1, w1_scales, w2, w2_scales,
-                                     y_perm, out_dt, scratch, stream, between);
+                                     y_perm, out_dt, scratch, stream, between, gather);
   if (dt == 0) {
     float* h = static_cast<float*>(scratch);
     const int nt1 = F / 32, nt2 = static_cast<int>(ceil_div(H, kF32BN));
     const unsigned g1 = grid_for(max_tiles<kF32BM>(rows, E, offsets == nullptr), nt1);
     hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(g1), dim3(kThreads), 0, stream,
                        static_cast<const float*>(x_perm), static_cast<const float*>(w1), offsets, rows, E,
-                       H, 2 * F, nt1, h);
+                       H, 2 * F, nt1, h, gather);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (between && (err = hipEventRecord(between, stream)) != hipSuccess) return err;
     const unsigned g2 = grid_for(max_tiles<kF32BM>(rows, E, offsets == nullptr), nt2);
     hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(g2), dim3(kThreads), 0, stream, h,
                        static_cast<const float*>(w2), offsets, rows, E, F, H, nt2,
-                       static_cast<float*>(y_perm));
+                       static_cast<float*>(y_perm), static_cast<const int32_t*>(nullptr));
     return hipGetLastError();
   }
   if (dt == 1) {
     // 256-row tiles when experts average >= 192 rows (the last, partial m-tile of an expert only
     // computes its live 32-row blocks), else 128-row tiles
     const bool big = offsets == nullptr ? rows >= 192 : rows >= 192 * static_cast<int64_t>(E);
-    return big ? launch_bf16_pair<256>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream, between)
-               : launch_bf16_pair<128>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream, between);
+    return big ? launch_bf16_pair<256>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream,
+                                       between, gather)
+               : launch_bf16_pair<128>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream,
+                                       between, gather);
   }
   return hipErrorNotSupported;
 }

@@ -50,7 +50,7 @@ template <bool SWIGLU, bool OUT_F32>
 __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ A_scales, const uint8_t* __restrict__ B,
     const float* __restrict__ B_scales, const int32_t* __restrict__ offsets, int64_t rows, int E, int K,
-    int ldb, int NT, void* __restrict__ out, float* __restrict__ out_scales) {
+    int ldb, int NT, void* __restrict__ out, float* __restrict__ out_scales, const int32_t* __restrict__ gather) {
   constexpr int NWAVE = kGemmThreads / kWave;  // 8
   constexpr int BM = kF8BM;
   constexpr int FM = 2, FN = 2;
@@ -87,6 +87,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
     const int r = (NWAVE * p + wave) * 8 + lane / 8;
     int64_t grow = tm.row0 + r;
     if (grow >= tm.row_end) grow = tm.row_end - 1;
+    if (gather) grow = gather[grow];  // fused dispatch: row p of the tile is token gather[p]
     a_src[p] = A + grow * K + (((lane % 8) ^ ((r >> 1) & 7)) * 16);
   }
   // row scales of the step: waves 0 and 1 gather 64 rows each (one dword per lane)
@@ -94,6 +95,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
   {
     int64_t grow = tm.row0 + (wave % 2) * 64 + lane;
     if (grow >= tm.row_end) grow = tm.row_end - 1;
+    if (gather) grow = gather[grow];
     as_src = A_scales + grow * nkb;
   }
   // B round p of wave w covers k-rows 4 (8p + w) + lane / 16 (1 KB = 4 k-rows x 256 B); stored
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
 template <bool SWIGLU, bool OUT_F32>
 hipError_t launch_fp8(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, const int32_t* offsets,
                       int64_t rows, int E, int K, int ldb, int NT, void* out, float* out_scales,
-                      hipStream_t stream) {
+                      hipStream_t stream, const int32_t* gather = nullptr) {
   constexpr int smem = kF8Smem;
   auto kern = gemm_fp8_kernel<SWIGLU, OUT_F32>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -346,7 +348,7 @@ hipError_t launch_fp8(const uint8_t* A, const float* As, const uint8_t* B, const
   if (attr != hipSuccess) return attr;
   const unsigned grid = grid_for(max_tiles<kF8BM>(rows, E, offsets == nullptr), NT);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), smem, stream, A, As, B, Bs, offsets, rows, E, K, ldb,
-                     NT, out, out_scales);
+                     NT, out, out_scales, gather);
   return hipGetLastError();
 }
 
@@ -359,12 +361,12 @@ size_t fp8_hidden_bytes(int64_t rows, int F) {
 hipError_t launch_grouped_swiglu_fp8(const void* x_perm, const float* x_scales, const int32_t* offsets,
                                      int64_t rows, int E, int H, int F, const void* w1, const float* w1_scales,
                                      const void* w2, const float* w2_scales, void* y_perm, int out_dt,
-                                     void* scratch, hipStream_t stream, hipEvent_t between) {
+                                     void* scratch, hipStream_t stream, hipEvent_t between, const int32_t* gather) {
   uint8_t* hq = static_cast<uint8_t*>(scratch);
   float* hs = reinterpret_cast<float*>(static_cast<char*>(scratch) + fp8_hidden_bytes(rows, F));
   hipError_t err = launch_fp8<true, false>(static_cast<const uint8_t*>(x_perm), x_scales,
                                            static_cast<const uint8_t*>(w1), w1_scales, offsets, rows, E, H, 2 * F,
-                                           F / 128, hq, hs, stream);
+                                           F / 128, hq, hs, stream, gather);
   if (err != hipSuccess) return err;
   if (between && (err = hipEventRecord(between, stream)) != hipSuccess) return err;
   const int nt2 = static_cast<int>(ceil_div(H, kBN));
