@@ -138,16 +138,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_split_kn_kernel(const flo
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4v;
 
-// A workgroup computes 16*TM tokens x 16*TN experts with v_mfma_f32_16x16x32_bf16; its 4 waves
-// split H four ways (each keeping U k-steps of loads in flight) and their partial sums are
-// added in LDS.  Operand layout: lane l holds row (l % 16), k = 8*(l/16) .. +8 of a 32-wide
+// A workgroup computes 16*TM tokens x 16*TN experts with v_mfma_f32_16x16x32_bf16; its NW waves
+// split H NW ways (each keeping U k-steps of loads in flight) and their partial sums are added
+// in LDS.  Operand layout: lane l holds row (l % 16), k = 8*(l/16) .. +8 of a 32-wide
 // k-step (A: token rows of x; B: expert rows of the split weight); accumulator slot r of lane l
 // is token 4*(l/16) + r, expert l % 16.
-template <int TM, int TN, int U>
-__global__ __launch_bounds__(kRouteThreads) void route_logits_mfma_kernel(
+template <int TM, int TN, int U, int NW = 4>
+__global__ __launch_bounds__(NW * 64) void route_logits_mfma_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ ws, float* __restrict__ logits, int64_t T,
     int H, int E, int Ep) {
-  constexpr int NW = kRouteThreads / kWave;
   __shared__ float part[NW][TM][TN][4][kWave];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -369,7 +368,8 @@ hipError_t launch_logits_bf16(const bf16_t* x, const float* w, float* logits, fl
   hipLaunchKernelGGL(route_split_kernel, dim3(gs), dim3(kRouteThreads), 0, stream, w, H, E, Ep, wsplit);
   if (Ep <= 16) {
     dim3 grid(static_cast<unsigned>(ceil_div(T, 16)), 1);
-    hipLaunchKernelGGL((route_logits_mfma_kernel<1, 1, 4>), grid, dim3(kRouteThreads), 0, stream, x, wsplit,
+    // few experts: 16 waves split H so that each CU keeps many x loads in flight
+    hipLaunchKernelGGL((route_logits_mfma_kernel<1, 1, 4, 16>), grid, dim3(16 * kWave), 0, stream, x, wsplit,
                        logits, T, H, E, Ep);
   } else if (Ep % 64 == 0) {
     dim3 grid(static_cast<unsigned>(ceil_div(T, 32)), static_cast<unsigned>(Ep / 64));
