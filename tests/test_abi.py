@@ -140,3 +140,19 @@ def test_forward_workspace_checks():
     assert L.moe_forward(ctypes.byref(lay), P, 64, P, None, None, need, None) == WS
     assert L.moe_forward(ctypes.byref(lay), P, 0, P, None, P, need, None) == _lib.MOE_OK
     assert L.moe_forward(None, P, 64, P, None, P, need, None) == INVALID
+
+
+def test_forward_checks_requested_debug_rows():
+    """moe_forward writes x_perm only on request; e4m3 rows need their scales with them."""
+    L = _lib.lib()
+    lay = _layer(w_dt=2, w1_scales=16384, w2_scales=16384)
+    need = L.moe_workspace_size(ctypes.byref(lay), 64)
+    assert need > 0
+    dbg = _lib.MoeDebugC()
+    dbg.x_perm = 16 * 1024
+    assert L.moe_forward(ctypes.byref(lay), P, 64, P, ctypes.byref(dbg), P, need, None) == INVALID
+    dbg2 = _lib.MoeDebugC()
+    dbg2.x_perm = 16 * 1024 + 2
+    lay16 = _layer()
+    need16 = L.moe_workspace_size(ctypes.byref(lay16), 64)
+    assert L.moe_forward(ctypes.byref(lay16), P, 64, P, ctypes.byref(dbg2), P, need16, None) == INVALID
