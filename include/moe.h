@@ -95,7 +95,8 @@ moe_status moe_route(const void* x, moe_dtype x_dt, const float* w_router, const
  *   src_token      [T*k] int32 out: token of permuted row p (inverse of row_map)
  *   x_perm         [T*k, H] out: x_perm[row_map[t, j]] = x[t].  perm_dt = x_dt copies the
  *                  bits; perm_dt = MOE_FP8_E4M3 (x_dt = MOE_BF16, H % 128 == 0) quantises
- *                  each row in 1x128 blocks: scale = amax / 448 (1 for an all-zero block),
+ *                  each row in 1x128 blocks: scale = the smallest power of two 2^q with
+ *                  448 * 2^q >= amax, q in [-127, 127] (1 for an all-zero block),
  *                  code = e4m3_rne(clamp(x / scale, +-448)); scales go to
  *   x_perm_scales  [T*k, H/128] fp32 out (FP8 only, else ignored).
  *   x_perm may be NULL to build only the maps.

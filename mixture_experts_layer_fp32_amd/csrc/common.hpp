@@ -59,6 +59,22 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return sign | code;                      // code >= 8 here, never a signed zero
 }
 
+// Scale of an e4m3 block with max magnitude amax: the smallest power of two 2^q with
+// 448 * 2^q >= amax, q clamped to [-127, 127] (an E8M0 value), or 1 for an all-zero block.
+// For a normal amax = 1.m * 2^(e - 127): 448 = 1.75 * 2^8, so q = e - 135, plus one when
+// 1.m > 1.75 (mantissa bits above 0x600000); a subnormal amax gives q < -127.
+__device__ __forceinline__ float e4m3_block_scale(float amax) {
+  if (!(amax > 0.0f)) return 1.0f;
+  const uint32_t u = __float_as_uint(amax);
+  const int e = static_cast<int>((u >> 23) & 0xFFu);
+  int q = e == 0 ? -127 : e - 135 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  q = q < -127 ? -127 : (q > 127 ? 127 : q);
+  return q == -127 ? __uint_as_float(0x00400000u) : __uint_as_float(static_cast<uint32_t>(q + 127) << 23);
+}
+
+// E8M0 byte of a power-of-two fp32 scale (its biased exponent; 2^-127 -> 0).
+__device__ __forceinline__ int e8m0_of(float s) { return static_cast<int>((__float_as_uint(s) >> 23) & 0xFFu); }
+
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   uint32_t s = (c & 0x80u) << 24;
   uint32_t e = (c >> 3) & 0xFu;

@@ -4,7 +4,8 @@
 // of Mixture-of-Experts Models with Megatron Core", summary page, "Key claims" [§5] and "Method"
 // second paragraph).  Operands: x_perm codes with one fp32 scale per row and 128-wide K block,
 // weights [K, N] codes with one fp32 scale per 128 x 128 block.  The SwiGLU activation h is
-// quantised to E4M3 in 1 x 128 blocks inside the path (scale = block amax / 448).
+// quantised to E4M3 in 1 x 128 blocks inside the path (scale: the smallest power of two that
+// maps the block's amax into +-448).
 //
 // Tile 128 x 256 x 128 (K step = one scale block), 8 waves in a 2 (M) x 4 (N) grid, each wave
 // 64 x 64 = 2 x 2 blocks of v_mfma_scale_f32_32x32x64_f8f6f4 issued with unit (E8M0 = 127)
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
         const int64_t grow = tm.row0 + row_t;
         if (grow >= tm.row_end) continue;
         const float m = fmaxf(fmaxf(red[row_t * 4 + 0], red[row_t * 4 + 1]), fmaxf(red[row_t * 4 + 2], red[row_t * 4 + 3]));
-        const float sc = m > 0.0f ? m / 448.0f : 1.0f;  // correctly rounded fp32 division
+        const float sc = e4m3_block_scale(m);  // a power of two
         const float v = fminf(fmaxf(h[i][r] / sc, -448.0f), 448.0f);
         const int64_t col = static_cast<int64_t>(tm.nt) * 128 + wn * 32 + lane % 32;
         hq[grow * F + col] = static_cast<uint8_t>(f32_to_e4m3(v));

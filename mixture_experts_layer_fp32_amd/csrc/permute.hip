@@ -146,8 +146,8 @@ __global__ __launch_bounds__(kScatterThreads) void perm_scatter_copy_kernel(
   }
 }
 
-// 8 bf16 values of a lane -> 8 e4m3 codes, with one fp32 scale per 1x128 block shared by the
-// 16 lanes that hold the block (lanes 16g .. 16g+15 of the wave).  Lanes with live == false
+// 8 bf16 values of a lane -> 8 e4m3 codes, with one power-of-two scale per 1x128 block shared by
+// the 16 lanes that hold the block (lanes 16g .. 16g+15 of the wave).  Lanes with live == false
 // contribute zeros to the block maximum.
 __device__ __forceinline__ uint2 quant_e4m3_x8(uint4 v, float& scale) {
   uint32_t wv[4] = {v.x, v.y, v.z, v.w};
@@ -161,7 +161,7 @@ __device__ __forceinline__ uint2 quant_e4m3_x8(uint4 v, float& scale) {
   }
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
-  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;  // correctly rounded fp32 division
+  const float s = e4m3_block_scale(amax);  // a power of two: the division below is exact
   uint32_t q[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {

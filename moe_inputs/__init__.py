@@ -112,11 +112,16 @@ def make_host_inputs(cfg: LayerConfig, seed: int = 0):
 
 
 def _block_fp8(w: torch.Tensor):
-    """fp32 [K, N] -> (float8_e4m3fn codes [K, N], fp32 scales [K/128, N/128]); input preparation only."""
+    """fp32 [K, N] -> (float8_e4m3fn codes [K, N], fp32 scales [K/128, N/128]); input preparation only.
+
+    Scale of a 128x128 block: the smallest power of two 2^q with 448 * 2^q >= its amax.
+    """
     K, N = w.shape
     wb = w.reshape(K // 128, 128, N // 128, 128)
     amax = wb.abs().amax(dim=(1, 3))
-    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    m, e = torch.frexp(amax)
+    q = (e - 9 + (m > 0.875).to(e.dtype)).clamp(-127, 127)
+    s = torch.where(amax > 0, torch.ldexp(torch.ones_like(amax), q), torch.ones_like(amax))
     q = (wb / s[:, None, :, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
     return q.reshape(K, N), s.contiguous()
 

@@ -15,10 +15,13 @@ Encoding rounds to nearest, ties to the code with an even mantissa LSB, after
 the caller has clamped to [-448, 448] (saturating quantisation).
 
 Block quantisation (the reading used throughout, since the pages fix no
-scaling recipe): scale = fl32(amax / 448) for a block whose max magnitude is
-amax > 0, else 1; code = e4m3_rne(clamp(fl32(v / scale), +-448)); the value it
-stands for is decode(code) * scale.  Activations use 1x128 blocks along the
-contraction dimension, weights 128x128 blocks.
+scaling recipe; they name FP8 recipes without their scale format): the scale of a
+block whose max magnitude is amax > 0 is the smallest power of two 2^q with
+448 * 2^q >= amax, q clamped to [-127, 127] (an E8M0 value, the scale format of
+MXFP8-style recipes, which the CDNA4 scaled MFMA applies in hardware), else 1;
+code = e4m3_rne(clamp(fl32(v / scale), +-448)); the value it stands for is
+decode(code) * scale.  Activations use 1x128 blocks along the contraction
+dimension, weights 128x128 blocks.
 """
 
 from __future__ import annotations
@@ -70,9 +73,16 @@ def encode_rne(v: np.ndarray) -> np.ndarray:
 
 
 def block_scale(amax: np.ndarray) -> np.ndarray:
-    """fp32 scale of a block with max magnitude ``amax``: fl32(amax / 448), or 1 for an all-zero block."""
-    a = np.asarray(amax, dtype=np.float32)
-    s = (a / np.float32(E4M3_MAX)).astype(np.float32)  # one correctly rounded fp32 division
+    """Scale of a block with max magnitude ``amax``: the smallest power of two 2^q with
+    448 * 2^q >= amax (q in [-127, 127]), or 1 for an all-zero block; returned as fp32.
+
+    With amax = m * 2^e, m in [0.5, 1) (frexp, exact) and 448 = 0.875 * 2^9, the condition
+    reads m * 2^e <= 0.875 * 2^(9 + q), so q = e - 9, plus one when m > 0.875.
+    """
+    a = np.asarray(amax, dtype=np.float32).astype(np.float64)
+    m, e = np.frexp(a)
+    q = np.clip(e - 9 + (m > 0.875), -127, 127)
+    s = np.ldexp(1.0, q).astype(np.float32)  # 2^-127 is an exact fp32 (subnormal) value
     return np.where(a > 0, s, np.float32(1.0)).astype(np.float32)
 
 

@@ -26,8 +26,12 @@ def test_fp8_weights_and_scales():
     d = moe_inputs.make_inputs(cfg, seed=0)
     assert d["w1"].dtype == torch.float8_e4m3fn and d["w1_scales"].shape == (3, 2, 2)
     assert d["w2_scales"].shape == (3, 1, 2) and d["ws1_scales"].shape == (2, 2)
-    q = d["w1"][0].float()
-    assert q.abs().max().item() == 448.0  # every block's amax lands on the top code
+    # power-of-two block scales: each block's amax lands in the top binade (224, 448]
+    q = d["w1"][0].float().reshape(2, 128, 2, 128).abs().amax(dim=(1, 3))
+    assert (q >= 224.0).all() and (q <= 448.0).all()
+    s = d["w1_scales"][0]
+    m, _ = torch.frexp(s)
+    assert (m == 0.5).all()
 
 
 def test_tie_heavy_router_logits_are_exact():

@@ -66,13 +66,13 @@ def test_block_quantisation_saturates_and_is_accurate():
     assert s.dtype == np.float32 and s.shape == (6, 2)
     assert s[2, 0] == 1.0 and (codes[2, :128] == 0).all()
     xd = e4m3.dequantise_rows_1x128(codes, s)
-    # every block's largest magnitude lands on the top code (+-448)
+    # every block's largest magnitude lands in the top binade, (224, 448] -> codes 0x76..0x7E
     for r in range(6):
         for c in range(2):
             blk = x[r, 128 * c:128 * c + 128]
             if np.abs(blk).max() > 0:
                 i = np.abs(blk).argmax()
-                assert (codes[r, 128 * c + i] & 0x7F) == 0x7E
+                assert 0x76 <= (codes[r, 128 * c + i] & 0x7F) <= 0x7E
     # normals carry 3 mantissa bits: relative error <= 2^-4; subnormal range: abs error <= 2^-10 * scale
     err = np.abs(xd - x)
     bound = np.maximum(np.abs(x) * 2.0 ** -4, np.repeat(s, 128, axis=1) * 2.0 ** -10)
@@ -86,5 +86,26 @@ def test_weight_block_quantisation_roundtrip():
     assert s.shape == (2, 3)
     wd = e4m3.dequantise_blocks_128x128(codes, s)
     assert np.abs(wd - w).max() <= np.abs(w).max() * 2.0 ** -4
-    # a block's scale is its amax / 448 in fp32
-    assert s[1, 2] == np.float32(np.abs(w[128:, 256:]).max() / np.float32(448.0))
+    # a block's scale is the smallest power of two that maps its amax into [-448, 448]
+    a = float(np.abs(w[128:, 256:]).max())
+    q = min(q for q in range(-130, 131) if 448.0 * 2.0 ** q >= a)
+    assert s[1, 2] == np.float32(2.0 ** q)
+
+
+def test_block_scale_by_search_over_powers_of_two():
+    """The scale rule against a direct search: smallest 2^q (q in [-127, 127]) with 448 * 2^q >= amax."""
+    rng = np.random.default_rng(5)
+    amax = np.concatenate([
+        np.float32(448.0) * np.exp2(rng.integers(-40, 40, 200)).astype(np.float32),  # exact 448 * 2^q
+        np.nextafter(np.float32(448.0) * np.exp2(rng.integers(-40, 40, 200)).astype(np.float32), np.float32(np.inf)),
+        np.exp2(rng.uniform(-140, 120, 3000)).astype(np.float32),
+        np.array([1e-45, 1e-40, 2.0 ** -126, 3.4e38, 1.0, 0.875, 0.9, 448.0, 449.0], dtype=np.float32)])
+    s = e4m3.block_scale(amax)
+    for a, got in zip(amax.astype(np.float64), s):
+        cands = [q for q in range(-127, 128) if 448.0 * 2.0 ** q >= a]
+        q = min(cands) if cands else 127
+        assert got == np.float32(2.0 ** q), (a, got, q)
+    assert e4m3.block_scale(np.float32(0.0)) == np.float32(1.0)
+    # a block at exactly 448 * 2^q keeps scale 2^q and maps its amax to code 0x7E
+    codes, sc = e4m3.quantise_rows_1x128(np.full((1, 128), 448.0 * 2.0 ** -3, dtype=np.float32))
+    assert sc[0, 0] == np.float32(2.0 ** -3) and (codes == 0x7E).all()
