@@ -134,8 +134,10 @@ def cpu_baseline(cfg, d, sample_tokens, min_seconds=10.0):
         sw1 = weight(d["ws1"], d["ws1_scales"])
         sw2 = weight(d["ws2"], d["ws2_scales"])
     copy_s[0] = 0.0
-    runs, dt = 0, 0.0
-    while runs == 0 or (dt < min_seconds and runs < 8):  # repeat the sample up to >= min_seconds
+    runs, dt, wall0 = 0, 0.0, time.perf_counter()
+    # repeat the sample until >= min_seconds of oracle time (at most 8 runs, and no new run once
+    # two minutes of wall time, weight copies and decoding included, have gone by)
+    while runs == 0 or (dt < min_seconds and runs < 8 and time.perf_counter() - wall0 < 120.0):
         t0 = time.perf_counter()
         c0 = copy_s[0]
         moe.forward(x, wr, lambda e: weight(d["w1"][e], None if d["w1_scales"] is None else d["w1_scales"][e]),
@@ -144,6 +146,8 @@ def cpu_baseline(cfg, d, sample_tokens, min_seconds=10.0):
                     fp8=fp8)
         dt += time.perf_counter() - t0 - (copy_s[0] - c0)
         runs += 1
+        print(f"[bench] cpu oracle run {runs}: {dt:.1f} s oracle time so far, {copy_s[0]:.1f} s weight "
+              f"copies", file=sys.stderr, flush=True)
     return {"value": runs * sample_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {sample_tokens} tokens of the same layer, {runs} run(s); float64 oracle {dt:.1f} s "
                       f"wall (+{copy_s[0]:.1f} s copying the experts it used to the host, not counted)"}
@@ -214,6 +218,7 @@ def main():
     dev = "cuda"
     d = moe_inputs.make_inputs(cfg, seed=0, weight_device=dev, act_device=dev)
     layer = moe_gpu.Layer.from_inputs(d, cfg.k, cfg.score, cfg.norm)
+    print(f"[bench] {args.workload}: inputs ready", file=sys.stderr, flush=True)
     x = d["x"]
     c_layer = layer.c_struct(x.dtype)
     L = _lib.lib()
@@ -251,6 +256,7 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    print(f"[bench] {W} warmup + {K} timed steps done: {elapsed * 1e3 / K:.3f} ms/step", file=sys.stderr, flush=True)
 
     stage_ms = {s: [] for s in STAGES}
     step_ms = []  # first to last stage event of each timed step (GPU time of one layer forward)

@@ -72,6 +72,15 @@ __device__ __forceinline__ float e4m3_block_scale(float amax) {
   return q == -127 ? __uint_as_float(0x00400000u) : __uint_as_float(static_cast<uint32_t>(q + 127) << 23);
 }
 
+// 1 / s for a scale from e4m3_block_scale (s = 2^q, q in [-127, 127], or 1): 2^-q, built from the
+// exponent bits, so x * pow2_inverse(s) is x / s rounded once, exactly like the division.
+__device__ __forceinline__ float pow2_inverse(float s) {
+  const uint32_t u = __float_as_uint(s);
+  if (u == 0x00400000u) return __uint_as_float(0x7F000000u);  // 1 / 2^-127 = 2^127
+  const uint32_t e = u >> 23;                                   // 1 .. 254 (s is positive, normal)
+  return e == 254u ? __uint_as_float(0x00400000u) : __uint_as_float((254u - e) << 23);
+}
+
 // E8M0 byte of a power-of-two fp32 scale (its biased exponent; 2^-127 -> 0).
 __device__ __forceinline__ int e8m0_of(float s) { return static_cast<int>((__float_as_uint(s) >> 23) & 0xFFu); }
 

@@ -452,8 +452,9 @@ hipError_t launch_bf16_pair(const void* x_perm, const void* w1, const void* w2, 
 size_t grouped_swiglu_scratch_bytes(int64_t rows, int F, int dt) {
   if (dt == 0) return static_cast<size_t>(rows) * F * 4;
   if (dt == 1) return static_cast<size_t>(rows) * F * 2;
-  // fp8: h codes + their 1x128 scales
-  return fp8_hidden_bytes(rows, F) + static_cast<size_t>(rows) * (F / 128) * 4;
+  // fp8: h codes + their 1x128 scales + the kernel-variant flag
+  return fp8_hidden_bytes(rows, F) + ((static_cast<size_t>(rows) * (F / 128) * 4 + 255) & ~static_cast<size_t>(255)) +
+         256;
 }
 
 hipError_t launch_dense_gemm_f32out(const void* A, const void* B, int64_t rows, int K, int N, float* out,

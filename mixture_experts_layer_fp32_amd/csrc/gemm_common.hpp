@@ -147,7 +147,8 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 // wait_vmcnt (vmcnt retires loads in issue order, so the compiler's own counts stay safe).
 __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
   // an SALU write of M0 needs one wait state before an LDS-DMA load reads it
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr)
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory", "m0");
 }
 

@@ -7,14 +7,11 @@
 // quantised to E4M3 in 1 x 128 blocks inside the path (scale: the smallest power of two that
 // maps the block's amax into +-448).
 //
-// Tile 128 x 256 x 128 (K step = one scale block), 8 waves in a 2 (M) x 4 (N) grid, each wave
-// 64 x 64 = 2 x 2 blocks of v_mfma_scale_f32_32x32x64_f8f6f4 issued with unit (E8M0 = 127)
-// scales.  Per K step the two 64-deep MFMAs of a block accumulate into a temporary, then
-//     acc += tmp * s_a[row] * s_b[block]
-// on the VALU.  Operands stream global -> LDS (global_load_lds_dwordx4; the row scales of the
-// step with global_load_lds_dword) through a ring of three LDS stages, so a tile's loads have
-// two iterations to land:
-//   A stage: 128 rows x 128 B, chunk c of row r at c ^ ((r >> 1) & 7) (as the bf16 kernel);
+// Tiles BM x 256 x 128 (K step = one scale block), 8 waves in a 2 (M) x 4 (N) grid, each wave
+// (BM / 2) x 64 in 32 x 32 blocks of v_mfma_scale_f32_32x32x64_f8f6f4.  Operands stream
+// global -> LDS (global_load_lds_dwordx4; the row scales of the step with global_load_lds_dword)
+// through a ring of LDS stages:
+//   A stage: BM rows x 128 B, chunk c of row r at c ^ ((r >> 1) & 7) (as the bf16 kernel);
 //   B stage: 128 k-rows x 256 B (untransposed), chunk c of k-row k at c ^ 2 (k & 7).
 // The weight block scales are wave-uniform and come through the scalar cache.
 // B fragments come from ds_read_b64_tr_b8: within a group of 16 lanes, lane 16g + 8a + b
@@ -28,13 +25,29 @@ namespace {
 
 using namespace gemm;
 
-constexpr int kF8BM = 128;    // rows per tile
 constexpr int kF8BK = 128;    // K per iteration = one scale block
 constexpr int kF8BRow = kBN;  // bytes per B k-row (256 fp8 columns)
-constexpr int kF8Stages = 3;
-constexpr int kF8Stage = kF8BM * kF8BK + kF8BK * kF8BRow;  // A + B of one K tile
-constexpr int kF8ScaleSlots = kF8Stages + 1;                // row-scale ring, one slot longer
-constexpr int kF8Smem = kF8Stages * kF8Stage + kF8ScaleSlots * kF8BM * 4;
+
+// Two variants share the kernel below:
+//  * general (BM = 128): any fp32 weight block scales.  Each 128-deep K block's two MFMAs go to a
+//    temporary with unit scales, then acc += tmp * s_a[row] * s_b[block] on the VALU; three
+//    LDS stages.
+//  * MX (BM = 192): every weight block scale is a power of two (as the activation scales always
+//    are), so the scaled MFMA applies both as E8M0 exponents and accumulates straight into acc:
+//    no temporary, no promotion, 96 x 64 wave tiles (128 x 64 would need more than the 256
+//    registers a wave has at two waves per SIMD); two LDS stages.
+// A device flag (set by fp8_scale_check_kernel) tells which variant runs; the other exits.
+template <int BM>
+struct F8Cfg {
+  static constexpr bool MX = BM != 128;
+  static constexpr int NS = MX ? 2 : 3;                      // LDS stages of A + B
+  static constexpr int A_BYTES = BM * kF8BK;
+  static constexpr int B_BYTES = kF8BK * kF8BRow;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int SLOTS = NS + 1;                       // scale ring, one slot longer
+  static constexpr int SLOT = BM * 4 + 256;                  // row scales + the tile's 2 weight scales
+  static constexpr int SMEM = NS * STAGE + SLOTS * SLOT;
+};
 
 typedef int v2i32_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i32_t lds_v2i32_t;
@@ -43,26 +56,52 @@ typedef __attribute__((address_space(3))) f32x4_t lds_f32x4_t;
 
 // 4 bytes per lane from global memory straight into LDS at lds_addr + 4 * lane.
 __device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_addr)
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory", "m0");
 }
 
-template <bool SWIGLU, bool OUT_F32>
+// flag = 1 unless every scale of the three arrays is a power of two 2^q, q in [-127, 127].
+__global__ __launch_bounds__(256) void fp8_scale_check_kernel(const float* __restrict__ s0, int64_t n0,
+                                                              const float* __restrict__ s1, int64_t n1,
+                                                              const float* __restrict__ s2, int64_t n2,
+                                                              int* __restrict__ flag) {
+  bool bad = false;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n0 + n1 + n2;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const float v = i < n0 ? s0[i] : (i < n0 + n1 ? s1[i - n0] : s2[i - n0 - n1]);
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t e = (u >> 23) & 0xFFu;
+    const bool pow2 = ((u & 0x807FFFFFu) == 0u && e != 0u && e != 0xFFu) || u == 0x00400000u;
+    bad = bad || !pow2;
+  }
+  if (__any(bad) && threadIdx.x % kWave == 0) atomicOr(flag, 1);
+}
+
+__global__ void fp8_flag_clear_kernel(int* flag) { *flag = 0; }
+
+template <int BM, bool SWIGLU, bool OUT_F32>
 __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ A_scales, const uint8_t* __restrict__ B,
     const float* __restrict__ B_scales, const int32_t* __restrict__ offsets, int64_t rows, int E, int K,
-    int ldb, int NT, void* __restrict__ out, float* __restrict__ out_scales, const int32_t* __restrict__ gather) {
-  constexpr int NWAVE = kGemmThreads / kWave;  // 8
-  constexpr int BM = kF8BM;
-  constexpr int FM = 2, FN = 2;
-  constexpr int A_BYTES = BM * kF8BK;           // 16 KB
-  constexpr int B_BYTES = kF8BK * kF8BRow;      // 32 KB
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int NS = kF8Stages;
-  constexpr int A_ROUNDS = A_BYTES / 1024 / NWAVE;  // 2
-  constexpr int B_ROUNDS = B_BYTES / 1024 / NWAVE;  // 4
-  constexpr int RPT = A_ROUNDS + B_ROUNDS;          // loads per wave per tile (+1 on waves 0, 1)
-  static_assert(STAGE == kF8Stage && NS * STAGE + kF8ScaleSlots * BM * 4 == kF8Smem, "LDS layout");
+    int ldb, int NT, void* __restrict__ out, float* __restrict__ out_scales, const int32_t* __restrict__ gather,
+    const int* __restrict__ mx_flag) {
+  using C = F8Cfg<BM>;
+  constexpr bool MX = C::MX;
+  constexpr int NWAVE = kGemmThreads / kWave;  // 8: 2 along M x 4 along N
+  constexpr int WROWS = BM / 2;                // rows per wave
+  constexpr int FM = WROWS / 32, FN = 2;
+  constexpr int A_BYTES = C::A_BYTES;
+  constexpr int STAGE = C::STAGE;
+  constexpr int NS = C::NS;
+  constexpr int SW = BM / 64;                       // waves gathering the row scales (64 rows each)
+  static_assert(BM % 64 == 0 && A_BYTES % (1024 * NWAVE) == 0, "tile height");
+  constexpr int A_ROUNDS = A_BYTES / 1024 / NWAVE;  // 2 or 4
+  constexpr int B_ROUNDS = C::B_BYTES / 1024 / NWAVE;  // 4
+  constexpr int RPT = A_ROUNDS + B_ROUNDS;          // loads per wave per tile (+1 on waves < SW)
+
+  // the variant the scales allow runs; the other exits before touching anything
+  if (mx_flag && ((*mx_flag == 0) != MX)) return;
 
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   __shared__ int s_pref[kMaxExpertsLds];
@@ -91,10 +130,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
     if (gather) grow = gather[grow];  // fused dispatch: row p of the tile is token gather[p]
     a_src[p] = A + grow * K + (((lane % 8) ^ ((r >> 1) & 7)) * 16);
   }
-  // row scales of the step: waves 0 and 1 gather 64 rows each (one dword per lane)
+  // row scales of the step: waves 0 .. SW-1 gather 64 rows each (one dword per lane)
   const float* as_src;
   {
-    int64_t grow = tm.row0 + (wave % 2) * 64 + lane;
+    int64_t grow = tm.row0 + (wave % SW) * 64 + lane;
     if (grow >= tm.row_end) grow = tm.row_end - 1;
     if (gather) grow = gather[grow];
     as_src = A_scales + grow * nkb;
@@ -114,30 +153,40 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
   const uint8_t* b_src = B + static_cast<int64_t>(tm.expert) * K * ldb +
                          static_cast<int64_t>(4 * wave + lane / 16) * ldb + b_col;
   const int64_t b_round = static_cast<int64_t>(4 * NWAVE) * ldb;
-  // weight block scales of this wave's two column blocks
+  // The tile's two weight column blocks (SwiGLU: the gate and the up block; else columns 0-127
+  // and 128-255 of the tile).  Wave SW loads their scales into the scale slot (lane l: block
+  // l % 2); the wave's block j uses slot entry wslot[j].
   const int nbn = ldb / 128;
-  int blk[FN];
-  if (SWIGLU) {
-    blk[0] = t_nt;
-    blk[1] = ldb / 256 + t_nt;
-  } else {
-    const int c0 = t_nt * 2 + wn / 2;
-    blk[0] = blk[1] = c0 < nbn ? c0 : 0;
+  int wslot[FN];
+  int64_t ws_off;
+  {
+    int b0, b1;
+    if (SWIGLU) {
+      b0 = t_nt;
+      b1 = ldb / 256 + t_nt;
+    } else {
+      b0 = t_nt * 2;
+      b1 = t_nt * 2 + 1 < nbn ? t_nt * 2 + 1 : 0;  // past the last column: unused
+    }
+    ws_off = static_cast<int64_t>(t_expert) * nkb * nbn + (lane % 2 ? b1 : b0);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) wslot[j] = SWIGLU ? j : wn / 2;
   }
-  const float* bs_src = B_scales + static_cast<int64_t>(t_expert) * nkb * nbn;
+  const float* ws_src = B_scales + ws_off;
 
   auto stage_base = [&](int kt) { return lds_base + static_cast<uint32_t>(kt % NS) * STAGE; };
-  // row scales of tile kt live in their own ring slot, which the loads issued at the barrier of
-  // iteration kt (tile kt + NS) do not touch, so they can be read after that barrier
+  // the scales of tile kt live in their own ring slot, which the loads issued at the barrier of
+  // iterations kt - 1 and kt (tiles kt - 1 + NS, kt + NS) do not touch
   auto scale_base = [&](int kt) {
-    return lds_base + NS * STAGE + static_cast<uint32_t>(kt % kF8ScaleSlots) * (BM * 4);
+    return lds_base + NS * STAGE + static_cast<uint32_t>(kt % C::SLOTS) * C::SLOT;
   };
   auto issue_loads = [&](int kt) {
     const uint32_t sbase = stage_base(kt);
 #pragma unroll
     for (int p = 0; p < A_ROUNDS; ++p)
       lds_dma16(a_src[p] + static_cast<int64_t>(kt) * kF8BK, sbase + (NWAVE * p + wave) * 1024);
-    if (wave < 2) lds_dma4(as_src + kt, scale_base(kt) + wave * 256);
+    if (wave < SW) lds_dma4(as_src + kt, scale_base(kt) + wave * 256);
+    if (wave == SW) lds_dma4(ws_src + static_cast<int64_t>(kt) * nbn, scale_base(kt) + BM * 4);
     const uint8_t* bs = b_src + static_cast<int64_t>(kt) * kF8BK * ldb;
 #pragma unroll
     for (int p = 0; p < B_ROUNDS; ++p)
@@ -148,7 +197,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
   uint32_t a_row_off[FM], a_sw[FM];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int r = wm * 64 + i * 32 + lane % 32;
+    const int r = wm * WROWS + i * 32 + lane % 32;
     a_row_off[i] = r * 128;
     a_sw[i] = (r >> 1) & 7;
   }
@@ -163,19 +212,18 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
     }
   }
 
-  f32x16_t acc[FM][FN], tmp[FM][FN];
+  f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  const f32x16_t zero16 = {};
 
   // Only the 32-row blocks of this wave that hold rows of the expert are computed (wave-uniform).
-  int nl_rows = static_cast<int>((tm.row_end - tm.row0 < BM ? tm.row_end - tm.row0 : BM)) - wm * 64;
+  int nl_rows = static_cast<int>((tm.row_end - tm.row0 < BM ? tm.row_end - tm.row0 : BM)) - wm * WROWS;
   nl_rows = nl_rows < 0 ? 0 : nl_rows;
-  const int nlive = __builtin_amdgcn_readfirstlane(nl_rows >= 64 ? FM : (nl_rows + 31) / 32);
+  const int nlive = __builtin_amdgcn_readfirstlane(nl_rows >= WROWS ? FM : (nl_rows + 31) / 32);
 
   const int nk = nkb;
   auto run = [&](auto nl_c) {
@@ -200,7 +248,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
       bfr[buf][j] = i32x8_t{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
     };
     // sub-step s (0, 1) of tile kt: 64 K bytes; A lane l holds k 32 (l / 32) .. +32 of it.
-    // Read in the order the MFMAs (i-major) consume them: B0, A0, B1, A1.
+    // Read in the order the MFMAs (i-major) consume them: B0, A0, B1, A1, ...
     auto read_frags = [&](int kt, int s, int buf) {
       if constexpr (NL > 0) {
         const uint32_t sbase = stage_base(kt);
@@ -212,61 +260,115 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
         for (int i = 1; i < NL; ++i) read_a(sbase, s, buf, i);
       }
     };
-    auto mfmas = [&](int buf, bool first) {
-#pragma unroll
-      for (int i = 0; i < NL; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          tmp[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[buf][i], bfr[buf][j],
-                                                                       first ? zero16 : tmp[i][j], 0, 0, 0, 127, 0, 127);
-    };
-    // row scales of this lane's 16 accumulator rows per block i: 4 runs of 4 consecutive rows
-    f32x4_t sa[NLA][4];
-    auto read_row_scales = [&](int kt) {
-      const uint32_t sbase = scale_base(kt);
-#pragma unroll
-      for (int i = 0; i < NL; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = wm * 64 + i * 32 + q * 8 + khalf * 4;
-          sa[i][q] = *reinterpret_cast<const lds_f32x4_t*>(static_cast<uintptr_t>(sbase + row * 4));
-        }
-    };
 
-    float sb[FN], sb_next[FN];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) sb[j] = bs_src[blk[j]];
+    // The first tile's loads, then the loop.  vmcnt per wave: RPT (+1 on the scale waves).
     const int pro = nk < NS ? nk : NS;  // tiles in flight before the loop
     for (int t = 0; t < pro; ++t) issue_loads(t);
-    if (wave < 2) wait_tiles<RPT + 1, NS - 1>(pro - 1); else wait_tiles<RPT, NS - 1>(pro - 1);  // tile 0 landed
+    if (wave <= SW) wait_tiles<RPT + 1, NS - 1>(pro - 1); else wait_tiles<RPT, NS - 1>(pro - 1);  // tile 0 landed
     lds_barrier();
     read_frags(0, 0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-      const int ktn = kt + 1 < nk ? kt + 1 : kt;
+
+    if constexpr (MX) {
+      // E8M0 exponents: per lane its A row's scale (one per 32-row block), per block j the weight
+      // block scale.  Tile kt + 1's are read from the scale ring right after the barrier that
+      // makes that tile readable, a sub-step before they are needed.
+      int sae[NLA], sbe[FN], sae_n[NLA], sbe_n[FN];
+      auto read_exps = [&](int kt) {
+        const uint32_t sbase = scale_base(kt);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) sb_next[j] = bs_src[static_cast<int64_t>(ktn) * nbn + blk[j]];
-      mfmas(0, true);
-      read_frags(kt, 1, 1);
-      if (kt + 1 < nk) {
-        wait_lgkm0();  // this wave's reads of tile kt are complete
-        // this wave's loads of tile kt + 1 have landed; tiles kt + 2 .. kt + NS - 1 may be in flight
-        const int later = nk - 2 - kt < NS - 2 ? nk - 2 - kt : NS - 2;
-        if (wave < 2) wait_tiles<RPT + 1, NS - 2>(later); else wait_tiles<RPT, NS - 2>(later);
-        lds_barrier();  // for every wave: tile kt + 1 readable, tile kt's stage free
-        if (kt + NS < nk) issue_loads(kt + NS);
-      }
-      mfmas(1, false);
-      read_frags(kt + 1, 0, 0);  // past the last tile this reads a stale stage (in bounds, unused)
-      read_row_scales(kt);
-      // promote the block: acc += tmp * s_a[row] * s_b[column block]
-#pragma unroll
-      for (int i = 0; i < NL; ++i)
+        for (int i = 0; i < NL; ++i)
+          sae_n[i] = e8m0_of(*reinterpret_cast<const __attribute__((address_space(3))) float*>(
+              static_cast<uintptr_t>(sbase + (wm * WROWS + i * 32 + lane % 32) * 4)));
 #pragma unroll
         for (int j = 0; j < FN; ++j)
+          sbe_n[j] = e8m0_of(*reinterpret_cast<const __attribute__((address_space(3))) float*>(
+              static_cast<uintptr_t>(sbase + BM * 4 + wslot[j] * 4)));
+      };
+      auto take_exps = [&]() {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(tmp[i][j][r], sa[i][r / 4][r % 4] * sb[j], acc[i][j][r]);
+        for (int i = 0; i < NL; ++i) sae[i] = sae_n[i];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) sb[j] = sb_next[j];
+        for (int j = 0; j < FN; ++j) sbe[j] = sbe_n[j];
+      };
+      auto mfmas = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0,
+                                                                         sae[i], 0, sbe[j]);
+      };
+      read_exps(0);
+      take_exps();
+      for (int kt = 0; kt < nk; ++kt) {
+        mfmas(0);
+        read_frags(kt, 1, 1);
+        if (kt + 1 < nk) {
+          wait_lgkm0();  // this wave's reads of tile kt are complete
+          const int later = nk - 2 - kt < NS - 2 ? nk - 2 - kt : NS - 2;
+          if (wave <= SW) wait_tiles<RPT + 1, NS - 2>(later); else wait_tiles<RPT, NS - 2>(later);
+          lds_barrier();  // for every wave: tile kt + 1 readable, tile kt's stage free
+          if (kt + NS < nk) issue_loads(kt + NS);
+          read_exps(kt + 1);
+        }
+        mfmas(1);
+        read_frags(kt + 1, 0, 0);  // past the last tile this reads a stale stage (in bounds, unused)
+        if (kt + 1 < nk) take_exps();
+      }
+    } else {
+      f32x16_t tmp[NLA][FN];
+      const f32x16_t zero16 = {};
+      auto mfmas = [&](int buf, bool first) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            tmp[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[buf][i], bfr[buf][j],
+                                                                         first ? zero16 : tmp[i][j], 0, 0, 0, 127, 0,
+                                                                         127);
+      };
+      // Scales of tile kt for the promotion at the end of its iteration, read before the next
+      // sub-step's fragments so that the promotion does not wait for those: per block i the row
+      // scales of this lane's 16 accumulator rows (4 runs of 4 consecutive rows), per block j the
+      // weight block's.
+      f32x4_t sa[NLA][4];
+      float sb[FN];
+      auto read_scales = [&](int kt) {
+        const uint32_t sbase = scale_base(kt);
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = wm * WROWS + i * 32 + q * 8 + khalf * 4;
+            sa[i][q] = *reinterpret_cast<const lds_f32x4_t*>(static_cast<uintptr_t>(sbase + row * 4));
+          }
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          sb[j] = *reinterpret_cast<const __attribute__((address_space(3))) float*>(
+              static_cast<uintptr_t>(sbase + BM * 4 + wslot[j] * 4));
+      };
+      for (int kt = 0; kt < nk; ++kt) {
+        mfmas(0, true);
+        read_frags(kt, 1, 1);
+        if (kt + 1 < nk) {
+          wait_lgkm0();  // this wave's reads of tile kt are complete
+          // this wave's loads of tile kt + 1 have landed; tiles kt + 2 .. kt + NS - 1 may be in flight
+          const int later = nk - 2 - kt < NS - 2 ? nk - 2 - kt : NS - 2;
+          if (wave <= SW) wait_tiles<RPT + 1, NS - 2>(later); else wait_tiles<RPT, NS - 2>(later);
+          lds_barrier();  // for every wave: tile kt + 1 readable, tile kt's stage free
+          if (kt + NS < nk) issue_loads(kt + NS);
+        }
+        mfmas(1, false);
+        read_scales(kt);
+        read_frags(kt + 1, 0, 0);  // past the last tile this reads a stale stage (in bounds, unused)
+        // promote the block: acc += tmp * s_a[row] * s_b[column block]
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(tmp[i][j][r], sa[i][r / 4][r % 4] * sb[j], acc[i][j][r]);
+      }
     }
   };
   dispatch_live<FM>(nlive, run);
@@ -274,83 +376,127 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
   // ---- epilogue.  32x32 accumulator layout: slot r of lane l is
   //      row (r / 4) * 8 + (l / 32) * 4 + (r % 4), column l % 32.
   if (SWIGLU) {
-    // h = SiLU(gate) * up for this lane's 2 x 16 rows, then E4M3 in 1 x 128 blocks: the tile's
-    // 128 h columns are one block, spread over the 4 N-waves (32 columns each).
+    // h = SiLU(gate) * up, staged through LDS as fp32 rows of the tile's 128 h columns (one 1 x 128
+    // quantisation block per row).  Read back by 8 consecutive lanes per row, 16 columns each:
+    // the block amax is a register max and 3 shuffles, and each lane stores 16 E4M3 codes at once.
+    constexpr int kHS = 136;  // row stride in floats: rows 4 apart (the two lane halves) start 32 banks apart
+    static_assert(BM * kHS * 4 <= NS * STAGE, "h staging fits in the operand ring");
     const int F = ldb / 2;
-    float h[FM][16];
-    float amax[FM][16];
+    wait_lgkm0();
+    __syncthreads();  // every wave is done with the operand ring
+    float* hl = reinterpret_cast<float*>(smem);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        h[i][r] = silu_fast(acc[i][0][r]) * acc[i][1][r];
-        float m = fabsf(h[i][r]);
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-        amax[i][r] = m;
+        const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
+        hl[row_t * kHS + wn * 32 + lane % 32] = silu_fast(acc[i][0][r]) * acc[i][1][r];
       }
-    wait_lgkm0();
-    __syncthreads();  // every wave is done with the LDS stages
-    float* red = reinterpret_cast<float*>(smem);  // [BM rows][4 N-waves]
-    if (lane % 32 == 0) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row_t = wm * 64 + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
-          red[row_t * 4 + wn] = amax[i][r];
-        }
-    }
     __syncthreads();
     uint8_t* hq = static_cast<uint8_t*>(out);
+    const int seg = tid % 8;
+#pragma unroll
+    for (int pass = 0; pass < BM / 64; ++pass) {
+      const int row_t = pass * 64 + tid / 8;
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(hl + row_t * kHS + seg * 16);
+      f32x4_t v[4];
+      float m = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = src[q];
+        m = fmaxf(fmaxf(m, fmaxf(fabsf(v[q][0]), fabsf(v[q][1]))), fmaxf(fabsf(v[q][2]), fabsf(v[q][3])));
+      }
+      m = fmaxf(m, __shfl_xor(m, 1, kWave));
+      m = fmaxf(m, __shfl_xor(m, 2, kWave));
+      m = fmaxf(m, __shfl_xor(m, 4, kWave));
+      const int64_t grow = tm.row0 + row_t;
+      if (grow < tm.row_end) {
+        const float sc = e4m3_block_scale(m);  // a power of two
+        const float inv = pow2_inverse(sc);    // exact: x * inv == x / sc
+        u32x4_t codes;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            w |= f32_to_e4m3(fminf(fmaxf(v[q][c] * inv, -448.0f), 448.0f)) << (8 * c);
+          codes[q] = w;
+        }
+        *reinterpret_cast<u32x4_t*>(hq + grow * F + static_cast<int64_t>(tm.nt) * 128 + seg * 16) = codes;
+        if (seg == 0) out_scales[grow * (F / 128) + tm.nt] = sc;
+      }
+    }
+  } else if (!OUT_F32) {
+    // bf16 y staged through LDS as [BM][256] (+ padding) and stored 16 bytes (8 columns) per lane
+    constexpr int kYS = 264;  // row stride in bf16: rows 4 apart (the two lane halves) 16 banks apart
+    static_assert(BM * kYS * 2 <= NS * STAGE, "y staging fits in the operand ring");
+    wait_lgkm0();
+    __syncthreads();  // every wave is done with the operand ring
+    bf16_t* yl = reinterpret_cast<bf16_t*>(smem);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row_t = wm * 64 + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
-        const int64_t grow = tm.row0 + row_t;
-        if (grow >= tm.row_end) continue;
-        const float m = fmaxf(fmaxf(red[row_t * 4 + 0], red[row_t * 4 + 1]), fmaxf(red[row_t * 4 + 2], red[row_t * 4 + 3]));
-        const float sc = e4m3_block_scale(m);  // a power of two
-        const float v = fminf(fmaxf(h[i][r] / sc, -448.0f), 448.0f);
-        const int64_t col = static_cast<int64_t>(tm.nt) * 128 + wn * 32 + lane % 32;
-        hq[grow * F + col] = static_cast<uint8_t>(f32_to_e4m3(v));
-        if (wn == 0 && lane % 32 == 0) out_scales[grow * (F / 128) + tm.nt] = sc;
+        const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) yl[row_t * kYS + wn * 64 + j * 32 + lane % 32] = f32_to_bf16(acc[i][j][r]);
       }
+    __syncthreads();
+    const int seg = tid % 32;  // 8 columns each, 32 lanes per row
+    const int64_t col = static_cast<int64_t>(tm.nt) * kBN + seg * 8;
+    if (col < ldb) {  // ldb % 128 == 0: an 8-column group is wholly in or out
+#pragma unroll
+      for (int pass = 0; pass < BM / 16; ++pass) {
+        const int row_t = pass * 16 + tid / 32;
+        const int64_t grow = tm.row0 + row_t;
+        if (grow < tm.row_end)
+          *reinterpret_cast<u32x4_t*>(static_cast<bf16_t*>(out) + grow * ldb + col) =
+              *reinterpret_cast<const u32x4_t*>(yl + row_t * kYS + seg * 8);
+      }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row_t = wm * 64 + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
+        const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
         const int64_t grow = tm.row0 + row_t;
         if (grow >= tm.row_end) continue;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int64_t col = static_cast<int64_t>(tm.nt) * kBN + wn * 64 + j * 32 + lane % 32;
-          if (col >= ldb) continue;
-          if (OUT_F32)
-            static_cast<float*>(out)[grow * ldb + col] = acc[i][j][r];
-          else
-            static_cast<bf16_t*>(out)[grow * ldb + col] = f32_to_bf16(acc[i][j][r]);
+          if (col < ldb) static_cast<float*>(out)[grow * ldb + col] = acc[i][j][r];
         }
       }
   }
 }
 
-template <bool SWIGLU, bool OUT_F32>
+template <int BM, bool SWIGLU, bool OUT_F32>
 hipError_t launch_fp8(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, const int32_t* offsets,
                       int64_t rows, int E, int K, int ldb, int NT, void* out, float* out_scales,
-                      hipStream_t stream, const int32_t* gather = nullptr) {
-  constexpr int smem = kF8Smem;
-  auto kern = gemm_fp8_kernel<SWIGLU, OUT_F32>;
+                      hipStream_t stream, const int32_t* gather, const int* mx_flag) {
+  constexpr int smem = F8Cfg<BM>::SMEM;
+  auto kern = gemm_fp8_kernel<BM, SWIGLU, OUT_F32>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (attr != hipSuccess) return attr;
-  const unsigned grid = grid_for(max_tiles<kF8BM>(rows, E, offsets == nullptr), NT);
+  const unsigned grid = grid_for(max_tiles<BM>(rows, E, offsets == nullptr), NT);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), smem, stream, A, As, B, Bs, offsets, rows, E, K, ldb,
-                     NT, out, out_scales, gather);
+                     NT, out, out_scales, gather, mx_flag);
   return hipGetLastError();
+}
+
+// Both variants of one GEMM; the device flag lets exactly one of them run.
+template <bool SWIGLU, bool OUT_F32>
+hipError_t launch_fp8_both(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs,
+                           const int32_t* offsets, int64_t rows, int E, int K, int ldb, int NT_mx, int NT_gen,
+                           void* out, float* out_scales, hipStream_t stream, const int32_t* gather,
+                           const int* mx_flag) {
+  hipError_t err = launch_fp8<192, SWIGLU, OUT_F32>(A, As, B, Bs, offsets, rows, E, K, ldb, NT_mx, out, out_scales,
+                                                    stream, gather, mx_flag);
+  if (err != hipSuccess) return err;
+  return launch_fp8<128, SWIGLU, OUT_F32>(A, As, B, Bs, offsets, rows, E, K, ldb, NT_gen, out, out_scales, stream,
+                                          gather, mx_flag);
 }
 
 }  // namespace
@@ -365,17 +511,30 @@ hipError_t launch_grouped_swiglu_fp8(const void* x_perm, const float* x_scales, 
                                      void* scratch, hipStream_t stream, hipEvent_t between, const int32_t* gather) {
   uint8_t* hq = static_cast<uint8_t*>(scratch);
   float* hs = reinterpret_cast<float*>(static_cast<char*>(scratch) + fp8_hidden_bytes(rows, F));
-  hipError_t err = launch_fp8<true, false>(static_cast<const uint8_t*>(x_perm), x_scales,
-                                           static_cast<const uint8_t*>(w1), w1_scales, offsets, rows, E, H, 2 * F,
-                                           F / 128, hq, hs, stream, gather);
+  int* flag = reinterpret_cast<int*>(static_cast<char*>(scratch) + fp8_hidden_bytes(rows, F) +
+                                     ((static_cast<size_t>(rows) * (F / 128) * 4 + 255) & ~static_cast<size_t>(255)));
+  // Which variant: every block scale a power of two -> MX.  Rows gathered through `gather` come
+  // from this library's own quantiser (power-of-two scales by construction); caller-supplied
+  // activation scales are checked with the weights'.
+  const int64_t n0 = gather ? 0 : rows * (H / 128);
+  const int64_t n1 = static_cast<int64_t>(E) * (H / 128) * (2 * F / 128), n2 = static_cast<int64_t>(E) * (F / 128) * (H / 128);
+  const int64_t nall = n0 + n1 + n2;
+  hipLaunchKernelGGL(fp8_flag_clear_kernel, dim3(1), dim3(1), 0, stream, flag);
+  const unsigned gc = static_cast<unsigned>(ceil_div(nall, 256) < 1024 ? ceil_div(nall, 256) : 1024);
+  hipLaunchKernelGGL(fp8_scale_check_kernel, dim3(gc), dim3(256), 0, stream, x_scales, n0, w1_scales, n1,
+                     w2_scales, n2, flag);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int nt1 = F / 128, nt2 = static_cast<int>(ceil_div(H, kBN));
+  err = launch_fp8_both<true, false>(static_cast<const uint8_t*>(x_perm), x_scales, static_cast<const uint8_t*>(w1),
+                                     w1_scales, offsets, rows, E, H, 2 * F, nt1, nt1, hq, hs, stream, gather, flag);
   if (err != hipSuccess) return err;
   if (between && (err = hipEventRecord(between, stream)) != hipSuccess) return err;
-  const int nt2 = static_cast<int>(ceil_div(H, kBN));
   if (out_dt == 0)
-    return launch_fp8<false, true>(hq, hs, static_cast<const uint8_t*>(w2), w2_scales, offsets, rows, E, F, H, nt2,
-                                   y_perm, nullptr, stream);
-  return launch_fp8<false, false>(hq, hs, static_cast<const uint8_t*>(w2), w2_scales, offsets, rows, E, F, H, nt2,
-                                  y_perm, nullptr, stream);
+    return launch_fp8_both<false, true>(hq, hs, static_cast<const uint8_t*>(w2), w2_scales, offsets, rows, E, F, H,
+                                        nt2, nt2, y_perm, nullptr, stream, nullptr, flag);
+  return launch_fp8_both<false, false>(hq, hs, static_cast<const uint8_t*>(w2), w2_scales, offsets, rows, E, F, H,
+                                       nt2, nt2, y_perm, nullptr, stream, nullptr, flag);
 }
 
 }  // namespace moe

@@ -44,6 +44,17 @@ def decode_codes(codes: np.ndarray) -> np.ndarray:
     return sign * mag
 
 
+# decode_codes of every byte, so large arrays decode by one table lookup (same values).
+_DECODE_TABLE = None
+
+
+def _decode_table_lookup(codes: np.ndarray) -> np.ndarray:
+    global _DECODE_TABLE
+    if _DECODE_TABLE is None:
+        _DECODE_TABLE = decode_codes(np.arange(256, dtype=np.uint8))
+    return _DECODE_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
 # The 127 non-negative finite codes 0x00..0x7E in increasing value order.
 _POS_CODES = np.arange(0x7F, dtype=np.uint8)
 _POS_VALUES = decode_codes(_POS_CODES)
@@ -112,7 +123,7 @@ def quantise_rows_1x128(x: np.ndarray, block: int = 128):
 def dequantise_rows_1x128(codes: np.ndarray, scales: np.ndarray, block: int = 128) -> np.ndarray:
     """float64 values decode(code) * scale of a 1 x ``block`` quantised matrix (exact in fp64)."""
     n, K = codes.shape
-    d = decode_codes(codes).reshape(n, K // block, block)
+    d = _decode_table_lookup(codes).reshape(n, K // block, block)
     return (d * np.asarray(scales, dtype=np.float64)[:, :, None]).reshape(n, K)
 
 
@@ -132,5 +143,5 @@ def quantise_blocks_128x128(w: np.ndarray, block: int = 128):
 def dequantise_blocks_128x128(codes: np.ndarray, scales: np.ndarray, block: int = 128) -> np.ndarray:
     """float64 values decode(code) * scale of a ``block`` x ``block`` quantised [K, N] matrix."""
     K, N = codes.shape
-    d = decode_codes(codes).reshape(K // block, block, N // block, block)
+    d = _decode_table_lookup(codes).reshape(K // block, block, N // block, block)
     return (d * np.asarray(scales, dtype=np.float64)[:, None, :, None]).reshape(K, N)

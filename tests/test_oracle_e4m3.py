@@ -109,3 +109,20 @@ def test_block_scale_by_search_over_powers_of_two():
     # a block at exactly 448 * 2^q keeps scale 2^q and maps its amax to code 0x7E
     codes, sc = e4m3.quantise_rows_1x128(np.full((1, 128), 448.0 * 2.0 ** -3, dtype=np.float32))
     assert sc[0, 0] == np.float32(2.0 ** -3) and (codes == 0x7E).all()
+
+
+def test_block_dequantisers_decode_every_code_like_torch():
+    """Both dequantisers (table lookup) give torch's E4M3 value times the block scale for all 256 codes."""
+    codes = np.tile(np.arange(256, dtype=np.uint8), 128).reshape(128, 256)  # every code in every block
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    s_w = np.array([[0.5, 2.0 ** -20]], dtype=np.float32)
+    dw = e4m3.dequantise_blocks_128x128(codes, s_w)
+    s_r = np.full((128, 2), 4.0, dtype=np.float32)
+    s_r[:, 1] = 0.375
+    dr = e4m3.dequantise_rows_1x128(codes, s_r)
+    for got, scale in ((dw, np.repeat(s_w.astype(np.float64), 128, axis=1)),
+                       (dr, np.repeat(s_r.astype(np.float64), 128, axis=1))):
+        want = ref * scale
+        assert np.array_equal(np.isnan(got), np.isnan(want))
+        ok = ~np.isnan(want)
+        assert np.array_equal(got[ok], want[ok])

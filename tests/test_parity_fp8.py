@@ -169,3 +169,43 @@ def test_fp8_special_values_quantise_exactly():
     codes, scales = e4m3.quantise_rows_1x128(host(xt))
     assert np.array_equal(host(p["x_perm_scales"]), scales)
     assert np.array_equal(host(p["x_perm"]), codes)
+
+
+@pytest.mark.parametrize("which", ["w1", "w2", "x"])
+def test_fp8_arbitrary_block_scales(which):
+    """Block scales that are not powers of two (one weight block, or the caller's activation
+    scales) take the kernels' general path, which must match the oracle like the power-of-two one."""
+    cfg = SMALL_FP8["fp8_small"]
+    print(f"[parity-fp8] arbitrary scales in {which}", flush=True)
+    d, _ = _make(cfg)
+    ids, _, _ = moe_gpu.route(d["x"], d["w_router"], cfg.k, cfg.score, cfg.norm, d["bias"], return_logits=True)
+    p = moe_gpu.permute(d["x"], ids, cfg.E, perm_dtype=torch.float8_e4m3fn)
+    xs = p["x_perm_scales"].clone()
+    w1s, w2s = d["w1_scales"].clone(), d["w2_scales"].clone()
+    if which == "w1":
+        w1s[cfg.E - 1, 1, 2] *= 1.1
+    elif which == "w2":
+        w2s[0, 2, 0] *= 0.7
+    else:
+        xs *= 1.3
+    yp = moe_gpu.grouped_swiglu(p["x_perm"], p["offsets"], d["w1"], d["w2"], x_perm_scales=xs,
+                                w1_scales=w1s, w2_scales=w2s, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    off = host(p["offsets"])
+    xp_hat = e4m3.dequantise_rows_1x128(host(p["x_perm"]), host(xs))
+    ref_hq = np.zeros((xp_hat.shape[0], cfg.H))
+    for e in range(cfg.E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            ref_hq[a:b] = _h_rounded_expert(xp_hat[a:b], weights_of(d["w1"], w1s, e), weights_of(d["w2"], w2s, e))
+    err = rel_frobenius(host(yp), ref_hq)
+    print(f"[parity-fp8] arbitrary scales in {which}: y_perm vs h-rounded steps {err:.3e}", flush=True)
+    assert err <= TOL_FP8_H_ROUNDED
+    if which != "x":  # the fused forward (rows gathered from x) on the same weights
+        layer = moe_gpu.Layer.from_inputs(dict(d, w1_scales=w1s, w2_scales=w2s), cfg.k, cfg.score, cfg.norm)
+        _, dbg = moe_gpu.forward(d["x"], layer, debug=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(dbg["expert_offsets"]), off)
+        err_f = rel_frobenius(host(dbg["y_perm"]), ref_hq)
+        print(f"[parity-fp8] arbitrary scales in {which}: forward y_perm {err_f:.3e}", flush=True)
+        assert err_f <= TOL_FP8_H_ROUNDED
