@@ -285,31 +285,61 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
 
   // ---- epilogue.  32x32 accumulator layout: slot r of lane l is
   //      row (r / 4) * 8 + (l / 32) * 4 + (r % 4), column l % 32.
+  if constexpr (!OUT_F32) {
+    // bf16 results (SwiGLU: h = SiLU(gate) * up) staged through LDS -- the operand rings are free
+    // once every wave is past its last reads -- then stored 16 bytes (8 columns) per lane.
+    constexpr int NTH = NWAVE * kWave;
+    constexpr int COLS = SWIGLU ? 128 : kBN;  // output columns of the tile
+    constexpr int LS = COLS + 8;              // row stride in bf16: rows 4 apart start 16 banks apart
+    static_assert(BM * LS * 2 <= R::SMEM, "output staging fits in the operand rings");
+    wait_lgkm0();
+    __syncthreads();
+    bf16_t* st = reinterpret_cast<bf16_t*>(smem);
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
-      const int64_t grow = tm.row0 + row_t;
-      if (grow >= tm.row_end) continue;
-      if (SWIGLU) {
-        const int F = ldb / 2;
-        const float g = acc[i][0][r], u = acc[i][1][r];
-        const float h = silu_fast(g) * u;
-        const int64_t col = static_cast<int64_t>(tm.nt) * 128 + wn * 32 + lane % 32;
-        if (OUT_F32)
-          static_cast<float*>(out)[grow * F + col] = h;
-        else
-          static_cast<bf16_t*>(out)[grow * F + col] = f32_to_bf16(h);
-      } else {
+      for (int r = 0; r < 16; ++r) {
+        const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
+        if (SWIGLU) {
+          st[row_t * LS + wn * 32 + lane % 32] = f32_to_bf16(silu_fast(acc[i][0][r]) * acc[i][1][r]);
+        } else {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int64_t col = static_cast<int64_t>(tm.nt) * kBN + wn * 64 + j * 32 + lane % 32;
-          if (col >= ldb) continue;
-          if (OUT_F32)
-            static_cast<float*>(out)[grow * ldb + col] = acc[i][j][r];
-          else
-            static_cast<bf16_t*>(out)[grow * ldb + col] = f32_to_bf16(acc[i][j][r]);
+          for (int j = 0; j < FN; ++j) st[row_t * LS + wn * 64 + j * 32 + lane % 32] = f32_to_bf16(acc[i][j][r]);
+        }
+      }
+    __syncthreads();
+    constexpr int SEGS = COLS / 8, RPP = NTH / SEGS;  // lanes per row, rows per pass
+    const int seg = tid % SEGS;
+    const int64_t ldo = SWIGLU ? ldb / 2 : ldb;
+    const int64_t col = static_cast<int64_t>(tm.nt) * COLS + seg * 8;
+    if (col < ldo) {  // ldo % 8 == 0: an 8-column group is wholly in or out
+#pragma unroll
+      for (int pass = 0; pass < BM / RPP; ++pass) {
+        const int row_t = pass * RPP + tid / SEGS;
+        const int64_t grow = tm.row0 + row_t;
+        if (grow < tm.row_end)
+          *reinterpret_cast<u32x4_t*>(static_cast<bf16_t*>(out) + grow * ldo + col) =
+              *reinterpret_cast<const u32x4_t*>(st + row_t * LS + seg * 8);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
+        const int64_t grow = tm.row0 + row_t;
+        if (grow >= tm.row_end) continue;
+        if (SWIGLU) {
+          const int F = ldb / 2;
+          const int64_t col = static_cast<int64_t>(tm.nt) * 128 + wn * 32 + lane % 32;
+          static_cast<float*>(out)[grow * F + col] = silu_fast(acc[i][0][r]) * acc[i][1][r];
+        } else {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int64_t col = static_cast<int64_t>(tm.nt) * kBN + wn * 64 + j * 32 + lane % 32;
+            if (col < ldb) static_cast<float*>(out)[grow * ldb + col] = acc[i][j][r];
+          }
         }
       }
     }

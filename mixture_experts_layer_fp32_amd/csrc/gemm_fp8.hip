@@ -31,22 +31,25 @@ constexpr int kF8BRow = kBN;  // bytes per B k-row (256 fp8 columns)
 // Two variants share the kernel below:
 //  * general (BM = 128): any fp32 weight block scales.  Each 128-deep K block's two MFMAs go to a
 //    temporary with unit scales, then acc += tmp * s_a[row] * s_b[block] on the VALU; three
-//    LDS stages.
+//    LDS stages of A and of B.
 //  * MX (BM = 192): every weight block scale is a power of two (as the activation scales always
 //    are), so the scaled MFMA applies both as E8M0 exponents and accumulates straight into acc:
 //    no temporary, no promotion, 96 x 64 wave tiles (128 x 64 would need more than the 256
-//    registers a wave has at two waves per SIMD); two LDS stages.
+//    registers a wave has at two waves per SIMD); two LDS stages of A and three of B (the
+//    weights, which miss L2 more often, get the deeper ring).
 // A device flag (set by fp8_scale_check_kernel) tells which variant runs; the other exits.
 template <int BM>
 struct F8Cfg {
   static constexpr bool MX = BM != 128;
-  static constexpr int NS = MX ? 2 : 3;                      // LDS stages of A + B
+  static constexpr int NA = MX ? 2 : 3;                      // LDS stages of A (activation rows)
+  static constexpr int NB = 3;                               // LDS stages of B (weights)
   static constexpr int A_BYTES = BM * kF8BK;
   static constexpr int B_BYTES = kF8BK * kF8BRow;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int SLOTS = NS + 1;                       // scale ring, one slot longer
+  static constexpr int SLOTS = NA + 1;                       // scale ring (travels with A), one longer
   static constexpr int SLOT = BM * 4 + 256;                  // row scales + the tile's 2 weight scales
-  static constexpr int SMEM = NS * STAGE + SLOTS * SLOT;
+  static constexpr int B_RING = NA * A_BYTES;
+  static constexpr int S_RING = B_RING + NB * B_BYTES;
+  static constexpr int SMEM = S_RING + SLOTS * SLOT;
 };
 
 typedef int v2i32_t __attribute__((ext_vector_type(2)));
@@ -91,14 +94,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
   constexpr int NWAVE = kGemmThreads / kWave;  // 8: 2 along M x 4 along N
   constexpr int WROWS = BM / 2;                // rows per wave
   constexpr int FM = WROWS / 32, FN = 2;
-  constexpr int A_BYTES = C::A_BYTES;
-  constexpr int STAGE = C::STAGE;
-  constexpr int NS = C::NS;
+  constexpr int A_BYTES = C::A_BYTES, B_BYTES = C::B_BYTES;
+  constexpr int NA = C::NA, NB = C::NB;
   constexpr int SW = BM / 64;                       // waves gathering the row scales (64 rows each)
   static_assert(BM % 64 == 0 && A_BYTES % (1024 * NWAVE) == 0, "tile height");
-  constexpr int A_ROUNDS = A_BYTES / 1024 / NWAVE;  // 2 or 4
-  constexpr int B_ROUNDS = C::B_BYTES / 1024 / NWAVE;  // 4
-  constexpr int RPT = A_ROUNDS + B_ROUNDS;          // loads per wave per tile (+1 on waves < SW)
+  static_assert(NA >= 2 && NB >= NA && SW < NWAVE, "ring depths");
+  constexpr int A_ROUNDS = A_BYTES / 1024 / NWAVE;  // 2 or 3
+  constexpr int B_ROUNDS = B_BYTES / 1024 / NWAVE;  // 4
+  // loads per wave per group: A part A_ROUNDS (+1 scale load on waves <= SW), B part B_ROUNDS
+  constexpr int RPT = A_ROUNDS + B_ROUNDS;
 
   // the variant the scales allow runs; the other exits before touching anything
   if (mx_flag && ((*mx_flag == 0) != MX)) return;
@@ -174,23 +178,42 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
   }
   const float* ws_src = B_scales + ws_off;
 
-  auto stage_base = [&](int kt) { return lds_base + static_cast<uint32_t>(kt % NS) * STAGE; };
-  // the scales of tile kt live in their own ring slot, which the loads issued at the barrier of
-  // iterations kt - 1 and kt (tiles kt - 1 + NS, kt + NS) do not touch
+  auto a_stage = [&](int kt) { return lds_base + static_cast<uint32_t>(kt % NA) * A_BYTES; };
+  auto b_stage = [&](int kt) { return lds_base + C::B_RING + static_cast<uint32_t>(kt % NB) * B_BYTES; };
+  // The scales of tile kt (loaded with A tile kt) live in their own ring slot, which the loads
+  // issued at the barriers of iterations kt - 1 and kt (A tiles kt - 1 + NA, kt + NA) do not touch.
   auto scale_base = [&](int kt) {
-    return lds_base + NS * STAGE + static_cast<uint32_t>(kt % C::SLOTS) * C::SLOT;
+    return lds_base + C::S_RING + static_cast<uint32_t>(kt % C::SLOTS) * C::SLOT;
   };
-  auto issue_loads = [&](int kt) {
-    const uint32_t sbase = stage_base(kt);
+  // Load group j (j >= -NB): A tile j + NA with its scales and B tile j + NB, each if it exists.
+  // Group j is issued at iteration j (the prologue issues groups -NB .. -1).
+  auto issue_group = [&](int j) {
+    const int ta = j + NA, tb = j + NB;
+    if (ta >= 0 && ta < nkb) {
+      const uint32_t abase = a_stage(ta);
 #pragma unroll
-    for (int p = 0; p < A_ROUNDS; ++p)
-      lds_dma16(a_src[p] + static_cast<int64_t>(kt) * kF8BK, sbase + (NWAVE * p + wave) * 1024);
-    if (wave < SW) lds_dma4(as_src + kt, scale_base(kt) + wave * 256);
-    if (wave == SW) lds_dma4(ws_src + static_cast<int64_t>(kt) * nbn, scale_base(kt) + BM * 4);
-    const uint8_t* bs = b_src + static_cast<int64_t>(kt) * kF8BK * ldb;
+      for (int p = 0; p < A_ROUNDS; ++p)
+        lds_dma16(a_src[p] + static_cast<int64_t>(ta) * kF8BK, abase + (NWAVE * p + wave) * 1024);
+      if (wave < SW) lds_dma4(as_src + ta, scale_base(ta) + wave * 256);
+      if (wave == SW) lds_dma4(ws_src + static_cast<int64_t>(ta) * nbn, scale_base(ta) + BM * 4);
+    }
+    if (tb < nkb) {
+      const uint32_t bbase = b_stage(tb);
+      const uint8_t* bs = b_src + static_cast<int64_t>(tb) * kF8BK * ldb;
 #pragma unroll
-    for (int p = 0; p < B_ROUNDS; ++p)
-      lds_dma16(bs + p * b_round, sbase + A_BYTES + (NWAVE * p + wave) * 1024);
+      for (int p = 0; p < B_ROUNDS; ++p) lds_dma16(bs + p * b_round, bbase + (NWAVE * p + wave) * 1024);
+    }
+  };
+  // vmcnt waits (per wave: RPTW = RPT, +1 on waves <= SW).  Tile 0 after the prologue: loads
+  // issued after A tile 0 are the B part of its group (when NB > NA) and NA - 1 whole groups, when
+  // every tile they name exists (NB <= nk).  Tile t + 1 at iteration t: the B part of its group
+  // and NA - 2 whole groups, when t + NB <= nk.  Otherwise wait for all.
+  constexpr int B_AFTER_A = NB > NA ? B_ROUNDS : 0;
+  auto wait_tile = [&](bool full, auto groups_c) {
+    constexpr int G = decltype(groups_c)::value;
+    if (!full) wait_vmcnt<0>();
+    else if (wave <= SW) wait_vmcnt<B_AFTER_A + G * (RPT + 1)>();
+    else wait_vmcnt<B_AFTER_A + G * RPT>();
   };
 
   // ---- fragment addresses
@@ -230,16 +253,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
     constexpr int NL = decltype(nl_c)::value;
     constexpr int NLA = NL > 0 ? NL : 1;
     i32x8_t af[2][NLA], bfr[2][FN];
-    auto read_a = [&](uint32_t sbase, int s, int buf, int i) {
+    auto read_a = [&](uint32_t abase, int s, int buf, int i) {
       const uint32_t c0 = 4 * s + 2 * khalf;
       u32x4_t lo = *reinterpret_cast<const lds_u32x4_t*>(
-          static_cast<uintptr_t>(sbase + a_row_off[i] + ((c0 ^ a_sw[i]) << 4)));
+          static_cast<uintptr_t>(abase + a_row_off[i] + ((c0 ^ a_sw[i]) << 4)));
       u32x4_t hi = *reinterpret_cast<const lds_u32x4_t*>(
-          static_cast<uintptr_t>(sbase + a_row_off[i] + (((c0 + 1) ^ a_sw[i]) << 4)));
+          static_cast<uintptr_t>(abase + a_row_off[i] + (((c0 + 1) ^ a_sw[i]) << 4)));
       af[buf][i] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     };
-    auto read_b = [&](uint32_t sbase, int s, int buf, int j) {
-      const uint32_t bbase = sbase + A_BYTES + s * 64 * kF8BRow;
+    auto read_b = [&](uint32_t bstage, int s, int buf, int j) {
+      const uint32_t bbase = bstage + s * 64 * kF8BRow;
       v2i32_t q[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -251,20 +274,19 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
     // Read in the order the MFMAs (i-major) consume them: B0, A0, B1, A1, ...
     auto read_frags = [&](int kt, int s, int buf) {
       if constexpr (NL > 0) {
-        const uint32_t sbase = stage_base(kt);
-        read_b(sbase, s, buf, 0);
-        read_a(sbase, s, buf, 0);
+        const uint32_t abase = a_stage(kt), bbase = b_stage(kt);
+        read_b(bbase, s, buf, 0);
+        read_a(abase, s, buf, 0);
 #pragma unroll
-        for (int j = 1; j < FN; ++j) read_b(sbase, s, buf, j);
+        for (int j = 1; j < FN; ++j) read_b(bbase, s, buf, j);
 #pragma unroll
-        for (int i = 1; i < NL; ++i) read_a(sbase, s, buf, i);
+        for (int i = 1; i < NL; ++i) read_a(abase, s, buf, i);
       }
     };
 
-    // The first tile's loads, then the loop.  vmcnt per wave: RPT (+1 on the scale waves).
-    const int pro = nk < NS ? nk : NS;  // tiles in flight before the loop
-    for (int t = 0; t < pro; ++t) issue_loads(t);
-    if (wave <= SW) wait_tiles<RPT + 1, NS - 1>(pro - 1); else wait_tiles<RPT, NS - 1>(pro - 1);  // tile 0 landed
+    // The first groups of loads, then the loop.
+    for (int j = -NB; j < 0; ++j) issue_group(j);
+    wait_tile(NB <= nk, std::integral_constant<int, NA - 1>{});  // tile 0 landed
     lds_barrier();
     read_frags(0, 0, 0);
 
@@ -305,10 +327,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
         read_frags(kt, 1, 1);
         if (kt + 1 < nk) {
           wait_lgkm0();  // this wave's reads of tile kt are complete
-          const int later = nk - 2 - kt < NS - 2 ? nk - 2 - kt : NS - 2;
-          if (wave <= SW) wait_tiles<RPT + 1, NS - 2>(later); else wait_tiles<RPT, NS - 2>(later);
-          lds_barrier();  // for every wave: tile kt + 1 readable, tile kt's stage free
-          if (kt + NS < nk) issue_loads(kt + NS);
+          wait_tile(kt + NB <= nk, std::integral_constant<int, NA - 2>{});  // tile kt + 1 landed
+          lds_barrier();  // for every wave: tile kt + 1 readable, tile kt's stages free
+          issue_group(kt);
           read_exps(kt + 1);
         }
         mfmas(1);
@@ -352,11 +373,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
         read_frags(kt, 1, 1);
         if (kt + 1 < nk) {
           wait_lgkm0();  // this wave's reads of tile kt are complete
-          // this wave's loads of tile kt + 1 have landed; tiles kt + 2 .. kt + NS - 1 may be in flight
-          const int later = nk - 2 - kt < NS - 2 ? nk - 2 - kt : NS - 2;
-          if (wave <= SW) wait_tiles<RPT + 1, NS - 2>(later); else wait_tiles<RPT, NS - 2>(later);
-          lds_barrier();  // for every wave: tile kt + 1 readable, tile kt's stage free
-          if (kt + NS < nk) issue_loads(kt + NS);
+          wait_tile(kt + NB <= nk, std::integral_constant<int, NA - 2>{});  // tile kt + 1 landed
+          lds_barrier();  // for every wave: tile kt + 1 readable, tile kt's stages free
+          issue_group(kt);
         }
         mfmas(1, false);
         read_scales(kt);
@@ -380,7 +399,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
     // quantisation block per row).  Read back by 8 consecutive lanes per row, 16 columns each:
     // the block amax is a register max and 3 shuffles, and each lane stores 16 E4M3 codes at once.
     constexpr int kHS = 136;  // row stride in floats: rows 4 apart (the two lane halves) start 32 banks apart
-    static_assert(BM * kHS * 4 <= NS * STAGE, "h staging fits in the operand ring");
+    static_assert(BM * kHS * 4 <= C::S_RING, "h staging fits in the operand rings");
     const int F = ldb / 2;
     wait_lgkm0();
     __syncthreads();  // every wave is done with the operand ring
@@ -429,7 +448,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
   } else if (!OUT_F32) {
     // bf16 y staged through LDS as [BM][256] (+ padding) and stored 16 bytes (8 columns) per lane
     constexpr int kYS = 264;  // row stride in bf16: rows 4 apart (the two lane halves) 16 banks apart
-    static_assert(BM * kYS * 2 <= NS * STAGE, "y staging fits in the operand ring");
+    static_assert(BM * kYS * 2 <= C::S_RING, "y staging fits in the operand rings");
     wait_lgkm0();
     __syncthreads();  // every wave is done with the operand ring
     bf16_t* yl = reinterpret_cast<bf16_t*>(smem);
