@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
   constexpr int NA = C::NA, NB = C::NB;
   constexpr int SW = BM / 64;                       // waves gathering the row scales (64 rows each)
   static_assert(BM % 64 == 0 && A_BYTES % (1024 * NWAVE) == 0, "tile height");
-  static_assert(NA >= 2 && NB >= NA && SW < NWAVE, "ring depths");
+  static_assert(NA >= 2 && NB >= 2 && SW < NWAVE, "ring depths");
   constexpr int A_ROUNDS = A_BYTES / 1024 / NWAVE;  // 2 or 3
   constexpr int B_ROUNDS = B_BYTES / 1024 / NWAVE;  // 4
   // loads per wave per group: A part A_ROUNDS (+1 scale load on waves <= SW), B part B_ROUNDS
@@ -185,8 +185,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
   auto scale_base = [&](int kt) {
     return lds_base + C::S_RING + static_cast<uint32_t>(kt % C::SLOTS) * C::SLOT;
   };
-  // Load group j (j >= -NB): A tile j + NA with its scales and B tile j + NB, each if it exists.
-  // Group j is issued at iteration j (the prologue issues groups -NB .. -1).
+  // Load group j: A tile j + NA with its scales and B tile j + NB, each if it exists.  Group j is
+  // issued at iteration j (the prologue issues groups -max(NA, NB) .. -1).
   auto issue_group = [&](int j) {
     const int ta = j + NA, tb = j + NB;
     if (ta >= 0 && ta < nkb) {
@@ -197,23 +197,25 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
       if (wave < SW) lds_dma4(as_src + ta, scale_base(ta) + wave * 256);
       if (wave == SW) lds_dma4(ws_src + static_cast<int64_t>(ta) * nbn, scale_base(ta) + BM * 4);
     }
-    if (tb < nkb) {
+    if (tb >= 0 && tb < nkb) {
       const uint32_t bbase = b_stage(tb);
       const uint8_t* bs = b_src + static_cast<int64_t>(tb) * kF8BK * ldb;
 #pragma unroll
       for (int p = 0; p < B_ROUNDS; ++p) lds_dma16(bs + p * b_round, bbase + (NWAVE * p + wave) * 1024);
     }
   };
-  // vmcnt waits (per wave: RPTW = RPT, +1 on waves <= SW).  Tile 0 after the prologue: loads
-  // issued after A tile 0 are the B part of its group (when NB > NA) and NA - 1 whole groups, when
-  // every tile they name exists (NB <= nk).  Tile t + 1 at iteration t: the B part of its group
-  // and NA - 2 whole groups, when t + NB <= nk.  Otherwise wait for all.
-  constexpr int B_AFTER_A = NB > NA ? B_ROUNDS : 0;
+  // vmcnt waits (per wave: RPTW = RPT, +1 on waves <= SW).  Tile t is complete once the later
+  // of its A and B parts has landed: loads issued after that part are the B part of its group
+  // (when NB > NA) and then whole groups -- min(NA, NB) - 1 after the prologue (tile 0), and
+  // min(NA, NB) - 2 at iteration t (tile t + 1) -- when every tile those groups name exists
+  // (max(NA, NB) <= nk, t + max(NA, NB) <= nk).  Otherwise wait for all.
+  constexpr int NM = NA > NB ? NA : NB, GM = NA < NB ? NA : NB;
+  constexpr int AFTER = NB > NA ? B_ROUNDS : 0;
   auto wait_tile = [&](bool full, auto groups_c) {
     constexpr int G = decltype(groups_c)::value;
     if (!full) wait_vmcnt<0>();
-    else if (wave <= SW) wait_vmcnt<B_AFTER_A + G * (RPT + 1)>();
-    else wait_vmcnt<B_AFTER_A + G * RPT>();
+    else if (wave <= SW) wait_vmcnt<AFTER + G * (RPT + 1)>();
+    else wait_vmcnt<AFTER + G * RPT>();
   };
 
   // ---- fragment addresses
@@ -285,8 +287,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
     };
 
     // The first groups of loads, then the loop.
-    for (int j = -NB; j < 0; ++j) issue_group(j);
-    wait_tile(NB <= nk, std::integral_constant<int, NA - 1>{});  // tile 0 landed
+    for (int j = -NM; j < 0; ++j) issue_group(j);
+    wait_tile(NM <= nk, std::integral_constant<int, GM - 1>{});  // tile 0 landed
     lds_barrier();
     read_frags(0, 0, 0);
 
@@ -327,7 +329,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
         read_frags(kt, 1, 1);
         if (kt + 1 < nk) {
           wait_lgkm0();  // this wave's reads of tile kt are complete
-          wait_tile(kt + NB <= nk, std::integral_constant<int, NA - 2>{});  // tile kt + 1 landed
+          wait_tile(kt + NM <= nk, std::integral_constant<int, GM - 2>{});  // tile kt + 1 landed
           lds_barrier();  // for every wave: tile kt + 1 readable, tile kt's stages free
           issue_group(kt);
           read_exps(kt + 1);
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
         read_frags(kt, 1, 1);
         if (kt + 1 < nk) {
           wait_lgkm0();  // this wave's reads of tile kt are complete
-          wait_tile(kt + NB <= nk, std::integral_constant<int, NA - 2>{});  // tile kt + 1 landed
+          wait_tile(kt + NM <= nk, std::integral_constant<int, GM - 2>{});  // tile kt + 1 landed
           lds_barrier();  // for every wave: tile kt + 1 readable, tile kt's stages free
           issue_group(kt);
         }
