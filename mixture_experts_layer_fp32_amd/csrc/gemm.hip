@@ -53,10 +53,11 @@ constexpr int kThreads = 256;  // fp32 path
 //
 // Iteration kt (four 16-deep k-steps): MFMAs of k-step s interleave with the LDS reads of the
 // fragments of k-step s + 1 (read in the order the MFMAs consume them).  Before the last k-step
-// the wave waits for its own reads of tile kt and its own loads of tile kt + 1, meets the other
-// waves at the single barrier of the iteration, issues the loads of A tile kt + NA and B tile
-// kt + NB into the stages tile kt used, and then runs the last k-step while reading tile
-// kt + 1's first fragments.  So A loads have NA - 1 iterations to land and B loads NB - 1.
+// the wave waits for its own reads of tile kt and its own loads of tile kt + 1 and meets the
+// other waves at the single barrier of the iteration; the last k-step then issues, after each of
+// its MFMAs, one of the loads of A tile kt + NA and B tile kt + NB (into the stages tile kt used)
+// and one of tile kt + 1's first fragment reads, so the MFMA pipe restarts right after the
+// barrier.  A loads have NA - 1 iterations to land and B loads NB - 1.
 // Loads are unconditional: rows past the expert's end re-read its last row and column groups
 // past the matrix edge re-read column 0; those results are never stored.
 constexpr int kBKT = 64;        // K per iteration / stage
@@ -272,13 +273,39 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
         wait_lgkm0();        // this wave's reads of tile kt are complete
         wait_tile_next(kt);  // this wave's loads of A and B tile kt + 1 have landed
         lds_barrier();       // ... for every wave: tile kt + 1 readable, tile kt's stages free
-        issue_group(kt);
       }
       __builtin_amdgcn_sched_barrier(0);
-      mfmas(1);
-      read_frags(kt + 1, 0, 0);  // past the last tile this reads a stale stage (in bounds, unused)
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
+      // last k-step: MFMA q, then load q of group kt, then fragment read q of tile kt + 1
+      {
+        const int ta = kt + NA, tb = kt + NB;
+        const bool do_a = kt + 1 < nk && ta < nk, do_b = kt + 1 < nk && tb < nk;
+        const uint32_t abase = a_stage(ta), bbase = b_stage(tb);
+        const bf16_t* bs = b_src + static_cast<int64_t>(tb) * b_kstep;
+        const uint32_t nabase = a_stage(kt + 1), nbbase = b_stage(kt + 1);
+        constexpr int NQ = NL * FN > RPT ? NL * FN : RPT;
+        constexpr int NR = NL > 0 ? NL + FN : 0;  // read units: B0, A0, B1, A1, A2, ...
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          if (q < NL * FN) {
+            const int i = q / FN, j = q % FN;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bfr[1][j], acc[i][j], 0, 0, 0);
+          }
+          if (q < A_ROUNDS) {
+            if (do_a) lds_dma16(a_src[q] + static_cast<int64_t>(ta) * kBKT, abase + (NWAVE * q + wave) * 1024);
+          } else if (q < RPT) {
+            if (do_b) lds_dma16(bs + (q - A_ROUNDS) * b_round, bbase + (NWAVE * (q - A_ROUNDS) + wave) * 1024);
+          }
+          if constexpr (NL > 0) {
+            if (q < NR) {
+              if (q == 0) read_b(nbbase, 0, 0, 0);
+              else if (q == 1) read_a(nabase, 0, 0, 0);
+              else if (q < 2 + FN - 1) read_b(nbbase, 0, 0, q - 1);
+              else read_a(nabase, 0, 0, q - FN);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
   };
   dispatch_live<FM>(nlive, run);

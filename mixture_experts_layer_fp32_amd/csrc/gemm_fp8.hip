@@ -331,11 +331,48 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
           wait_lgkm0();  // this wave's reads of tile kt are complete
           wait_tile(kt + NM <= nk, std::integral_constant<int, GM - 2>{});  // tile kt + 1 landed
           lds_barrier();  // for every wave: tile kt + 1 readable, tile kt's stages free
-          issue_group(kt);
           read_exps(kt + 1);
         }
-        mfmas(1);
-        read_frags(kt + 1, 0, 0);  // past the last tile this reads a stale stage (in bounds, unused)
+        __builtin_amdgcn_sched_barrier(0);
+        // Second sub-step: after each MFMA, one load of group kt (A rounds, the scale load, B
+        // rounds -- the order issue_group uses) and one fragment read of tile kt + 1, so the
+        // MFMA pipe restarts right after the barrier.
+        {
+          const int ta = kt + NA, tb = kt + NB;
+          const bool do_a = kt + 1 < nk && ta < nk, do_b = kt + 1 < nk && tb < nk;
+          const uint32_t abase = a_stage(ta), bbase = b_stage(tb);
+          const uint8_t* bs = b_src + static_cast<int64_t>(tb) * kF8BK * ldb;
+          const uint32_t nabase = a_stage(kt + 1), nbbase = b_stage(kt + 1);
+          constexpr int NLD = A_ROUNDS + 1 + B_ROUNDS;  // load slots (the scale slot is empty on waves > SW)
+          constexpr int NQ = NL * FN > NLD ? NL * FN : NLD;
+          constexpr int NR = NL > 0 ? NL + FN : 0;  // read units: B0, A0, B1, A1, A2, ...
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            if (q < NL * FN) {
+              const int i = q / FN, j = q % FN;
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[1][i], bfr[1][j], acc[i][j], 0, 0, 0,
+                                                                           sae[i], 0, sbe[j]);
+            }
+            if (q < A_ROUNDS) {
+              if (do_a) lds_dma16(a_src[q] + static_cast<int64_t>(ta) * kF8BK, abase + (NWAVE * q + wave) * 1024);
+            } else if (q == A_ROUNDS) {
+              if (do_a && wave < SW) lds_dma4(as_src + ta, scale_base(ta) + wave * 256);
+              if (do_a && wave == SW) lds_dma4(ws_src + static_cast<int64_t>(ta) * nbn, scale_base(ta) + BM * 4);
+            } else if (q < NLD) {
+              const int p = q - A_ROUNDS - 1;
+              if (do_b) lds_dma16(bs + p * b_round, bbase + (NWAVE * p + wave) * 1024);
+            }
+            if constexpr (NL > 0) {
+              if (q < NR) {
+                if (q == 0) read_b(nbbase, 0, 0, 0);
+                else if (q == 1) read_a(nabase, 0, 0, 0);
+                else if (q < 2 + FN - 1) read_b(nbbase, 0, 0, q - 1);
+                else read_a(nabase, 0, 0, q - FN);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
         if (kt + 1 < nk) take_exps();
       }
     } else {
