@@ -95,7 +95,12 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   // The per-expert m-tile prefix of the tile map lives in the first B stage until the first loads.
   TileMap tm;
-  if (!map_tile<BM>(offsets, rows, E, NT, reinterpret_cast<int*>(smem + B_RING), tm, ncu, S)) return;
+  // skewed loads: SwiGLU GEMMs spread every expert over the XCDs (measured: the second GEMM,
+  // whose activation rows are as large as its weights, runs better on the contiguous map)
+  int* s_pref = reinterpret_cast<int*>(smem + B_RING);
+  if (SWIGLU ? !map_tile_auto<BM>(offsets, rows, E, NT, s_pref, tm, ncu, S)
+             : !map_tile<BM>(offsets, rows, E, NT, s_pref, tm, ncu, S))
+    return;
   __syncthreads();
   const int nk = K / kBKT;
 
@@ -473,7 +478,8 @@ hipError_t launch_bf16(const bf16_t* A, const bf16_t* B, const int32_t* offsets,
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (attr != hipSuccess) return attr;
-  const unsigned grid = grid_for(max_tiles<BM>(rows, E, offsets == nullptr), NT, ncu, S);
+  const int64_t mt = max_tiles<BM>(rows, E, offsets == nullptr);
+  const unsigned grid = SWIGLU ? grid_for_any(mt, NT, E, offsets == nullptr, ncu, S) : grid_for(mt, NT, ncu, S);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256 * WM), smem, stream, A, B, offsets, rows, E, K, ldb, NT, out, ncu,
                      gather);
   return hipGetLastError();

@@ -19,6 +19,45 @@ struct TileMap {
   int64_t row0, row_end;  // this tile's first row and the expert's end row
 };
 
+// Words of the prefix buffer past E + 1 (E <= 512) where the scan leaves two statistics of
+// the scanned values: their maximum and how many are non-zero.
+constexpr int kStatMax = kMaxExpertsLds - 2, kStatNonzero = kMaxExpertsLds - 1;
+
+// In-place inclusive scan of s_pref[1..E] by one wave (E <= 512, chunks of 64), s_pref[0] = 0,
+// and the statistics above; every thread of the workgroup calls it after writing s_pref[1..E].
+__device__ void scan_prefix(int* s_pref, int E) {
+  const int tid = threadIdx.x;
+  if (tid == 0) s_pref[0] = 0;
+  __syncthreads();
+  if (tid < kWave) {
+    int carry = 0, mx = 0, nz = 0;
+    for (int base = 1; base <= E; base += kWave) {
+      int i = base + tid;
+      int v = i <= E ? s_pref[i] : 0;
+      mx = v > mx ? v : mx;
+      nz += v != 0;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        int u = __shfl_up(v, o, kWave);
+        if (tid >= o) v += u;
+      }
+      if (i <= E) s_pref[i] = v + carry;
+      carry += __shfl(v, kWave - 1, kWave);
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int m2 = __shfl_xor(mx, o, kWave);
+      mx = m2 > mx ? m2 : mx;
+      nz += __shfl_xor(nz, o, kWave);
+    }
+    if (tid == 0) {
+      s_pref[kStatMax] = mx;
+      s_pref[kStatNonzero] = nz;
+    }
+  }
+  __syncthreads();
+}
+
 // Tile count (m-tiles summed over experts, times NT); builds the m-tile prefix in s_pref.
 template <int BM>
 __device__ int count_tiles(const int32_t* offsets, int64_t rows, int E, int NT, int* s_pref) {
@@ -29,25 +68,10 @@ __device__ int count_tiles(const int32_t* offsets, int64_t rows, int E, int NT, 
     int c = offsets[e + 1] - offsets[e];
     s_pref[e + 1] = (c + BM - 1) / BM;
   }
-  if (tid == 0) s_pref[0] = 0;
-  __syncthreads();
-  if (tid < kWave) {  // one wave scans E <= 512 entries in chunks of 64
-    int carry = 0;
-    for (int base = 1; base <= E; base += kWave) {
-      int i = base + tid;
-      int v = i <= E ? s_pref[i] : 0;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        int u = __shfl_up(v, o, kWave);
-        if (tid >= o) v += u;
-      }
-      if (i <= E) s_pref[i] = v + carry;
-      carry += __shfl(v, kWave - 1, kWave);
-    }
-  }
-  __syncthreads();
+  scan_prefix(s_pref, E);
   return s_pref[E] * NT;
 }
+
 
 // Tiles that do not fill the last wave of `ncu` workgroups when run whole (at most `ncu` - 1): with
 // S > 1 each of them is cut into up to S row bands (so the last wave holds several times as many
@@ -102,9 +126,8 @@ __device__ void locate_tile(const int32_t* offsets, int64_t rows, int E, int NT,
 // [0, 8 ceil(W / 8)) take the W whole tiles, XCD-remapped (consecutive tiles on one XCD share
 // weights and rows in its L2); the following ones take the S row bands of each tail tile.
 template <int BM>
-__device__ bool map_tile(const int32_t* offsets, int64_t rows, int E, int NT, int* s_pref, TileMap& tm,
-                         int ncu = 0, int S = 1) {
-  const int total = count_tiles<BM>(offsets, rows, E, NT, s_pref);
+__device__ bool map_tile_counted(const int32_t* offsets, int64_t rows, int E, int NT, const int* s_pref,
+                                 int total, TileMap& tm, int ncu, int S) {
   const int whole = whole_tiles(total, ncu, S);
   const int per = (whole + 7) / 8;
   const int w = blockIdx.x;
@@ -133,6 +156,69 @@ __device__ bool map_tile(const int32_t* offsets, int64_t rows, int E, int NT, in
   const int64_t band_end = tm.row0 + band_rows;
   if (band_end < tm.row_end) tm.row_end = band_end;
   return tm.row0 < tm.row_end;  // band past the tile's last row, or an empty tile
+}
+
+template <int BM>
+__device__ bool map_tile(const int32_t* offsets, int64_t rows, int E, int NT, int* s_pref, TileMap& tm,
+                         int ncu = 0, int S = 1) {
+  const int total = count_tiles<BM>(offsets, rows, E, NT, s_pref);
+  return map_tile_counted<BM>(offsets, rows, E, NT, s_pref, total, tm, ncu, S);
+}
+
+// Alternative whole-tile map that spreads every expert's work evenly over the 8 XCDs: the NT m_e
+// tiles of expert e, in n-tile -> m-tile order, are cut into 8 contiguous ranges of equal size
+// (+-1), range x for XCD x.  On its XCD, workgroup w / 8 takes that XCD's tiles expert by expert,
+// so the m-tiles sharing a weight tile stay adjacent and share it through that XCD's L2 (only a
+// weight tile cut by a range boundary is fetched by two XCDs).  With skewed loads (a few experts
+// with many m-tiles) the map above gives each XCD a contiguous range of equal tile count but very
+// unequal work; here each XCD gets the same share of every expert.  On entry `s_pref` holds the
+// m-tile prefix (count_tiles).  The launch needs grid_for_spread workgroups.
+template <int BM>
+__device__ bool map_tile_spread(const int32_t* offsets, int E, int NT, int* s_pref, TileMap& tm) {
+  const int x = static_cast<int>(blockIdx.x % 8), i = static_cast<int>(blockIdx.x / 8);
+  auto range_start = [&](int me, int xx) { return static_cast<int>(static_cast<int64_t>(xx) * me * NT / 8); };
+  // A thread owns experts tid and tid + blockDim (blockDim >= 256, E <= 512).
+  const int e0 = static_cast<int>(threadIdx.x), e1 = e0 + static_cast<int>(blockDim.x);
+  const int me0 = e0 < E ? s_pref[e0 + 1] - s_pref[e0] : 0;
+  const int me1 = e1 < E ? s_pref[e1 + 1] - s_pref[e1] : 0;
+  __syncthreads();
+  if (e0 < E) s_pref[e0 + 1] = range_start(me0, x + 1) - range_start(me0, x);  // this XCD's tiles of e0
+  if (e1 < E) s_pref[e1 + 1] = range_start(me1, x + 1) - range_start(me1, x);
+  scan_prefix(s_pref, E);
+  if (i >= s_pref[E]) return false;
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (s_pref[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int64_t base = offsets[e], M = offsets[e + 1] - base;
+  const int me = static_cast<int>(ceil_div(M, BM));
+  const int j = range_start(me, x) + (i - s_pref[e]);  // tile of expert e, n-major
+  tm.expert = e;
+  tm.nt = j / me;
+  tm.mt = j % me;
+  const int64_t rpt = balanced_rows<BM>(M, me);
+  tm.row0 = base + static_cast<int64_t>(tm.mt) * rpt;
+  tm.row_end = tm.row0 + rpt < base + M ? tm.row0 + rpt : base + M;
+  return tm.row0 < tm.row_end;
+}
+
+// Picks the tile map: map_tile_spread when the expert loads are skewed (the busiest expert has
+// more than 3x the mean m-tile count of the experts with rows), else map_tile.  The statistics
+// come out of the m-tile prefix scan, so every workgroup reaches the same decision from the
+// same offsets at no extra cost.  The grid must cover both maps (grid_for_any).  `s_pref` is
+// LDS of kMaxExpertsLds ints (E <= 512).
+template <int BM>
+__device__ bool map_tile_auto(const int32_t* offsets, int64_t rows, int E, int NT, int* s_pref, TileMap& tm,
+                              int ncu = 0, int S = 1) {
+  const int total = count_tiles<BM>(offsets, rows, E, NT, s_pref);
+  if (offsets != nullptr) {
+    const int64_t mtiles = s_pref[E];
+    if (static_cast<int64_t>(s_pref[kStatMax]) * s_pref[kStatNonzero] > 3 * mtiles)
+      return map_tile_spread<BM>(offsets, E, NT, s_pref, tm);
+  }
+  return map_tile_counted<BM>(offsets, rows, E, NT, s_pref, total, tm, ncu, S);
 }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -207,10 +293,22 @@ inline int64_t max_tiles(int64_t rows, int E, bool dense) {
   return dense ? ceil_div(rows, BM) : (rows + static_cast<int64_t>(E) * (BM - 1)) / BM;
 }
 
+inline unsigned grid_for_spread(int64_t mtiles, int NT, int E) {
+  return static_cast<unsigned>(8 * (ceil_div(mtiles * NT, 8) + E));  // per XCD: sum_e ceil(NT m_e / 8)
+}
+
 inline unsigned grid_for(int64_t mtiles, int NT, int ncu = 0, int S = 1) {
   int64_t g = mtiles * NT;
   if (S > 1) g += 7 + 7 * S + static_cast<int64_t>(ncu - 1) * (S - 1);  // roundings to 8 + tail bands
   return static_cast<unsigned>(ceil_div(g, 8) * 8);
+}
+
+// Workgroups for map_tile_auto: enough for either map.
+inline unsigned grid_for_any(int64_t mtiles, int NT, int E, bool dense, int ncu = 0, int S = 1) {
+  const unsigned a = grid_for(mtiles, NT, ncu, S);
+  if (dense) return a;  // one expert: always the contiguous map
+  const unsigned b = grid_for_spread(mtiles, NT, E);
+  return a > b ? a : b;
 }
 
 }  // namespace gemm

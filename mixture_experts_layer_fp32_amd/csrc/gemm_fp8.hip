@@ -111,7 +111,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
   __shared__ int s_pref[kMaxExpertsLds];
 
   TileMap tm;
-  if (!map_tile<BM>(offsets, rows, E, NT, s_pref, tm)) return;
+  // skewed loads: the SwiGLU GEMM spreads every expert over the XCDs (the second GEMM, whose
+  // activation rows are as large as its weights, measured better on the contiguous map)
+  if (SWIGLU ? !map_tile_auto<BM>(offsets, rows, E, NT, s_pref, tm) : !map_tile<BM>(offsets, rows, E, NT, s_pref, tm))
+    return;
   const int t_expert = __builtin_amdgcn_readfirstlane(tm.expert);  // uniform: scalar address math
   const int t_nt = __builtin_amdgcn_readfirstlane(tm.nt);
 
@@ -538,7 +541,8 @@ hipError_t launch_fp8(const uint8_t* A, const float* As, const uint8_t* B, const
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (attr != hipSuccess) return attr;
-  const unsigned grid = grid_for(max_tiles<BM>(rows, E, offsets == nullptr), NT);
+  const int64_t mt = max_tiles<BM>(rows, E, offsets == nullptr);
+  const unsigned grid = SWIGLU ? grid_for_any(mt, NT, E, offsets == nullptr) : grid_for(mt, NT);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), smem, stream, A, As, B, Bs, offsets, rows, E, K, ldb,
                      NT, out, out_scales, gather, mx_flag);
   return hipGetLastError();

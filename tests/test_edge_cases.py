@@ -154,10 +154,15 @@ def test_guard_bands_untouched():
     assert not (yp.view(torch.int16) == 12345).all(dim=1).any()  # every row was written
 
 
-def test_hip_graph_capture_and_replay():
+@pytest.mark.parametrize("w_dtype", ["bf16", "e4m3"])
+def test_hip_graph_capture_and_replay(w_dtype):
     """The fused forward records into a HIP graph (no sync, no allocation inside) and every
-    replay, with eager work in between, reproduces the eager result bit for bit."""
-    cfg = moe_inputs.CONFIGS["deepseek_v3"].replace(T=512, H=256, E=16, k=4, F=128, Fs=128)
+    replay, with eager work in between, reproduces the eager result bit for bit (in e4m3 the
+    graph also holds the scale check that picks the GEMM variant)."""
+    base = "deepseek_v3" if w_dtype == "bf16" else "deepseek_v3_fp8_zipf"
+    cfg = moe_inputs.CONFIGS[base].replace(T=512, H=256, E=16, k=4, F=128, Fs=128)
+    if w_dtype == "e4m3":
+        cfg = cfg.replace(zipf_bias=False)
     d = moe_inputs.make_inputs(cfg, seed=2, weight_device=DEV, act_device=DEV)
     layer = moe_gpu.Layer.from_inputs(d, cfg.k, cfg.score, cfg.norm)
     ws = torch.empty(moe_gpu.workspace_size(layer, cfg.T, d["x"].dtype), dtype=torch.uint8, device=DEV)
