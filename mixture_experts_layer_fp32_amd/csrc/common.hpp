@@ -139,9 +139,11 @@ hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int 
                                  const int32_t* gather = nullptr);
 
 // Dense out[rows, N] (fp32) = A[rows, K] . B[K, N] with bf16 A and B (B N-contiguous),
-// K % 64 == 0, N % 8 == 0: the grouped-GEMM kernel with one expert.
+// K % 64 == 0, N % 8 == 0: the grouped-GEMM kernel with one expert.  With ksplit > 1 (K / 64 a
+// multiple of ksplit) K is cut into ksplit equal slices and out[s] (at out + s * rows * N) gets
+// slice s's partial product; the caller sums them.
 hipError_t launch_dense_gemm_f32out(const void* A, const void* B, int64_t rows, int K, int N, float* out,
-                                    hipStream_t stream);
+                                    hipStream_t stream, int ksplit = 1);
 
 // FP8 (E4M3) path: x_perm codes + [rows, H/128] scales, weights as codes + 128x128-block scales;
 // the SwiGLU output h is re-quantised to E4M3 in 1x128 blocks in the scratch buffer

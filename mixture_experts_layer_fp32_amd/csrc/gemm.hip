@@ -76,7 +76,7 @@ template <int BM, int WM, bool SWIGLU, bool OUT_F32, int S>
 __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const int32_t* __restrict__ offsets,
     int64_t rows, int E, int K, int ldb, int NT, void* __restrict__ out, int ncu,
-    const int32_t* __restrict__ gather) {
+    const int32_t* __restrict__ gather, int ksplit) {
   using R = Bf16Rings<BM>;
   constexpr int NA = R::NA, NB = R::NB;
   constexpr int NWAVE = 4 * WM;                // WM along M x 4 along N
@@ -102,7 +102,18 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
              : !map_tile<BM>(offsets, rows, E, NT, s_pref, tm, ncu, S))
     return;
   __syncthreads();
-  const int nk = K / kBKT;
+  // Split K (one dense matrix, fp32 out): n-tile index ks * NT / ksplit + n covers n-tile n over
+  // the ks-th 1/ksplit of K and writes its partial product to out + ks * rows * ldb.
+  int nk = K / kBKT;
+  int64_t k_first = 0;  // first K element of this tile
+  if (ksplit > 1) {
+    const int ntr = NT / ksplit;
+    const int ks = tm.nt / ntr;
+    tm.nt -= ks * ntr;
+    nk /= ksplit;
+    k_first = static_cast<int64_t>(ks) * nk * kBKT;
+    out = static_cast<float*>(out) + static_cast<int64_t>(ks) * rows * ldb;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -121,7 +132,7 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     int64_t grow = tm.row0 + r;
     if (grow >= tm.row_end) grow = tm.row_end - 1;
     if (gather) grow = gather[grow];  // fused dispatch: row p of the tile is token gather[p]
-    a_src[p] = A + grow * K + (((lane % 8) ^ ((r >> 1) & 7)) * 8);
+    a_src[p] = A + grow * K + k_first + (((lane % 8) ^ ((r >> 1) & 7)) * 8);
   }
   // B round p of wave w covers k-rows 2 (8p + w) + lane / 32 (1 KB = 2 k-rows x 512 B); stored
   // chunk lane % 32 holds logical chunk (lane % 32) ^ 4 ((2w + lane / 32) & 3).
@@ -137,7 +148,7 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
       b_col = static_cast<int64_t>(tm.nt) * kBN + b_lchunk * 8;
     }
     if (b_col >= ldb) b_col = 0;  // ldb % 8 == 0: an 8-column group is wholly in or out
-    b_src = B + static_cast<int64_t>(tm.expert) * K * ldb + static_cast<int64_t>(2 * wave + lane / 32) * ldb + b_col;
+    b_src = B + static_cast<int64_t>(tm.expert) * K * ldb + (k_first + 2 * wave + lane / 32) * ldb + b_col;
   }
   const int64_t b_round = static_cast<int64_t>(2 * NWAVE) * ldb;
   const int64_t b_kstep = static_cast<int64_t>(kBKT) * ldb;
@@ -471,7 +482,7 @@ int device_cus() {
 template <int BM, bool SWIGLU, bool OUT_F32, int WM = 2, int S = 1>
 hipError_t launch_bf16(const bf16_t* A, const bf16_t* B, const int32_t* offsets, int64_t rows, int E,
                        int K, int ldb, int NT, void* out, hipStream_t stream, int ncu = 0,
-                       const int32_t* gather = nullptr) {
+                       const int32_t* gather = nullptr, int ksplit = 1) {
   constexpr int smem = Bf16Rings<BM>::SMEM;
   auto kern = gemm_bf16_kernel<BM, WM, SWIGLU, OUT_F32, S>;
   // once per instantiation (and never inside a stream capture after the first eager call)
@@ -481,7 +492,7 @@ hipError_t launch_bf16(const bf16_t* A, const bf16_t* B, const int32_t* offsets,
   const int64_t mt = max_tiles<BM>(rows, E, offsets == nullptr);
   const unsigned grid = SWIGLU ? grid_for_any(mt, NT, E, offsets == nullptr, ncu, S) : grid_for(mt, NT, ncu, S);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256 * WM), smem, stream, A, B, offsets, rows, E, K, ldb, NT, out, ncu,
-                     gather);
+                     gather, ksplit);
   return hipGetLastError();
 }
 
@@ -521,10 +532,12 @@ size_t grouped_swiglu_scratch_bytes(int64_t rows, int F, int dt) {
 }
 
 hipError_t launch_dense_gemm_f32out(const void* A, const void* B, int64_t rows, int K, int N, float* out,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, int ksplit) {
   if (rows <= 0) return hipSuccess;
+  if (ksplit < 1 || (K / kBKT) % ksplit != 0) return hipErrorInvalidValue;
   return launch_bf16<128, false, true>(static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B), nullptr, rows,
-                                       1, K, N, static_cast<int>(ceil_div(N, kBN)), out, stream);
+                                       1, K, N, static_cast<int>(ceil_div(N, kBN)) * ksplit, out, stream, 0, nullptr,
+                                       ksplit);
 }
 
 hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int dt,

@@ -238,8 +238,8 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
 // With `parts` (the [T][3 Ep] products of x with the three weight parts) the logit is
 // (lo + mid) + hi, written to `logits`; otherwise the logits are read from `logits`.
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
-    float* __restrict__ logits, const float* __restrict__ parts, int Ep, const float* __restrict__ bias, int64_t T,
-    int E, int k, int score, int norm, int32_t* __restrict__ ids, float* __restrict__ gates) {
+    float* __restrict__ logits, const float* __restrict__ parts, int Ep, int ksplit, const float* __restrict__ bias,
+    int64_t T, int E, int k, int score, int norm, int32_t* __restrict__ ids, float* __restrict__ gates) {
   const int lane = threadIdx.x % kWave;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * (kRouteThreads / kWave) + threadIdx.x / kWave;
   if (t >= T) return;  // whole wave exits together
@@ -253,7 +253,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     int e = lane + i * kWave;
     if (e < E) {
       if (pt) {
-        lg[i] = (pt[2 * Ep + e] + pt[Ep + e]) + pt[e];
+        // each part summed over the K slices in order, then smallest part first
+        const int64_t slice = T * 3 * Ep;
+        float p0 = pt[e], p1 = pt[Ep + e], p2 = pt[2 * Ep + e];
+        for (int s = 1; s < ksplit; ++s) {
+          p0 += pt[s * slice + e];
+          p1 += pt[s * slice + Ep + e];
+          p2 += pt[s * slice + 2 * Ep + e];
+        }
+        lg[i] = (p2 + p1) + p0;
         lt[e] = lg[i];
       } else {
         lg[i] = lt[e];
@@ -350,8 +358,20 @@ size_t split_bytes(int H, int E) { return static_cast<size_t>(3) * padded_expert
 // grouped-GEMM kernel (fp32 output, one row band per 128 tokens), summed per expert by top-k.
 bool logits_by_gemm(int H, int E) { return padded_experts(E) >= 64 && H % 64 == 0; }
 
-size_t parts_bytes(int64_t T, int E) {
-  return (static_cast<size_t>(T) * 3 * padded_experts(E) * sizeof(float) + 255) & ~static_cast<size_t>(255);
+// K slices of the router GEMM: with few output tiles (T/128 x 3Ep/256 of them) the projection
+// would leave CUs idle, so K is cut until there are >= 512 tiles (two waves of 256 CUs), keeping
+// >= 8 K steps of 64 per slice.
+int router_ksplit(int64_t T, int H, int E) {
+  const int64_t tiles = ceil_div(T, 128) * ceil_div(3 * padded_experts(E), 256);
+  const int nk = H / 64;
+  int ks = 1;
+  while (ks < 8 && tiles * ks < 512 && nk % (2 * ks) == 0 && nk / (2 * ks) >= 8) ks *= 2;
+  return ks;
+}
+
+size_t parts_bytes(int64_t T, int H, int E) {
+  return (static_cast<size_t>(router_ksplit(T, H, E)) * T * 3 * padded_experts(E) * sizeof(float) + 255) &
+         ~static_cast<size_t>(255);
 }
 
 hipError_t launch_logits_bf16(const bf16_t* x, const float* w, float* logits, float* parts, int64_t T, int H,
@@ -363,7 +383,7 @@ hipError_t launch_logits_bf16(const bf16_t* x, const float* w, float* logits, fl
     hipLaunchKernelGGL(route_split_kn_kernel, dim3(gs), dim3(kRouteThreads), 0, stream, w, H, E, Ep, wsplit);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return launch_dense_gemm_f32out(x, wsplit, T, H, 3 * Ep, parts, stream);
+    return launch_dense_gemm_f32out(x, wsplit, T, H, 3 * Ep, parts, stream, router_ksplit(T, H, E));
   }
   hipLaunchKernelGGL(route_split_kernel, dim3(gs), dim3(kRouteThreads), 0, stream, w, H, E, Ep, wsplit);
   if (Ep <= 16) {
@@ -388,7 +408,7 @@ hipError_t launch_logits_bf16(const bf16_t* x, const float* w, float* logits, fl
 size_t route_scratch_bytes(int64_t T, int H, int E, bool logits_given) {
   size_t a = logits_given ? 0 : (static_cast<size_t>(T) * E * sizeof(float) + 255) & ~static_cast<size_t>(255);
   a += (split_bytes(H, E) + 255) & ~static_cast<size_t>(255);
-  if (logits_by_gemm(H, E)) a += parts_bytes(T, E);
+  if (logits_by_gemm(H, E)) a += parts_bytes(T, H, E);
   return a;
 }
 
@@ -410,8 +430,8 @@ hipError_t launch_route(const void* x, int x_dt, const float* w_router, const fl
                                             stream);
   if (err != hipSuccess) return err;
   dim3 grid(static_cast<unsigned>(ceil_div(T, kRouteThreads / kWave)));
-  hipLaunchKernelGGL(route_topk_kernel, grid, dim3(kRouteThreads), 0, stream, lg, parts, padded_experts(E), bias,
-                     T, E, k, score, norm, ids, gates);
+  hipLaunchKernelGGL(route_topk_kernel, grid, dim3(kRouteThreads), 0, stream, lg, parts, padded_experts(E),
+                     parts ? router_ksplit(T, H, E) : 1, bias, T, E, k, score, norm, ids, gates);
   return hipGetLastError();
 }
 
