@@ -34,6 +34,8 @@ SMALL = {
     "mixtral_bigtile": _small("mixtral_8x7b", T=1700, H=320, E=3, k=2, F=384),
     # >= 64 experts: router logits through the dense GEMM kernel (3 x 96 columns: a ragged N tile)
     "qwen3_e96": _small("qwen3_235b", T=300, H=256, E=96, k=8, F=128),
+    # few router tiles and a long H: the router GEMM splits K into 8 slices
+    "qwen3_router_ksplit": _small("qwen3_235b", T=300, H=4096, E=64, k=8, F=128),
 }
 
 

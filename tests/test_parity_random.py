@@ -44,6 +44,24 @@ def test_random_layer_matches_oracle(seed):
     d = moe_inputs.make_inputs(cfg, seed=seed, weight_device=DEV, act_device=DEV)
     if skew:
         d["bias"] = torch.linspace(2.0, -2.0, cfg.E, dtype=torch.float32, device=DEV)
+    _check_layer(cfg, d, seed)
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "e4m3"])
+def test_one_dominant_expert_matches_oracle(w_dtype):
+    """One expert takes most rows (the grouped GEMMs' skewed-load tile map), the rest a few each."""
+    base = moe_inputs.CONFIGS["deepseek_v3" if w_dtype == "bf16" else "deepseek_v3_fp8_zipf"]
+    cfg = base.replace(T=2000, H=256, E=16, k=2, F=256, Fs=0, zipf_bias=False)
+    d = moe_inputs.make_inputs(cfg, seed=5, weight_device=DEV, act_device=DEV)
+    d["bias"] = torch.zeros(cfg.E, dtype=torch.float32, device=DEV)
+    d["bias"][3] = 8.0
+    print(f"[parity-random] dominant expert, {w_dtype}", flush=True)
+    counts = _check_layer(cfg, d, "dominant")
+    m_tiles = -(-counts // 192)  # 192- and 256-row tiles give the same verdict here
+    assert m_tiles.max() * (m_tiles > 0).sum() > 3 * m_tiles.sum()
+
+
+def _check_layer(cfg, d, seed):
     layer = moe_gpu.Layer.from_inputs(d, cfg.k, cfg.score, cfg.norm)
     y, dbg = moe_gpu.forward(d["x"], layer, debug=True)
     torch.cuda.synchronize()
@@ -68,3 +86,4 @@ def test_random_layer_matches_oracle(seed):
     print(f"[parity-random] seed {seed}: rows {o['counts'].tolist()[:12]} rel_frob y_perm {e_yp:.3e} y {e_y:.3e}",
           flush=True)
     assert e_yp <= tol and e_y <= tol
+    return o["counts"]
