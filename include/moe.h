@@ -121,7 +121,10 @@ moe_status moe_permute(const void* x, moe_dtype x_dt, const int32_t* topk_ids, i
  *   dt = MOE_BF16: x_perm, w1, w2 bf16; h rounded to bf16; y_perm bf16 or fp32.
  *   dt = MOE_FP8_E4M3: x_perm e4m3 with x_perm_scales [rows, H/128]; w1/w2 e4m3 with
  *        w1_scales [E, H/128, 2F/128], w2_scales [E, F/128, H/128] (128x128 blocks); h is
- *        quantised to e4m3 in 1x128 blocks inside the path; y_perm bf16 or fp32.
+ *        quantised to e4m3 in 1x128 blocks inside the path; y_perm bf16 or fp32.  Scales are
+ *        any positive finite fp32 values; when all of them are powers of two (as the ones
+ *        moe_permute writes) the scaled MFMA applies them exactly as exponents, otherwise a
+ *        slower path multiplies them in fp32 (chosen on the device, no host sync).
  * Sizes: bf16: H a multiple of 64 and F of 128; e4m3: both multiples of 128; fp32: both of 32.
  * workspace: at least moe_grouped_swiglu_workspace_size(rows, F, dt) bytes (holds h).
  * Rows beyond offsets[E] are not written.

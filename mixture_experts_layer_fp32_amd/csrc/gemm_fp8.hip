@@ -9,11 +9,11 @@
 //
 // Tiles BM x 256 x 128 (K step = one scale block), 8 waves in a 2 (M) x 4 (N) grid, each wave
 // (BM / 2) x 64 in 32 x 32 blocks of v_mfma_scale_f32_32x32x64_f8f6f4.  Operands stream
-// global -> LDS (global_load_lds_dwordx4; the row scales of the step with global_load_lds_dword)
-// through a ring of LDS stages:
+// global -> LDS (global_load_lds_dwordx4) through two rings of LDS stages:
 //   A stage: BM rows x 128 B, chunk c of row r at c ^ ((r >> 1) & 7) (as the bf16 kernel);
-//   B stage: 128 k-rows x 256 B (untransposed), chunk c of k-row k at c ^ 2 (k & 7).
-// The weight block scales are wave-uniform and come through the scalar cache.
+//   B stage: 128 k-rows x 256 B (untransposed), chunk c of k-row k at c ^ 2 (k & 7);
+// and, loaded with each A stage (global_load_lds_dword), a slot of scales: the row scales of
+// the step and the tile's two weight block scales.
 // B fragments come from ds_read_b64_tr_b8: within a group of 16 lanes, lane 16g + 8a + b
 // receives byte b of the 8-byte pieces addressed by lanes 16g + a + 2e (e = 0..7), so source
 // lane s addresses k-row 8 q + (s % 16) / 2 (+ 32 (s / 32)) at column 16 ((s / 16) % 2) + 8 (s % 2)
