@@ -161,11 +161,12 @@ __device__ __forceinline__ uint2 quant_e4m3_x8(uint4 v, float& scale) {
   }
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
-  const float s = e4m3_block_scale(amax);  // a power of two: the division below is exact
+  const float s = e4m3_block_scale(amax);  // a power of two
+  const float inv = pow2_inverse(s);        // x * inv is x / s rounded once
   uint32_t q[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    float r = f[i] / s;
+    float r = f[i] * inv;
     r = fminf(fmaxf(r, -448.0f), 448.0f);
     q[i] = f32_to_e4m3(r);
   }
@@ -212,23 +213,34 @@ __global__ __launch_bounds__(kScatterThreads) void perm_scatter_fp8_kernel(
   }
 }
 
-// Dense per-row quantisation (the shared expert's input): one wavefront per row.
+// Dense per-row quantisation (each token once, for the fused forward and the shared expert):
+// one wavefront per row, four 16-byte loads per lane in flight before any is quantised.
 __global__ __launch_bounds__(kScatterThreads) void quant_rows_fp8_kernel(const uint4* __restrict__ x, int64_t T,
                                                                           int H, uint2* __restrict__ codes,
                                                                           float* __restrict__ scales) {
+  constexpr int U = 4;
   const int lane = threadIdx.x % kWave;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + threadIdx.x / kWave;
   if (t >= T) return;
   const int row_vecs = H / 8;
   const int nsb = H / 128;
-  for (int c0 = 0; c0 < row_vecs; c0 += kWave) {
-    const int c = c0 + lane;
-    const bool live = c < row_vecs;
-    float s;
-    const uint2 packed = quant_e4m3_x8(live ? x[t * row_vecs + c] : make_uint4(0, 0, 0, 0), s);
-    if (live) {
-      codes[t * row_vecs + c] = packed;
-      if ((lane & 15) == 0) scales[t * nsb + c / 16] = s;
+  const uint4* src = x + t * row_vecs;
+  for (int c0 = 0; c0 < row_vecs; c0 += U * kWave) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave + lane;
+      v[u] = c < row_vecs ? src[c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave + lane;
+      float s;
+      const uint2 packed = quant_e4m3_x8(v[u], s);  // H % 128 == 0: a 16-lane group is wholly in or out
+      if (c < row_vecs) {
+        codes[t * row_vecs + c] = packed;
+        if ((lane & 15) == 0) scales[t * nsb + c / 16] = s;
+      }
     }
   }
 }
