@@ -51,13 +51,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
     g = gates[t * k + lane];
   }
   const int n8 = H / 8;
-  auto finish = [&](int c, float* acc) {
-    if (shared_out) {
-      float f[8];
-      load8(shared_out, YDT, t * n8 + c, f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += f[i];
-    }
+  auto store = [&](int c, const float* acc) {
     if (ODT == 0) {
       float4* p = static_cast<float4*>(y) + (t * n8 + c) * 2;
       p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -82,6 +76,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
       // raw 16-byte pieces (bf16: one per chunk, fp32: two), widened only at the FMA
       constexpr int NV = YDT == 0 ? 2 : 1;
       uint4 raw[2][KT][NV];
+      float sh[2][8];  // the shared expert's output, loaded with the gathers
 #pragma unroll
       for (int j = 0; j < KT; ++j)
 #pragma unroll
@@ -90,6 +85,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
           raw[0][j][v] = src[static_cast<int64_t>(c0) * NV];
           if (two) raw[1][j][v] = src[static_cast<int64_t>(c1) * NV];
         }
+      if (shared_out) {
+        load8(shared_out, YDT, t * n8 + c0, sh[0]);
+        if (two) load8(shared_out, YDT, t * n8 + c1, sh[1]);
+      }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         if (u == 1 && !two) break;
@@ -115,7 +114,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
 #pragma unroll
           for (int i = 0; i < 8; ++i) acc[i] = fmaf(gs[j], f[i], acc[i]);
         }
-        finish(u ? c1 : c0, acc);
+        if (shared_out) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += sh[u][i];
+        }
+        store(u ? c1 : c0, acc);
       }
     }
   } else {
@@ -131,7 +134,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = fmaf(gj, f[i], acc[i]);
       }
-      finish(c, acc);
+      if (shared_out) {
+        float f[8];
+        load8(shared_out, YDT, t * n8 + c, f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += f[i];
+      }
+      store(c, acc);
     }
   }
 }
