@@ -82,8 +82,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
           const uint4* src = static_cast<const uint4*>(y_perm) + (static_cast<int64_t>(rows[j]) * n8) * NV + v;
-          raw[0][j][v] = src[static_cast<int64_t>(c0) * NV];
-          if (two) raw[1][j][v] = src[static_cast<int64_t>(c1) * NV];
+          const u32x4_t* s4 = reinterpret_cast<const u32x4_t*>(src);
+          const u32x4_t a = __builtin_nontemporal_load(s4 + static_cast<int64_t>(c0) * NV);
+          raw[0][j][v] = make_uint4(a[0], a[1], a[2], a[3]);
+          if (two) {
+            const u32x4_t b = __builtin_nontemporal_load(s4 + static_cast<int64_t>(c1) * NV);
+            raw[1][j][v] = make_uint4(b[0], b[1], b[2], b[3]);
+          }
         }
       if (shared_out) {
         load8(shared_out, YDT, t * n8 + c0, sh[0]);
