@@ -88,7 +88,9 @@ moe_status moe_route(const void* x, moe_dtype x_dt, const float* w_router, const
 /* ---------------------------------------------------------------------------------------
  * Dispatch (summary page, "Method", first paragraph: tokens permuted so same-expert
  * tokens are contiguous, as the grouped GEMM requires).
- *   topk_ids       [T, k] int32, each in [0, E) and distinct within a token (not checked)
+ *   topk_ids       [T, k] int32, each in [0, E) and distinct within a token.  Not checked on
+ *                  the host (device data); the kernels take an id outside [0, E) as expert 0 and
+ *                  stay in bounds either way, but the outputs are then meaningless.
  *   expert_counts  [E] int32 out, or NULL: rows per expert (sum = T*k)
  *   expert_offsets [E+1] int32 out: exclusive prefix sum of the counts
  *   row_map        [T, k] int32 out: permuted row of (t, j)

@@ -24,6 +24,11 @@ constexpr int kBT = 256;           // tokens per count block (= threads)
 constexpr int kScanThreads = 1024;
 constexpr int kMaxE = 512;
 
+// An expert id from the caller outside [0, E) is taken as expert 0 (in every kernel alike, so
+// counts, ranks and rows stay consistent and every access stays in bounds; the caller's results
+// are then meaningless, which the interface states).
+__device__ __forceinline__ int valid_id(int e, int E) { return static_cast<unsigned>(e) < static_cast<unsigned>(E) ? e : 0; }
+
 __global__ __launch_bounds__(kBT) void perm_count_kernel(const int32_t* __restrict__ ids, int64_t T,
                                                          int E, int k, int nblk,
                                                          int32_t* __restrict__ blk_counts,
@@ -37,12 +42,12 @@ __global__ __launch_bounds__(kBT) void perm_count_kernel(const int32_t* __restri
   const int w = tid / 64;
   const unsigned long long bit = 1ull << (tid % 64);
   if (t < T) {
-    for (int j = 0; j < k; ++j) atomicOr(&bm[ids[t * k + j]][w], bit);
+    for (int j = 0; j < k; ++j) atomicOr(&bm[valid_id(ids[t * k + j], E)][w], bit);
   }
   __syncthreads();
   if (t < T) {
     for (int j = 0; j < k; ++j) {
-      int e = ids[t * k + j];
+      int e = valid_id(ids[t * k + j], E);
       int r = __popcll(bm[e][w] & (bit - 1ull));
       for (int ww = 0; ww < w; ++ww) r += __popcll(bm[e][ww]);
       local_rank[t * k + j] = r;
@@ -101,11 +106,11 @@ constexpr int kTokPerBlock = kScatterThreads / kWave;
 
 // Resolve the k permuted rows of token t in lanes 0..k-1 (others: 0) and publish the maps.
 __device__ __forceinline__ int resolve_row(const int32_t* ids, const int32_t* base,
-                                           const int32_t* local_rank, int64_t t, int k, int nblk,
+                                           const int32_t* local_rank, int64_t t, int k, int E, int nblk,
                                            int lane, int32_t* row_map, int32_t* src_token) {
   int row = 0;
   if (lane < k) {
-    int e = ids[t * k + lane];
+    int e = valid_id(ids[t * k + lane], E);
     row = base[static_cast<int64_t>(e) * nblk + t / kBT] + local_rank[t * k + lane];
     row_map[t * k + lane] = row;
     src_token[row] = static_cast<int32_t>(t);
@@ -116,12 +121,12 @@ __device__ __forceinline__ int resolve_row(const int32_t* ids, const int32_t* ba
 // Bit copy: VEC = 16 bytes per lane.
 __global__ __launch_bounds__(kScatterThreads) void perm_scatter_copy_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ ids, const int32_t* __restrict__ base,
-    const int32_t* __restrict__ local_rank, int64_t T, int row_vecs, int k, int nblk,
+    const int32_t* __restrict__ local_rank, int64_t T, int row_vecs, int k, int E, int nblk,
     uint4* __restrict__ x_perm, int32_t* __restrict__ row_map, int32_t* __restrict__ src_token) {
   const int lane = threadIdx.x % kWave;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + threadIdx.x / kWave;
   if (t >= T) return;
-  int row = resolve_row(ids, base, local_rank, t, k, nblk, lane, row_map, src_token);
+  int row = resolve_row(ids, base, local_rank, t, k, E, nblk, lane, row_map, src_token);
   if (!x_perm) return;
   const uint4* src = x + t * row_vecs;
   // four 16-byte loads in flight per lane before their k stores each
@@ -177,13 +182,13 @@ __device__ __forceinline__ uint2 quant_e4m3_x8(uint4 v, float& scale) {
 // bf16 -> e4m3 with one fp32 scale per 1x128 block (16 lanes x 8 values).
 __global__ __launch_bounds__(kScatterThreads) void perm_scatter_fp8_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ ids, const int32_t* __restrict__ base,
-    const int32_t* __restrict__ local_rank, int64_t T, int H, int k, int nblk,
+    const int32_t* __restrict__ local_rank, int64_t T, int H, int k, int E, int nblk,
     uint2* __restrict__ x_perm, float* __restrict__ scales, int32_t* __restrict__ row_map,
     int32_t* __restrict__ src_token) {
   const int lane = threadIdx.x % kWave;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + threadIdx.x / kWave;
   if (t >= T) return;
-  int row = resolve_row(ids, base, local_rank, t, k, nblk, lane, row_map, src_token);
+  int row = resolve_row(ids, base, local_rank, t, k, E, nblk, lane, row_map, src_token);
   if (!x_perm) return;
   const int row_vecs = H / 8;
   const int nsb = H / 128;
@@ -271,13 +276,13 @@ hipError_t launch_permute(const void* x, int x_dt, const int32_t* ids, int64_t T
   dim3 grid(static_cast<unsigned>(ceil_div(T, kTokPerBlock)));
   if (perm_dt == 2) {
     hipLaunchKernelGGL(perm_scatter_fp8_kernel, grid, dim3(kScatterThreads), 0, stream,
-                       static_cast<const uint4*>(x), ids, blk, local_rank, T, H, k, nblk,
+                       static_cast<const uint4*>(x), ids, blk, local_rank, T, H, k, E, nblk,
                        static_cast<uint2*>(x_perm), x_perm_scales, row_map, src_token);
   } else {
     const int elt = (x_dt == 0) ? 4 : 2;
     const int row_vecs = H * elt / 16;
     hipLaunchKernelGGL(perm_scatter_copy_kernel, grid, dim3(kScatterThreads), 0, stream,
-                       static_cast<const uint4*>(x), ids, blk, local_rank, T, row_vecs, k, nblk,
+                       static_cast<const uint4*>(x), ids, blk, local_rank, T, row_vecs, k, E, nblk,
                        static_cast<uint4*>(x_perm), row_map, src_token);
   }
   return hipGetLastError();

@@ -183,3 +183,25 @@ def test_hip_graph_capture_and_replay(w_dtype):
         torch.cuda.synchronize()
         assert torch.equal(y_g.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
         del junk
+
+
+def test_out_of_range_ids_are_taken_as_expert_zero():
+    """Caller-supplied ids outside [0, E) (negative, E, huge) stay in bounds: they are routed to
+    expert 0, exactly as the oracle's permutation of the same ids with those entries set to 0."""
+    T, H, E, k = 300, 256, 8, 2
+    rng = np.random.default_rng(7)
+    ids = np.stack([rng.integers(1, E, T), rng.integers(1, E, T)], axis=1).astype(np.int32)
+    ids[ids[:, 0] == ids[:, 1], 1] = (ids[ids[:, 0] == ids[:, 1], 0] % (E - 1)) + 1  # distinct per token
+    bad = rng.random(T) < 0.3
+    ids[bad, 1] = rng.choice(np.array([-1, E, 1 << 20, -(1 << 30)], dtype=np.int32), int(bad.sum()))
+    x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    p = moe_gpu.permute(x, torch.from_numpy(ids).to(DEV), E)
+    torch.cuda.synchronize()
+    fixed = np.where((ids >= 0) & (ids < E), ids, 0)
+    assert (fixed[:, 0] != fixed[:, 1]).all()
+    cnt = moe.expert_counts(fixed, E)
+    off = moe.expert_offsets(cnt)
+    row_map, src = moe.permutation(fixed)
+    assert np.array_equal(host(p["counts"]), cnt) and np.array_equal(host(p["offsets"]), off)
+    assert np.array_equal(host(p["row_map"]), row_map) and np.array_equal(host(p["src_token"]), src)
+    assert np.array_equal(host(p["x_perm"]), host(x)[src])
