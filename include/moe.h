@@ -118,7 +118,9 @@ moe_status moe_permute(const void* x, moe_dtype x_dt, const int32_t* topk_ids, i
  *     h = SiLU(u[:F]) * u[F:]        SiLU(z) = z / (1 + exp(-z))
  *     y_perm[p] = h . W2[e]          W2 [E, F, H]
  * Per-expert row counts are read from expert_offsets in DEVICE memory only; `rows` is the
- * host-known bound T*k used to size the launch (offsets[E] <= rows is required).
+ * host-known bound T*k used to size the launch (offsets non-decreasing from 0 with
+ * offsets[E] <= rows is required; offsets breaking this are clamped into [0, rows], which keeps
+ * every access in bounds but makes the results meaningless).
  *   dt = MOE_F32:  x_perm, w1, w2 fp32; h fp32; y_perm fp32 (out_dt MOE_F32).
  *   dt = MOE_BF16: x_perm, w1, w2 bf16; h rounded to bf16; y_perm bf16 or fp32.
  *   dt = MOE_FP8_E4M3: x_perm e4m3 with x_perm_scales [rows, H/128]; w1/w2 e4m3 with
@@ -144,6 +146,8 @@ moe_status moe_grouped_swiglu(const void* x_perm, const float* x_perm_scales, mo
  * accumulated in fp32 over j ascending and rounded once to out_dt.
  *   y_perm [T*k, H] y_dt (MOE_F32 | MOE_BF16); shared_out [T, H] y_dt or NULL;
  *   y [T, H] out_dt (MOE_F32 | MOE_BF16).
+ *   row_map entries must lie in [0, T*k); an entry outside is read as row 0 (in bounds, but
+ *   the result is then meaningless).
  * ------------------------------------------------------------------------------------- */
 moe_status moe_unpermute_combine(const void* y_perm, moe_dtype y_dt, const int32_t* row_map,
                                  const float* topk_gates, const void* shared_out, int64_t T,

@@ -48,6 +48,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
   float g = 0.0f;
   if (lane < k) {
     row = row_map[t * k + lane];
+    // a caller's row outside [0, T k) is read as row 0: every access stays inside y_perm
+    row = static_cast<uint64_t>(row) < static_cast<uint64_t>(T * k) ? row : 0;
     g = gates[t * k + lane];
   }
   const int n8 = H / 8;

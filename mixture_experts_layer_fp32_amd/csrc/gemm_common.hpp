@@ -23,6 +23,19 @@ struct TileMap {
 // the scanned values: their maximum and how many are non-zero.
 constexpr int kStatMax = kMaxExpertsLds - 2, kStatNonzero = kMaxExpertsLds - 1;
 
+// Rows [base, base + M) of expert e: the caller's offsets clamped into [0, rows] and made
+// non-decreasing, so that offsets breaking the contract (not monotone, or past `rows`, the
+// bound the launch was sized for) can drop or repeat work but never address rows outside
+// [0, rows).
+__device__ __forceinline__ void expert_rows(const int32_t* offsets, int e, int64_t rows, int64_t& base,
+                                            int64_t& M) {
+  int64_t lo = offsets[e], hi = offsets[e + 1];
+  lo = lo < 0 ? 0 : (lo > rows ? rows : lo);
+  hi = hi < lo ? lo : (hi > rows ? rows : hi);
+  base = lo;
+  M = hi - lo;
+}
+
 // In-place inclusive scan of s_pref[1..E] by one wave (E <= 512, chunks of 64), s_pref[0] = 0,
 // and the statistics above; every thread of the workgroup calls it after writing s_pref[1..E].
 __device__ void scan_prefix(int* s_pref, int E) {
@@ -65,8 +78,9 @@ __device__ int count_tiles(const int32_t* offsets, int64_t rows, int E, int NT, 
   const int tid = threadIdx.x;
   // m-tiles per expert, exclusive prefix in s_pref[0..E]
   for (int e = tid; e < E; e += static_cast<int>(blockDim.x)) {
-    int c = offsets[e + 1] - offsets[e];
-    s_pref[e + 1] = (c + BM - 1) / BM;
+    int64_t base, c;
+    expert_rows(offsets, e, rows, base, c);
+    s_pref[e + 1] = static_cast<int>((c + BM - 1) / BM);
   }
   scan_prefix(s_pref, E);
   return s_pref[E] * NT;
@@ -117,9 +131,11 @@ __device__ void locate_tile(const int32_t* offsets, int64_t rows, int E, int NT,
   tm.expert = e;
   tm.nt = idx / me;
   tm.mt = idx % me;
-  const int64_t rpt = balanced_rows<BM>(offsets[e + 1] - offsets[e], me);
-  tm.row0 = static_cast<int64_t>(offsets[e]) + static_cast<int64_t>(tm.mt) * rpt;
-  tm.row_end = tm.row0 + rpt < offsets[e + 1] ? tm.row0 + rpt : offsets[e + 1];
+  int64_t base, M;
+  expert_rows(offsets, e, rows, base, M);
+  const int64_t rpt = balanced_rows<BM>(M, me);
+  tm.row0 = base + static_cast<int64_t>(tm.mt) * rpt;
+  tm.row_end = tm.row0 + rpt < base + M ? tm.row0 + rpt : base + M;
 }
 
 // Returns false if this workgroup has no tile.  `s_pref` is LDS of >= E+1 ints.  Workgroups
@@ -174,7 +190,7 @@ __device__ bool map_tile(const int32_t* offsets, int64_t rows, int E, int NT, in
 // unequal work; here each XCD gets the same share of every expert.  On entry `s_pref` holds the
 // m-tile prefix (count_tiles).  The launch needs grid_for_spread workgroups.
 template <int BM>
-__device__ bool map_tile_spread(const int32_t* offsets, int E, int NT, int* s_pref, TileMap& tm) {
+__device__ bool map_tile_spread(const int32_t* offsets, int64_t rows, int E, int NT, int* s_pref, TileMap& tm) {
   const int x = static_cast<int>(blockIdx.x % 8), i = static_cast<int>(blockIdx.x / 8);
   auto range_start = [&](int me, int xx) { return static_cast<int>(static_cast<int64_t>(xx) * me * NT / 8); };
   // A thread owns experts tid and tid + blockDim (blockDim >= 256, E <= 512).
@@ -192,7 +208,8 @@ __device__ bool map_tile_spread(const int32_t* offsets, int E, int NT, int* s_pr
     if (s_pref[mid] <= i) lo = mid; else hi = mid - 1;
   }
   const int e = lo;
-  const int64_t base = offsets[e], M = offsets[e + 1] - base;
+  int64_t base, M;
+  expert_rows(offsets, e, rows, base, M);
   const int me = static_cast<int>(ceil_div(M, BM));
   const int j = range_start(me, x) + (i - s_pref[e]);  // tile of expert e, n-major
   tm.expert = e;
@@ -216,7 +233,7 @@ __device__ bool map_tile_auto(const int32_t* offsets, int64_t rows, int E, int N
   if (offsets != nullptr) {
     const int64_t mtiles = s_pref[E];
     if (static_cast<int64_t>(s_pref[kStatMax]) * s_pref[kStatNonzero] > 3 * mtiles)
-      return map_tile_spread<BM>(offsets, E, NT, s_pref, tm);
+      return map_tile_spread<BM>(offsets, rows, E, NT, s_pref, tm);
   }
   return map_tile_counted<BM>(offsets, rows, E, NT, s_pref, total, tm, ncu, S);
 }

@@ -205,3 +205,33 @@ def test_out_of_range_ids_are_taken_as_expert_zero():
     assert np.array_equal(host(p["counts"]), cnt) and np.array_equal(host(p["offsets"]), off)
     assert np.array_equal(host(p["row_map"]), row_map) and np.array_equal(host(p["src_token"]), src)
     assert np.array_equal(host(p["x_perm"]), host(x)[src])
+
+
+def test_offsets_past_rows_are_clamped():
+    """expert_offsets ending past `rows` (a broken contract) stay in bounds: each expert's range is
+    clamped into [0, rows], so expert 1 here covers rows 120..299 of the 300."""
+    rows, H, F, E = 300, 256, 256, 2
+    gen = torch.Generator().manual_seed(11)
+    x = (torch.randn(rows, H, generator=gen)).to(torch.bfloat16).to(DEV)
+    w1 = (torch.randn(E, H, 2 * F, generator=gen) * H ** -0.5).to(torch.bfloat16).to(DEV)
+    w2 = (torch.randn(E, F, H, generator=gen) * F ** -0.5).to(torch.bfloat16).to(DEV)
+    off = torch.tensor([0, 120, 1000], dtype=torch.int32, device=DEV)
+    yp = moe_gpu.grouped_swiglu(x, off, w1, w2, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = moe.grouped_experts(host(x), np.array([0, 120, rows]), lambda e: host(w1[e]), lambda e: host(w2[e]))
+    assert rel_frobenius(host(yp), ref) <= TOL["bf16"]
+
+
+def test_row_map_outside_range_reads_row_zero():
+    """row_map entries outside [0, T k) are read as row 0 by the combine (in bounds)."""
+    T, k, H = 50, 4, 128
+    gen = torch.Generator().manual_seed(12)
+    yp = torch.randn(T * k, H, generator=gen).to(DEV)
+    rm = torch.randperm(T * k, generator=gen).reshape(T, k).to(torch.int32)
+    rm[3, 1], rm[7, 0], rm[9, 3] = -1, T * k, 1 << 30
+    g = torch.rand(T, k, generator=gen)
+    y = moe_gpu.unpermute_combine(yp, rm.to(DEV), g.to(DEV))
+    torch.cuda.synchronize()
+    fixed = torch.where((rm >= 0) & (rm < T * k), rm, torch.zeros_like(rm))
+    ref = moe.combine(host(yp), fixed.numpy(), g.numpy().astype(np.float64))
+    assert rel_frobenius(host(y), ref) <= TOL["f32"]
