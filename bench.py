@@ -38,10 +38,16 @@ GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_fp32_amd", "csrc", f)
 
 
 def gemm_source_sha256():
+    """SHA-256 of the GEMM sources with // comments and blank lines removed (a comment edit does
+    not change the kernel the counters were taken on)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
-        h.update(open(f, "rb").read())
+        for line in open(f, encoding="utf-8"):
+            code = re.sub(r"//.*", "", line).strip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 

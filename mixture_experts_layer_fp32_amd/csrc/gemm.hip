@@ -11,7 +11,9 @@
 // (expert_offsets).  The host launches a grid sized by the bound
 //     sum_e ceil(M_e / BM) <= floor((rows + E * (BM - 1)) / BM)
 // and every workgroup rebuilds the per-expert m-tile prefix from the offsets in LDS, maps its
-// (XCD-remapped) linear id to (expert, m-tile, n-tile), and exits if it has none.
+// (XCD-remapped) linear id to (expert, m-tile, n-tile), and exits if it has none.  With skewed
+// expert loads the SwiGLU GEMM instead gives every XCD an equal share of every expert's tiles
+// (gemm_common.hpp: map_tile_auto).
 //
 // bf16 kernel (gfx950): 512 threads = 8 waves, tile BM x 256 x 64, v_mfma_f32_32x32x16_bf16,
 // operands streamed global -> LDS by direct loads into a ring of LDS stages (details at the
