@@ -138,9 +138,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_split_kn_kernel(const flo
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4v;
 
-// A workgroup computes 16*TM tokens x 16*TN experts with v_mfma_f32_16x16x32_bf16; its NW waves
-// split H NW ways (each keeping U k-steps of loads in flight) and their partial sums are added
-// in LDS.  Operand layout: lane l holds row (l % 16), k = 8*(l/16) .. +8 of a 32-wide
+// A workgroup computes 16*TM tokens x 16*TN experts with v_mfma_f32_16x16x32_bf16 over the
+// blockIdx.z-th of gridDim.z slices of H; its NW waves split the slice NW ways (each keeping U
+// k-steps of loads in flight) and their partial sums are added in LDS.  With one slice the
+// workgroup writes the logits; with several, `logits` is a [slices][T][E] scratch array and the
+// workgroup writes its slice's partial logits there (summed by the top-k kernel in slice order).  Operand layout: lane l holds row (l % 16), k = 8*(l/16) .. +8 of a 32-wide
 // k-step (A: token rows of x; B: expert rows of the split weight); accumulator slot r of lane l
 // is token 4*(l/16) + r, expert l % 16.
 template <int TM, int TN, int U, int NW = 4>
@@ -170,9 +172,11 @@ __global__ __launch_bounds__(NW * 64) void route_logits_mfma_kernel(
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
-  // this wave's share of the 32-wide k-steps
-  const int steps = (H + 31) / 32;
-  const int s0 = wave * steps / NW, s1 = (wave + 1) * steps / NW;
+  // this wave's share of this slice's 32-wide k-steps
+  const int steps = (H + 31) / 32, nz = static_cast<int>(gridDim.z), z = static_cast<int>(blockIdx.z);
+  const int z0 = z * steps / nz, z1 = (z + 1) * steps / nz;
+  const int s0 = z0 + wave * (z1 - z0) / NW, s1 = z0 + (wave + 1) * (z1 - z0) / NW;
+  logits += static_cast<int64_t>(z) * T * E;
   for (int sb = s0; sb < s1; sb += U) {
     bf16x8_t a[U][TM], b[U][TN][3];
 #pragma unroll
@@ -238,8 +242,9 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
 // With `parts` (the [T][3 Ep] products of x with the three weight parts) the logit is
 // (lo + mid) + hi, written to `logits`; otherwise the logits are read from `logits`.
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
-    float* __restrict__ logits, const float* __restrict__ parts, int Ep, int ksplit, const float* __restrict__ bias,
-    int64_t T, int E, int k, int score, int norm, int32_t* __restrict__ ids, float* __restrict__ gates) {
+    float* __restrict__ logits, const float* __restrict__ parts, int Ep, int ksplit, int slices,
+    const float* __restrict__ bias, int64_t T, int E, int k, int score, int norm, int32_t* __restrict__ ids,
+    float* __restrict__ gates) {
   const int lane = threadIdx.x % kWave;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * (kRouteThreads / kWave) + threadIdx.x / kWave;
   if (t >= T) return;  // whole wave exits together
@@ -252,7 +257,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   for (int i = 0; i < kMaxPerLane; ++i) {
     int e = lane + i * kWave;
     if (e < E) {
-      if (pt) {
+      if (slices > 1) {
+        // partial logits of the H slices ([slices][T][E] in `parts`), added in slice order
+        const float* ps = parts + t * E + e;
+        float v = ps[0];
+        for (int s = 1; s < slices; ++s) v += ps[s * T * E];
+        lg[i] = v;
+        lt[e] = v;
+      } else if (pt) {
         // each part summed over the K slices in order, then smallest part first
         const int64_t slice = T * 3 * Ep;
         float p0 = pt[e], p1 = pt[Ep + e], p2 = pt[2 * Ep + e];
@@ -369,13 +381,30 @@ int router_ksplit(int64_t T, int H, int E) {
   return ks;
 }
 
+// H slices of the few-expert (Ep <= 16) router kernel: 64 tokens per workgroup would leave CUs
+// idle for short batches and, with one slice, every workgroup streams the whole split weight
+// for only 64 tokens; H is cut until there are >= 256 workgroups, each wave keeping >= 1 k-step.
+int router_hslices(int64_t T, int H, int E) {
+  if (padded_experts(E) > 16) return 1;
+  const int64_t chunks = ceil_div(T, 64);
+  const int steps = (H + 31) / 32;
+  int hs = 1;
+  while (hs < 8 && chunks * hs < 256 && steps / (2 * hs) >= 16) hs *= 2;
+  return hs;
+}
+
+size_t hslice_bytes(int64_t T, int H, int E) {
+  const int hs = router_hslices(T, H, E);
+  return hs > 1 ? ((static_cast<size_t>(hs) * T * E * sizeof(float) + 255) & ~static_cast<size_t>(255)) : 0;
+}
+
 size_t parts_bytes(int64_t T, int H, int E) {
   return (static_cast<size_t>(router_ksplit(T, H, E)) * T * 3 * padded_experts(E) * sizeof(float) + 255) &
          ~static_cast<size_t>(255);
 }
 
-hipError_t launch_logits_bf16(const bf16_t* x, const float* w, float* logits, float* parts, int64_t T, int H,
-                              int E, bf16_t* wsplit, hipStream_t stream) {
+hipError_t launch_logits_bf16(const bf16_t* x, const float* w, float* logits, float* parts, float* hparts,
+                              int64_t T, int H, int E, bf16_t* wsplit, hipStream_t stream) {
   const int Ep = padded_experts(E);
   const int64_t n = static_cast<int64_t>(Ep) * H;
   const unsigned gs = static_cast<unsigned>(ceil_div(n, kRouteThreads) < 2048 ? ceil_div(n, kRouteThreads) : 2048);
@@ -387,10 +416,12 @@ hipError_t launch_logits_bf16(const bf16_t* x, const float* w, float* logits, fl
   }
   hipLaunchKernelGGL(route_split_kernel, dim3(gs), dim3(kRouteThreads), 0, stream, w, H, E, Ep, wsplit);
   if (Ep <= 16) {
-    dim3 grid(static_cast<unsigned>(ceil_div(T, 16)), 1);
-    // few experts: 16 waves split H so that each CU keeps many x loads in flight
-    hipLaunchKernelGGL((route_logits_mfma_kernel<1, 1, 4, 16>), grid, dim3(16 * kWave), 0, stream, x, wsplit,
-                       logits, T, H, E, Ep);
+    // few experts: 64 tokens per workgroup, 16 waves split the workgroup's slice of H so that each
+    // CU keeps many x loads in flight; with several slices the partial logits go to hparts
+    const int hs = router_hslices(T, H, E);
+    dim3 grid(static_cast<unsigned>(ceil_div(T, 64)), 1, static_cast<unsigned>(hs));
+    hipLaunchKernelGGL((route_logits_mfma_kernel<4, 1, 2, 16>), grid, dim3(16 * kWave), 0, stream, x, wsplit,
+                       hs > 1 ? hparts : logits, T, H, E, Ep);
   } else if (Ep % 64 == 0) {
     dim3 grid(static_cast<unsigned>(ceil_div(T, 32)), static_cast<unsigned>(Ep / 64));
     hipLaunchKernelGGL((route_logits_mfma_kernel<2, 4, 2>), grid, dim3(kRouteThreads), 0, stream, x, wsplit,
@@ -409,6 +440,7 @@ size_t route_scratch_bytes(int64_t T, int H, int E, bool logits_given) {
   size_t a = logits_given ? 0 : (static_cast<size_t>(T) * E * sizeof(float) + 255) & ~static_cast<size_t>(255);
   a += (split_bytes(H, E) + 255) & ~static_cast<size_t>(255);
   if (logits_by_gemm(H, E)) a += parts_bytes(T, H, E);
+  a += hslice_bytes(T, H, E);
   return a;
 }
 
@@ -424,14 +456,18 @@ hipError_t launch_route(const void* x, int x_dt, const float* w_router, const fl
   bf16_t* wsplit = reinterpret_cast<bf16_t*>(sp);
   sp += (split_bytes(H, E) + 255) & ~static_cast<size_t>(255);
   float* parts = (x_dt != 0 && logits_by_gemm(H, E)) ? reinterpret_cast<float*>(sp) : nullptr;
+  if (logits_by_gemm(H, E)) sp += parts_bytes(T, H, E);
+  const int hs = x_dt != 0 ? router_hslices(T, H, E) : 1;
+  float* hparts = hs > 1 ? reinterpret_cast<float*>(sp) : nullptr;
   hipError_t err = (x_dt == 0)
                        ? launch_logits(static_cast<const float*>(x), w_router, lg, T, H, E, stream)
-                       : launch_logits_bf16(static_cast<const bf16_t*>(x), w_router, lg, parts, T, H, E, wsplit,
-                                            stream);
+                       : launch_logits_bf16(static_cast<const bf16_t*>(x), w_router, lg, parts, hparts, T, H, E,
+                                            wsplit, stream);
   if (err != hipSuccess) return err;
   dim3 grid(static_cast<unsigned>(ceil_div(T, kRouteThreads / kWave)));
-  hipLaunchKernelGGL(route_topk_kernel, grid, dim3(kRouteThreads), 0, stream, lg, parts, padded_experts(E),
-                     parts ? router_ksplit(T, H, E) : 1, bias, T, E, k, score, norm, ids, gates);
+  hipLaunchKernelGGL(route_topk_kernel, grid, dim3(kRouteThreads), 0, stream, lg, hs > 1 ? hparts : parts,
+                     padded_experts(E), parts ? router_ksplit(T, H, E) : 1, hs, bias, T, E, k, score, norm, ids,
+                     gates);
   return hipGetLastError();
 }
 
