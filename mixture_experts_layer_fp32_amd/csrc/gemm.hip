@@ -57,9 +57,12 @@ constexpr int kThreads = 256;  // fp32 path
 // fragments of k-step s + 1 (read in the order the MFMAs consume them).  Before the last k-step
 // the wave waits for its own reads of tile kt and its own loads of tile kt + 1 and meets the
 // other waves at the single barrier of the iteration; the last k-step then issues, after each of
-// its MFMAs, one of the loads of A tile kt + NA and B tile kt + NB (into the stages tile kt used)
-// and one of tile kt + 1's first fragment reads, so the MFMA pipe restarts right after the
-// barrier.  A loads have NA - 1 iterations to land and B loads NB - 1.
+// its MFMAs, one of tile kt + 1's first fragment reads and then one load of A tile kt + NA (into
+// the stage tile kt used), so the MFMA pipe restarts right after the barrier.  The loads of B
+// tile kt + NB follow the same way in k-step 0 of iteration kt + 1.  Every load goes out after
+// the fragment read it is paired with: a direct load issued ahead of a wave's LDS reads delays
+// them (measured: 3-7% slower GEMMs).  A loads have NA - 1 iterations to land, B loads about
+// NB - 1.25.
 // Loads are unconditional: rows past the expert's end re-read its last row and column groups
 // past the matrix edge re-read column 0; those results are never stored.
 constexpr int kBKT = 64;        // K per iteration / stage
@@ -174,9 +177,10 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
       for (int p = 0; p < B_ROUNDS; ++p) lds_dma16(bs + p * b_round, bbase + (NWAVE * p + wave) * 1024);
     }
   };
-  // Loads issued after both A and B tile t + 1 while groups up to t - 1 are out, when every tile
-  // they name exists (t + NB <= nk): the B part of A tile t + 1's group (when NB > NA, B tile
-  // t + 1 came in an earlier group), then NA - 2 whole groups.  Otherwise wait for all.
+  // Loads issued after both A and B tile t + 1 by the time iteration t waits (load group j: A
+  // tile j + NA at the end of iteration j, B tile j + NB at the start of iteration j + 1), when
+  // every tile they name exists (t + NB <= nk): B tile t + 2 when NB > NA (its A partner came
+  // earlier), then NA - 2 whole groups.  Otherwise wait for all.
   constexpr int B_AFTER_A = NB > NA ? B_ROUNDS : 0;
   auto wait_tile_next = [&](int t) {
     if (t + NB <= nk) wait_vmcnt<B_AFTER_A + (NA - 2) * RPT>();
@@ -275,10 +279,34 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     lds_barrier();
     read_frags(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
-      mfmas(0);
-      read_frags(kt, 1, 1);
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
+      {
+        // k-step 0: MFMA q, fragment read q of k-step 1, then load q of B tile kt - 1 + NB (the B
+        // part of load group kt - 1; its stage was freed at the previous iteration's barrier)
+        const int tb = kt - 1 + NB;
+        const bool do_b = kt >= 1 && tb < nk;
+        const uint32_t bbase = b_stage(tb);
+        const bf16_t* bs = b_src + static_cast<int64_t>(tb) * b_kstep;
+        const uint32_t abase1 = a_stage(kt), bbase1 = b_stage(kt);
+        constexpr int NR = NL > 0 ? NL + FN : 0;  // read units: B0, A0, B1, A1, A2, ...
+        constexpr int NQ = cmax(cmax(NL * FN, NR), B_ROUNDS);  // slots: every MFMA, read and load
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          if (q < NL * FN) {
+            const int i = q / FN, j = q % FN;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bfr[0][j], acc[i][j], 0, 0, 0);
+          }
+          if constexpr (NL > 0) {
+            if (q < NR) {
+              if (q == 0) read_b(bbase1, 1, 1, 0);
+              else if (q == 1) read_a(abase1, 1, 1, 0);
+              else if (q < 2 + FN - 1) read_b(bbase1, 1, 1, q - 1);
+              else read_a(abase1, 1, 1, q - FN);
+            }
+          }
+          if (q < B_ROUNDS && do_b) lds_dma16(bs + q * b_round, bbase + (NWAVE * q + wave) * 1024);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       mfmas(1);
       read_frags(kt, 2, 0);
       interleave();
@@ -293,25 +321,20 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
         lds_barrier();       // ... for every wave: tile kt + 1 readable, tile kt's stages free
       }
       __builtin_amdgcn_sched_barrier(0);
-      // last k-step: MFMA q, then load q of group kt, then fragment read q of tile kt + 1
+      // last k-step: MFMA q, fragment read q of tile kt + 1, then load q of A tile kt + NA (the A
+      // part of load group kt, into the stage tile kt just left)
       {
-        const int ta = kt + NA, tb = kt + NB;
-        const bool do_a = kt + 1 < nk && ta < nk, do_b = kt + 1 < nk && tb < nk;
-        const uint32_t abase = a_stage(ta), bbase = b_stage(tb);
-        const bf16_t* bs = b_src + static_cast<int64_t>(tb) * b_kstep;
+        const int ta = kt + NA;
+        const bool do_a = kt + 1 < nk && ta < nk;
+        const uint32_t abase = a_stage(ta);
         const uint32_t nabase = a_stage(kt + 1), nbbase = b_stage(kt + 1);
-        constexpr int NQ = NL * FN > RPT ? NL * FN : RPT;
-        constexpr int NR = NL > 0 ? NL + FN : 0;  // read units: B0, A0, B1, A1, A2, ...
+        constexpr int NR = NL > 0 ? NL + FN : 0;
+        constexpr int NQ = cmax(cmax(NL * FN, NR), A_ROUNDS);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
           if (q < NL * FN) {
             const int i = q / FN, j = q % FN;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bfr[1][j], acc[i][j], 0, 0, 0);
-          }
-          if (q < A_ROUNDS) {
-            if (do_a) lds_dma16(a_src[q] + static_cast<int64_t>(ta) * kBKT, abase + (NWAVE * q + wave) * 1024);
-          } else if (q < RPT) {
-            if (do_b) lds_dma16(bs + (q - A_ROUNDS) * b_round, bbase + (NWAVE * (q - A_ROUNDS) + wave) * 1024);
           }
           if constexpr (NL > 0) {
             if (q < NR) {
@@ -321,6 +344,8 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
               else read_a(nabase, 0, 0, q - FN);
             }
           }
+          if (q < A_ROUNDS && do_a)
+            lds_dma16(a_src[q] + static_cast<int64_t>(ta) * kBKT, abase + (NWAVE * q + wave) * 1024);
           __builtin_amdgcn_sched_barrier(0);
         }
       }

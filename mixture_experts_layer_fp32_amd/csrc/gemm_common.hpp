@@ -238,6 +238,8 @@ __device__ bool map_tile_auto(const int32_t* offsets, int64_t rows, int E, int N
   return map_tile_counted<BM>(offsets, rows, E, NT, s_pref, total, tm, ncu, S);
 }
 
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 typedef __attribute__((address_space(3))) void lds_void_t;

@@ -190,8 +190,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
   };
   // Load group j: A tile j + NA with its scales and B tile j + NB, each if it exists.  Group j is
   // issued at iteration j (the prologue issues groups -max(NA, NB) .. -1).
-  auto issue_group = [&](int j) {
-    const int ta = j + NA, tb = j + NB;
+  auto issue_a = [&](int j) {
+    const int ta = j + NA;
     if (ta >= 0 && ta < nkb) {
       const uint32_t abase = a_stage(ta);
 #pragma unroll
@@ -200,18 +200,27 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
       if (wave < SW) lds_dma4(as_src + ta, scale_base(ta) + wave * 256);
       if (wave == SW) lds_dma4(ws_src + static_cast<int64_t>(ta) * nbn, scale_base(ta) + BM * 4);
     }
+  };
+  auto b_load = [&](int tb, int p) {
+    lds_dma16(b_src + static_cast<int64_t>(tb) * kF8BK * ldb + p * b_round, b_stage(tb) + (NWAVE * p + wave) * 1024);
+  };
+  auto issue_group = [&](int j) {
+    issue_a(j);
+    const int tb = j + NB;
     if (tb >= 0 && tb < nkb) {
-      const uint32_t bbase = b_stage(tb);
-      const uint8_t* bs = b_src + static_cast<int64_t>(tb) * kF8BK * ldb;
 #pragma unroll
-      for (int p = 0; p < B_ROUNDS; ++p) lds_dma16(bs + p * b_round, bbase + (NWAVE * p + wave) * 1024);
+      for (int p = 0; p < B_ROUNDS; ++p) b_load(tb, p);
     }
   };
-  // vmcnt waits (per wave: RPTW = RPT, +1 on waves <= SW).  Tile t is complete once the later
-  // of its A and B parts has landed: loads issued after that part are the B part of its group
-  // (when NB > NA) and then whole groups -- min(NA, NB) - 1 after the prologue (tile 0), and
-  // min(NA, NB) - 2 at iteration t (tile t + 1) -- when every tile those groups name exists
-  // (max(NA, NB) <= nk, t + max(NA, NB) <= nk).  Otherwise wait for all.
+  // vmcnt waits (per wave: RPTW = RPT, +1 on waves <= SW).  In the loop group j goes out at the
+  // barrier of iteration j; with power-of-two scales (MX) only its A part (with the scales) does,
+  // one load after each MFMA and fragment read of the second sub-step, and its B part follows in
+  // the first sub-step of iteration j + 1 in the same way (a direct load issued ahead of a wave's
+  // LDS reads delays them).  The prologue issues whole groups.  Tile t
+  // is complete once the later of its A and B parts has landed: loads issued after that part are
+  // the B part of its group (when NB > NA) and then whole groups -- min(NA, NB) - 1 after the
+  // prologue (tile 0), and min(NA, NB) - 2 at iteration t (tile t + 1) -- when every tile those
+  // groups name exists (max(NA, NB) <= nk, t + max(NA, NB) <= nk).  Otherwise wait for all.
   constexpr int NM = NA > NB ? NA : NB, GM = NA < NB ? NA : NB;
   constexpr int AFTER = NB > NA ? B_ROUNDS : 0;
   auto wait_tile = [&](bool full, auto groups_c) {
@@ -327,9 +336,37 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
       };
       read_exps(0);
       take_exps();
+      constexpr int NR = NL > 0 ? NL + FN : 0;  // read units: B0, A0, B1, A1, A2, ...
+      // read unit q of sub-step s of tile kt into buffer buf
+      auto read_unit = [&](int kt, int s, int buf, int q) {
+        if constexpr (NL > 0) {
+          if (q < NR) {
+            if (q == 0) read_b(b_stage(kt), s, buf, 0);
+            else if (q == 1) read_a(a_stage(kt), s, buf, 0);
+            else if (q < 2 + FN - 1) read_b(b_stage(kt), s, buf, q - 1);
+            else read_a(a_stage(kt), s, buf, q - FN);
+          }
+        }
+      };
       for (int kt = 0; kt < nk; ++kt) {
-        mfmas(0);
-        read_frags(kt, 1, 1);
+        // First sub-step: MFMA q, fragment read q of the second sub-step, then load q of B tile
+        // kt - 1 + NB (the B part of group kt - 1; its stage was freed at the last barrier).
+        {
+          const int tb = kt - 1 + NB;
+          const bool do_b = kt >= 1 && tb < nk;
+          constexpr int NQ = cmax(cmax(NL * FN, NR), B_ROUNDS);  // slots: every MFMA, read and load
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            if (q < NL * FN) {
+              const int i = q / FN, j = q % FN;
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[0][i], bfr[0][j], acc[i][j], 0, 0, 0,
+                                                                           sae[i], 0, sbe[j]);
+            }
+            read_unit(kt, 1, 1, q);
+            if (q < B_ROUNDS && do_b) b_load(tb, q);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
         if (kt + 1 < nk) {
           wait_lgkm0();  // this wave's reads of tile kt are complete
           wait_tile(kt + NM <= nk, std::integral_constant<int, GM - 2>{});  // tile kt + 1 landed
@@ -337,18 +374,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
           read_exps(kt + 1);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // Second sub-step: after each MFMA, one load of group kt (A rounds, the scale load, B
-        // rounds -- the order issue_group uses) and one fragment read of tile kt + 1, so the
-        // MFMA pipe restarts right after the barrier.
+        // Second sub-step: MFMA q, fragment read q of tile kt + 1, then load q of the A part of
+        // group kt (A rounds, then the scale load), so the MFMA pipe restarts right after the
+        // barrier.
         {
-          const int ta = kt + NA, tb = kt + NB;
-          const bool do_a = kt + 1 < nk && ta < nk, do_b = kt + 1 < nk && tb < nk;
-          const uint32_t abase = a_stage(ta), bbase = b_stage(tb);
-          const uint8_t* bs = b_src + static_cast<int64_t>(tb) * kF8BK * ldb;
-          const uint32_t nabase = a_stage(kt + 1), nbbase = b_stage(kt + 1);
-          constexpr int NLD = A_ROUNDS + 1 + B_ROUNDS;  // load slots (the scale slot is empty on waves > SW)
-          constexpr int NQ = NL * FN > NLD ? NL * FN : NLD;
-          constexpr int NR = NL > 0 ? NL + FN : 0;  // read units: B0, A0, B1, A1, A2, ...
+          const int ta = kt + NA;
+          const bool do_a = kt + 1 < nk && ta < nk;
+          const uint32_t abase = a_stage(ta);
+          constexpr int NLD = A_ROUNDS + 1;  // load slots (the scale slot is empty on waves > SW)
+          constexpr int NQ = cmax(cmax(NL * FN, NR), NLD);
 #pragma unroll
           for (int q = 0; q < NQ; ++q) {
             if (q < NL * FN) {
@@ -356,22 +390,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
               acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[1][i], bfr[1][j], acc[i][j], 0, 0, 0,
                                                                            sae[i], 0, sbe[j]);
             }
+            if (kt + 1 < nk) read_unit(kt + 1, 0, 0, q);
             if (q < A_ROUNDS) {
               if (do_a) lds_dma16(a_src[q] + static_cast<int64_t>(ta) * kF8BK, abase + (NWAVE * q + wave) * 1024);
             } else if (q == A_ROUNDS) {
               if (do_a && wave < SW) lds_dma4(as_src + ta, scale_base(ta) + wave * 256);
               if (do_a && wave == SW) lds_dma4(ws_src + static_cast<int64_t>(ta) * nbn, scale_base(ta) + BM * 4);
-            } else if (q < NLD) {
-              const int p = q - A_ROUNDS - 1;
-              if (do_b) lds_dma16(bs + p * b_round, bbase + (NWAVE * p + wave) * 1024);
-            }
-            if constexpr (NL > 0) {
-              if (q < NR) {
-                if (q == 0) read_b(nbbase, 0, 0, 0);
-                else if (q == 1) read_a(nabase, 0, 0, 0);
-                else if (q < 2 + FN - 1) read_b(nbbase, 0, 0, q - 1);
-                else read_a(nabase, 0, 0, q - FN);
-              }
             }
             __builtin_amdgcn_sched_barrier(0);
           }
