@@ -53,16 +53,16 @@ constexpr int kThreads = 256;  // fp32 path
 // 4 (s % 4) of the fragment and destination lane d collects column d % 32 for 4 consecutive k.
 // The swizzles spread every fragment read of a 16-lane group over distinct banks.
 //
-// Iteration kt (four 16-deep k-steps): MFMAs of k-step s interleave with the LDS reads of the
-// fragments of k-step s + 1 (read in the order the MFMAs consume them).  Before the last k-step
-// the wave waits for its own reads of tile kt and its own loads of tile kt + 1 and meets the
-// other waves at the single barrier of the iteration; the last k-step then issues, after each of
-// its MFMAs, one of tile kt + 1's first fragment reads and then one load of A tile kt + NA (into
-// the stage tile kt used), so the MFMA pipe restarts right after the barrier.  The loads of B
-// tile kt + NB follow the same way in k-step 0 of iteration kt + 1.  Every load goes out after
-// the fragment read it is paired with: a direct load issued ahead of a wave's LDS reads delays
-// them (measured: 3-7% slower GEMMs).  A loads have NA - 1 iterations to land, B loads about
-// NB - 1.25.
+// Iteration kt (four 16-deep k-steps): each MFMA of k-step s is followed by one LDS read of the
+// fragments of k-step s + 1 (in the order the MFMAs consume them) and, in some slots, one direct
+// load.  Before the last k-step the wave waits for its own reads of tile kt and its own loads of
+// tile kt + 1 and meets the other waves at the single barrier of the iteration; the last k-step
+// then reads tile kt + 1's first fragments, so the MFMA pipe restarts right after the barrier,
+// and in its last slots loads A tile kt + NA into the stage tile kt used.  The loads of B tile
+// kt + NB follow in k-steps 1 and 2 of iteration kt + 1.  Loads go out after the reads and away
+// from the barrier: a direct load issued ahead of a wave's LDS reads delays them (measured: the
+// GEMMs ran 6-9% slower with each load issued right after the barrier, before its read).  A
+// loads have most of an iteration to land, B loads more than NB - 2.
 // Loads are unconditional: rows past the expert's end re-read its last row and column groups
 // past the matrix edge re-read column 0; those results are never stored.
 constexpr int kBKT = 64;        // K per iteration / stage
@@ -244,32 +244,38 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
       af[buf][i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
           static_cast<uintptr_t>(abase + a_row_off[i] + ((chunk ^ a_sw[i]) << 4)));
     };
-    // in the order the MFMAs (i-major) consume them: B0, A0, B1, A1, A2, ...
-    auto read_frags = [&](int kt, int ks, int buf) {
+    // read unit q (B0, A0, B1, A1, A2, ...: the order the i-major MFMAs consume them) of k-step ks
+    // of tile kt into buffer buf
+    auto read_unit = [&](int kt, int ks, int buf, int q) {
       if constexpr (NL > 0) {
-        const uint32_t abase = a_stage(kt), bbase = b_stage(kt);
-        read_b(bbase, ks, buf, 0);
-        read_a(abase, ks, buf, 0);
-#pragma unroll
-        for (int j = 1; j < FN; ++j) read_b(bbase, ks, buf, j);
-#pragma unroll
-        for (int i = 1; i < NL; ++i) read_a(abase, ks, buf, i);
+        if (q == 0) read_b(b_stage(kt), ks, buf, 0);
+        else if (q == 1) read_a(a_stage(kt), ks, buf, 0);
+        else if (q < 2 + FN - 1) read_b(b_stage(kt), ks, buf, q - 1);
+        else if (q < NL + FN) read_a(a_stage(kt), ks, buf, q - FN);
       }
     };
-    auto mfmas = [&](int buf) {
+    constexpr int NR = NL > 0 ? NL + FN : 0;  // read units per k-step
+    static_assert(B_ROUNDS % 2 == 0, "B loads split over two k-steps");
+    // k-step ks (0..2) of tile kt: MFMA q, fragment read q of k-step ks + 1, then, in k-steps 1
+    // and 2, half of the loads of B tile kt - 1 + NB (the B part of load group kt - 1, into the
+    // stage freed at the previous iteration's barrier)
+    auto kstep = [&](auto ks_c, int kt) {
+      constexpr int ks = decltype(ks_c)::value;
+      constexpr int BL = ks == 0 ? 0 : B_ROUNDS / 2, B0 = ks == 2 ? B_ROUNDS / 2 : 0;
+      constexpr int NQ = cmax(cmax(NL * FN, NR), BL);
+      const int tb = kt - 1 + NB;
+      const bool do_b = kt >= 1 && tb < nk;
+      const uint32_t bbase = b_stage(tb);
+      const bf16_t* bs = b_src + static_cast<int64_t>(tb) * b_kstep;
 #pragma unroll
-      for (int i = 0; i < NL; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0);
-    };
-    // MFMAs of one k-step interleaved with the LDS reads of the next k-step's fragments
-    auto interleave = [&]() {
-      if constexpr (NL > 0) {
-        constexpr int NREADS = NL + 2 * FN;
-        constexpr int NMFMA = NL * FN;
-        constexpr int RPM = (NREADS + NMFMA - 1) / NMFMA;  // LDS reads per MFMA slot
-        sched_mfma_reads<0, NMFMA, NREADS, RPM>();
+      for (int q = 0; q < NQ; ++q) {
+        if (q < NL * FN) {
+          const int i = q / FN, j = q % FN;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks % 2][i], bfr[ks % 2][j], acc[i][j], 0, 0, 0);
+        }
+        if (q < NR) read_unit(kt, ks + 1, (ks + 1) % 2, q);
+        if (q < BL && do_b) lds_dma16(bs + (B0 + q) * b_round, bbase + (NWAVE * (B0 + q) + wave) * 1024);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
 
@@ -277,75 +283,38 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     // tile 0: groups -NA + 1 .. -1 (and B(NB - NA) when NB > NA) may still be in flight
     if (NB <= nk) wait_vmcnt<B_AFTER_A + (NA - 1) * RPT>(); else wait_vmcnt<0>();
     lds_barrier();
-    read_frags(0, 0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-      {
-        // k-step 0: MFMA q, fragment read q of k-step 1, then load q of B tile kt - 1 + NB (the B
-        // part of load group kt - 1; its stage was freed at the previous iteration's barrier)
-        const int tb = kt - 1 + NB;
-        const bool do_b = kt >= 1 && tb < nk;
-        const uint32_t bbase = b_stage(tb);
-        const bf16_t* bs = b_src + static_cast<int64_t>(tb) * b_kstep;
-        const uint32_t abase1 = a_stage(kt), bbase1 = b_stage(kt);
-        constexpr int NR = NL > 0 ? NL + FN : 0;  // read units: B0, A0, B1, A1, A2, ...
-        constexpr int NQ = cmax(cmax(NL * FN, NR), B_ROUNDS);  // slots: every MFMA, read and load
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          if (q < NL * FN) {
-            const int i = q / FN, j = q % FN;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bfr[0][j], acc[i][j], 0, 0, 0);
-          }
-          if constexpr (NL > 0) {
-            if (q < NR) {
-              if (q == 0) read_b(bbase1, 1, 1, 0);
-              else if (q == 1) read_a(abase1, 1, 1, 0);
-              else if (q < 2 + FN - 1) read_b(bbase1, 1, 1, q - 1);
-              else read_a(abase1, 1, 1, q - FN);
-            }
-          }
-          if (q < B_ROUNDS && do_b) lds_dma16(bs + q * b_round, bbase + (NWAVE * q + wave) * 1024);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      mfmas(1);
-      read_frags(kt, 2, 0);
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(0);
-      read_frags(kt, 3, 1);
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < NR; ++q) read_unit(0, 0, 0, q);
+    for (int kt = 0; kt < nk; ++kt) {
+      kstep(std::integral_constant<int, 0>{}, kt);
+      kstep(std::integral_constant<int, 1>{}, kt);
+      kstep(std::integral_constant<int, 2>{}, kt);
       if (kt + 1 < nk) {
         wait_lgkm0();        // this wave's reads of tile kt are complete
         wait_tile_next(kt);  // this wave's loads of A and B tile kt + 1 have landed
         lds_barrier();       // ... for every wave: tile kt + 1 readable, tile kt's stages free
       }
       __builtin_amdgcn_sched_barrier(0);
-      // last k-step: MFMA q, fragment read q of tile kt + 1, then load q of A tile kt + NA (the A
-      // part of load group kt, into the stage tile kt just left)
+      // last k-step: MFMA q, fragment read q of tile kt + 1 (restarting the MFMA pipe right after
+      // the barrier), and in its last slots the loads of A tile kt + NA (the A part of load group
+      // kt, into the stage tile kt just left)
       {
         const int ta = kt + NA;
         const bool do_a = kt + 1 < nk && ta < nk;
         const uint32_t abase = a_stage(ta);
-        const uint32_t nabase = a_stage(kt + 1), nbbase = b_stage(kt + 1);
-        constexpr int NR = NL > 0 ? NL + FN : 0;
         constexpr int NQ = cmax(cmax(NL * FN, NR), A_ROUNDS);
+        constexpr int AQ = NQ - A_ROUNDS;  // first slot with an A load
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
           if (q < NL * FN) {
             const int i = q / FN, j = q % FN;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bfr[1][j], acc[i][j], 0, 0, 0);
           }
-          if constexpr (NL > 0) {
-            if (q < NR) {
-              if (q == 0) read_b(nbbase, 0, 0, 0);
-              else if (q == 1) read_a(nabase, 0, 0, 0);
-              else if (q < 2 + FN - 1) read_b(nbbase, 0, 0, q - 1);
-              else read_a(nabase, 0, 0, q - FN);
-            }
-          }
-          if (q < A_ROUNDS && do_a)
-            lds_dma16(a_src[q] + static_cast<int64_t>(ta) * kBKT, abase + (NWAVE * q + wave) * 1024);
+          // unconditional: past the last tile this reads a stale stage (in bounds, never used); a
+          // branch here would make the compiler wait for these reads before the next MFMAs
+          if (q < NR) read_unit(kt + 1, 0, 0, q);
+          if (q >= AQ && do_a)
+            lds_dma16(a_src[q - AQ] + static_cast<int64_t>(ta) * kBKT, abase + (NWAVE * (q - AQ) + wave) * 1024);
           __builtin_amdgcn_sched_barrier(0);
         }
       }

@@ -277,18 +277,6 @@ __device__ __forceinline__ void wait_tiles(int tiles) {
 
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14)); }
 
-// Scheduling groups for one k-step: NM MFMAs, each followed by up to RPM of the NR LDS reads.
-template <int Q, int NM, int NR, int RPM>
-__device__ __forceinline__ void sched_mfma_reads() {
-  if constexpr (Q < NM) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    constexpr int left = NR - Q * RPM;
-    constexpr int nr = left < RPM ? left : RPM;
-    if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);  // LDS reads
-    sched_mfma_reads<Q + 1, NM, NR, RPM>();
-  }
-}
-
 // SiLU for the epilogue: z * 1 / (1 + 2^(-z log2 e)) with the hardware exp2 and reciprocal
 // (about 1e-6 relative error, far below the bf16 rounding of h).
 __device__ __forceinline__ float silu_fast(float z) {
