@@ -363,7 +363,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
                                                                            sae[i], 0, sbe[j]);
             }
             read_unit(kt, 1, 1, q);
-            if (q < B_ROUNDS && do_b) b_load(tb, q);
+            if (q >= NQ - B_ROUNDS && do_b) b_load(tb, q - (NQ - B_ROUNDS));
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -390,10 +390,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
               acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[1][i], bfr[1][j], acc[i][j], 0, 0, 0,
                                                                            sae[i], 0, sbe[j]);
             }
-            if (kt + 1 < nk) read_unit(kt + 1, 0, 0, q);
-            if (q < A_ROUNDS) {
-              if (do_a) lds_dma16(a_src[q] + static_cast<int64_t>(ta) * kF8BK, abase + (NWAVE * q + wave) * 1024);
-            } else if (q == A_ROUNDS) {
+            read_unit(kt + 1, 0, 0, q);  // unconditional: a branch would make the compiler wait for it
+            const int p = q - (NQ - NLD);  // the loads take the last NLD slots
+            if (p >= 0 && p < A_ROUNDS) {
+              if (do_a) lds_dma16(a_src[p] + static_cast<int64_t>(ta) * kF8BK, abase + (NWAVE * p + wave) * 1024);
+            } else if (p == A_ROUNDS) {
               if (do_a && wave < SW) lds_dma4(as_src + ta, scale_base(ta) + wave * 256);
               if (do_a && wave == SW) lds_dma4(ws_src + static_cast<int64_t>(ta) * nbn, scale_base(ta) + BM * 4);
             }
