@@ -36,6 +36,10 @@ SMALL = {
     "qwen3_e96": _small("qwen3_235b", T=300, H=256, E=96, k=8, F=128),
     # few router tiles and a long H: the router GEMM splits K into 8 slices
     "qwen3_router_ksplit": _small("qwen3_235b", T=300, H=4096, E=64, k=8, F=128),
+    # <= 16 experts, a long H and few tokens: the router cuts H over 4 (8) workgroup slices whose
+    # partial logits the top-k kernel adds; T = 1000 leaves a partial last 64-token block
+    "mixtral_router_4slices": _small("mixtral_8x7b", T=1000, H=2048, F=256),
+    "mixtral_router_8slices": _small("mixtral_8x7b", T=200, H=4096, F=128),
 }
 
 
