@@ -370,15 +370,29 @@ size_t split_bytes(int H, int E) { return static_cast<size_t>(3) * padded_expert
 // grouped-GEMM kernel (fp32 output, one row band per 128 tokens), summed per expert by top-k.
 bool logits_by_gemm(int H, int E) { return padded_experts(E) >= 64 && H % 64 == 0; }
 
-// K slices of the router GEMM: with few output tiles (T/128 x 3Ep/256 of them) the projection
-// would leave CUs idle, so K is cut until there are >= 512 tiles (two waves of 256 CUs), keeping
-// >= 8 K steps of 64 per slice.
+// K slices of the router GEMM.  With few output tiles (T/128 x 3Ep/256 of them) the projection
+// leaves CUs idle, but every slice writes a [T][3Ep] fp32 partial product that the top-k kernel
+// reads back.  Estimated cost, in 64-deep K steps of one tile: rounds of 256 single-workgroup
+// CUs x K steps per slice, plus the partial products at about 4 MB of HBM traffic per K step
+// (measured on the DeepSeek- and Qwen3-shaped routers: 1 and 2 slices, against 4 from a rule
+// that only filled two rounds of CUs: 169 -> 164 us and 98 -> 85 us).  Powers of two up to 8
+// that keep >= 8 K steps per slice; ties go to fewer slices.  A pure function of (T, H, E): the
+// workspace size and the launch must agree.
 int router_ksplit(int64_t T, int H, int E) {
   const int64_t tiles = ceil_div(T, 128) * ceil_div(3 * padded_experts(E), 256);
   const int nk = H / 64;
-  int ks = 1;
-  while (ks < 8 && tiles * ks < 512 && nk % (2 * ks) == 0 && nk / (2 * ks) >= 8) ks *= 2;
-  return ks;
+  const double slice_steps = static_cast<double>(T) * 3 * padded_experts(E) * 8 / 4.0e6;
+  int best = 1;
+  double best_cost = 0.0;
+  for (int ks = 1; ks <= 8; ks *= 2) {
+    if (nk % ks != 0 || (ks > 1 && nk / ks < 8)) break;
+    const double cost = static_cast<double>(ceil_div(tiles * ks, 256)) * (nk / ks) + ks * slice_steps;
+    if (ks == 1 || cost < best_cost) {
+      best = ks;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 // H slices of the few-expert (Ep <= 16) router kernel: 64 tokens per workgroup would leave CUs
