@@ -75,8 +75,10 @@ typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
  *   topk_gates [T, k] fp32 out: softmax over all E of the logits, or sigmoid of the
  *            logit, taken at the selected experts; divided by their sum if norm_topk != 0.
  *   workspace device scratch of at least moe_route_workspace_size(T, H, E, logits != NULL)
- *            bytes (the router weight split into bf16 parts, and the logits when the caller
- *            does not ask for them).
+ *            bytes: the router weight split into bf16 parts, the logits when the caller does
+ *            not ask for them, and the partial products of the projection when it is cut
+ *            over H or K (few experts and few tokens; many experts and few output tiles).
+ *            The size is a function of (T, H, E, logits_given) only.
  * H must be a multiple of 8.
  * ------------------------------------------------------------------------------------- */
 size_t moe_route_workspace_size(int64_t T, int32_t H, int32_t E, int32_t logits_given);

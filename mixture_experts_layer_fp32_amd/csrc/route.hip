@@ -239,8 +239,12 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
-// With `parts` (the [T][3 Ep] products of x with the three weight parts) the logit is
-// (lo + mid) + hi, written to `logits`; otherwise the logits are read from `logits`.
+// Where the logits come from: with slices > 1, `parts` holds the few-expert kernel's partial
+// logits of `slices` H slices ([slices][T][E]), added in slice order; with slices == 1 and
+// `parts`, it holds the router GEMM's [ksplit][T][3 Ep] products of x with the three weight
+// parts, each part summed over the K slices in order and the logit taken as (lo + mid) + hi;
+// either way the logit is also written to `logits`.  Without `parts` the logits are read from
+// `logits`.
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     float* __restrict__ logits, const float* __restrict__ parts, int Ep, int ksplit, int slices,
     const float* __restrict__ bias, int64_t T, int E, int k, int score, int norm, int32_t* __restrict__ ids,
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   const int64_t t = static_cast<int64_t>(blockIdx.x) * (kRouteThreads / kWave) + threadIdx.x / kWave;
   if (t >= T) return;  // whole wave exits together
   float* lt = logits + t * E;
-  const float* pt = parts ? parts + t * 3 * Ep : nullptr;
+  const float* pt = parts && slices == 1 ? parts + t * 3 * Ep : nullptr;
 
   float lg[kMaxPerLane], key[kMaxPerLane];
   float lmax = -INFINITY;
