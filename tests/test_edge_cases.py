@@ -37,6 +37,15 @@ def test_few_tokens(T):
     assert err <= TOL["bf16"]
 
 
+def test_api_maxima():
+    """MOE_MAX_EXPERTS experts and MOE_MAX_TOPK slots: full top-k lanes (8 keys per lane), the
+    largest expert prefix in LDS, the dense-GEMM router with 3 x 512 columns, the generic combine."""
+    cfg = moe_inputs.CONFIGS["deepseek_v3"].replace(T=300, H=256, E=512, k=16, F=128, Fs=0)
+    err, d, dbg, _ = _run_and_check(cfg)
+    assert err <= TOL["bf16"]
+    assert int(host(dbg["expert_counts"]).sum()) == cfg.T * cfg.k
+
+
 def test_k_equals_E():
     cfg = moe_inputs.CONFIGS["qwen3_235b"].replace(T=130, H=128, E=6, k=6, F=128)
     err, d, dbg, _ = _run_and_check(cfg)

@@ -33,6 +33,8 @@ SMALL_FP8 = {
     "fp8_k128": _cfg(T=130, H=384, E=4, k=2, F=128, Fs=128),
     # k = E: every expert gets every token
     "fp8_all_experts": _cfg(T=70, H=256, E=4, k=4, F=256, Fs=0),
+    # the API maxima: 512 experts (the largest tile-map prefix), top-16
+    "fp8_api_maxima": _cfg(T=200, H=256, E=512, k=16, F=128, Fs=0),
 }
 
 
