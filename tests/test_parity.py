@@ -40,6 +40,13 @@ SMALL = {
     # partial logits the top-k kernel adds; T = 1000 leaves a partial last 64-token block
     "mixtral_router_4slices": _small("mixtral_8x7b", T=1000, H=2048, F=256),
     "mixtral_router_8slices": _small("mixtral_8x7b", T=200, H=4096, F=128),
+    # <= 16 experts and >= 192 blocks of 16 tokens: the fused route kernel, with the three weight
+    # parts packed as 1, 2 and 3 column tiles (E = 5, 8 and 16) and parts of two experts sharing a
+    # tile (E = 6); softmax, sigmoid with selection bias, renormalised gates
+    "fused_route_e8": _small("mixtral_8x7b", T=3100, H=256, F=128),
+    "fused_route_e5_sigmoid": _small("deepseek_v3", T=3072 + 1, H=320, E=5, k=2, F=128, Fs=0),
+    "fused_route_e16": _small("qwen3_235b", T=3200, H=512, E=16, k=4, F=128),
+    "fused_route_e6": _small("mixtral_8x7b", T=3100, H=192, E=6, k=3, F=128),
 }
 
 
