@@ -304,26 +304,38 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   int my_id = 0;
   float gsum = 0.0f;
   for (int j = 0; j < k; ++j) {
-    float bk = -INFINITY, bl = 0.0f;
-    int bi = 0x7FFFFFFF;
+    // the largest key still free, then its lowest expert index: expert e = lane + 64 i, so the
+    // first slot i whose ballot of "free and equal to the maximum" is non-empty, and in it the
+    // lowest lane (larger key wins, equal keys -> lower index; +0 and -0 compare equal)
+    float lk = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i)
+      if (lane + i * kWave < E && !(taken & (1u << i))) lk = fmaxf(lk, key[i]);
+    const float mk = wave_max(lk);
+    int bi = -1;
+    float bl = 0.0f;
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
-      int e = lane + i * kWave;
-      if (e < E && !(taken & (1u << i)) && better(key[i], e, bk, bi)) {
-        bk = key[i];
-        bi = e;
-        bl = lg[i];
+      if (bi < 0) {  // wave-uniform
+        const uint64_t b = __ballot(lane + i * kWave < E && !(taken & (1u << i)) && key[i] == mk);
+        if (b) {
+          const int ln = __builtin_ctzll(b);
+          bi = i * kWave + ln;
+          bl = __shfl(lg[i], ln, kWave);
+        }
       }
     }
+    if (bi < 0) {  // only NaN keys left: the lowest free expert
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      float ok = __shfl_xor(bk, o, kWave);
-      int oi = __shfl_xor(bi, o, kWave);
-      float ol = __shfl_xor(bl, o, kWave);
-      if (better(ok, oi, bk, bi)) {
-        bk = ok;
-        bi = oi;
-        bl = ol;
+      for (int i = 0; i < kMaxPerLane; ++i) {
+        if (bi < 0) {
+          const uint64_t b = __ballot(lane + i * kWave < E && !(taken & (1u << i)));
+          if (b) {
+            const int ln = __builtin_ctzll(b);
+            bi = i * kWave + ln;
+            bl = __shfl(lg[i], ln, kWave);
+          }
+        }
       }
     }
     // every lane now holds the winner (bi, its logit bl)
