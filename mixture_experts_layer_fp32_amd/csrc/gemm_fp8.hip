@@ -326,14 +326,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
 #pragma unroll
         for (int j = 0; j < FN; ++j) sbe[j] = sbe_n[j];
       };
-      auto mfmas = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < NL; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0,
-                                                                         sae[i], 0, sbe[j]);
-      };
       read_exps(0);
       take_exps();
       constexpr int NR = NL > 0 ? NL + FN : 0;  // read units: B0, A0, B1, A1, A2, ...

@@ -15,9 +15,13 @@
 //     split weight stays in L2.
 //  1'. logits, fp32 x: a register-tiled fp32 FMA skinny GEMM (a workgroup owns BT tokens x
 //     BE experts and walks H in KC-wide chunks staged in LDS).
-//  2. route_topk: one wavefront per token.  Lane l holds experts l, l+64, ...; k rounds of a
-//     wave-wide arg-max (larger key wins, equal keys -> lower index) pick the slots in key
-//     order; softmax statistics come from wave reductions over all E logits.
+//  2. route_topk: one wavefront per token.  Lane l holds experts l, l+64, ...; k rounds, each a
+//     wave-wide maximum of the free keys and ballots for its lowest expert index (larger key
+//     wins, equal keys -> lower index), pick the slots in key order; softmax statistics come
+//     from wave reductions over all E logits.
+//  3. For <= 16 experts and long batches, 1 and 2 in one kernel (route_fused_few_kernel): the
+//     three weight parts packed as MFMA columns, the logits and the top k of 16 tokens per
+//     workgroup.
 #include "common.hpp"
 
 namespace moe {
@@ -30,8 +34,6 @@ template <typename XT>
 __device__ __forceinline__ float load_x(const XT* p);
 template <>
 __device__ __forceinline__ float load_x<float>(const float* p) { return *p; }
-template <>
-__device__ __forceinline__ float load_x<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
 
 // TN experts per thread along E (TX = BE / TN threads), TM tokens per thread (TY = 256 / TX).
 template <typename XT, int BE, int TN, int TM>
