@@ -160,8 +160,9 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
 
   auto a_stage = [&](int kt) { return lds_base + static_cast<uint32_t>(kt % NA) * A_BYTES; };
   auto b_stage = [&](int kt) { return lds_base + B_RING + static_cast<uint32_t>(kt % NB) * B_BYTES; };
-  // Load group j (j >= -NB): A tile j + NA and B tile j + NB, each if it exists.  Group j is
-  // issued at iteration j (the prologue issues groups -NB .. -1).
+  // Load group j (j >= -NB): A tile j + NA and B tile j + NB, each if it exists.  The prologue
+  // issues groups -NB .. -1 whole with this; in the loop the A part of group j goes out in
+  // iteration j and its B part in iteration j + 1 (the k-step slots below).
   auto issue_group = [&](int j) {
     const int ta = j + NA, tb = j + NB;
     if (ta >= 0 && ta < nk) {
