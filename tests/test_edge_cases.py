@@ -8,7 +8,7 @@ import moe_inputs
 import mixture_experts_layer_fp32_amd as moe_gpu
 from oracle import moe
 from tests.checks import check_permutation, rel_frobenius
-from tests.gpu_oracle import TOL, host, routing_from_logits, weights_of
+from tests.gpu_oracle import TOL, TOL_GATES, TOL_LOGITS, host, routing_from_logits, weights_of
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -44,6 +44,22 @@ def test_api_maxima():
     err, d, dbg, _ = _run_and_check(cfg)
     assert err <= TOL["bf16"]
     assert int(host(dbg["expert_counts"]).sum()) == cfg.T * cfg.k
+
+
+@pytest.mark.parametrize("T", [300, 3200])  # the H-sliced router kernel, the fused route kernel
+def test_route_h_not_a_multiple_of_32(T):
+    """H = 264 = 8 x 32 + 8: the last 32-wide k-step of the few-expert router kernels holds a single
+    8-element chunk.  Logits to the fp32 tolerance, ids bit-exact and gates given those logits."""
+    cfg = moe_inputs.CONFIGS["mixtral_8x7b"].replace(T=T, H=264, F=128)
+    d = moe_inputs.make_inputs(cfg, seed=3, weight_device=DEV, act_device=DEV)
+    ids, gates, logits = moe_gpu.route(d["x"], d["w_router"], cfg.k, cfg.score, cfg.norm, d["bias"],
+                                       return_logits=True)
+    torch.cuda.synchronize()
+    ref = moe.router_logits(host(d["x"]), host(d["w_router"]))
+    assert rel_frobenius(host(logits), ref) <= TOL_LOGITS
+    r = routing_from_logits(logits, d["bias"], cfg.k, cfg.score, cfg.norm, cfg.E)
+    assert np.array_equal(host(ids), r["ids"])
+    assert rel_frobenius(host(gates), r["gates"]) <= TOL_GATES
 
 
 def test_k_equals_E():
