@@ -46,11 +46,13 @@ def test_api_maxima():
     assert int(host(dbg["expert_counts"]).sum()) == cfg.T * cfg.k
 
 
-@pytest.mark.parametrize("T", [300, 3200])  # the H-sliced router kernel, the fused route kernel
-def test_route_h_not_a_multiple_of_32(T):
-    """H = 264 = 8 x 32 + 8: the last 32-wide k-step of the few-expert router kernels holds a single
-    8-element chunk.  Logits to the fp32 tolerance, ids bit-exact and gates given those logits."""
-    cfg = moe_inputs.CONFIGS["mixtral_8x7b"].replace(T=T, H=264, F=128)
+# the H-sliced few-expert kernel, the fused route kernel, the MFMA logits kernel with 16-expert
+# column tiles (E = 40) and with 64-expert tiles (E = 64 with H % 64 != 0: not the router GEMM)
+@pytest.mark.parametrize("T,E", [(300, 8), (3200, 8), (300, 40), (300, 64)])
+def test_route_h_not_a_multiple_of_32(T, E):
+    """H = 264 = 8 x 32 + 8: the last 32-wide k-step of the router kernels holds a single 8-element
+    chunk.  Logits to the fp32 tolerance, ids bit-exact and gates given those logits."""
+    cfg = moe_inputs.CONFIGS["mixtral_8x7b"].replace(T=T, H=264, E=E, F=128)
     d = moe_inputs.make_inputs(cfg, seed=3, weight_device=DEV, act_device=DEV)
     ids, gates, logits = moe_gpu.route(d["x"], d["w_router"], cfg.k, cfg.score, cfg.norm, d["bias"],
                                        return_logits=True)
