@@ -64,6 +64,24 @@ def test_route_h_not_a_multiple_of_32(T, E):
     assert rel_frobenius(host(gates), r["gates"]) <= TOL_GATES
 
 
+@pytest.mark.parametrize("E", [70, 130])
+def test_route_fp32_many_experts(E):
+    """fp32 activations with >= 64 experts: the fp32 FMA logits kernel's 64-expert tiles, the last
+    one partial (70, 130 = 2 x 64 + 2).  The logits are exact fp32 dot products up to summation
+    order: logits to the fp32 tolerance, ids bit-exact and gates given those logits."""
+    cfg = moe_inputs.CONFIGS["tiny_fp32"].replace(T=300, H=160, E=E, k=6, F=128)
+    d = moe_inputs.make_inputs(cfg, seed=4, weight_device=DEV, act_device=DEV)
+    assert d["x"].dtype == torch.float32
+    ids, gates, logits = moe_gpu.route(d["x"], d["w_router"], cfg.k, cfg.score, cfg.norm, d["bias"],
+                                       return_logits=True)
+    torch.cuda.synchronize()
+    ref = moe.router_logits(host(d["x"]), host(d["w_router"]))
+    assert rel_frobenius(host(logits), ref) <= TOL_LOGITS
+    r = routing_from_logits(logits, d["bias"], cfg.k, cfg.score, cfg.norm, cfg.E)
+    assert np.array_equal(host(ids), r["ids"])
+    assert rel_frobenius(host(gates), r["gates"]) <= TOL_GATES
+
+
 def test_k_equals_E():
     cfg = moe_inputs.CONFIGS["qwen3_235b"].replace(T=130, H=128, E=6, k=6, F=128)
     err, d, dbg, _ = _run_and_check(cfg)
