@@ -204,6 +204,67 @@ size_t moe_workspace_size(const moe_layer* L, int64_t T);
 moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, const moe_debug* dbg,
                        void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Backward of the whole layer.  The pages measure this layer in training ("Scalable Training
+ * of Mixture-of-Experts Models with Megatron Core": abstract; summary page, "Method", second
+ * paragraph: fine-grained activation recomputation).  Given dy = dL/dy for one moe_forward
+ * call, it writes the gradients of L with respect to x and every weight, by the chain rule
+ * through the forward's stages:
+ *   combine  dL/dg_tj = <dy_t, y_perm[row_map(t, j)]>; each expert row receives g_tj dy_t
+ *   experts  u = x_perm W1[e] (recomputed: the forward keeps no activations), a | b = u,
+ *            h = SiLU(a) b; dh = dyp W2[e]^T, dW2[e] = h^T dyp,
+ *            du = [dh b SiLU'(a) | dh SiLU(a)], dx_perm = du W1[e]^T, dW1[e] = x_perm^T du
+ *   dispatch dx_t = sum_j dx_perm[row_map(t, j)]
+ *   route    dL/dlogits through softmax (over all E) or sigmoid, and the renormalisation
+ *            when norm_topk; top-k selection and the selection bias pass no gradient;
+ *            dx += dlogits W_r^T, dW_r = x^T dlogits
+ *   shared   the expert rule on all T rows with gate 1
+ *   L        the layer as given to moe_forward; w_dt = x_dt = MOE_F32 or MOE_BF16
+ *            (MOE_FP8_E4M3 returns MOE_ERR_UNSUPPORTED).  out_dt is not used.
+ *   x        [T, H] x_dt, the forward's input
+ *   dy       [T, H] x_dt
+ *   r        the forward's routing, as written through moe_debug: logits [T, E] fp32,
+ *            topk_ids [T, k], topk_gates [T, k] fp32, expert_offsets [E+1], row_map [T, k],
+ *            src_token [T*k].  Index entries are clamped into range on the device (in bounds,
+ *            but meaningless results if they do not come from moe_forward).
+ *   g        outputs, all written in full: dx [T, H] x_dt; dw_router [H, E], dw1 [E, H, 2F],
+ *            dw2 [E, F, H], dws1 [H, 2Fs], dws2 [Fs, H] fp32 (the shared pair only when
+ *            Fs > 0, else ignored).  An expert that received no rows gets zero gradients.
+ *   stage_events NULL or MOE_NUM_BWD_STAGE_EVENTS hipEvent_t handles (NULL entries skipped),
+ *            recorded on `stream`: 0 at the start; after the routed experts' recomputed u (1),
+ *            dh (2), SwiGLU backward (3), dW2 (4), dx_perm (5) and dW1 (6); after the shared
+ *            expert (7); at the end (8).
+ *   workspace at least moe_backward_workspace_size(L, T) bytes: u [T*k, 2F] and
+ *            dy W2^T [T*k, F] fp32, du [T*k, 2F] and g h [T*k, F] in x_dt, dg [T*k],
+ *            dx_perm [T*k, H], dlogits [T, E], dlogits W_r^T [T, H] fp32, and the shared
+ *            expert's counterparts.
+ * Accumulation is fp32 throughout (fp32 MFMA for fp32 operands, bf16 MFMA with fp32 accumulate
+ * for bf16 ones); du and g h are rounded to x_dt before their GEMMs.  Sizes as for moe_forward.
+ * ------------------------------------------------------------------------------------- */
+#define MOE_NUM_BWD_STAGE_EVENTS 9
+typedef struct {
+  const float* logits;
+  const int32_t* topk_ids;
+  const float* topk_gates;
+  const int32_t* expert_offsets;
+  const int32_t* row_map;
+  const int32_t* src_token;
+} moe_routing;
+
+typedef struct {
+  void* dx;
+  float* dw_router;
+  float* dw1;
+  float* dw2;
+  float* dws1;
+  float* dws2;
+} moe_grads;
+
+size_t moe_backward_workspace_size(const moe_layer* L, int64_t T);
+moe_status moe_backward(const moe_layer* L, const void* x, const void* dy, int64_t T, const moe_routing* r,
+                        const moe_grads* g, void* const* stage_events, void* workspace, size_t workspace_bytes,
+                        moe_stream_t stream);
+
 const char* moe_status_str(moe_status s);
 int32_t moe_abi_version(void);
 

@@ -214,3 +214,51 @@ def forward(x, layer: Layer, debug: bool = False, workspace=None):
                                             ctypes.byref(dbg_c) if dbg_c is not None else None,
                                             _ptr(workspace), workspace.numel(), _stream()))
     return (y, dbg) if debug else y
+
+
+ROUTING_KEYS = ("logits", "topk_ids", "topk_gates", "expert_offsets", "row_map", "src_token")
+
+
+def backward_workspace_size(layer: Layer, T: int, x_dtype) -> int:
+    c = layer.c_struct(x_dtype)
+    return int(_lib.lib().moe_backward_workspace_size(ctypes.byref(c), T))
+
+
+def backward(x, dy, layer: Layer, routing: dict, workspace=None, stage_events=None):
+    """Gradients of the layer for upstream gradient dy, in one library call.
+
+    ``routing`` holds the forward's routing state as ``forward(..., debug=True)`` returns it
+    (logits, topk_ids, topk_gates, expert_offsets, row_map, src_token).  Returns a dict with
+    dx [T, H] (x's dtype) and fp32 dw_router [H, E], dw1 [E, H, 2F], dw2 [E, F, H] and, with a
+    shared expert, dws1 [H, 2Fs] and dws2 [Fs, H].  ``stage_events``: None or a list of
+    MOE_NUM_BWD_STAGE_EVENTS raw hipEvent_t handles (ctypes.c_void_p, int or None) recorded at
+    the stage boundaries.
+    """
+    rt = [routing[kk] for kk in ROUTING_KEYS]
+    _need_gpu(x, dy, layer.w_router, layer.w1, layer.w2, layer.ws1, layer.ws2, *rt)
+    T, H = x.shape
+    E = layer.w_router.shape[1]
+    F = layer.w2.shape[1]
+    dev = x.device
+    c = layer.c_struct(x.dtype)
+    f32 = torch.float32
+    g = {"dx": torch.empty(T, H, dtype=x.dtype, device=dev),
+         "dw_router": torch.empty(H, E, dtype=f32, device=dev),
+         "dw1": torch.empty(layer.w1.shape[0], H, 2 * F, dtype=f32, device=dev),
+         "dw2": torch.empty(layer.w2.shape[0], F, H, dtype=f32, device=dev),
+         "dws1": None if layer.ws1 is None else torch.empty(tuple(layer.ws1.shape), dtype=f32, device=dev),
+         "dws2": None if layer.ws2 is None else torch.empty(tuple(layer.ws2.shape), dtype=f32, device=dev)}
+    L = _lib.lib()
+    need = int(L.moe_backward_workspace_size(ctypes.byref(c), T))
+    if workspace is None or workspace.numel() < need:
+        workspace = _ws(need, dev)
+    r_c = _lib.MoeRoutingC(**{kk: t.data_ptr() for kk, t in zip(ROUTING_KEYS, rt)})
+    g_c = _lib.MoeGradsC(**{kk: (None if t is None else t.data_ptr()) for kk, t in g.items()})
+    ev_c = None
+    if stage_events is not None:
+        ev_c = (ctypes.c_void_p * _lib.MOE_NUM_BWD_STAGE_EVENTS)(
+            *[ev.value if isinstance(ev, ctypes.c_void_p) else ev for ev in stage_events])
+    _lib.check("moe_backward", L.moe_backward(ctypes.byref(c), _ptr(x), _ptr(dy), T, ctypes.byref(r_c),
+                                              ctypes.byref(g_c), ev_c, _ptr(workspace), workspace.numel(),
+                                              _stream()))
+    return g

@@ -29,6 +29,8 @@ SIGNATURES = {
     "moe_unpermute_combine": ([_vp, _i32, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _vp], _i32),
     "moe_workspace_size": ([_vp, _i64], _sz),
     "moe_forward": ([_vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp], _i32),
+    "moe_backward_workspace_size": ([_vp, _i64], _sz),
+    "moe_backward": ([_vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
 }
 
 
@@ -45,6 +47,20 @@ class MoeDebugC(_c.Structure):
     _fields_ = [("logits", _vp), ("topk_ids", _vp), ("topk_gates", _vp), ("expert_counts", _vp),
                 ("expert_offsets", _vp), ("row_map", _vp), ("src_token", _vp), ("x_perm", _vp),
                 ("x_perm_scales", _vp), ("y_perm", _vp), ("stage_events", _vp * 7)]
+
+
+MOE_NUM_BWD_STAGE_EVENTS = 9
+
+
+class MoeRoutingC(_c.Structure):
+    """struct moe_routing."""
+    _fields_ = [("logits", _vp), ("topk_ids", _vp), ("topk_gates", _vp), ("expert_offsets", _vp),
+                ("row_map", _vp), ("src_token", _vp)]
+
+
+class MoeGradsC(_c.Structure):
+    """struct moe_grads."""
+    _fields_ = [("dx", _vp), ("dw_router", _vp), ("dw1", _vp), ("dw2", _vp), ("dws1", _vp), ("dws2", _vp)]
 
 
 class MoeError(RuntimeError):

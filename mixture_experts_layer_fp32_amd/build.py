@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["api.hip", "route.hip", "permute.hip", "gemm.hip", "gemm_fp8.hip", "combine.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "gemm.hip", "gemm_fp8.hip", "combine.hip", "backward.hip"]
 ARCH = "gfx950"
 
 

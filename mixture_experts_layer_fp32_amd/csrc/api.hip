@@ -290,4 +290,52 @@ moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, co
   return from_hip(e);
 }
 
+// ------------------------------------------------------------------------------ backward
+namespace {
+
+moe::BackwardShape backward_shape(const moe_layer* L, int64_t T) {
+  return moe::BackwardShape{T, L->H, L->E, L->k, L->F, L->Fs, L->score == MOE_SIGMOID ? 1 : 0, L->norm_topk ? 1 : 0};
+}
+
+size_t backward_bytes(const moe_layer* L, int64_t T) {
+  size_t n = 0;
+  moe::carve_backward(backward_shape(L, T), L->x_dt == MOE_F32 ? 0 : 1, nullptr, &n);
+  return n;
+}
+
+}  // namespace
+
+size_t moe_backward_workspace_size(const moe_layer* L, int64_t T) {
+  if (validate_layer(L) != MOE_OK || L->w_dt == MOE_FP8_E4M3 || T < 0) return 0;
+  return backward_bytes(L, T);
+}
+
+moe_status moe_backward(const moe_layer* L, const void* x, const void* dy, int64_t T, const moe_routing* r,
+                        const moe_grads* g, void* const* stage_events, void* workspace, size_t workspace_bytes,
+                        moe_stream_t stream) {
+  moe_status st = validate_layer(L);
+  if (st != MOE_OK) return st;
+  if (L->w_dt == MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  st = check_common(T, L->H, L->E, L->k);
+  if (st != MOE_OK) return st;
+  if (!r || !g) return MOE_ERR_INVALID_ARG;
+  auto ok = [](const void* p) { return p != nullptr && aligned16(p); };
+  // weight gradients always exist (zero for T = 0); token-sized tensors only when T > 0
+  if (!ok(g->dw_router) || !ok(g->dw1) || !ok(g->dw2)) return MOE_ERR_INVALID_ARG;
+  if (L->Fs > 0 && (!ok(g->dws1) || !ok(g->dws2))) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!ok(x) || !ok(dy) || !ok(g->dx) || !ok(r->logits) || !ok(r->topk_ids) || !ok(r->topk_gates) ||
+                !ok(r->expert_offsets) || !ok(r->row_map) || !ok(r->src_token)))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need = backward_bytes(L, T);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+  const int dt = L->x_dt == MOE_F32 ? 0 : 1;
+  const moe::BackwardShape sh = backward_shape(L, T);
+  const moe::BackwardScratch ws = moe::carve_backward(sh, dt, workspace, nullptr);
+  moe::BackwardIO io{x,          dy,          L->w_router,   L->w1,          L->w2,      L->ws1,       L->ws2,
+                     r->logits,  r->topk_ids, r->topk_gates, r->expert_offsets, r->row_map, r->src_token, g->dx,
+                     g->dw_router, g->dw1,    g->dw2,        g->dws1,        g->dws2};
+  return from_hip(moe::launch_layer_backward(sh, dt, io, ws, static_cast<hipStream_t>(stream),
+                                             reinterpret_cast<hipEvent_t const*>(stage_events)));
+}
+
 }  // extern "C"

@@ -1,0 +1,658 @@
+// backward.hip -- gradients of the MoE layer: the forward's stages differentiated in reverse.
+//
+// The pages measure this layer in training ("Scalable Training of Mixture-of-Experts Models
+// with Megatron Core": abstract; summary page, "Method", second paragraph, which counts
+// fine-grained activation recomputation among the memory recipes).  Given dy = dL/dy:
+//   combine:  dyp[p] = g_p dy[t_p],  dg_p = <dy[t_p], yp[p]>        (p = row_map(t, j), t_p = t)
+//   experts:  u = xp W1 (recomputed here, not kept from the forward), a | b = u, h = SiLU(a) b,
+//             dh = dyp W2^T, dW2 = h^T dyp, du = [dh b SiLU'(a) | dh SiLU(a)],
+//             dxp = du W1^T, dW1 = xp^T du
+//   dispatch: dx[t] = sum_j dxp[row_map(t, j)]
+//   route:    dlogits from dg through the gate function; dx += dlogits W_r^T, dW_r = x^T dlogits
+// Two rewrites keep y_perm and the gate-weighted rows g_p dy[t_p] out of memory: dh' = dy[t_p] W2^T
+// is formed once without the gate, so dg_p = <dh'_p, h_p> (= <dy[t_p], h_p W2>) and dh = g_p dh'_p;
+// and dW2 = (g h)^T dy[t_p] takes the gate on the h side.  Every GEMM reads the token rows of x and
+// dy through src_token (the dispatch permutation fused into the loads), so neither x_perm nor a
+// permuted dy is materialised.
+//
+// Kernels:
+//  * bwd_gemm_kernel<layout, TA, TB>: one grouped GEMM for the three operand layouts the chain
+//    needs, 128 x 128 output tiles, 4 waves of 64 x 64, v_mfma_f32_32x32x16_bf16 (both operands
+//    bf16) or v_mfma_f32_32x32x2f32 (an fp32 operand), fp32 accumulate and output.  Operands are
+//    staged through registers into k-contiguous LDS tiles, two buffers, one barrier per K step:
+//      NN  C[p, n]   = sum_k A[g(p), k] B_e[k, n]      p over expert e's rows   (u)
+//      NT  C[p, n]   = sum_k A[g(p), k] B_e[n, k]      p over expert e's rows   (dh', dxp)
+//      TN  C_e[m, n] = sum_p A[g(p), m] B[g'(p), n]    contraction over e's rows (dW1, dW2)
+//    An expert without rows gets a zero weight gradient (its TN tiles have no K steps).
+//  * bwd_swiglu_kernel: per permuted row, the SwiGLU backward and the gate gradient dg_p.
+//  * bwd_gate_kernel: per token, the softmax / sigmoid (+ renormalisation) Jacobian.
+//  * bwd_dx_kernel: per token, dx = sum_j dxp[row_map(t, j)] + shared expert + router terms.
+#include "gemm_common.hpp"
+
+namespace moe {
+namespace {
+
+using namespace gemm;
+
+enum Layout { kNN = 0, kNT = 1, kTN = 2 };
+
+constexpr int kBT = 256;    // threads of a backward GEMM workgroup: 4 waves in 2 (M) x 2 (N)
+constexpr int kTile = 128;  // output tile edge
+
+template <typename T>
+struct Elt;
+template <>
+struct Elt<float> {
+  static constexpr int kVec = 4;  // elements per 16-byte chunk
+};
+template <>
+struct Elt<bf16_t> {
+  static constexpr int kVec = 8;
+};
+
+template <typename TA, typename TB>
+struct BwdCfg {
+  static constexpr bool kBf16 = std::is_same<TA, bf16_t>::value && std::is_same<TB, bf16_t>::value;
+  using CT = typename std::conditional<kBf16, bf16_t, float>::type;  // LDS / MFMA operand type
+  static constexpr int BK = kBf16 ? 32 : 16;                         // K per LDS tile
+  static constexpr int LD = BK + (kBf16 ? 8 : 4);                    // LDS row pitch: 80 bytes
+};
+
+template <typename TA, typename TB>
+struct GemmArgs {
+  const TA* A;
+  int64_t lda;
+  const int32_t* gA;  // row gather of A (NN / NT: output rows; TN: contraction rows) or null
+  int64_t gA_rows;    // rows of A a gathered index may name (indices are clamped into it)
+  const TB* B;
+  int64_t ldb;
+  int64_t sB;         // NN / NT: element stride between experts' B matrices
+  const int32_t* gB;  // TN: row gather of B or null
+  int64_t gB_rows;
+  const int32_t* offsets;  // [G + 1] in device memory, or null: one group of `rows` rows
+  int64_t rows;            // host bound of the grouped rows (T * k, or T)
+  int G;
+  int M, N, K;             // TN: M x N per group; NN / NT: N output columns, K contraction
+  float* C;
+  int64_t ldc;
+  int64_t sC;              // TN: element stride between groups' outputs
+  int vecA, vecB;          // 16-byte loads allowed: base 16-byte aligned, strides multiples of a chunk
+};
+
+__device__ __forceinline__ int64_t clamp_row(int64_t r, int64_t n) { return r < 0 ? 0 : (r >= n ? n - 1 : r); }
+
+// One 16-byte chunk (4 fp32 or 8 bf16) starting at p, of which the first n_ok elements exist;
+// the rest read as zero.  p is dereferenced only for existing elements.
+template <typename T>
+__device__ __forceinline__ u32x4_t load_chunk(const T* p, int n_ok, int vec) {
+  constexpr int V = Elt<T>::kVec;
+  if (vec && n_ok == V) return *reinterpret_cast<const u32x4_t*>(p);
+  u32x4_t r = {0u, 0u, 0u, 0u};
+  if constexpr (V == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < n_ok) r[i] = __float_as_uint(p[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < n_ok) r[i / 2] |= static_cast<uint32_t>(p[i]) << (16 * (i % 2));
+  }
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ float chunk_f32(const u32x4_t& c, int i) {
+  if constexpr (Elt<T>::kVec == 4) return __uint_as_float(c[i]);
+  else return bf16_to_f32(static_cast<bf16_t>((c[i / 2] >> (16 * (i % 2))) & 0xFFFFu));
+}
+
+// Chunk of source type TS to LDS row `row`, columns kc.. (k-contiguous in both).
+template <typename TS, typename CT, int LD>
+__device__ __forceinline__ void store_k(CT* s, const u32x4_t& c, int row, int kc) {
+  if constexpr (std::is_same<TS, CT>::value) {
+    *reinterpret_cast<u32x4_t*>(s + row * LD + kc) = c;
+  } else {  // bf16 source, fp32 tile: 8 floats
+    u32x4_t lo, hi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = __float_as_uint(chunk_f32<TS>(c, i));
+      hi[i] = __float_as_uint(chunk_f32<TS>(c, 4 + i));
+    }
+    *reinterpret_cast<u32x4_t*>(s + row * LD + kc) = lo;
+    *reinterpret_cast<u32x4_t*>(s + row * LD + kc + 4) = hi;
+  }
+}
+
+// Chunk of source type TS holding consecutive rows mc.. of LDS column k (a transposed store).
+template <typename TS, typename CT, int LD>
+__device__ __forceinline__ void store_t(CT* s, const u32x4_t& c, int mc, int k) {
+  constexpr int V = Elt<TS>::kVec;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    if constexpr (std::is_same<CT, bf16_t>::value)
+      s[(mc + i) * LD + k] = static_cast<bf16_t>((c[i / 2] >> (16 * (i % 2))) & 0xFFFFu);
+    else
+      s[(mc + i) * LD + k] = chunk_f32<TS>(c, i);
+  }
+}
+
+template <int LAY, typename TA, typename TB>
+__global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g) {
+  using Cfg = BwdCfg<TA, TB>;
+  using CT = typename Cfg::CT;
+  constexpr int BK = Cfg::BK, LD = Cfg::LD;
+  constexpr int VA = Elt<TA>::kVec, VB = Elt<TB>::kVec;
+  constexpr int RA = kTile * BK / VA / kBT, RB = kTile * BK / VB / kBT;  // chunks per thread
+  static_assert(RA >= 1 && RB >= 1 && RA * VA * kBT == kTile * BK && RB * VB * kBT == kTile * BK, "tile split");
+  __shared__ __align__(16) CT sA[2][kTile * LD];
+  __shared__ __align__(16) CT sB[2][kTile * LD];
+  __shared__ int s_pref[kMaxExpertsLds];
+
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wm = wave / 2, wn = wave % 2;
+  int e = 0, m0 = 0, n0 = 0;
+  int64_t row0 = 0, row_end = 0, kbeg = 0, kend = 0;
+  if constexpr (LAY == kTN) {
+    const int tiles_n = static_cast<int>(ceil_div(g.N, kTile));
+    e = static_cast<int>(blockIdx.y);
+    m0 = static_cast<int>(blockIdx.x) / tiles_n * kTile;
+    n0 = static_cast<int>(blockIdx.x) % tiles_n * kTile;
+    if (g.offsets != nullptr) {
+      int64_t base, cnt;
+      expert_rows(g.offsets, e, g.rows, base, cnt);
+      kbeg = base;
+      kend = base + cnt;
+    } else {
+      kend = g.rows;
+    }
+  } else {
+    TileMap tm;
+    if (!map_tile<kTile>(g.offsets, g.rows, g.G, static_cast<int>(ceil_div(g.N, kTile)), s_pref, tm)) return;
+    e = tm.expert;
+    row0 = tm.row0;
+    row_end = tm.row_end;
+    n0 = tm.nt * kTile;
+    kend = g.K;
+  }
+  const TB* Bg = g.B + (LAY == kTN ? 0 : static_cast<int64_t>(e) * g.sB);
+
+  u32x4_t ra[RA], rb[RB];
+  auto load_a = [&](int64_t kb) {
+#pragma unroll
+    for (int i = 0; i < RA; ++i) {
+      const int c = tid + i * kBT;
+      const TA* p = g.A;
+      int n_ok = 0;
+      if constexpr (LAY == kTN) {  // A [rows, M]: m contiguous, the contraction runs over rows
+        const int kr = c / (kTile / VA), m = m0 + c % (kTile / VA) * VA;
+        const int64_t r = kb + kr;
+        if (r < kend && m < g.M) {
+          const int64_t src = g.gA ? clamp_row(g.gA[r], g.gA_rows) : r;
+          p = g.A + src * g.lda + m;
+          n_ok = g.M - m < VA ? g.M - m : VA;
+        }
+      } else {  // A [rows, K]: k contiguous
+        const int r = c / (BK / VA);
+        const int64_t grow = row0 + r, kk = kb + c % (BK / VA) * VA;
+        if (grow < row_end && kk < kend) {
+          const int64_t src = g.gA ? clamp_row(g.gA[grow], g.gA_rows) : grow;
+          p = g.A + src * g.lda + kk;
+          n_ok = kend - kk < VA ? static_cast<int>(kend - kk) : VA;
+        }
+      }
+      ra[i] = load_chunk(p, n_ok, g.vecA);
+    }
+  };
+  auto load_b = [&](int64_t kb) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int c = tid + i * kBT;
+      const TB* p = g.B;
+      int n_ok = 0;
+      if constexpr (LAY == kNT) {  // B_e [N, K]: k contiguous
+        const int n = n0 + c / (BK / VB);
+        const int64_t kk = kb + c % (BK / VB) * VB;
+        if (n < g.N && kk < kend) {
+          p = Bg + static_cast<int64_t>(n) * g.ldb + kk;
+          n_ok = kend - kk < VB ? static_cast<int>(kend - kk) : VB;
+        }
+      } else {  // NN: B_e [K, N]; TN: B [rows, N] (gathered rows): n contiguous
+        const int64_t r = kb + c / (kTile / VB);
+        const int n = n0 + c % (kTile / VB) * VB;
+        if (r < kend && n < g.N) {
+          const int64_t src = (LAY == kTN && g.gB) ? clamp_row(g.gB[r], g.gB_rows) : r;
+          p = Bg + src * g.ldb + n;
+          n_ok = g.N - n < VB ? g.N - n : VB;
+        }
+      }
+      rb[i] = load_chunk(p, n_ok, g.vecB);
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < RA; ++i) {
+      const int c = tid + i * kBT;
+      if constexpr (LAY == kTN)
+        store_t<TA, CT, LD>(sA[buf], ra[i], c % (kTile / VA) * VA, c / (kTile / VA));
+      else
+        store_k<TA, CT, LD>(sA[buf], ra[i], c / (BK / VA), c % (BK / VA) * VA);
+    }
+  };
+  auto store_b = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int c = tid + i * kBT;
+      if constexpr (LAY == kNT)
+        store_k<TB, CT, LD>(sB[buf], rb[i], c / (BK / VB), c % (BK / VB) * VB);
+      else
+        store_t<TB, CT, LD>(sB[buf], rb[i], c % (kTile / VB) * VB, c / (kTile / VB));
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto compute = [&](int buf) {
+    const CT* as = sA[buf] + (wm * 64 + lane % 32) * LD;
+    const CT* bs = sB[buf] + (wn * 64 + lane % 32) * LD;
+    if constexpr (Cfg::kBf16) {
+#pragma unroll
+      for (int ks = 0; ks < BK; ks += 16) {
+        bf16x8_t af[2], bfr[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          af[i] = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * LD + ks + (lane / 32) * 8);
+          bfr[i] = *reinterpret_cast<const bf16x8_t*>(bs + i * 32 * LD + ks + (lane / 32) * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < BK; ks += 2) {
+        float af[2], bfr[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          af[i] = as[i * 32 * LD + ks + lane / 32];
+          bfr[i] = bs[i * 32 * LD + ks + lane / 32];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+
+  if (kbeg < kend) {
+    load_a(kbeg);
+    load_b(kbeg);
+    store_a(0);
+    store_b(0);
+    __syncthreads();
+    int buf = 0;
+    for (int64_t kb = kbeg; kb < kend; kb += BK) {
+      const bool more = kb + BK < kend;
+      if (more) {  // next tile's global loads overlap this tile's MFMAs
+        load_a(kb + BK);
+        load_b(kb + BK);
+      }
+      compute(buf);
+      if (more) {  // the other buffer was last read before the previous barrier
+        store_a(buf ^ 1);
+        store_b(buf ^ 1);
+      }
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
+        const int col = wn * 64 + j * 32 + lane % 32;
+        if constexpr (LAY == kTN) {
+          const int m = m0 + row, n = n0 + col;
+          if (m < g.M && n < g.N) g.C[e * g.sC + static_cast<int64_t>(m) * g.ldc + n] = acc[i][j][r];
+        } else {
+          const int64_t grow = row0 + row;
+          const int n = n0 + col;
+          if (grow < row_end && n < g.N) g.C[grow * g.ldc + n] = acc[i][j][r];
+        }
+      }
+}
+
+template <int LAY, typename TA, typename TB>
+hipError_t launch_bwd_gemm(const GemmArgs<TA, TB>& g, hipStream_t stream) {
+  const int64_t tiles_n = ceil_div(g.N, kTile);
+  dim3 grid;
+  if (LAY == kTN)
+    grid = dim3(static_cast<unsigned>(ceil_div(g.M, kTile) * tiles_n), static_cast<unsigned>(g.G));
+  else
+    grid = dim3(grid_for(max_tiles<kTile>(g.rows, g.G, g.offsets == nullptr), static_cast<int>(tiles_n)));
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_gemm_kernel<LAY, TA, TB>), grid, dim3(kBT), 0, stream, g);
+  return hipGetLastError();
+}
+
+template <typename T>
+bool vec_ok(const T* p, int64_t ld, int64_t stride) {
+  constexpr int V = Elt<T>::kVec;
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0 && ld % V == 0 && stride % V == 0;
+}
+
+template <typename TA, typename TB>
+GemmArgs<TA, TB> args(const TA* A, int64_t lda, const int32_t* gA, int64_t gA_rows, const TB* B, int64_t ldb,
+                      int64_t sB, const int32_t* gB, int64_t gB_rows, const int32_t* offsets, int64_t rows, int G,
+                      int M, int N, int K, float* C, int64_t ldc, int64_t sC) {
+  GemmArgs<TA, TB> g{A, lda, gA, gA_rows, B, ldb, sB, gB, gB_rows, offsets, rows, G, M, N, K, C, ldc, sC, 0, 0};
+  g.vecA = vec_ok(A, lda, 0);
+  g.vecB = vec_ok(B, ldb, sB);
+  return g;
+}
+
+// ------------------------------------------------------------------- elementwise backward
+template <typename CT>
+__device__ __forceinline__ void store4(CT* p, float a, float b, float c, float d) {
+  if constexpr (std::is_same<CT, float>::value) {
+    f32x4_t v = {a, b, c, d};
+    *reinterpret_cast<f32x4_t*>(p) = v;
+  } else {
+    uint2 v;
+    v.x = pack_bf16x2(a, b);
+    v.y = pack_bf16x2(c, d);
+    *reinterpret_cast<uint2*>(p) = v;
+  }
+}
+
+// One workgroup per row p of u [rows, 2F] (fp32) and dh' [rows, F] (fp32, no gate).  The gate of
+// row p is that of the (t, j) pair with row_map(t, j) = p, t = src[p]; without src (the shared
+// expert) it is 1 and dg is not written.  SiLU'(a) = s (1 + a (1 - s)), s = 1 / (1 + e^-a).
+template <typename CT>
+__global__ __launch_bounds__(256) void bwd_swiglu_kernel(const float* __restrict__ u, const float* __restrict__ dhp,
+                                                         const float* __restrict__ gates,
+                                                         const int32_t* __restrict__ row_map,
+                                                         const int32_t* __restrict__ src, int64_t T, int k, int F,
+                                                         CT* __restrict__ du, CT* __restrict__ gh,
+                                                         float* __restrict__ dg) {
+  __shared__ float s_gate;
+  __shared__ float s_part[256 / kWave];
+  const int64_t p = blockIdx.x;
+  const int tid = threadIdx.x;
+  float gate = 1.0f;
+  if (src != nullptr) {
+    if (tid == 0) {
+      const int64_t t = clamp_row(src[p], T);
+      float gg = 0.0f;
+      for (int j = 0; j < k; ++j)
+        if (row_map[t * k + j] == p) gg = gates[t * k + j];
+      s_gate = gg;
+    }
+    __syncthreads();
+    gate = s_gate;
+  }
+  const float* up = u + p * 2 * F;
+  const float* dp = dhp + p * F;
+  CT* dup = du + p * 2 * F;
+  CT* ghp = gh + p * F;
+  float part = 0.0f;
+  for (int f = tid * 4; f < F; f += 256 * 4) {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(up + f);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(up + F + f);
+    const f32x4_t d = *reinterpret_cast<const f32x4_t*>(dp + f);
+    float da[4], db[4], hg[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s = 1.0f / (1.0f + expf(-a[i]));
+      const float sl = a[i] * s;
+      const float h = sl * b[i];
+      part += d[i] * h;
+      const float dh = gate * d[i];
+      da[i] = dh * b[i] * (s * (1.0f + a[i] * (1.0f - s)));
+      db[i] = dh * sl;
+      hg[i] = gate * h;
+    }
+    store4(dup + f, da[0], da[1], da[2], da[3]);
+    store4(dup + F + f, db[0], db[1], db[2], db[3]);
+    store4(ghp + f, hg[0], hg[1], hg[2], hg[3]);
+  }
+  if (dg != nullptr) {
+    part = wave_sum(part);
+    if (tid % kWave == 0) s_part[tid / kWave] = part;
+    __syncthreads();
+    if (tid == 0) dg[p] = ((s_part[0] + s_part[1]) + s_part[2]) + s_part[3];
+  }
+}
+
+// One wave per token: dlogits [T, E] from dg_perm (the gate gradients in permuted-row order).
+// Scores s_j: softmax over all E at the selected experts, or the logistic function of the
+// selected logit; with `norm` the gates are s_j / S.  Unselected experts get p_e (0 - B) under
+// softmax and 0 under sigmoid.
+__global__ __launch_bounds__(256) void bwd_gate_kernel(const float* __restrict__ logits,
+                                                       const int32_t* __restrict__ ids,
+                                                       const float* __restrict__ dg_perm,
+                                                       const int32_t* __restrict__ row_map, int64_t T, int E, int k,
+                                                       int score, int norm, int64_t R, float* __restrict__ dl) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (256 / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;  // whole waves; no barriers below
+  const float* lt = logits + t * E;
+  int id = 0;
+  float dgj = 0.0f;
+  if (lane < k) {
+    const int v = ids[t * k + lane];
+    id = v < 0 ? 0 : (v >= E ? E - 1 : v);
+    dgj = dg_perm[clamp_row(row_map[t * k + lane], R)];
+  }
+  float m = -INFINITY, z = 0.0f, sj = 0.0f;
+  if (score == 0) {
+    for (int e = lane; e < E; e += kWave) m = fmaxf(m, lt[e]);
+    m = wave_max(m);
+    for (int e = lane; e < E; e += kWave) z += expf(lt[e] - m);
+    z = wave_sum(z);
+    if (lane < k) sj = expf(lt[id] - m) / z;
+  } else if (lane < k) {
+    sj = 1.0f / (1.0f + expf(-lt[id]));
+  }
+  float dsj = dgj;
+  if (norm) {
+    const float S = wave_sum(sj);
+    const float A = wave_sum(dgj * (sj / S));
+    dsj = lane < k ? (dgj - A) / S : 0.0f;
+  }
+  const float B = score == 0 ? wave_sum(dsj * sj) : 0.0f;
+  int idj[kMaxTopk];
+  float dsk[kMaxTopk];
+#pragma unroll
+  for (int j = 0; j < kMaxTopk; ++j) {
+    idj[j] = __shfl(id, j, kWave);
+    dsk[j] = __shfl(dsj, j, kWave);
+  }
+  for (int e = lane; e < E; e += kWave) {
+    float d = 0.0f;
+    bool sel = false;
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j)
+      if (j < k && idj[j] == e) {
+        d = dsk[j];
+        sel = true;
+      }
+    float v;
+    if (score == 0) {
+      v = expf(lt[e] - m) / z * (d - B);
+    } else {
+      const float s = 1.0f / (1.0f + expf(-lt[e]));
+      v = sel ? d * (s * (1.0f - s)) : 0.0f;
+    }
+    dl[t * E + e] = v;
+  }
+}
+
+// One workgroup per token: dx[t] = sum_j dxp[row_map(t, j)] (j ascending) + extra0[t] + extra1[t].
+template <typename XT>
+__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dxp, const int32_t* __restrict__ row_map,
+                                                     int64_t R, int k, const float* __restrict__ extra0,
+                                                     const float* __restrict__ extra1, int H, XT* __restrict__ dx) {
+  __shared__ int64_t s_rows[kMaxTopk];
+  const int64_t t = blockIdx.x;
+  if (threadIdx.x < k) s_rows[threadIdx.x] = clamp_row(row_map[t * k + threadIdx.x], R);
+  __syncthreads();
+  for (int h = threadIdx.x * 4; h < H; h += 256 * 4) {
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < k; ++j) acc += *reinterpret_cast<const f32x4_t*>(dxp + s_rows[j] * H + h);
+    if (extra0) acc += *reinterpret_cast<const f32x4_t*>(extra0 + t * H + h);
+    if (extra1) acc += *reinterpret_cast<const f32x4_t*>(extra1 + t * H + h);
+    store4(dx + t * H + h, acc[0], acc[1], acc[2], acc[3]);
+  }
+}
+
+// The backward of one SwiGLU expert group (routed: offsets/src/gates given; shared: all null).
+template <typename WT>
+hipError_t expert_group_backward(const WT* x, const WT* dy, const WT* w1, const WT* w2, const int32_t* offsets,
+                                 const int32_t* src, const float* gates, const int32_t* row_map, int64_t T, int k,
+                                 int64_t rows, int G, int H, int F, float* u, float* dhp, WT* du, WT* gh, float* dg,
+                                 float* dxp, float* dw1, float* dw2, hipStream_t s, hipEvent_t const* ev) {
+  auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord(ev[i], s) : hipSuccess; };
+  const int64_t gx = src ? T : rows;
+  if (rows == 0) {  // no rows: every weight gradient is zero (TN tiles without K steps), nothing else runs
+    hipError_t e = launch_bwd_gemm<kTN>(args(gh, F, static_cast<const int32_t*>(nullptr), 0, dy, H, 0,
+                                             static_cast<const int32_t*>(nullptr), 0, nullptr, 0, G, F, H, 0, dw2,
+                                             H, int64_t{F} * H),
+                                        s);
+    if (e == hipSuccess)
+      e = launch_bwd_gemm<kTN>(args(x, H, static_cast<const int32_t*>(nullptr), 0, static_cast<const WT*>(du), 2 * F,
+                                    0, static_cast<const int32_t*>(nullptr), 0, nullptr, 0, G, H, 2 * F, 0, dw1,
+                                    2 * F, int64_t{H} * 2 * F),
+                               s);
+    for (int i = 1; i <= 6 && e == hipSuccess; ++i) e = mark(i);
+    return e;
+  }
+  hipError_t e = launch_bwd_gemm<kNN>(args(x, H, src, gx, w1, 2 * F, int64_t{H} * 2 * F, nullptr, 0, offsets, rows,
+                                           G, 0, 2 * F, H, u, 2 * F, 0),
+                                      s);
+  if (e == hipSuccess) e = mark(1);
+  if (e == hipSuccess)
+    e = launch_bwd_gemm<kNT>(args(dy, H, src, gx, w2, H, int64_t{F} * H, nullptr, 0, offsets, rows, G, 0, F, H, dhp,
+                                  F, 0),
+                             s);
+  if (e == hipSuccess) e = mark(2);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_swiglu_kernel<WT>, dim3(static_cast<unsigned>(rows)), dim3(256), 0, s, u, dhp, gates,
+                     row_map, src, T, k, F, du, gh, dg);
+  e = hipGetLastError();
+  if (e == hipSuccess) e = mark(3);
+  if (e == hipSuccess)
+    e = launch_bwd_gemm<kTN>(args(gh, F, static_cast<const int32_t*>(nullptr), rows, dy, H, 0, src, gx, offsets, rows,
+                                  G, F, H, 0, dw2, H, int64_t{F} * H),
+                             s);
+  if (e == hipSuccess) e = mark(4);
+  if (e == hipSuccess)
+    e = launch_bwd_gemm<kNT>(args(static_cast<const WT*>(du), 2 * F, static_cast<const int32_t*>(nullptr), rows, w1,
+                                  2 * F, int64_t{H} * 2 * F, nullptr, 0, offsets, rows, G, 0, H, 2 * F, dxp, H, 0),
+                             s);
+  if (e == hipSuccess) e = mark(5);
+  if (e == hipSuccess)
+    e = launch_bwd_gemm<kTN>(args(x, H, src, gx, static_cast<const WT*>(du), 2 * F, 0, static_cast<const int32_t*>(nullptr),
+                                  rows, offsets, rows, G, H, 2 * F, 0, dw1, 2 * F, int64_t{H} * 2 * F),
+                             s);
+  if (e == hipSuccess) e = mark(6);
+  return e;
+}
+
+template <typename WT>
+hipError_t layer_backward(const BackwardShape& sh, const BackwardIO& io, const BackwardScratch& ws, hipStream_t s,
+                          hipEvent_t const* ev) {
+  auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord(ev[i], s) : hipSuccess; };
+  const int64_t T = sh.T, R = T * sh.k;
+  const WT* x = static_cast<const WT*>(io.x);
+  const WT* dy = static_cast<const WT*>(io.dy);
+  hipError_t e = mark(0);
+  if (e == hipSuccess)
+    e = expert_group_backward<WT>(x, dy, static_cast<const WT*>(io.w1), static_cast<const WT*>(io.w2), io.offsets,
+                                  io.src_token, io.gates, io.row_map, T, sh.k, R, sh.E, sh.H, sh.F, ws.u, ws.dhp,
+                                  static_cast<WT*>(ws.du), static_cast<WT*>(ws.gh), ws.dg, ws.dxp, io.dw1, io.dw2, s,
+                                  ev);
+  if (e == hipSuccess && sh.Fs > 0)
+    e = expert_group_backward<WT>(x, dy, static_cast<const WT*>(io.ws1), static_cast<const WT*>(io.ws2), nullptr,
+                                  nullptr, nullptr, nullptr, T, 1, T, 1, sh.H, sh.Fs, ws.us, ws.dhs,
+                                  static_cast<WT*>(ws.dus), static_cast<WT*>(ws.ghs), nullptr, ws.dxs, io.dws1,
+                                  io.dws2, s, nullptr);
+  if (e == hipSuccess) e = mark(7);
+  if (e != hipSuccess) return e;
+  if (T > 0) {
+    hipLaunchKernelGGL(bwd_gate_kernel, dim3(static_cast<unsigned>(ceil_div(T, 256 / kWave))), dim3(256), 0, s,
+                       io.logits, io.ids, ws.dg, io.row_map, T, sh.E, sh.k, sh.score, sh.norm, R, ws.dl);
+    e = hipGetLastError();
+  }
+  // dx_router = dl W_r^T (W_r [H, E] read as [N = H, K = E]); dW_r = x^T dl
+  if (e == hipSuccess)
+    e = launch_bwd_gemm<kNT>(args(static_cast<const float*>(ws.dl), sh.E, static_cast<const int32_t*>(nullptr), T,
+                                  io.w_router, sh.E, 0, nullptr, 0, nullptr, T, 1, 0, sh.H, sh.E, ws.dxr, sh.H, 0),
+                             s);
+  if (e == hipSuccess)
+    e = launch_bwd_gemm<kTN>(args(x, sh.H, static_cast<const int32_t*>(nullptr), T, static_cast<const float*>(ws.dl),
+                                  sh.E, 0, static_cast<const int32_t*>(nullptr), T, nullptr, T, 1, sh.H, sh.E, 0,
+                                  io.dw_router, sh.E, 0),
+                             s);
+  if (e == hipSuccess && T > 0) {
+    hipLaunchKernelGGL(bwd_dx_kernel<WT>, dim3(static_cast<unsigned>(T)), dim3(256), 0, s, ws.dxp, io.row_map, R,
+                       sh.k, sh.Fs > 0 ? static_cast<const float*>(ws.dxs) : nullptr,
+                       static_cast<const float*>(ws.dxr), sh.H, static_cast<WT*>(io.dx));
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = mark(8);
+  return e;
+}
+
+}  // namespace
+
+BackwardScratch carve_backward(const BackwardShape& sh, int dt, void* base, size_t* bytes) {
+  const size_t cts = dt == 0 ? 4 : 2;
+  const int64_t T = sh.T, R = T * sh.k;
+  char* b = static_cast<char*>(base);
+  size_t used = 0;
+  auto take = [&](size_t n) -> void* {
+    void* p = b ? b + used : nullptr;
+    used += (n + 255) & ~static_cast<size_t>(255);
+    return p;
+  };
+  BackwardScratch w{};
+  w.u = static_cast<float*>(take(R * 2 * sh.F * 4));
+  w.dhp = static_cast<float*>(take(R * sh.F * 4));
+  w.du = take(R * 2 * sh.F * cts);
+  w.gh = take(R * sh.F * cts);
+  w.dg = static_cast<float*>(take(R * 4));
+  w.dxp = static_cast<float*>(take(R * sh.H * 4));
+  w.dl = static_cast<float*>(take(T * sh.E * 4));
+  w.dxr = static_cast<float*>(take(T * sh.H * 4));
+  if (sh.Fs > 0) {
+    w.us = static_cast<float*>(take(T * 2 * sh.Fs * 4));
+    w.dhs = static_cast<float*>(take(T * sh.Fs * 4));
+    w.dus = take(T * 2 * sh.Fs * cts);
+    w.ghs = take(T * sh.Fs * cts);
+    w.dxs = static_cast<float*>(take(T * sh.H * 4));
+  }
+  if (bytes) *bytes = used;
+  return w;
+}
+
+hipError_t launch_layer_backward(const BackwardShape& sh, int dt, const BackwardIO& io, const BackwardScratch& ws,
+                                 hipStream_t stream, hipEvent_t const* events) {
+  if (dt == 0) return layer_backward<float>(sh, io, ws, stream, events);
+  if (dt == 1) return layer_backward<bf16_t>(sh, io, ws, stream, events);
+  return hipErrorNotSupported;
+}
+
+}  // namespace moe

@@ -162,4 +162,42 @@ hipError_t launch_combine(const void* y_perm, int y_dt, const int32_t* row_map, 
                           const void* shared_out, int64_t T, int H, int k, void* y, int out_dt,
                           hipStream_t stream);
 
+// ------------------------------------------------------------------------ backward
+constexpr int kMaxTopk = 16;
+
+struct BackwardShape {
+  int64_t T;
+  int H, E, k, F, Fs, score, norm;
+};
+// Inputs and outputs of the layer backward (device pointers; shapes as in moe.h).
+struct BackwardIO {
+  const void *x, *dy;  // [T, H] in the layer's dtype
+  const float* w_router;
+  const void *w1, *w2, *ws1, *ws2;
+  const float* logits;  // forward routing state
+  const int32_t* ids;
+  const float* gates;
+  const int32_t *offsets, *row_map, *src_token;
+  void* dx;  // [T, H] in the layer's dtype
+  float *dw_router, *dw1, *dw2, *dws1, *dws2;
+};
+// Workspace pieces: u = x W1 [R, 2F] and dh' = dy W2^T [R, F] in fp32; du [R, 2F] and g h [R, F]
+// in the GEMM operand type; dg [R]; dxp [R, H]; dlogits [T, E]; dlogits W_r^T [T, H]; the shared
+// expert's u, dh', du, h and dx.
+struct BackwardScratch {
+  float *u, *dhp;
+  void *du, *gh;
+  float *dg, *dxp, *dl, *dxr;
+  float *us, *dhs;
+  void *dus, *ghs;
+  float* dxs;
+};
+// Carves the workspace from `base` (null: sizes only); *bytes receives the total.
+BackwardScratch carve_backward(const BackwardShape& sh, int dt, void* base, size_t* bytes);
+// dt: 0 = fp32, 1 = bf16 (activations, weights and dy alike).  events: null or 9 hipEvent_t
+// (null entries skipped) recorded before the backward, after the routed experts' u, dh', SwiGLU
+// backward, dW2, dxp and dW1 steps, after the shared expert, and at the end.
+hipError_t launch_layer_backward(const BackwardShape& sh, int dt, const BackwardIO& io, const BackwardScratch& ws,
+                                 hipStream_t stream, hipEvent_t const* events);
+
 }  // namespace moe

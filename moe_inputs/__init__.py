@@ -175,6 +175,15 @@ def make_inputs(cfg: LayerConfig, seed: int = 0, weight_device: str = "cpu", act
     }
 
 
+def make_upstream_grad(cfg: LayerConfig, seed: int = 0, device: str = "cpu", T: int | None = None) -> torch.Tensor:
+    """dL/dy for the backward: [T, H] standard normal (its own generator, seed + 2), in the
+    activation dtype."""
+    g = torch.Generator(device="cpu").manual_seed(seed + 2)
+    T = cfg.T if T is None else T
+    dy = torch.randn(T, cfg.H, generator=g, dtype=torch.float32)
+    return dy.to(_TORCH_DT[cfg.act_dtype]).to(device)
+
+
 def tie_heavy_router(cfg: LayerConfig, seed: int = 0):
     """Integer-valued x in {-2..2} and W_r in {-1, 0, 1}/8: router logits are exact multiples of
     1/8 in any summation order, so many keys tie exactly.  Returns (x, w_router) on the host."""

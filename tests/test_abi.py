@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     assert set(names) == set(_lib.SIGNATURES)
 
 
@@ -156,3 +156,59 @@ def test_forward_checks_requested_debug_rows():
     lay16 = _layer()
     need16 = L.moe_workspace_size(ctypes.byref(lay16), 64)
     assert L.moe_forward(ctypes.byref(lay16), P, 64, P, ctypes.byref(dbg2), P, need16, None) == INVALID
+
+
+def _grads(**over):
+    f = dict(dx=16384, dw_router=16384, dw1=16384, dw2=16384, dws1=None, dws2=None)
+    f.update(over)
+    return _lib.MoeGradsC(**f)
+
+
+def _routing(**over):
+    f = dict(logits=16384, topk_ids=16384, topk_gates=16384, expert_offsets=16384, row_map=16384, src_token=16384)
+    f.update(over)
+    return _lib.MoeRoutingC(**f)
+
+
+def test_backward_workspace_size():
+    """u, dh' (fp32), du, g h (bf16), dg, dx_perm, dlogits and the router's dx term, 256-byte aligned."""
+    L = _lib.lib()
+    lay = _layer()
+    T, H, E, k, F = 64, 256, 8, 2, 256
+    R = T * k
+    want = R * 2 * F * 4 + R * F * 4 + R * 2 * F * 2 + R * F * 2 + R * 4 + R * H * 4 + T * E * 4 + T * H * 4
+    assert L.moe_backward_workspace_size(ctypes.byref(lay), T) == want
+    assert L.moe_backward_workspace_size(ctypes.byref(_layer(w_dt=2, w1_scales=16384, w2_scales=16384)), T) == 0
+    assert L.moe_backward_workspace_size(ctypes.byref(_layer(k=9)), T) == 0
+
+
+@pytest.mark.parametrize("case,code", [
+    ("fp8", UNSUP), ("no_grads", INVALID), ("no_dw1", INVALID), ("misaligned_dx", INVALID),
+    ("no_routing", INVALID), ("no_offsets", INVALID), ("shared_without_dws", INVALID),
+    ("small_workspace", WS), ("no_workspace", WS), ("bad_layer", INVALID)])
+def test_backward_rejects(case, code):
+    L = _lib.lib()
+    lay = _layer()
+    r, g, ws = ctypes.byref(_routing()), ctypes.byref(_grads()), 1 << 30
+    wsp = P
+    if case == "fp8":
+        lay = _layer(w_dt=2, w1_scales=16384, w2_scales=16384)
+    elif case == "no_grads":
+        g = None
+    elif case == "no_dw1":
+        g = ctypes.byref(_grads(dw1=None))
+    elif case == "misaligned_dx":
+        g = ctypes.byref(_grads(dx=16384 + 4))
+    elif case == "no_routing":
+        r = None
+    elif case == "no_offsets":
+        r = ctypes.byref(_routing(expert_offsets=None))
+    elif case == "shared_without_dws":
+        lay = _layer(Fs=256, ws1=16384, ws2=16384)
+    elif case == "small_workspace":
+        ws = L.moe_backward_workspace_size(ctypes.byref(lay), 64) - 1
+    elif case == "no_workspace":
+        wsp = None
+    elif case == "bad_layer":
+        lay = _layer(F=100)
+    assert L.moe_backward(ctypes.byref(lay), P, P, 64, r, g, None, wsp, ws, None) == code
