@@ -11,7 +11,11 @@ Prints ONE JSON line: tokens/s over the timed steps, active TFLOP/s, per-stage t
 events recorded by the library on the compute stream, the roofline of the dominant kernel (the
 first grouped GEMM with the fused SwiGLU epilogue), and the CPU oracle timed on a bounded sample.
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+With --backward a step is one call of the layer backward instead (gradients of x and of every
+weight for a dy drawn from its own seed, routing state from one untimed forward); the line then
+carries the backward's stages and the roofline of its longest expert GEMM.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--backward] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -159,6 +163,181 @@ def cpu_baseline(cfg, d, sample_tokens, min_seconds=10.0):
                       f"wall (+{copy_s[0]:.1f} s copying the experts it used to the host, not counted)"}
 
 
+BWD_STAGES = ["recompute_u", "dgrad_h", "swiglu_bwd", "wgrad_w2", "dgrad_x", "wgrad_w1", "shared_expert",
+              "router_dx"]
+BWD_METRIC = "MoE-layer bwd tokens/s at 1 GPU (gradients of x and every weight); % of MFMA / HBM peak"
+
+
+def algorithmic_backward(cfg, active_experts=None):
+    """FLOPs and unique HBM bytes of each stage of moe_backward (u = x W1 recomputed in fp32;
+    dh' = dy W2^T fp32; du and g h in the operand dtype; weight gradients fp32)."""
+    T, H, E, k, F, Fs = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
+    R = T * k
+    Ea = E if active_experts is None else active_experts
+    a = 4 if cfg.act_dtype == "f32" else 2
+
+    def group(rows, tokens, ne, Fg):
+        return {
+            "recompute_u": dict(flops=4 * rows * H * Fg, bytes=tokens * H * a + ne * H * 2 * Fg * a + rows * 2 * Fg * 4),
+            "dgrad_h": dict(flops=2 * rows * Fg * H, bytes=tokens * H * a + ne * Fg * H * a + rows * Fg * 4),
+            "swiglu_bwd": dict(flops=0, bytes=rows * 3 * Fg * 4 + rows * 3 * Fg * a + rows * 4),
+            "wgrad_w2": dict(flops=2 * rows * Fg * H, bytes=rows * Fg * a + tokens * H * a + ne * Fg * H * 4),
+            "dgrad_x": dict(flops=4 * rows * Fg * H, bytes=rows * 2 * Fg * a + ne * H * 2 * Fg * a + rows * H * 4),
+            "wgrad_w1": dict(flops=4 * rows * H * Fg, bytes=tokens * H * a + rows * 2 * Fg * a + ne * H * 2 * Fg * 4),
+        }
+    out = group(R, T, Ea, F)
+    sh = group(T, T, 1, Fs) if Fs else None
+    out["shared_expert"] = dict(flops=sum(v["flops"] for v in sh.values()) if sh else 0,
+                                bytes=sum(v["bytes"] for v in sh.values()) if sh else 0)
+    out["router_dx"] = dict(flops=4 * T * H * E,
+                            bytes=T * E * 12 + R * 12 + H * E * 8 + T * H * a + R * H * 4 + T * H * 4 * (3 if Fs else 2)
+                            + T * H * a)
+    out["total_flops"] = sum(out[s]["flops"] for s in BWD_STAGES)
+    return out
+
+
+def cpu_baseline_backward(cfg, d, dy, sample_tokens, min_seconds=10.0):
+    """The float64 oracle backward (as it stands) on the first `sample_tokens` tokens of the layer.
+
+    Its forward dict (the routing and the permuted rows the backward consumes) is built by the
+    oracle forward first and not timed; expert weights are copied to the host once, untimed."""
+    from oracle import backward as obw, moe
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    w1 = [d["w1"][e].float().cpu().numpy() for e in range(cfg.E)]
+    w2 = [d["w2"][e].float().cpu().numpy() for e in range(cfg.E)]
+    sw1 = d["ws1"].float().cpu().numpy() if cfg.Fs else None
+    sw2 = d["ws2"].float().cpu().numpy() if cfg.Fs else None
+    copy_s = time.perf_counter() - t0
+    x = d["x"][:sample_tokens].float().cpu().numpy()
+    g = dy[:sample_tokens].float().cpu().numpy()
+    wr = d["w_router"].cpu().numpy()
+    bias = None if d["bias"] is None else d["bias"].cpu().numpy()
+    fw = moe.forward(x, wr, lambda e: w1[e], lambda e: w2[e], E=cfg.E, k=cfg.k, score=cfg.score, norm=cfg.norm,
+                     bias=bias, shared_w1=sw1, shared_w2=sw2)
+    runs, dt = 0, 0.0
+    while runs == 0 or (dt < min_seconds and runs < 8):
+        t0 = time.perf_counter()
+        obw.backward(fw, x, wr, lambda e: w1[e], lambda e: w2[e], g, score=cfg.score, norm=cfg.norm,
+                     shared_w1=sw1, shared_w2=sw2)
+        dt += time.perf_counter() - t0
+        runs += 1
+        print(f"[bench] cpu oracle backward run {runs}: {dt:.1f} s so far", file=sys.stderr, flush=True)
+    return {"value": runs * sample_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {sample_tokens} tokens of the same layer, {runs} run(s) of the float64 oracle "
+                      f"backward, {dt:.1f} s (its forward dict and {copy_s:.1f} s of weight copies not counted)"}
+
+
+def bench_backward(args, cfg, d, layer, torch, moe_gpu, _lib):
+    """Time K calls of moe_backward (one step = the whole layer backward for the batch); the
+    routing state comes from one untimed forward, and every input is resident in HBM."""
+    import moe_inputs
+    dev = "cuda"
+    x = d["x"]
+    _, dbg = moe_gpu.forward(x, layer, debug=True)
+    dy = moe_inputs.make_upstream_grad(cfg, seed=0, device=dev)
+    c_layer = layer.c_struct(x.dtype)
+    L = _lib.lib()
+    need = int(L.moe_backward_workspace_size(ctypes.byref(c_layer), cfg.T))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    f32 = torch.float32
+    grads = {"dx": torch.empty_like(x), "dw_router": torch.empty(cfg.H, cfg.E, dtype=f32, device=dev),
+             "dw1": torch.empty(cfg.E, cfg.H, 2 * cfg.F, dtype=f32, device=dev),
+             "dw2": torch.empty(cfg.E, cfg.F, cfg.H, dtype=f32, device=dev),
+             "dws1": torch.empty(cfg.H, 2 * cfg.Fs, dtype=f32, device=dev) if cfg.Fs else None,
+             "dws2": torch.empty(cfg.Fs, cfg.H, dtype=f32, device=dev) if cfg.Fs else None}
+    r_c = _lib.MoeRoutingC(**{kk: dbg[kk].data_ptr() for kk in moe_gpu.ROUTING_KEYS})
+    g_c = _lib.MoeGradsC(**{kk: (None if t is None else t.data_ptr()) for kk, t in grads.items()})
+    stream = torch.cuda.current_stream()
+    hip = _hip()
+    K, W = args.steps, args.warmup
+    n_ev = _lib.MOE_NUM_BWD_STAGE_EVENTS
+    events = []
+    for _ in range(K):
+        row = (ctypes.c_void_p * n_ev)()
+        for i in range(n_ev):
+            ev = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(ev)) == 0
+            row[i] = ev.value
+        events.append(row)
+
+    def step(ev_row=None):
+        _lib.check("moe_backward", L.moe_backward(ctypes.byref(c_layer), ctypes.c_void_p(x.data_ptr()),
+                                                  ctypes.c_void_p(dy.data_ptr()), cfg.T, ctypes.byref(r_c),
+                                                  ctypes.byref(g_c), ev_row, ctypes.c_void_p(ws.data_ptr()), need,
+                                                  ctypes.c_void_p(stream.cuda_stream)))
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] backward: {W} warmup steps done", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    print(f"[bench] backward: {K} timed steps done: {elapsed * 1e3 / K:.3f} ms/step", file=sys.stderr, flush=True)
+    stage_ms = {s: [] for s in BWD_STAGES}
+    for row in events:
+        for i, s in enumerate(BWD_STAGES):
+            ms = ctypes.c_float()
+            assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(row[i]), ctypes.c_void_p(row[i + 1])) == 0
+            stage_ms[s].append(ms.value)
+        for ev in row:
+            hip.hipEventDestroy(ctypes.c_void_p(ev))
+    avg_ms = {s: sum(v) / len(v) for s, v in stage_ms.items()}
+    active = int((dbg["expert_counts"] > 0).sum().item())
+    alg = algorithmic_backward(cfg, active)
+    mm_dtype = cfg.act_dtype
+    peak_tf = PEAK_TFLOPS[mm_dtype]
+    ms_per_step = elapsed * 1e3 / K
+    stages = {}
+    for s in BWD_STAGES:
+        ms = avg_ms[s]
+        if ms <= 0 or (alg[s]["flops"] == 0 and alg[s]["bytes"] == 0):
+            continue
+        rec = {"us": round(ms * 1e3, 2), "GB_s": round(alg[s]["bytes"] / (ms * 1e-3) / 1e9, 1),
+               "frac_hbm_peak": round(alg[s]["bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        if alg[s]["flops"]:
+            rec["TFLOP_s"] = round(alg[s]["flops"] / (ms * 1e-3) / 1e12, 1)
+            rec["frac_mfma_peak"] = round(rec["TFLOP_s"] / peak_tf, 4)
+        stages[s] = rec
+    # dominant kernel: the longest single-launch stage among the routed expert GEMMs
+    dom = max(["recompute_u", "dgrad_h", "wgrad_w2", "dgrad_x", "wgrad_w1"], key=lambda s: avg_ms[s])
+    a_s = alg[dom]
+    t_s = avg_ms[dom] * 1e-3
+    mfma_bound = a_s["flops"] / (peak_tf * 1e12) >= a_s["bytes"] / (PEAK_HBM_GBS * 1e9)
+    layout = {"recompute_u": "NN", "dgrad_h": "NT", "dgrad_x": "NT", "wgrad_w2": "TN", "wgrad_w1": "TN"}[dom]
+    if mfma_bound:
+        achieved, peak, unit = a_s["flops"] / t_s / 1e12, peak_tf, "TFLOP/s"
+    else:
+        achieved, peak, unit = a_s["bytes"] / t_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    roofline = {"kernel": f"bwd_gemm_kernel<{layout}> ({dom})", "bound": "mfma" if mfma_bound else "hbm",
+                "achieved": round(achieved, 1), "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                "traffic": None, "flops_per_launch": a_s["flops"], "algorithmic_bytes_per_launch": a_s["bytes"],
+                "avg_launch_us": round(avg_ms[dom] * 1e3, 2)}
+    out = {
+        "metric": BWD_METRIC, "value": round(cfg.T * K / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": mm_dtype, "data": "synthetic",
+        "config": {"workload": cfg.description + " -- backward", "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
+                   "F": cfg.F, "Fs": cfg.Fs, "experts_with_rows": active, "parallelism": "single GPU"},
+        "tflops": round(alg["total_flops"] / (ms_per_step * 1e-3) / 1e12, 1),
+        "frac_mfma_peak": round(alg["total_flops"] / (ms_per_step * 1e-3) / 1e12 / peak_tf, 4),
+        "stages": stages,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        default_sample = {"mixtral_8x7b": 512, "qwen3_235b": 64, "deepseek_v3": 32, "tiny_fp32": 256}
+        out["cpu_baseline"] = cpu_baseline_backward(cfg, d, dy, args.cpu_sample_tokens or
+                                                    default_sample.get(args.workload, 64))
+    print(json.dumps(out), flush=True)
+
+
 def practical_ceilings(torch):
     """Same-run context figures (not targets): a 2 GiB device copy and a bf16 8192^3 library matmul."""
     out = {}
@@ -199,6 +378,8 @@ def main():
                     help="tokens in the CPU oracle sample (default: about 10-30 s of oracle work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the same-run copy / matmul ceilings")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the layer backward (moe_backward) instead of the forward (bf16 / fp32 workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM counters) and exit")
     args = ap.parse_args()
@@ -224,6 +405,9 @@ def main():
     dev = "cuda"
     d = moe_inputs.make_inputs(cfg, seed=0, weight_device=dev, act_device=dev)
     layer = moe_gpu.Layer.from_inputs(d, cfg.k, cfg.score, cfg.norm)
+    if args.backward:
+        bench_backward(args, cfg, d, layer, torch, moe_gpu, _lib)
+        return
     print(f"[bench] {args.workload}: inputs ready", file=sys.stderr, flush=True)
     x = d["x"]
     c_layer = layer.c_struct(x.dtype)
