@@ -136,6 +136,21 @@ __device__ __forceinline__ void store_t(CT* s, const u32x4_t& c, int mc, int k) 
   }
 }
 
+// Four bf16 at p (8 bytes), of which the first n_ok exist; the rest read as zero.
+__device__ __forceinline__ uint2 load8(const bf16_t* p, int n_ok, int vec) {
+  if (vec && n_ok == 4) return *reinterpret_cast<const uint2*>(p);
+  uint2 r = make_uint2(0u, 0u);
+  if (n_ok > 0) r.x = p[0];
+  if (n_ok > 1) r.x |= static_cast<uint32_t>(p[1]) << 16;
+  if (n_ok > 2) r.y = p[2];
+  if (n_ok > 3) r.y |= static_cast<uint32_t>(p[3]) << 16;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t half_of(const uint2& q, int j) {
+  return ((j < 2 ? q.x : q.y) >> (16 * (j % 2))) & 0xFFFFu;
+}
+
 template <int LAY, typename TA, typename TB>
 __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g) {
   using Cfg = BwdCfg<TA, TB>;
@@ -176,8 +191,42 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g)
   }
   const TB* Bg = g.B + (LAY == kTN ? 0 : static_cast<int64_t>(e) * g.sB);
 
+  // bf16 operands laid out n- (or m-) contiguous in memory (TN: A and B; NN: B): a thread takes
+  // a 4 (k) x 4 (n) block as four 8-byte loads, transposes it in registers and writes four
+  // 8-byte k-contiguous LDS rows, instead of eight 2-byte LDS stores per 16-byte chunk.
+  constexpr bool kTrA = Cfg::kBf16 && LAY == kTN;
+  constexpr bool kTrB = Cfg::kBf16 && LAY != kNT;
+  uint2 qa[4], qb[4];
+  auto load_tr = [&](const bf16_t* base, int64_t ld, const int32_t* gat, int64_t glim, int col0, int ncols,
+                     int64_t kb, int vec, uint2(&q)[4]) {
+    const int c = col0 + (tid % 32) * 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = kb + (tid / 32) * 4 + r;
+      q[r] = make_uint2(0u, 0u);
+      if (row < kend && c < ncols) {
+        const int64_t src = gat ? clamp_row(gat[row], glim) : row;
+        q[r] = load8(base + src * ld + c, ncols - c < 4 ? ncols - c : 4, vec);
+      }
+    }
+  };
+  auto store_tr = [&](bf16_t* sm, const uint2(&q)[4]) {
+    const int nb = (tid % 32) * 4, kq = (tid / 32) * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint2 v;
+      v.x = half_of(q[0], j) | (half_of(q[1], j) << 16);
+      v.y = half_of(q[2], j) | (half_of(q[3], j) << 16);
+      *reinterpret_cast<uint2*>(sm + (nb + j) * LD + kq) = v;
+    }
+  };
+
   u32x4_t ra[RA], rb[RB];
   auto load_a = [&](int64_t kb) {
+    if constexpr (kTrA) {
+      load_tr(g.A, g.lda, g.gA, g.gA_rows, m0, g.M, kb, g.vecA, qa);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < RA; ++i) {
       const int c = tid + i * kBT;
@@ -204,6 +253,11 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g)
     }
   };
   auto load_b = [&](int64_t kb) {
+    if constexpr (kTrB) {
+      if constexpr (LAY == kTN) load_tr(g.B, g.ldb, g.gB, g.gB_rows, n0, g.N, kb, g.vecB, qb);
+      else load_tr(Bg, g.ldb, nullptr, 0, n0, g.N, kb, g.vecB, qb);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int c = tid + i * kBT;
@@ -229,6 +283,10 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g)
     }
   };
   auto store_a = [&](int buf) {
+    if constexpr (kTrA) {
+      store_tr(sA[buf], qa);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < RA; ++i) {
       const int c = tid + i * kBT;
@@ -239,6 +297,10 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g)
     }
   };
   auto store_b = [&](int buf) {
+    if constexpr (kTrB) {
+      store_tr(sB[buf], qb);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int c = tid + i * kBT;
