@@ -225,8 +225,9 @@ moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, co
  *   dy       [T, H] x_dt
  *   r        the forward's routing, as written through moe_debug: logits [T, E] fp32,
  *            topk_ids [T, k], topk_gates [T, k] fp32, expert_offsets [E+1], row_map [T, k],
- *            src_token [T*k].  Index entries are clamped into range on the device (in bounds,
- *            but meaningless results if they do not come from moe_forward).
+ *            src_token [T*k].  src_token entries must lie in [0, T), as moe_forward writes
+ *            them (the recomputation of u gathers x rows through them unchecked); the other
+ *            index entries are clamped into range on the device.
  *   g        outputs, all written in full: dx [T, H] x_dt; dw_router [H, E], dw1 [E, H, 2F],
  *            dw2 [E, F, H], dws1 [H, 2Fs], dws2 [Fs, H] fp32 (the shared pair only when
  *            Fs > 0, else ignored).  An expert that received no rows gets zero gradients.
@@ -237,7 +238,8 @@ moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, co
  *   workspace at least moe_backward_workspace_size(L, T) bytes: u [T*k, 2F] and
  *            dy W2^T [T*k, F] fp32, du [T*k, 2F] and g h [T*k, F] in x_dt, dg [T*k],
  *            dx_perm [T*k, H], dlogits [T, E], dlogits W_r^T [T, H] fp32, and the shared
- *            expert's counterparts.
+ *            expert's counterparts, and with many tokens per router-gradient tile up to 32
+ *            row slices of partial router-weight gradients [slices, H, E] fp32.
  * Accumulation is fp32 throughout (fp32 MFMA for fp32 operands, bf16 MFMA with fp32 accumulate
  * for bf16 ones); du and g h are rounded to x_dt before their GEMMs.  Sizes as for moe_forward.
  * ------------------------------------------------------------------------------------- */

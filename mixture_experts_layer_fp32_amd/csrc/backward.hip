@@ -177,8 +177,10 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g)
       expert_rows(g.offsets, e, g.rows, base, cnt);
       kbeg = base;
       kend = base + cnt;
-    } else {
-      kend = g.rows;
+    } else {  // one dense group: blockIdx.y cuts its rows into gridDim.y slices (C + y sC each)
+      const int64_t S = gridDim.y;
+      kbeg = g.rows * e / S;
+      kend = g.rows * (e + 1) / S;
     }
   } else {
     TileMap tm;
@@ -562,6 +564,16 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const float* __restrict__
   }
 }
 
+// out[i] = sum_s part[s n + i], slices in order.
+__global__ __launch_bounds__(256) void bwd_sum_slices_kernel(const float* __restrict__ part, int S, int64_t n,
+                                                             float* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  float acc = part[i];
+  for (int s = 1; s < S; ++s) acc += part[s * n + i];
+  out[i] = acc;
+}
+
 // One workgroup per token: dx[t] = sum_j dxp[row_map(t, j)] (j ascending) + extra0[t] + extra1[t].
 template <typename XT>
 __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dxp, const int32_t* __restrict__ row_map,
@@ -601,9 +613,14 @@ hipError_t expert_group_backward(const WT* x, const WT* dy, const WT* w1, const 
     for (int i = 1; i <= 6 && e == hipSuccess; ++i) e = mark(i);
     return e;
   }
-  hipError_t e = launch_bwd_gemm<kNN>(args(x, H, src, gx, w1, 2 * F, int64_t{H} * 2 * F, nullptr, 0, offsets, rows,
-                                           G, 0, 2 * F, H, u, 2 * F, 0),
-                                      s);
+  // u = x[src] W1: bf16 on the forward's grouped-GEMM kernel (no SwiGLU epilogue, fp32 out)
+  hipError_t e;
+  if constexpr (std::is_same<WT, bf16_t>::value)
+    e = launch_grouped_gemm_f32out(x, w1, offsets, rows, G, H, 2 * F, u, s, src);
+  else
+    e = launch_bwd_gemm<kNN>(args(x, H, src, gx, w1, 2 * F, int64_t{H} * 2 * F, nullptr, 0, offsets, rows, G, 0,
+                                  2 * F, H, u, 2 * F, 0),
+                             s);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess)
     e = launch_bwd_gemm<kNT>(args(dy, H, src, gx, w2, H, int64_t{F} * H, nullptr, 0, offsets, rows, G, 0, F, H, dhp,
@@ -663,11 +680,18 @@ hipError_t layer_backward(const BackwardShape& sh, const BackwardIO& io, const B
     e = launch_bwd_gemm<kNT>(args(static_cast<const float*>(ws.dl), sh.E, static_cast<const int32_t*>(nullptr), T,
                                   io.w_router, sh.E, 0, nullptr, 0, nullptr, T, 1, 0, sh.H, sh.E, ws.dxr, sh.H, 0),
                              s);
+  const int S = router_slices(T, sh.H, sh.E);
   if (e == hipSuccess)
     e = launch_bwd_gemm<kTN>(args(x, sh.H, static_cast<const int32_t*>(nullptr), T, static_cast<const float*>(ws.dl),
-                                  sh.E, 0, static_cast<const int32_t*>(nullptr), T, nullptr, T, 1, sh.H, sh.E, 0,
-                                  io.dw_router, sh.E, 0),
+                                  sh.E, 0, static_cast<const int32_t*>(nullptr), T, nullptr, T, S, sh.H, sh.E, 0,
+                                  S > 1 ? ws.dwr_part : io.dw_router, sh.E, int64_t{sh.H} * sh.E),
                              s);
+  if (e == hipSuccess && S > 1) {
+    const int64_t n = int64_t{sh.H} * sh.E;
+    hipLaunchKernelGGL(bwd_sum_slices_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, s,
+                       ws.dwr_part, S, n, io.dw_router);
+    e = hipGetLastError();
+  }
   if (e == hipSuccess && T > 0) {
     hipLaunchKernelGGL(bwd_dx_kernel<WT>, dim3(static_cast<unsigned>(T)), dim3(256), 0, s, ws.dxp, io.row_map, R,
                        sh.k, sh.Fs > 0 ? static_cast<const float*>(ws.dxs) : nullptr,
@@ -680,6 +704,15 @@ hipError_t layer_backward(const BackwardShape& sh, const BackwardIO& io, const B
 
 }  // namespace
 
+int router_slices(int64_t T, int H, int E) {
+  // enough slices for ~512 workgroups, each of at least 64 rows, at most 32
+  const int64_t tiles = ceil_div(H, kTile) * ceil_div(E, kTile);
+  int64_t S = ceil_div(512, tiles);
+  if (S > T / 64) S = T / 64;
+  if (S > 32) S = 32;
+  return S < 1 ? 1 : static_cast<int>(S);
+}
+
 BackwardScratch carve_backward(const BackwardShape& sh, int dt, void* base, size_t* bytes) {
   const size_t cts = dt == 0 ? 4 : 2;
   const int64_t T = sh.T, R = T * sh.k;
@@ -691,6 +724,8 @@ BackwardScratch carve_backward(const BackwardShape& sh, int dt, void* base, size
     return p;
   };
   BackwardScratch w{};
+  const int S = router_slices(T, sh.H, sh.E);
+  w.dwr_part = S > 1 ? static_cast<float*>(take(static_cast<size_t>(S) * sh.H * sh.E * 4)) : nullptr;
   w.u = static_cast<float*>(take(R * 2 * sh.F * 4));
   w.dhp = static_cast<float*>(take(R * sh.F * 4));
   w.du = take(R * 2 * sh.F * cts);

@@ -145,6 +145,12 @@ hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int 
 hipError_t launch_dense_gemm_f32out(const void* A, const void* B, int64_t rows, int K, int N, float* out,
                                     hipStream_t stream, int ksplit = 1);
 
+// Grouped out[p, :] (fp32) = A[gather ? gather[p] : p] . B_e over the rows of each expert, bf16
+// operands (B [E, K, N] N-contiguous, K % 64 == 0, N % 256 == 0): the grouped-GEMM kernel without
+// the SwiGLU epilogue.  gather entries must lie inside A.
+hipError_t launch_grouped_gemm_f32out(const void* A, const void* B, const int32_t* offsets, int64_t rows, int E,
+                                      int K, int N, float* out, hipStream_t stream, const int32_t* gather);
+
 // FP8 (E4M3) path: x_perm codes + [rows, H/128] scales, weights as codes + 128x128-block scales;
 // the SwiGLU output h is re-quantised to E4M3 in 1x128 blocks in the scratch buffer
 // (fp8_hidden_bytes(rows, F) bytes of codes, then [rows, F/128] fp32 scales).
@@ -185,6 +191,7 @@ struct BackwardIO {
 // in the GEMM operand type; dg [R]; dxp [R, H]; dlogits [T, E]; dlogits W_r^T [T, H]; the shared
 // expert's u, dh', du, h and dx.
 struct BackwardScratch {
+  float* dwr_part;  // [router_slices, H, E] partial router-weight gradients (null for one slice)
   float *u, *dhp;
   void *du, *gh;
   float *dg, *dxp, *dl, *dxr;
@@ -192,6 +199,8 @@ struct BackwardScratch {
   void *dus, *ghs;
   float* dxs;
 };
+// Row slices of the router-weight gradient x^T dlogits (its [H, E] output has few tiles).
+int router_slices(int64_t T, int H, int E);
 // Carves the workspace from `base` (null: sizes only); *bytes receives the total.
 BackwardScratch carve_backward(const BackwardShape& sh, int dt, void* base, size_t* bytes);
 // dt: 0 = fp32, 1 = bf16 (activations, weights and dy alike).  events: null or 9 hipEvent_t

@@ -537,6 +537,17 @@ hipError_t launch_dense_gemm_f32out(const void* A, const void* B, int64_t rows, 
                                        ksplit);
 }
 
+hipError_t launch_grouped_gemm_f32out(const void* A, const void* B, const int32_t* offsets, int64_t rows, int E,
+                                      int K, int N, float* out, hipStream_t stream, const int32_t* gather) {
+  if (rows <= 0) return hipSuccess;
+  const bool big = offsets == nullptr ? rows >= 192 : rows >= 192 * static_cast<int64_t>(E);
+  const int nt = static_cast<int>(ceil_div(N, kBN));
+  const bf16_t* a = static_cast<const bf16_t*>(A);
+  const bf16_t* b = static_cast<const bf16_t*>(B);
+  return big ? launch_bf16<256, false, true>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather)
+             : launch_bf16<128, false, true>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather);
+}
+
 hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int dt,
                                  const int32_t* offsets, int64_t rows, int E, int H, int F,
                                  const void* w1, const float* w1_scales, const void* w2,
