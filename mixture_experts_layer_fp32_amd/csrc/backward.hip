@@ -198,18 +198,24 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g)
   // 8-byte k-contiguous LDS rows, instead of eight 2-byte LDS stores per 16-byte chunk.
   constexpr bool kTrA = Cfg::kBf16 && LAY == kTN;
   constexpr bool kTrB = Cfg::kBf16 && LAY != kNT;
+  // The source rows (gathered or not) of the tile fetched next are read one K step ahead of its
+  // data, so a data load never waits on the index load issued just before it (ix = -1: no row).
   uint2 qa[4], qb[4];
-  auto load_tr = [&](const bf16_t* base, int64_t ld, const int32_t* gat, int64_t glim, int col0, int ncols,
-                     int64_t kb, int vec, uint2(&q)[4]) {
-    const int c = col0 + (tid % 32) * 4;
+  int64_t ia[4], ib[4];
+  auto load_idx = [&](const int32_t* gat, int64_t glim, int64_t kb, int64_t(&ix)[4]) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t row = kb + (tid / 32) * 4 + r;
+      ix[r] = row < kend ? (gat ? clamp_row(gat[row], glim) : row) : -1;
+    }
+  };
+  auto load_tr = [&](const bf16_t* base, int64_t ld, const int64_t(&ix)[4], int col0, int ncols, int vec,
+                     uint2(&q)[4]) {
+    const int c = col0 + (tid % 32) * 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
       q[r] = make_uint2(0u, 0u);
-      if (row < kend && c < ncols) {
-        const int64_t src = gat ? clamp_row(gat[row], glim) : row;
-        q[r] = load8(base + src * ld + c, ncols - c < 4 ? ncols - c : 4, vec);
-      }
+      if (ix[r] >= 0 && c < ncols) q[r] = load8(base + ix[r] * ld + c, ncols - c < 4 ? ncols - c : 4, vec);
     }
   };
   auto store_tr = [&](bf16_t* sm, const uint2(&q)[4]) {
@@ -226,7 +232,8 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g)
   u32x4_t ra[RA], rb[RB];
   auto load_a = [&](int64_t kb) {
     if constexpr (kTrA) {
-      load_tr(g.A, g.lda, g.gA, g.gA_rows, m0, g.M, kb, g.vecA, qa);
+      load_tr(g.A, g.lda, ia, m0, g.M, g.vecA, qa);
+      load_idx(g.gA, g.gA_rows, kb + BK, ia);
       return;
     }
 #pragma unroll
@@ -256,8 +263,8 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g)
   };
   auto load_b = [&](int64_t kb) {
     if constexpr (kTrB) {
-      if constexpr (LAY == kTN) load_tr(g.B, g.ldb, g.gB, g.gB_rows, n0, g.N, kb, g.vecB, qb);
-      else load_tr(Bg, g.ldb, nullptr, 0, n0, g.N, kb, g.vecB, qb);
+      load_tr(LAY == kTN ? g.B : Bg, g.ldb, ib, n0, g.N, g.vecB, qb);
+      load_idx(LAY == kTN ? g.gB : nullptr, g.gB_rows, kb + BK, ib);
       return;
     }
 #pragma unroll
@@ -357,6 +364,8 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g)
   };
 
   if (kbeg < kend) {
+    if constexpr (kTrA) load_idx(g.gA, g.gA_rows, kbeg, ia);
+    if constexpr (kTrB) load_idx(LAY == kTN ? g.gB : nullptr, g.gB_rows, kbeg, ib);
     load_a(kbeg);
     load_b(kbeg);
     store_a(0);
