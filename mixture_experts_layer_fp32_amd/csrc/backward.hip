@@ -36,8 +36,7 @@ using namespace gemm;
 
 enum Layout { kNN = 0, kNT = 1, kTN = 2 };
 
-constexpr int kBT = 256;    // threads of a backward GEMM workgroup: 4 waves in 2 (M) x 2 (N)
-constexpr int kTile = 128;  // output tile edge
+constexpr int kTile = 128;  // output tile columns (rows: 256 or 128)
 
 template <typename T>
 struct Elt;
@@ -151,15 +150,16 @@ __device__ __forceinline__ uint32_t half_of(const uint2& q, int j) {
   return ((j < 2 ? q.x : q.y) >> (16 * (j % 2))) & 0xFFFFu;
 }
 
-template <int LAY, typename TA, typename TB>
-__global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g) {
+template <int LAY, typename TA, typename TB, int BM>
+__global__ __launch_bounds__(2 * BM, BM == 256 ? 4 : 1) void bwd_gemm_kernel(const GemmArgs<TA, TB> g) {
   using Cfg = BwdCfg<TA, TB>;
   using CT = typename Cfg::CT;
+  constexpr int NTH = 2 * BM;  // BM / 32 waves: BM / 64 along M x 2 along N, each 64 x 64
   constexpr int BK = Cfg::BK, LD = Cfg::LD;
   constexpr int VA = Elt<TA>::kVec, VB = Elt<TB>::kVec;
-  constexpr int RA = kTile * BK / VA / kBT, RB = kTile * BK / VB / kBT;  // chunks per thread
-  static_assert(RA >= 1 && RB >= 1 && RA * VA * kBT == kTile * BK && RB * VB * kBT == kTile * BK, "tile split");
-  __shared__ __align__(16) CT sA[2][kTile * LD];
+  constexpr int RA = BM * BK / VA / NTH, RB = kTile * BK / VB / NTH;  // chunks per thread
+  static_assert(RA >= 1 && RB >= 1 && RA * VA * NTH == BM * BK && RB * VB * NTH == kTile * BK, "tile split");
+  __shared__ __align__(16) CT sA[2][BM * LD];
   __shared__ __align__(16) CT sB[2][kTile * LD];
   __shared__ int s_pref[kMaxExpertsLds];
 
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g)
   if constexpr (LAY == kTN) {
     const int tiles_n = static_cast<int>(ceil_div(g.N, kTile));
     e = static_cast<int>(blockIdx.y);
-    m0 = static_cast<int>(blockIdx.x) / tiles_n * kTile;
+    m0 = static_cast<int>(blockIdx.x) / tiles_n * BM;
     n0 = static_cast<int>(blockIdx.x) % tiles_n * kTile;
     if (g.offsets != nullptr) {
       int64_t base, cnt;
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g)
     }
   } else {
     TileMap tm;
-    if (!map_tile<kTile>(g.offsets, g.rows, g.G, static_cast<int>(ceil_div(g.N, kTile)), s_pref, tm)) return;
+    if (!map_tile<BM>(g.offsets, g.rows, g.G, static_cast<int>(ceil_div(g.N, kTile)), s_pref, tm)) return;
     e = tm.expert;
     row0 = tm.row0;
     row_end = tm.row_end;
@@ -200,49 +200,66 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g)
   constexpr bool kTrB = Cfg::kBf16 && LAY != kNT;
   // The source rows (gathered or not) of the tile fetched next are read one K step ahead of its
   // data, so a data load never waits on the index load issued just before it (ix = -1: no row).
-  uint2 qa[4], qb[4];
-  int64_t ia[4], ib[4];
-  auto load_idx = [&](const int32_t* gat, int64_t glim, int64_t kb, int64_t(&ix)[4]) {
+  // An operand tile of COLS columns: COLS / 4 column groups of 4; each thread takes TR k rows of
+  // its group (TR = BK COLS / 4 / NTH: 4 for A, 4 or 2 for B).
+  using CGA = std::integral_constant<int, BM / 4>;
+  using CGB = std::integral_constant<int, kTile / 4>;
+  constexpr int TRA = BK * CGA::value / NTH, TRB = BK * CGB::value / NTH;
+  static_assert(TRA % 2 == 0 && TRB % 2 == 0 && TRA <= 4 && TRB <= 4, "transpose blocks");
+  uint2 qa[TRA], qb[TRB];
+  int64_t ia[TRA], ib[TRB];
+  auto load_idx = [&](auto cg, const int32_t* gat, int64_t glim, int64_t kb, auto& ix) {
+    constexpr int CG = decltype(cg)::value;
+    constexpr int TR = std::extent<std::remove_reference_t<decltype(ix)>>::value;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = kb + (tid / 32) * 4 + r;
+    for (int r = 0; r < TR; ++r) {
+      const int64_t row = kb + (tid / CG) * TR + r;
       ix[r] = row < kend ? (gat ? clamp_row(gat[row], glim) : row) : -1;
     }
   };
-  auto load_tr = [&](const bf16_t* base, int64_t ld, const int64_t(&ix)[4], int col0, int ncols, int vec,
-                     uint2(&q)[4]) {
-    const int c = col0 + (tid % 32) * 4;
+  auto load_tr = [&](auto cg, const bf16_t* base, int64_t ld, const auto& ix, int col0, int ncols, int vec,
+                     auto& q) {
+    constexpr int CG = decltype(cg)::value;
+    constexpr int TR = std::extent<std::remove_reference_t<decltype(q)>>::value;
+    const int c = col0 + (tid % CG) * 4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < TR; ++r) {
       q[r] = make_uint2(0u, 0u);
       if (ix[r] >= 0 && c < ncols) q[r] = load8(base + ix[r] * ld + c, ncols - c < 4 ? ncols - c : 4, vec);
     }
   };
-  auto store_tr = [&](bf16_t* sm, const uint2(&q)[4]) {
-    const int nb = (tid % 32) * 4, kq = (tid / 32) * 4;
+  auto store_tr = [&](auto cg, bf16_t* sm, const auto& q) {
+    constexpr int CG = decltype(cg)::value;
+    constexpr int TR = std::extent<std::remove_reference_t<decltype(q)>>::value;
+    const int nb = (tid % CG) * 4, kq = (tid / CG) * TR;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint2 v;
-      v.x = half_of(q[0], j) | (half_of(q[1], j) << 16);
-      v.y = half_of(q[2], j) | (half_of(q[3], j) << 16);
-      *reinterpret_cast<uint2*>(sm + (nb + j) * LD + kq) = v;
+      const uint32_t w0 = half_of(q[0], j) | (half_of(q[1], j) << 16);
+      if constexpr (TR == 4) {
+        uint2 v;
+        v.x = w0;
+        v.y = half_of(q[2], j) | (half_of(q[3], j) << 16);
+        *reinterpret_cast<uint2*>(sm + (nb + j) * LD + kq) = v;
+      } else {
+        *reinterpret_cast<uint32_t*>(sm + (nb + j) * LD + kq) = w0;
+      }
     }
   };
 
   u32x4_t ra[RA], rb[RB];
   auto load_a = [&](int64_t kb) {
     if constexpr (kTrA) {
-      load_tr(g.A, g.lda, ia, m0, g.M, g.vecA, qa);
-      load_idx(g.gA, g.gA_rows, kb + BK, ia);
+      load_tr(CGA{}, g.A, g.lda, ia, m0, g.M, g.vecA, qa);
+      load_idx(CGA{}, g.gA, g.gA_rows, kb + BK, ia);
       return;
     }
 #pragma unroll
     for (int i = 0; i < RA; ++i) {
-      const int c = tid + i * kBT;
+      const int c = tid + i * NTH;
       const TA* p = g.A;
       int n_ok = 0;
       if constexpr (LAY == kTN) {  // A [rows, M]: m contiguous, the contraction runs over rows
-        const int kr = c / (kTile / VA), m = m0 + c % (kTile / VA) * VA;
+        const int kr = c / (BM / VA), m = m0 + c % (BM / VA) * VA;
         const int64_t r = kb + kr;
         if (r < kend && m < g.M) {
           const int64_t src = g.gA ? clamp_row(g.gA[r], g.gA_rows) : r;
@@ -263,13 +280,13 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g)
   };
   auto load_b = [&](int64_t kb) {
     if constexpr (kTrB) {
-      load_tr(LAY == kTN ? g.B : Bg, g.ldb, ib, n0, g.N, g.vecB, qb);
-      load_idx(LAY == kTN ? g.gB : nullptr, g.gB_rows, kb + BK, ib);
+      load_tr(CGB{}, LAY == kTN ? g.B : Bg, g.ldb, ib, n0, g.N, g.vecB, qb);
+      load_idx(CGB{}, LAY == kTN ? g.gB : nullptr, g.gB_rows, kb + BK, ib);
       return;
     }
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      const int c = tid + i * kBT;
+      const int c = tid + i * NTH;
       const TB* p = g.B;
       int n_ok = 0;
       if constexpr (LAY == kNT) {  // B_e [N, K]: k contiguous
@@ -293,26 +310,26 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g)
   };
   auto store_a = [&](int buf) {
     if constexpr (kTrA) {
-      store_tr(sA[buf], qa);
+      store_tr(CGA{}, sA[buf], qa);
       return;
     }
 #pragma unroll
     for (int i = 0; i < RA; ++i) {
-      const int c = tid + i * kBT;
+      const int c = tid + i * NTH;
       if constexpr (LAY == kTN)
-        store_t<TA, CT, LD>(sA[buf], ra[i], c % (kTile / VA) * VA, c / (kTile / VA));
+        store_t<TA, CT, LD>(sA[buf], ra[i], c % (BM / VA) * VA, c / (BM / VA));
       else
         store_k<TA, CT, LD>(sA[buf], ra[i], c / (BK / VA), c % (BK / VA) * VA);
     }
   };
   auto store_b = [&](int buf) {
     if constexpr (kTrB) {
-      store_tr(sB[buf], qb);
+      store_tr(CGB{}, sB[buf], qb);
       return;
     }
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      const int c = tid + i * kBT;
+      const int c = tid + i * NTH;
       if constexpr (LAY == kNT)
         store_k<TB, CT, LD>(sB[buf], rb[i], c / (BK / VB), c % (BK / VB) * VB);
       else
@@ -364,8 +381,8 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g)
   };
 
   if (kbeg < kend) {
-    if constexpr (kTrA) load_idx(g.gA, g.gA_rows, kbeg, ia);
-    if constexpr (kTrB) load_idx(LAY == kTN ? g.gB : nullptr, g.gB_rows, kbeg, ib);
+    if constexpr (kTrA) load_idx(CGA{}, g.gA, g.gA_rows, kbeg, ia);
+    if constexpr (kTrB) load_idx(CGB{}, LAY == kTN ? g.gB : nullptr, g.gB_rows, kbeg, ib);
     load_a(kbeg);
     load_b(kbeg);
     store_a(0);
@@ -407,16 +424,18 @@ __global__ __launch_bounds__(kBT) void bwd_gemm_kernel(const GemmArgs<TA, TB> g)
       }
 }
 
+// bf16 operands: 256-row tiles (8 waves); an fp32 operand: 128-row tiles (4 waves).
 template <int LAY, typename TA, typename TB>
 hipError_t launch_bwd_gemm(const GemmArgs<TA, TB>& g, hipStream_t stream) {
+  constexpr int BM = BwdCfg<TA, TB>::kBf16 ? 256 : 128;
   const int64_t tiles_n = ceil_div(g.N, kTile);
   dim3 grid;
   if (LAY == kTN)
-    grid = dim3(static_cast<unsigned>(ceil_div(g.M, kTile) * tiles_n), static_cast<unsigned>(g.G));
+    grid = dim3(static_cast<unsigned>(ceil_div(g.M, BM) * tiles_n), static_cast<unsigned>(g.G));
   else
-    grid = dim3(grid_for(max_tiles<kTile>(g.rows, g.G, g.offsets == nullptr), static_cast<int>(tiles_n)));
+    grid = dim3(grid_for(max_tiles<BM>(g.rows, g.G, g.offsets == nullptr), static_cast<int>(tiles_n)));
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_gemm_kernel<LAY, TA, TB>), grid, dim3(kBT), 0, stream, g);
+  hipLaunchKernelGGL((bwd_gemm_kernel<LAY, TA, TB, BM>), grid, dim3(2 * BM), 0, stream, g);
   return hipGetLastError();
 }
 
