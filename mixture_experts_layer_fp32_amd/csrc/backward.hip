@@ -168,10 +168,17 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 4 : 1) void bwd_gemm_kernel(con
   int e = 0, m0 = 0, n0 = 0;
   int64_t row0 = 0, row_end = 0, kbeg = 0, kend = 0;
   if constexpr (LAY == kTN) {
+    // Workgroups go round-robin to the 8 XCDs; tile L = (w % 8) per + w / 8 gives each XCD a
+    // contiguous range of tiles, m-major, so the tiles sharing an A block run on one XCD's L2.
     const int tiles_n = static_cast<int>(ceil_div(g.N, kTile));
+    const int tiles = static_cast<int>(ceil_div(g.M, BM)) * tiles_n;
+    const int per = (tiles + 7) / 8;
+    const int w = static_cast<int>(blockIdx.x);
+    const int L = (w % 8) * per + w / 8;
+    if (L >= tiles) return;  // whole workgroup, before any barrier
     e = static_cast<int>(blockIdx.y);
-    m0 = static_cast<int>(blockIdx.x) / tiles_n * BM;
-    n0 = static_cast<int>(blockIdx.x) % tiles_n * kTile;
+    m0 = L / tiles_n * BM;
+    n0 = L % tiles_n * kTile;
     if (g.offsets != nullptr) {
       int64_t base, cnt;
       expert_rows(g.offsets, e, g.rows, base, cnt);
@@ -431,7 +438,7 @@ hipError_t launch_bwd_gemm(const GemmArgs<TA, TB>& g, hipStream_t stream) {
   const int64_t tiles_n = ceil_div(g.N, kTile);
   dim3 grid;
   if (LAY == kTN)
-    grid = dim3(static_cast<unsigned>(ceil_div(g.M, BM) * tiles_n), static_cast<unsigned>(g.G));
+    grid = dim3(static_cast<unsigned>(8 * ceil_div(ceil_div(g.M, BM) * tiles_n, 8)), static_cast<unsigned>(g.G));
   else
     grid = dim3(grid_for(max_tiles<BM>(g.rows, g.G, g.offsets == nullptr), static_cast<int>(tiles_n)));
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
