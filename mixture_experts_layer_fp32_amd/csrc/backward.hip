@@ -78,6 +78,11 @@ struct GemmArgs {
   int vecA, vecB;          // 16-byte loads allowed: base 16-byte aligned, strides multiples of a chunk
 };
 
+// bf16 LDS tiles: the four 16-byte k-chunks of row r sit at chunk ^ ((r >> 4) & 3), so the
+// transposing stores (a wave's lanes write rows 4 apart) spread over the banks; every read and
+// write of a bf16 tile goes through it.
+__device__ __forceinline__ int swz(int row, int k) { return (((k >> 3) ^ ((row >> 4) & 3)) << 3) | (k & 7); }
+
 __device__ __forceinline__ int64_t clamp_row(int64_t r, int64_t n) { return r < 0 ? 0 : (r >= n ? n - 1 : r); }
 
 // One 16-byte chunk (4 fp32 or 8 bf16) starting at p, of which the first n_ok elements exist;
@@ -109,7 +114,7 @@ __device__ __forceinline__ float chunk_f32(const u32x4_t& c, int i) {
 template <typename TS, typename CT, int LD>
 __device__ __forceinline__ void store_k(CT* s, const u32x4_t& c, int row, int kc) {
   if constexpr (std::is_same<TS, CT>::value) {
-    *reinterpret_cast<u32x4_t*>(s + row * LD + kc) = c;
+    *reinterpret_cast<u32x4_t*>(s + row * LD + (std::is_same<CT, bf16_t>::value ? swz(row, kc) : kc)) = c;
   } else {  // bf16 source, fp32 tile: 8 floats
     u32x4_t lo, hi;
 #pragma unroll
@@ -129,7 +134,7 @@ __device__ __forceinline__ void store_t(CT* s, const u32x4_t& c, int mc, int k) 
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     if constexpr (std::is_same<CT, bf16_t>::value)
-      s[(mc + i) * LD + k] = static_cast<bf16_t>((c[i / 2] >> (16 * (i % 2))) & 0xFFFFu);
+      s[(mc + i) * LD + swz(mc + i, k)] = static_cast<bf16_t>((c[i / 2] >> (16 * (i % 2))) & 0xFFFFu);
     else
       s[(mc + i) * LD + k] = chunk_f32<TS>(c, i);
   }
@@ -246,9 +251,9 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 4 : 1) void bwd_gemm_kernel(con
         uint2 v;
         v.x = w0;
         v.y = half_of(q[2], j) | (half_of(q[3], j) << 16);
-        *reinterpret_cast<uint2*>(sm + (nb + j) * LD + kq) = v;
+        *reinterpret_cast<uint2*>(sm + (nb + j) * LD + swz(nb + j, kq)) = v;
       } else {
-        *reinterpret_cast<uint32_t*>(sm + (nb + j) * LD + kq) = w0;
+        *reinterpret_cast<uint32_t*>(sm + (nb + j) * LD + swz(nb + j, kq)) = w0;
       }
     }
   };
@@ -361,8 +366,9 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 4 : 1) void bwd_gemm_kernel(con
         bf16x8_t af[2], bfr[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          af[i] = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * LD + ks + (lane / 32) * 8);
-          bfr[i] = *reinterpret_cast<const bf16x8_t*>(bs + i * 32 * LD + ks + (lane / 32) * 8);
+          const int k = ks + (lane / 32) * 8;
+          af[i] = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * LD + swz(wm * 64 + i * 32 + lane % 32, k));
+          bfr[i] = *reinterpret_cast<const bf16x8_t*>(bs + i * 32 * LD + swz(wn * 64 + i * 32 + lane % 32, k));
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
