@@ -32,6 +32,9 @@ CASES = {
     "tiny_fp32": moe_inputs.CONFIGS["tiny_fp32"],
     # fp32, 5 experts (K = E = 5 and N = E = 5 in the router GEMMs: chunk tails), sigmoid, no norm
     "fp32_e5_sigmoid": _cfg("tiny_fp32", T=77, H=96, E=5, k=2, F=64, score="sigmoid", norm=False),
+    # fp32 with a shared expert and renormalised sigmoid gates (96-wide ragged tiles)
+    "fp32_shared_sigmoid": _cfg("tiny_fp32", T=150, H=96, E=6, k=3, F=96, Fs=64, score="sigmoid",
+                                     norm=True),
     "mixtral_small": _cfg("mixtral_8x7b", T=300, H=256, F=384),
     "qwen3_small": _cfg("qwen3_235b", T=333, H=320, E=16, k=4, F=256),
     "deepseek_small": _cfg("deepseek_v3", T=257, H=512, E=32, k=8, F=256, Fs=384),
