@@ -155,27 +155,28 @@ __device__ __forceinline__ uint32_t half_of(const uint2& q, int j) {
   return ((j < 2 ? q.x : q.y) >> (16 * (j % 2))) & 0xFFFFu;
 }
 
-template <int LAY, typename TA, typename TB, int BM>
-__global__ __launch_bounds__(2 * BM, BM == 256 ? 4 : 1) void bwd_gemm_kernel(const GemmArgs<TA, TB> g) {
+template <int LAY, typename TA, typename TB, int BM, int BN>
+__global__ __launch_bounds__(BM * BN / 64, BM * BN == 32768 ? 4 : 1) void bwd_gemm_kernel(const GemmArgs<TA, TB> g) {
   using Cfg = BwdCfg<TA, TB>;
   using CT = typename Cfg::CT;
-  constexpr int NTH = 2 * BM;  // BM / 32 waves: BM / 64 along M x 2 along N, each 64 x 64
+  constexpr int NTH = BM * BN / 64;  // (BM / 64) x (BN / 64) waves, each 64 x 64
+  constexpr int WN = BN / 64;
   constexpr int BK = Cfg::BK, LD = Cfg::LD;
   constexpr int VA = Elt<TA>::kVec, VB = Elt<TB>::kVec;
-  constexpr int RA = BM * BK / VA / NTH, RB = kTile * BK / VB / NTH;  // chunks per thread
-  static_assert(RA >= 1 && RB >= 1 && RA * VA * NTH == BM * BK && RB * VB * NTH == kTile * BK, "tile split");
+  constexpr int RA = BM * BK / VA / NTH, RB = BN * BK / VB / NTH;  // chunks per thread
+  static_assert(RA >= 1 && RB >= 1 && RA * VA * NTH == BM * BK && RB * VB * NTH == BN * BK, "tile split");
   __shared__ __align__(16) CT sA[2][BM * LD];
-  __shared__ __align__(16) CT sB[2][kTile * LD];
+  __shared__ __align__(16) CT sB[2][BN * LD];
   __shared__ int s_pref[kMaxExpertsLds];
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int wm = wave / 2, wn = wave % 2;
+  const int wm = wave / WN, wn = wave % WN;
   int e = 0, m0 = 0, n0 = 0;
   int64_t row0 = 0, row_end = 0, kbeg = 0, kend = 0;
   if constexpr (LAY == kTN) {
     // Workgroups go round-robin to the 8 XCDs; tile L = (w % 8) per + w / 8 gives each XCD a
     // contiguous range of tiles, m-major, so the tiles sharing an A block run on one XCD's L2.
-    const int tiles_n = static_cast<int>(ceil_div(g.N, kTile));
+    const int tiles_n = static_cast<int>(ceil_div(g.N, BN));
     const int tiles = static_cast<int>(ceil_div(g.M, BM)) * tiles_n;
     const int per = (tiles + 7) / 8;
     const int w = static_cast<int>(blockIdx.x);
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 4 : 1) void bwd_gemm_kernel(con
     if (L >= tiles) return;  // whole workgroup, before any barrier
     e = static_cast<int>(blockIdx.y);
     m0 = L / tiles_n * BM;
-    n0 = L % tiles_n * kTile;
+    n0 = L % tiles_n * BN;
     if (g.offsets != nullptr) {
       int64_t base, cnt;
       expert_rows(g.offsets, e, g.rows, base, cnt);
@@ -196,11 +197,11 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 4 : 1) void bwd_gemm_kernel(con
     }
   } else {
     TileMap tm;
-    if (!map_tile<BM>(g.offsets, g.rows, g.G, static_cast<int>(ceil_div(g.N, kTile)), s_pref, tm)) return;
+    if (!map_tile<BM>(g.offsets, g.rows, g.G, static_cast<int>(ceil_div(g.N, BN)), s_pref, tm)) return;
     e = tm.expert;
     row0 = tm.row0;
     row_end = tm.row_end;
-    n0 = tm.nt * kTile;
+    n0 = tm.nt * BN;
     kend = g.K;
   }
   const TB* Bg = g.B + (LAY == kTN ? 0 : static_cast<int64_t>(e) * g.sB);
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 4 : 1) void bwd_gemm_kernel(con
   // An operand tile of COLS columns: COLS / 4 column groups of 4; each thread takes TR k rows of
   // its group (TR = BK COLS / 4 / NTH: 4 for A, 4 or 2 for B).
   using CGA = std::integral_constant<int, BM / 4>;
-  using CGB = std::integral_constant<int, kTile / 4>;
+  using CGB = std::integral_constant<int, BN / 4>;
   constexpr int TRA = BK * CGA::value / NTH, TRB = BK * CGB::value / NTH;
   static_assert(TRA % 2 == 0 && TRB % 2 == 0 && TRA <= 4 && TRB <= 4, "transpose blocks");
   uint2 qa[TRA], qb[TRB];
@@ -309,8 +310,8 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 4 : 1) void bwd_gemm_kernel(con
           n_ok = kend - kk < VB ? static_cast<int>(kend - kk) : VB;
         }
       } else {  // NN: B_e [K, N]; TN: B [rows, N] (gathered rows): n contiguous
-        const int64_t r = kb + c / (kTile / VB);
-        const int n = n0 + c % (kTile / VB) * VB;
+        const int64_t r = kb + c / (BN / VB);
+        const int n = n0 + c % (BN / VB) * VB;
         if (r < kend && n < g.N) {
           const int64_t src = (LAY == kTN && g.gB) ? clamp_row(g.gB[r], g.gB_rows) : r;
           p = Bg + src * g.ldb + n;
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 4 : 1) void bwd_gemm_kernel(con
       if constexpr (LAY == kNT)
         store_k<TB, CT, LD>(sB[buf], rb[i], c / (BK / VB), c % (BK / VB) * VB);
       else
-        store_t<TB, CT, LD>(sB[buf], rb[i], c % (kTile / VB) * VB, c / (kTile / VB));
+        store_t<TB, CT, LD>(sB[buf], rb[i], c % (BN / VB) * VB, c / (BN / VB));
     }
   };
 
@@ -437,18 +438,21 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 4 : 1) void bwd_gemm_kernel(con
       }
 }
 
-// bf16 operands: 256-row tiles (8 waves); an fp32 operand: 128-row tiles (4 waves).
+// bf16 operands: 8 waves, 128 x 256 tiles for NT (the activation rows, re-read once per column
+// tile, are the larger stream) and 256 x 128 otherwise; an fp32 operand: 128 x 128 (4 waves).
 template <int LAY, typename TA, typename TB>
 hipError_t launch_bwd_gemm(const GemmArgs<TA, TB>& g, hipStream_t stream) {
-  constexpr int BM = BwdCfg<TA, TB>::kBf16 ? 256 : 128;
-  const int64_t tiles_n = ceil_div(g.N, kTile);
+  constexpr bool bf = BwdCfg<TA, TB>::kBf16;
+  constexpr int BM = bf ? (LAY == kNT ? 128 : 256) : 128;
+  constexpr int BN = bf ? (LAY == kNT ? 256 : 128) : 128;
+  const int64_t tiles_n = ceil_div(g.N, BN);
   dim3 grid;
   if (LAY == kTN)
     grid = dim3(static_cast<unsigned>(8 * ceil_div(ceil_div(g.M, BM) * tiles_n, 8)), static_cast<unsigned>(g.G));
   else
     grid = dim3(grid_for(max_tiles<BM>(g.rows, g.G, g.offsets == nullptr), static_cast<int>(tiles_n)));
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_gemm_kernel<LAY, TA, TB, BM>), grid, dim3(2 * BM), 0, stream, g);
+  hipLaunchKernelGGL((bwd_gemm_kernel<LAY, TA, TB, BM, BN>), grid, dim3(BM * BN / 64), 0, stream, g);
   return hipGetLastError();
 }
 
