@@ -55,6 +55,39 @@ def gemm_source_sha256():
     return h.hexdigest()
 
 
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wgrad_w1_backward_mixtral_8x7b_hbm_traffic.txt")
+BWD_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_fp32_amd", "csrc", f)
+               for f in ("backward.hip", "gemm_common.hpp", "common.hpp")]
+
+
+def backward_source_sha256():
+    """SHA-256 of the backward GEMM's sources, // comments and blank lines removed."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in BWD_SOURCES:
+        for line in open(f, encoding="utf-8"):
+            code = re.sub(r"//.*", "", line).strip()
+            if code:
+                h.update(code.encode() + b"\n")
+    return h.hexdigest()
+
+
+def measured_backward_traffic():
+    """HBM bytes per launch of the backward's dW1 GEMM from the committed PMC summary, or None
+    when its sources changed since the counters were taken."""
+    if not os.path.exists(BWD_TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(BWD_TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("backward_source_sha256") != backward_source_sha256() or "traffic_bytes_per_launch" not in kv:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
 def measured_traffic():
     """HBM bytes per launch of the first grouped GEMM from the committed PMC summary, or None
     when the kernel source changed since the counters were taken."""
@@ -318,7 +351,9 @@ def bench_backward(args, cfg, d, layer, torch, moe_gpu, _lib):
         achieved, peak, unit = a_s["bytes"] / t_s / 1e9, PEAK_HBM_GBS, "GB/s"
     roofline = {"kernel": f"bwd_gemm_kernel<{layout}> ({dom})", "bound": "mfma" if mfma_bound else "hbm",
                 "achieved": round(achieved, 1), "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
-                "traffic": None, "flops_per_launch": a_s["flops"], "algorithmic_bytes_per_launch": a_s["bytes"],
+                "traffic": measured_backward_traffic() if (args.workload == "mixtral_8x7b" and dom == "wgrad_w1")
+                else None,
+                "flops_per_launch": a_s["flops"], "algorithmic_bytes_per_launch": a_s["bytes"],
                 "avg_launch_us": round(avg_ms[dom] * 1e3, 2)}
     out = {
         "metric": BWD_METRIC, "value": round(cfg.T * K / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
