@@ -182,9 +182,14 @@ __global__ __launch_bounds__(BM * BN / 64, BM * BN == 32768 ? 4 : 1) void bwd_ge
     const int w = static_cast<int>(blockIdx.x);
     const int L = (w % 8) * per + w / 8;
     if (L >= tiles) return;  // whole workgroup, before any barrier
+    // inside that range, groups of 8 m-tiles walked n-major: the tiles running together form
+    // ~8 x 8 blocks that share their A and B blocks in L2
+    const int tiles_m = tiles / tiles_n;
+    const int grp = L / (8 * tiles_n), idx = L % (8 * tiles_n);
+    const int gm = tiles_m - grp * 8 < 8 ? tiles_m - grp * 8 : 8;
     e = static_cast<int>(blockIdx.y);
-    m0 = L / tiles_n * BM;
-    n0 = L % tiles_n * BN;
+    m0 = (grp * 8 + idx % gm) * BM;
+    n0 = idx / gm * BN;
     if (g.offsets != nullptr) {
       int64_t base, cnt;
       expert_rows(g.offsets, e, g.rows, base, cnt);
