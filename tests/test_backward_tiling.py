@@ -100,3 +100,18 @@ def test_router_row_slices_partition_the_rows(rows, S):
     bounds = [(rows * y // S, rows * (y + 1) // S) for y in range(S)]
     assert bounds[0][0] == 0 and bounds[-1][1] == rows
     assert all(a[1] == b[0] for a, b in zip(bounds, bounds[1:]))
+
+
+@pytest.mark.parametrize("tiles_m", list(range(1, 20)) + [16, 28, 56])
+@pytest.mark.parametrize("tiles_n", [1, 2, 3, 7, 32, 224])
+def test_grouped_tn_order_is_a_bijection(tiles_m, tiles_n):
+    """Inside an XCD's range, tile L -> groups of 8 m-tiles walked n-major (the last group may be
+    narrower): every (m, n) tile exactly once."""
+    seen = set()
+    for L in range(tiles_m * tiles_n):
+        grp, idx = L // (8 * tiles_n), L % (8 * tiles_n)
+        gm = min(8, tiles_m - grp * 8)
+        m, n = grp * 8 + idx % gm, idx // gm
+        assert 0 <= m < tiles_m and 0 <= n < tiles_n
+        seen.add((m, n))
+    assert len(seen) == tiles_m * tiles_n
