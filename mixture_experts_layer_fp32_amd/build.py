@@ -2,7 +2,8 @@
 
 Usage: python -m mixture_experts_layer_fp32_amd.build   (or __graft_entry__.build()).
 Every call recompiles all sources (one hipcc process per source, in parallel) and links
-the shared library next to this file.
+the shared library next to this file, plus the benchmark's helper library
+libmoe_bench_util.so (a streaming copy and a cache-flush fill; not part of the layer).
 """
 
 from __future__ import annotations
@@ -20,6 +21,9 @@ BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["api.hip", "route.hip", "permute.hip", "gemm.hip", "gemm_fp8.hip", "combine.hip", "backward.hip"]
+BENCH_UTIL_SOURCE = "bench_util.hip"
+BENCH_UTIL_NAME = "libmoe_bench_util.so"
+BENCH_UTIL_PATH = os.path.join(PKG, BENCH_UTIL_NAME)
 ARCH = "gfx950"
 
 
@@ -48,18 +52,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path):
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + [BENCH_UTIL_SOURCE]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB_PATH)
+    _link(objs[len(SOURCES):], BENCH_UTIL_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {BENCH_UTIL_PATH}")
     return LIB_PATH
 
 
