@@ -13,13 +13,14 @@
  *
  * Conventions for every entry point:
  *  - Tensor pointers are DEVICE pointers to row-major, densely packed arrays, owned
- *    by the caller; the library allocates no memory and keeps no per-call state.
+ *    by the caller; the library allocates no memory and keeps no per-call state (the one
+ *    static device array of moe_forward_static aside).
  *    Pointers must be 16-byte aligned.  Inputs and outputs must not alias.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream),
  *    never synchronise, never copy to the host, and are HIP-graph capturable.
  *  - Arguments are validated on the host before anything is launched; a failed check
- *    returns MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED / MOE_ERR_WORKSPACE and
- *    launches nothing.  A launch failure returns MOE_ERR_HIP.  Faults inside kernels
+ *    returns MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED / MOE_ERR_WORKSPACE /
+ *    MOE_ERR_TOO_LARGE and launches nothing.  A launch failure returns MOE_ERR_HIP.  Faults inside kernels
  *    surface at the caller's next synchronisation.
  *  - Integer outputs (expert ids, counts, offsets, permutation) are deterministic:
  *    the same inputs give the same bits on every run.  No floating-point atomics are
@@ -52,7 +53,8 @@ typedef enum {
   MOE_ERR_INVALID_ARG = 1, /* null pointer, size out of range, inconsistent sizes     */
   MOE_ERR_UNSUPPORTED = 2, /* valid request this build does not implement            */
   MOE_ERR_WORKSPACE = 3,   /* workspace pointer missing or smaller than required     */
-  MOE_ERR_HIP = 4          /* a HIP launch failed (hipGetLastError after the launch) */
+  MOE_ERR_HIP = 4,         /* a HIP launch failed (hipGetLastError after the launch) */
+  MOE_ERR_TOO_LARGE = 5    /* moe_forward_static: more scratch needed than it holds     */
 } moe_status;
 
 typedef enum {
@@ -266,6 +268,28 @@ size_t moe_backward_workspace_size(const moe_layer* L, int64_t T);
 moe_status moe_backward(const moe_layer* L, const void* x, const void* dy, int64_t T, const moe_routing* r,
                         const moe_grads* g, void* const* stage_events, void* workspace, size_t workspace_bytes,
                         moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * The fused forward without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, stages and results as moe_forward (same kernels, so bit-identical outputs for
+ * the same inputs); the caller still owns x, y and every moe_debug buffer.  The workspace is a
+ * static device array of MOE_STATIC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends; nothing is allocated or freed by any call.
+ *   Limit: a call needing more than MOE_STATIC_SCRATCH_BYTES of workspace, i.e.
+ *   moe_workspace_size(L, T) > MOE_STATIC_SCRATCH_BYTES, returns MOE_ERR_TOO_LARGE, launching
+ *   nothing.  Decode-sized batches fit: up to 292 tokens of a DeepSeek-V3-shaped bf16 layer
+ *   (H 7168, 256 experts, top-8, F 2048, shared expert), 620 of a Qwen3-235B-shaped one, 900 of a
+ *   Mixtral-8x7B-shaped one.
+ *   Sharing: every call on one GPU uses that GPU's one array, and no kernel relies on its previous
+ *   contents; calls that overlap in time on one GPU (different streams or threads without
+ *   ordering between them) race on it and must not be issued.
+ *   The first call on each device looks up the array's device address (hipGetSymbolAddress) and
+ *   keeps it; make that first call outside a graph capture.
+ * ------------------------------------------------------------------------------------- */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_static(const moe_layer* L, const void* x, int64_t T, void* y, const moe_debug* dbg,
+                              moe_stream_t stream);
 
 const char* moe_status_str(moe_status s);
 int32_t moe_abi_version(void);

@@ -20,7 +20,7 @@ import torch
 from . import _lib
 from ._lib import MoeError  # noqa: F401
 
-__all__ = ["route", "permute", "grouped_swiglu", "unpermute_combine", "forward", "Layer",
+__all__ = ["route", "permute", "grouped_swiglu", "unpermute_combine", "forward", "forward_static", "Layer",
            "workspace_size", "MoeError"]
 
 _DT = {torch.float32: _lib.MOE_F32, torch.bfloat16: _lib.MOE_BF16, torch.float8_e4m3fn: _lib.MOE_FP8_E4M3}
@@ -214,6 +214,19 @@ def forward(x, layer: Layer, debug: bool = False, workspace=None):
                                             ctypes.byref(dbg_c) if dbg_c is not None else None,
                                             _ptr(workspace), workspace.numel(), _stream()))
     return (y, dbg) if debug else y
+
+
+def forward_static(x, layer: Layer, out=None):
+    """The whole layer on the library's static device scratch (moe_forward_static): no workspace is
+    passed and the library allocates nothing; ``out`` ([T, H], optional) receives y.  Raises
+    MoeError (MOE_ERR_TOO_LARGE) past the static limit."""
+    _need_gpu(x, layer.w_router, layer.w1, layer.w2, layer.bias, layer.ws1, layer.ws2, out)
+    T, H = x.shape
+    c = layer.c_struct(x.dtype)
+    y = out if out is not None else torch.empty(T, H, dtype=layer.out_dtype or x.dtype, device=x.device)
+    _lib.check("moe_forward_static", _lib.lib().moe_forward_static(ctypes.byref(c), _ptr(x), T, _ptr(y), None,
+                                                                    _stream()))
+    return y
 
 
 ROUTING_KEYS = ("logits", "topk_ids", "topk_gates", "expert_offsets", "row_map", "src_token")

@@ -1,8 +1,16 @@
 // api.hip -- the extern "C" boundary declared in include/moe.h: host-side validation,
 // workspace carving and stage launches.  No device memory is allocated, nothing is copied to
 // the host and nothing synchronises, so every entry point is HIP-graph capturable.
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "common.hpp"
+
+// Scratch of moe_forward_static, for callers that cannot allocate: one copy of this array on every
+// GPU the library runs on, held until the process ends.  Host code never uses its name as an
+// address (on the host the name is a stand-in, not device memory): static_scratch() resolves the
+// device address with hipGetSymbolAddress once per device and every use goes through that.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -63,6 +71,8 @@ const char* moe_status_str(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: not supported by this build";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+    case MOE_ERR_TOO_LARGE:
+      return "MOE_ERR_TOO_LARGE: the call needs more scratch than the static MOE_STATIC_SCRATCH_BYTES";
   }
   return "unknown moe_status";
 }
@@ -336,6 +346,46 @@ moe_status moe_backward(const moe_layer* L, const void* x, const void* dy, int64
                      g->dw_router, g->dw1,    g->dw2,        g->dws1,        g->dws2};
   return from_hip(moe::launch_layer_backward(sh, dt, io, ws, static_cast<hipStream_t>(stream),
                                              reinterpret_cast<hipEvent_t const*>(stage_events)));
+}
+
+// ------------------------------------------------------------------------------ no allocation
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, resolved once per device (with that device
+// current) and kept.
+moe_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+moe_status moe_forward_static(const moe_layer* L, const void* x, int64_t T, void* y, const moe_debug* dbg,
+                              moe_stream_t stream) {
+  moe_status st = validate_layer(L);
+  if (st != MOE_OK) return st;
+  st = check_common(T, L->H, L->E, L->k);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (plan(L, T, nullptr, nullptr).bytes > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != MOE_OK) return st;
+  return moe_forward(L, x, T, y, dbg, ws, MOE_STATIC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

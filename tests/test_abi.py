@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     assert set(names) == set(_lib.SIGNATURES)
 
 
@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(L, name), name
     assert L.moe_abi_version() == 1
-    for s in range(5):
+    for s in range(6):
         assert L.moe_status_str(s).startswith(b"MOE_")
 
 
@@ -212,3 +212,19 @@ def test_backward_rejects(case, code):
     elif case == "bad_layer":
         lay = _layer(F=100)
     assert L.moe_backward(ctypes.byref(lay), P, P, 64, r, g, None, wsp, ws, None) == code
+
+
+def test_forward_static_rejects_on_the_host():
+    """moe_forward_static checks the layer and its scratch need before touching the device: a
+    DeepSeek-V3-shaped layer fits MOE_STATIC_SCRATCH_BYTES up to 292 tokens, not 293."""
+    L = _lib.lib()
+    c = _lib.MoeLayerC(H=7168, E=256, k=8, F=2048, Fs=2048, x_dt=_lib.MOE_BF16, w_dt=_lib.MOE_BF16,
+                       out_dt=_lib.MOE_BF16, score=_lib.MOE_SIGMOID, norm_topk=1, w_router=16, bias=None, w1=16,
+                       w2=16, ws1=16, ws2=16, w1_scales=None, w2_scales=None, ws1_scales=None, ws2_scales=None)
+    assert L.moe_workspace_size(ctypes.byref(c), 292) <= _lib.MOE_STATIC_SCRATCH_BYTES
+    assert L.moe_workspace_size(ctypes.byref(c), 293) > _lib.MOE_STATIC_SCRATCH_BYTES
+    assert L.moe_forward_static(ctypes.byref(c), P, 293, P, None, None) == _lib.MOE_ERR_TOO_LARGE
+    assert L.moe_forward_static(ctypes.byref(c), P, 0, P, None, None) == _lib.MOE_OK
+    assert L.moe_forward_static(None, P, 8, P, None, None) == INVALID
+    c.k = 0
+    assert L.moe_forward_static(ctypes.byref(c), P, 8, P, None, None) == INVALID
