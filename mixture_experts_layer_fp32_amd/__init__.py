@@ -232,6 +232,32 @@ def forward_static(x, layer: Layer, out=None):
 ROUTING_KEYS = ("logits", "topk_ids", "topk_gates", "expert_offsets", "row_map", "src_token")
 
 
+def _check_backward_args(x, dy, layer: Layer, routing: dict):
+    """The kernels read dy in x's dtype and index the routing tensors by T, k and E unchecked: a
+    mismatch would make them read past the caller's buffers, so it is refused here."""
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, H], got {tuple(x.shape)}")
+    T, H = x.shape
+    E = layer.w_router.shape[1]
+    k = layer.k
+    if dy.dtype != x.dtype or tuple(dy.shape) != (T, H):
+        raise ValueError(f"dy must match x ({x.dtype}, {(T, H)}), got {dy.dtype}, {tuple(dy.shape)}")
+    if dy.device != x.device:
+        raise ValueError("dy must be on x's device")
+    want = {"logits": (torch.float32, (T, E)), "topk_ids": (torch.int32, (T, k)),
+            "topk_gates": (torch.float32, (T, k)), "expert_offsets": (torch.int32, (E + 1,)),
+            "row_map": (torch.int32, (T, k)), "src_token": (torch.int32, (T * k,))}
+    for key, (dt, shape) in want.items():
+        t = routing.get(key)
+        if t is None:
+            raise ValueError(f"routing[{key!r}] is missing")
+        if t.dtype != dt or tuple(t.shape) != shape:
+            raise ValueError(f"routing[{key!r}] must be {dt} {shape} for T={T}, k={k}, E={E}; "
+                             f"got {t.dtype} {tuple(t.shape)}")
+        if t.device != x.device:
+            raise ValueError(f"routing[{key!r}] must be on x's device")
+
+
 def backward_workspace_size(layer: Layer, T: int, x_dtype) -> int:
     c = layer.c_struct(x_dtype)
     return int(_lib.lib().moe_backward_workspace_size(ctypes.byref(c), T))
@@ -247,6 +273,7 @@ def backward(x, dy, layer: Layer, routing: dict, workspace=None, stage_events=No
     MOE_NUM_BWD_STAGE_EVENTS raw hipEvent_t handles (ctypes.c_void_p, int or None) recorded at
     the stage boundaries.
     """
+    _check_backward_args(x, dy, layer, routing)
     rt = [routing[kk] for kk in ROUTING_KEYS]
     _need_gpu(x, dy, layer.w_router, layer.w1, layer.w2, layer.ws1, layer.ws2, *rt)
     T, H = x.shape

@@ -20,8 +20,9 @@ Recipe (all workloads, seed 0 unless stated):
              shared expert ``ws1`` [H, 2Fs], ``ws2`` [Fs, H], from a second
              generator seeded with seed + 1 on ``weight_device``;
 * FP8 workloads: each weight matrix is drawn in fp32 as above and stored as
-  E4M3 codes with one fp32 scale per 128x128 block (scale = block amax / 448,
-  codes by torch's own float8_e4m3fn cast after clamping to +-448);
+  E4M3 codes with one fp32 scale per 128x128 block (scale = the smallest power
+  of two 2^q with 448 * 2^q >= the block's amax, 1 for an all-zero block;
+  codes by torch's own float8_e4m3fn cast of w / scale after clamping to +-448);
 * the skewed-routing workload adds a per-expert routing bias read from
   ``tests/golden/zipf_bias_deepseek_v3_fp8.txt`` (written by
   ``tests/golden/make_zipf_bias.py``), calibrated so expert loads follow a Zipf

@@ -45,3 +45,20 @@ def check_permutation(ids, counts, offsets, row_map, src_token):
         a, b = offsets[e], offsets[e + 1]
         assert (exp_of_row[a:b] == e).all(), f"rows of expert {e} are not contiguous"
         assert (np.diff(src[a:b]) > 0).all(), f"rows of expert {e} are not in increasing token order"
+
+
+def max_row_rel(got, ref) -> float:
+    """max over rows i of ||got_i - ref_i|| / ||ref_i|| (float64): a bound that one wrong row or tile
+    cannot hide behind the whole-tensor norm.  Rows whose reference is all zero must match exactly."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    got = got.reshape(got.shape[0], -1)
+    ref = ref.reshape(ref.shape[0], -1)
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.linalg.norm(ref, axis=1)
+    zero = den == 0.0
+    if (num[zero] != 0.0).any():
+        return float("inf")
+    if zero.all():
+        return 0.0
+    return float((num[~zero] / den[~zero]).max())

@@ -228,3 +228,56 @@ def test_forward_static_rejects_on_the_host():
     assert L.moe_forward_static(None, P, 8, P, None, None) == INVALID
     c.k = 0
     assert L.moe_forward_static(ctypes.byref(c), P, 8, P, None, None) == INVALID
+
+
+def _bwd_args(T=6, H=64, E=4, k=2, F=128, dt=None):
+    import torch
+    import mixture_experts_layer_fp32_amd as moe_gpu
+    dt = dt or torch.bfloat16
+    layer = moe_gpu.Layer(w_router=torch.zeros(H, E), w1=torch.zeros(E, H, 2 * F, dtype=dt),
+                          w2=torch.zeros(E, F, H, dtype=dt), k=k)
+    x = torch.zeros(T, H, dtype=dt)
+    i32, f32 = torch.int32, torch.float32
+    routing = {"logits": torch.zeros(T, E, dtype=f32), "topk_ids": torch.zeros(T, k, dtype=i32),
+               "topk_gates": torch.zeros(T, k, dtype=f32), "expert_offsets": torch.zeros(E + 1, dtype=i32),
+               "row_map": torch.zeros(T, k, dtype=i32), "src_token": torch.zeros(T * k, dtype=i32)}
+    return x, torch.zeros_like(x), layer, routing
+
+
+@pytest.mark.parametrize("bad", ["dy_dtype", "dy_shape", "logits", "topk_ids_dtype", "topk_gates", "offsets",
+                                 "row_map", "src_token", "missing"])
+def test_backward_binding_rejects_mismatched_tensors(bad):
+    """The binding refuses, before any device call, a dy or routing state that does not match x, k
+    and E (the kernels would read past the caller's buffers)."""
+    import torch
+    import mixture_experts_layer_fp32_amd as moe_gpu
+    x, dy, layer, r = _bwd_args()
+    T, H = x.shape
+    if bad == "dy_dtype":
+        dy = dy.float()
+    elif bad == "dy_shape":
+        dy = torch.zeros(T + 1, H, dtype=x.dtype)
+    elif bad == "logits":
+        r["logits"] = torch.zeros(T, 5)
+    elif bad == "topk_ids_dtype":
+        r["topk_ids"] = r["topk_ids"].long()
+    elif bad == "topk_gates":
+        r["topk_gates"] = torch.zeros(T, 3)
+    elif bad == "offsets":
+        r["expert_offsets"] = torch.zeros(4, dtype=torch.int32)
+    elif bad == "row_map":
+        r["row_map"] = torch.zeros(T - 1, 2, dtype=torch.int32)
+    elif bad == "src_token":
+        r["src_token"] = torch.zeros(T, dtype=torch.int32)
+    elif bad == "missing":
+        del r["row_map"]
+    with pytest.raises(ValueError):
+        moe_gpu.backward(x, dy, layer, r)
+
+
+def test_backward_binding_accepts_matching_tensors_up_to_the_device_check():
+    """Matching host tensors pass the shape checks and stop at the device check (no CPU path)."""
+    import mixture_experts_layer_fp32_amd as moe_gpu
+    x, dy, layer, r = _bwd_args()
+    with pytest.raises(ValueError, match="GPU"):
+        moe_gpu.backward(x, dy, layer, r)

@@ -280,3 +280,85 @@ def test_row_map_outside_range_reads_row_zero():
     fixed = torch.where((rm >= 0) & (rm < T * k), rm, torch.zeros_like(rm))
     ref = moe.combine(host(yp), fixed.numpy(), g.numpy().astype(np.float64))
     assert rel_frobenius(host(y), ref) <= TOL["f32"]
+
+
+def _guarded(n_bytes, pad=4096):
+    """A byte buffer with `pad` sentinel bytes (0xA5) on each side of an n_bytes region (16-byte
+    aligned: pad is a multiple of 16)."""
+    buf = torch.full((n_bytes + 2 * pad,), 0xA5, dtype=torch.uint8, device=DEV)
+    return buf, buf[pad:pad + n_bytes]
+
+
+def _bands_intact(buf, pad=4096):
+    h = buf.cpu()
+    return bool((h[:pad] == 0xA5).all() and (h[-pad:] == 0xA5).all())
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "e4m3"])
+def test_forward_outputs_stay_inside_their_buffers(w_dtype):
+    """moe_forward writes y and every requested intermediate only inside their own extent: each
+    lives in a buffer with sentinel bytes before and after, which must be untouched; y must also
+    match the oracle (so the call did write it)."""
+    import ctypes
+    from mixture_experts_layer_fp32_amd import _lib
+    base = "deepseek_v3" if w_dtype == "bf16" else "deepseek_v3_fp8_zipf"
+    cfg = moe_inputs.CONFIGS[base].replace(T=301, H=384, E=16, k=4, F=256, Fs=128, zipf_bias=False)
+    d = moe_inputs.make_inputs(cfg, seed=2, weight_device=DEV, act_device=DEV)
+    layer = moe_gpu.Layer.from_inputs(d, cfg.k, cfg.score, cfg.norm)
+    T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
+    R = T * k
+    fp8 = w_dtype == "e4m3"
+    sizes = {"y": T * H * 2, "logits": T * E * 4, "topk_ids": R * 4, "topk_gates": R * 4, "expert_counts": E * 4,
+             "expert_offsets": (E + 1) * 4, "row_map": R * 4, "src_token": R * 4,
+             "x_perm": R * H * (1 if fp8 else 2), "y_perm": R * H * 2}
+    if fp8:
+        sizes["x_perm_scales"] = R * (H // 128) * 4
+    bufs = {n: _guarded(s) for n, s in sizes.items()}
+    dbg = _lib.MoeDebugC(**{n: bufs[n][1].data_ptr() for n in sizes if n != "y"})
+    c = layer.c_struct(torch.bfloat16)
+    L = _lib.lib()
+    need = int(L.moe_workspace_size(ctypes.byref(c), T))
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    st = L.moe_forward(ctypes.byref(c), ctypes.c_void_p(d["x"].data_ptr()), T, ctypes.c_void_p(bufs["y"][1].data_ptr()),
+                       ctypes.byref(dbg), ctypes.c_void_p(ws.data_ptr()), need,
+                       ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    for n, (buf, _) in bufs.items():
+        assert _bands_intact(buf), f"{n} written outside its extent"
+    y = bufs["y"][1].view(torch.bfloat16).view(T, H)
+    y_ref = moe_gpu.forward(d["x"], layer)
+    assert torch.equal(y, y_ref)
+
+
+def test_backward_outputs_stay_inside_their_buffers():
+    """moe_backward writes dx and every weight gradient only inside their own extent (sentinel
+    bytes on both sides of each, untouched), and the result equals an unguarded call's."""
+    cfg = moe_inputs.CONFIGS["deepseek_v3"].replace(T=150, H=320, E=8, k=4, F=256, Fs=128)
+    d = moe_inputs.make_inputs(cfg, seed=4, weight_device=DEV, act_device=DEV)
+    layer = moe_gpu.Layer.from_inputs(d, cfg.k, cfg.score, cfg.norm)
+    T, H, E, F, Fs = cfg.T, cfg.H, cfg.E, cfg.F, cfg.Fs
+    _, dbg = moe_gpu.forward(d["x"], layer, debug=True)
+    dy = moe_inputs.make_upstream_grad(cfg, seed=4, device=DEV)
+    ref = moe_gpu.backward(d["x"], dy, layer, dbg)
+    import ctypes
+    from mixture_experts_layer_fp32_amd import _lib
+    sizes = {"dx": T * H * 2, "dw_router": H * E * 4, "dw1": E * H * 2 * F * 4, "dw2": E * F * H * 4,
+             "dws1": H * 2 * Fs * 4, "dws2": Fs * H * 4}
+    bufs = {n: _guarded(s) for n, s in sizes.items()}
+    c = layer.c_struct(torch.bfloat16)
+    L = _lib.lib()
+    need = int(L.moe_backward_workspace_size(ctypes.byref(c), T))
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    r_c = _lib.MoeRoutingC(**{kk: dbg[kk].data_ptr() for kk in moe_gpu.ROUTING_KEYS})
+    g_c = _lib.MoeGradsC(**{n: bufs[n][1].data_ptr() for n in sizes})
+    st = L.moe_backward(ctypes.byref(c), ctypes.c_void_p(d["x"].data_ptr()), ctypes.c_void_p(dy.data_ptr()), T,
+                        ctypes.byref(r_c), ctypes.byref(g_c), None, ctypes.c_void_p(ws.data_ptr()), need,
+                        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    for n, (buf, _) in bufs.items():
+        assert _bands_intact(buf), f"{n} written outside its extent"
+    assert torch.equal(bufs["dx"][1].view(torch.bfloat16).view(T, H), ref["dx"])
+    for n in ("dw_router", "dw1", "dw2", "dws1", "dws2"):
+        assert torch.equal(bufs[n][1].view(torch.float32).view(ref[n].shape), ref[n]), n

@@ -182,3 +182,30 @@ def test_pins_catch_planted_mistakes(name, monkeypatch):
     monkeypatch.setattr(moe, attr, fn)
     out = _forward(x, wr, w1, w2, E=5, **kw)
     assert rel_frobenius(out["y"], np.array(y_bf)) > 1e-6, f"mutation {name} went unnoticed"
+
+
+def test_swiglu_hidden_pins():
+    """swiglu_hidden (the activation the e4m3 parity checks quantise) against a pure-Python loop
+    (math.exp, no numpy matmul), against torch's SiLU in float64, and against swiglu_expert: its
+    product with W2 is the expert output.  A swapped gate/up split or a sign error in SiLU fails
+    the loop comparison (SiLU(a) b != SiLU(b) a for these values)."""
+    import math
+    rng = np.random.default_rng(21)
+    n, H, F = 5, 7, 6
+    rows = rng.standard_normal((n, H))
+    w1 = rng.standard_normal((H, 2 * F)) * 0.6
+    w2 = rng.standard_normal((F, H)) * 0.6
+    h = moe.swiglu_hidden(rows, w1)
+    loop = np.empty((n, F))
+    for i in range(n):
+        for f in range(F):
+            a = sum(float(rows[i, c]) * float(w1[c, f]) for c in range(H))
+            b = sum(float(rows[i, c]) * float(w1[c, F + f]) for c in range(H))
+            loop[i, f] = a / (1.0 + math.exp(-a)) * b
+    assert np.allclose(h, loop, rtol=1e-13, atol=1e-13)
+    t_rows, t_w1 = torch.from_numpy(rows), torch.from_numpy(w1)
+    ref = torch.nn.functional.silu(t_rows @ t_w1[:, :F]) * (t_rows @ t_w1[:, F:])
+    assert rel_frobenius(h, ref.numpy()) <= 1e-14
+    assert rel_frobenius(h @ w2, moe.swiglu_expert(rows, w1, w2)) <= 1e-14
+    swapped = np.concatenate([w1[:, F:], w1[:, :F]], axis=1)
+    assert rel_frobenius(moe.swiglu_hidden(rows, swapped), loop) > 0.1

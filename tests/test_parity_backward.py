@@ -42,6 +42,12 @@ CASES = {
     "mixtral_ragged": _cfg("mixtral_8x7b", T=700, H=320, E=3, k=2, F=384),
     # most experts without rows: their weight gradients must be exactly zero
     "empty_experts": _cfg("qwen3_235b", T=5, H=128, E=64, k=2, F=128),
+    # more than 8 output m-tiles in the weight-gradient GEMMs, a count not a multiple of 8 (the
+    # grouped TN tile order walks groups of 8 m-tiles n-major; its last group is narrower):
+    # bf16 256-row tiles, dW1 over H = 2368 (10 m-tiles) and dW2 over F = 2432 (10 m-tiles)
+    "bf16_multi_group": _cfg("mixtral_8x7b", T=64, H=2368, E=4, k=2, F=2432),
+    # fp32 128-row tiles, dW1 over H = 1184 (10 m-tiles), dW2 over F = 1152 (9 m-tiles)
+    "fp32_multi_group": _cfg("tiny_fp32", T=40, H=1184, E=3, k=2, F=1152),
 }
 
 
