@@ -890,7 +890,9 @@ def bench_forward(args, cfg, d, layer, torch, _lib, util, moe_gpu):
         "warmup": W, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": mm_dtype, "data": "synthetic",
         "config": {"workload": cfg.description, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "F": cfg.F,
-                   "Fs": cfg.Fs, "router": router, "experts_with_rows": active, "parallelism": "single GPU"},
+                   "Fs": cfg.Fs, "router": router, "experts_with_rows": active,
+                   "gate": "folded into the SwiGLU epilogue" if layer.gate_in_expert else "applied in combine",
+                   "parallelism": "single GPU"},
         "active_tflops": round(active_tflops, 1),
         "frac_mfma_peak": round(active_tflops / peak_tf, 4),
         "stages": stages,
@@ -931,6 +933,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the same-run copy / matmul ceilings")
     ap.add_argument("--no-stage-bench", action="store_true", help="skip timing the stage entry points alone")
+    ap.add_argument("--gate-in-expert", action="store_true",
+                    help="fold the routing gate into the experts' SwiGLU epilogue (combine sums unweighted)")
     ap.add_argument("--backward", action="store_true",
                     help="time the layer backward (moe_backward) instead of the forward (bf16 / fp32 workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -971,7 +975,7 @@ def main():
 
     cfg = moe_inputs.CONFIGS[args.workload]
     d = moe_inputs.make_inputs(cfg, seed=0, weight_device="cuda", act_device="cuda")
-    layer = moe_gpu.Layer.from_inputs(d, cfg.k, cfg.score, cfg.norm)
+    layer = moe_gpu.Layer.from_inputs(d, cfg.k, cfg.score, cfg.norm, gate_in_expert=args.gate_in_expert)
     if args.backward:
         bench_backward(args, cfg, d, layer, torch, moe_gpu, _lib, util)
         return

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_EXPERTS 512
 
@@ -159,7 +159,8 @@ moe_status moe_unpermute_combine(const void* y_perm, moe_dtype y_dt, const int32
 
 /* ---------------------------------------------------------------------------------------
  * The whole layer in one call: route -> permute -> grouped SwiGLU -> (shared expert) ->
- * combine, launched in that order on `stream`.
+ * combine, launched in that order on `stream` (summary page, "Method", first paragraph, the
+ * four stages; second paragraph, sync-free dropless execution).
  * ------------------------------------------------------------------------------------- */
 typedef struct {
   int32_t H, E, k, F;
@@ -176,12 +177,19 @@ typedef struct {
   const void* ws1;       /* [H, 2Fs] or NULL                                             */
   const void* ws2;       /* [Fs, H] or NULL                                              */
   const float* w1_scales, *w2_scales, *ws1_scales, *ws2_scales; /* FP8 only, else NULL  */
+  int32_t gate_in_expert; /* 0: combine weights the expert rows by their gates.  1: the gate  */
+                          /* is folded into the experts: the first GEMM's SwiGLU epilogue     */
+                          /* multiplies each permuted row's h by its gate before rounding, so */
+                          /* y_perm rows come out gate-weighted and combine sums the k rows   */
+                          /* unweighted (summary page, "Method", second paragraph: memory-    */
+                          /* efficient permutation, kernel fusion).  The shared expert keeps  */
+                          /* gate 1 either way; moe_backward does not depend on it.           */
 } moe_layer;
 
 /* Optional views of the intermediates: every non-NULL pointer receives that stage's
  * output (shapes as in the stage calls; x_perm / y_perm in the dtypes moe_forward uses:
  * x_perm in w_dt (e4m3 codes for FP8, with x_perm_scales, which is then required), y_perm in
- * x_dt).  moe_forward itself does not materialise x_perm: its first grouped GEMM reads the
+ * x_dt; with gate_in_expert, y_perm rows are the gate-weighted ones the experts wrote).  moe_forward itself does not materialise x_perm: its first grouped GEMM reads the
  * token rows of x (for FP8: of x quantised once per token) through src_token; x_perm is
  * written only when requested here.  All pointers 16-byte aligned.
  * stage_events: optional hipEvent_t handles recorded on `stream` at the stage boundaries

@@ -145,13 +145,15 @@ class Layer:
     ws1_scales: torch.Tensor | None = None
     ws2_scales: torch.Tensor | None = None
     out_dtype: torch.dtype | None = None
+    gate_in_expert: bool = False  # fold the routing gate into the experts' SwiGLU epilogue
 
     @classmethod
-    def from_inputs(cls, d: dict, k: int, score: str, norm: bool, out_dtype=None) -> "Layer":
+    def from_inputs(cls, d: dict, k: int, score: str, norm: bool, out_dtype=None,
+                    gate_in_expert: bool = False) -> "Layer":
         return cls(w_router=d["w_router"], w1=d["w1"], w2=d["w2"], k=k, score=score, norm=norm,
                    bias=d.get("bias"), ws1=d.get("ws1"), ws2=d.get("ws2"), w1_scales=d.get("w1_scales"),
                    w2_scales=d.get("w2_scales"), ws1_scales=d.get("ws1_scales"),
-                   ws2_scales=d.get("ws2_scales"), out_dtype=out_dtype)
+                   ws2_scales=d.get("ws2_scales"), out_dtype=out_dtype, gate_in_expert=gate_in_expert)
 
     def c_struct(self, x_dtype) -> _lib.MoeLayerC:
         H, E = self.w_router.shape
@@ -167,7 +169,8 @@ class Layer:
             w1_scales=None if self.w1_scales is None else self.w1_scales.data_ptr(),
             w2_scales=None if self.w2_scales is None else self.w2_scales.data_ptr(),
             ws1_scales=None if self.ws1_scales is None else self.ws1_scales.data_ptr(),
-            ws2_scales=None if self.ws2_scales is None else self.ws2_scales.data_ptr())
+            ws2_scales=None if self.ws2_scales is None else self.ws2_scales.data_ptr(),
+            gate_in_expert=int(self.gate_in_expert))
 
 
 def workspace_size(layer: Layer, T: int, x_dtype) -> int:

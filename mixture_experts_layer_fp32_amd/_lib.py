@@ -41,7 +41,8 @@ class MoeLayerC(_c.Structure):
     _fields_ = [("H", _i32), ("E", _i32), ("k", _i32), ("F", _i32), ("Fs", _i32),
                 ("x_dt", _i32), ("w_dt", _i32), ("out_dt", _i32), ("score", _i32), ("norm_topk", _i32),
                 ("w_router", _vp), ("bias", _vp), ("w1", _vp), ("w2", _vp), ("ws1", _vp), ("ws2", _vp),
-                ("w1_scales", _vp), ("w2_scales", _vp), ("ws1_scales", _vp), ("ws2_scales", _vp)]
+                ("w1_scales", _vp), ("w2_scales", _vp), ("ws1_scales", _vp), ("ws2_scales", _vp),
+                ("gate_in_expert", _i32)]
 
 
 class MoeDebugC(_c.Structure):

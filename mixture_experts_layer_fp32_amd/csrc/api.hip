@@ -173,7 +173,7 @@ namespace {
 
 struct ForwardPlan {
   void *logits, *route_ws, *ids, *gates, *counts, *offsets, *row_map, *src, *perm_ws, *x_perm, *x_scales, *xq,
-      *xq_scales, *gemm_ws, *y_perm, *sh_ws, *sh_out;
+      *xq_scales, *gemm_ws, *y_perm, *sh_ws, *sh_out, *gate_perm;
   size_t bytes;
 };
 
@@ -183,6 +183,7 @@ moe_status validate_layer(const moe_layer* L) {
   if (st != MOE_OK) return st;
   if (!act_dtype_ok(L->x_dt) || !act_dtype_ok(L->out_dt)) return MOE_ERR_INVALID_ARG;
   if (L->score != MOE_SOFTMAX && L->score != MOE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (L->gate_in_expert != 0 && L->gate_in_expert != 1) return MOE_ERR_INVALID_ARG;
   if (L->w_dt == MOE_F32 && (L->x_dt != MOE_F32)) return MOE_ERR_INVALID_ARG;
   if (L->w_dt == MOE_BF16 && L->x_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (L->w_dt == MOE_FP8_E4M3 && L->x_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
@@ -231,6 +232,7 @@ ForwardPlan plan(const moe_layer* L, int64_t T, void* ws, const moe_debug* dbg) 
     p.sh_ws = c.take(moe::grouped_swiglu_scratch_bytes(T, L->Fs, L->w_dt));
     p.sh_out = c.take(T * L->H * xe);
   }
+  p.gate_perm = L->gate_in_expert ? c.take(R * 4) : nullptr;  // each permuted row's gate
   p.bytes = c.used;
   return p;
 }
@@ -268,10 +270,14 @@ moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, co
                                    static_cast<int32_t*>(p.ids), static_cast<float*>(p.gates), p.route_ws, s);
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return from_hip(e);
+  // gate folded into the experts: dispatch also writes each permuted row's gate, the first GEMM's
+  // SwiGLU epilogue scales h by it, and combine sums the k rows unweighted
+  float* gate_perm = static_cast<float*>(p.gate_perm);
   e = moe::launch_permute(x, L->x_dt, static_cast<int32_t*>(p.ids), T, L->H, L->E, L->k, p.x_perm,
                           L->w_dt, static_cast<float*>(p.x_scales), static_cast<int32_t*>(p.row_map),
                           static_cast<int32_t*>(p.src), static_cast<int32_t*>(p.counts),
-                          static_cast<int32_t*>(p.offsets), p.perm_ws, s);
+                          static_cast<int32_t*>(p.offsets), p.perm_ws, s,
+                          gate_perm ? static_cast<float*>(p.gates) : nullptr, gate_perm);
   // the e4m3 path quantises each token once (1x128 blocks); the GEMM gathers its rows
   const void* a = x;
   if (e == hipSuccess && fp8) {
@@ -283,7 +289,7 @@ moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, co
   if (e != hipSuccess) return from_hip(e);
   e = moe::launch_grouped_swiglu(a, static_cast<float*>(p.xq_scales), L->w_dt, static_cast<int32_t*>(p.offsets),
                                  R, L->E, L->H, L->F, L->w1, L->w1_scales, L->w2, L->w2_scales, p.y_perm, L->x_dt,
-                                 p.gemm_ws, s, ev(3), static_cast<int32_t*>(p.src));
+                                 p.gemm_ws, s, ev(3), static_cast<int32_t*>(p.src), gate_perm);
   if (e == hipSuccess) e = mark(4);
   if (e != hipSuccess) return from_hip(e);
   if (L->Fs > 0) {  // every token, unpermuted (quantised like the routed rows in the e4m3 path)
@@ -294,8 +300,8 @@ moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, co
   e = mark(5);
   if (e != hipSuccess) return from_hip(e);
   e = moe::launch_combine(p.y_perm, L->x_dt, static_cast<int32_t*>(p.row_map),
-                          static_cast<float*>(p.gates), L->Fs > 0 ? p.sh_out : nullptr, T, L->H, L->k, y,
-                          L->out_dt, s);
+                          gate_perm ? nullptr : static_cast<float*>(p.gates), L->Fs > 0 ? p.sh_out : nullptr, T,
+                          L->H, L->k, y, L->out_dt, s);
   if (e == hipSuccess) e = mark(6);
   return from_hip(e);
 }

@@ -2,7 +2,8 @@
 //
 // y[t] = sum_j g[t, j] * y_perm[row_map[t, j]] (+ shared expert output, gate 1), the combine
 // of "Scalable Training of Mixture-of-Experts Models with Megatron Core", summary page,
-// "Method", first paragraph.  One wavefront per token; each lane owns 8 consecutive
+// "Method", first paragraph.  Without gates (the gate folded into the experts' SwiGLU epilogue,
+// so y_perm rows arrive scaled) every weight is 1: fmaf(1, v, acc) is the plain sum.  One wavefront per token; each lane owns 8 consecutive
 // columns (16-byte loads of bf16, two 16-byte loads of fp32), accumulates in fp32 over
 // j = 0..k-1 in order, and rounds once to the output dtype.  No atomics: deterministic.
 // The sum order is the same in every variant, so results do not depend on the unrolling.
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
     row = row_map[t * k + lane];
     // a caller's row outside [0, T k) is read as row 0: every access stays inside y_perm
     row = static_cast<uint64_t>(row) < static_cast<uint64_t>(T * k) ? row : 0;
-    g = gates[t * k + lane];
+    g = gates ? gates[t * k + lane] : 1.0f;  // no gates: rows already scaled by them
   }
   const int n8 = H / 8;
   auto store = [&](int c, const float* acc) {

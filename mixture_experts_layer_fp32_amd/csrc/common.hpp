@@ -122,21 +122,25 @@ hipError_t launch_route(const void* x, int x_dt, const float* w_router, const fl
 size_t route_scratch_bytes(int64_t T, int H, int E, bool logits_given);
 
 size_t permute_scratch_bytes(int64_t T, int E, int k);
+// With gates [T, k] and gate_perm [T k] (both or neither), also writes each permuted row's gate:
+// gate_perm[row_map[t, j]] = gates[t, j].
 hipError_t launch_permute(const void* x, int x_dt, const int32_t* ids, int64_t T, int H, int E, int k,
                           void* x_perm, int perm_dt, float* x_perm_scales, int32_t* row_map,
                           int32_t* src_token, int32_t* counts, int32_t* offsets, void* scratch,
-                          hipStream_t stream);
+                          hipStream_t stream, const float* gates = nullptr, float* gate_perm = nullptr);
 
 size_t grouped_swiglu_scratch_bytes(int64_t rows, int F, int dt);
 // offsets == nullptr means one expert owning rows [0, rows) (the shared expert).  With
 // `gather`, row p of the first GEMM's A operand is row gather[p] of x_perm (and of x_scales):
 // the dispatch permutation fused into the GEMM's loads, so x_perm can be the unpermuted input.
+// With `row_scale` [rows], the SwiGLU epilogue multiplies row p of h by row_scale[p] before it is
+// rounded (the routing gate folded into the expert), so y_perm row p comes out scaled by it.
 hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int dt,
                                  const int32_t* offsets, int64_t rows, int E, int H, int F,
                                  const void* w1, const float* w1_scales, const void* w2,
                                  const float* w2_scales, void* y_perm, int out_dt, void* scratch,
                                  hipStream_t stream, hipEvent_t between = nullptr,
-                                 const int32_t* gather = nullptr);
+                                 const int32_t* gather = nullptr, const float* row_scale = nullptr);
 
 // Dense out[rows, N] (fp32) = A[rows, K] . B[K, N] with bf16 A and B (B N-contiguous),
 // K % 64 == 0, N % 8 == 0: the grouped-GEMM kernel with one expert.  With ksplit > 1 (K / 64 a
@@ -159,11 +163,12 @@ hipError_t launch_grouped_swiglu_fp8(const void* x_perm, const float* x_scales, 
                                      int64_t rows, int E, int H, int F, const void* w1, const float* w1_scales,
                                      const void* w2, const float* w2_scales, void* y_perm, int out_dt,
                                      void* scratch, hipStream_t stream, hipEvent_t between,
-                                     const int32_t* gather);
+                                     const int32_t* gather, const float* row_scale = nullptr);
 // Per-row 1x128 E4M3 quantisation of a dense [T, H] bf16 / fp32 matrix (shared-expert input).
 hipError_t launch_quant_rows_fp8(const void* x, int x_dt, int64_t T, int H, uint8_t* codes, float* scales,
                                  hipStream_t stream);
 
+// gates == nullptr: every weight is 1 (rows already scaled by their gates).
 hipError_t launch_combine(const void* y_perm, int y_dt, const int32_t* row_map, const float* gates,
                           const void* shared_out, int64_t T, int H, int k, void* y, int out_dt,
                           hipStream_t stream);

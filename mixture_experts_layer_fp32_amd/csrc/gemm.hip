@@ -81,7 +81,7 @@ template <int BM, int WM, bool SWIGLU, bool OUT_F32, int S>
 __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const int32_t* __restrict__ offsets,
     int64_t rows, int E, int K, int ldb, int NT, void* __restrict__ out, int ncu,
-    const int32_t* __restrict__ gather, int ksplit) {
+    const int32_t* __restrict__ gather, int ksplit, const float* __restrict__ row_scale) {
   using R = Bf16Rings<BM>;
   constexpr int NA = R::NA, NB = R::NB;
   constexpr int NWAVE = 4 * WM;                // WM along M x 4 along N
@@ -331,17 +331,28 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     constexpr int NTH = NWAVE * kWave;
     constexpr int COLS = SWIGLU ? 128 : kBN;  // output columns of the tile
     constexpr int LS = COLS + 8;              // row stride in bf16: rows 4 apart start 16 banks apart
-    static_assert(BM * LS * 2 <= R::SMEM, "output staging fits in the operand rings");
+    static_assert(BM * LS * 2 + BM * 4 <= R::SMEM, "output staging and row gates fit in the operand rings");
     wait_lgkm0();
     __syncthreads();
     bf16_t* st = reinterpret_cast<bf16_t*>(smem);
+    // gate folded into the expert: the tile's row gates, staged after the output rows
+    float* s_gate = reinterpret_cast<float*>(smem + BM * LS * 2);
+    if (SWIGLU && row_scale != nullptr) {
+      if (tid < BM) {
+        const int64_t g = tm.row0 + tid;
+        s_gate[tid] = row_scale[g < tm.row_end ? g : tm.row_end - 1];
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
         if (SWIGLU) {
-          st[row_t * LS + wn * 32 + lane % 32] = f32_to_bf16(silu_fast(acc[i][0][r]) * acc[i][1][r]);
+          float hv = silu_fast(acc[i][0][r]) * acc[i][1][r];
+          if (row_scale != nullptr) hv *= s_gate[row_t];
+          st[row_t * LS + wn * 32 + lane % 32] = f32_to_bf16(hv);
         } else {
 #pragma unroll
           for (int j = 0; j < FN; ++j) st[row_t * LS + wn * 64 + j * 32 + lane % 32] = f32_to_bf16(acc[i][j][r]);
@@ -373,7 +384,9 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
         if (SWIGLU) {
           const int F = ldb / 2;
           const int64_t col = static_cast<int64_t>(tm.nt) * 128 + wn * 32 + lane % 32;
-          static_cast<float*>(out)[grow * F + col] = silu_fast(acc[i][0][r]) * acc[i][1][r];
+          float hv = silu_fast(acc[i][0][r]) * acc[i][1][r];
+          if (row_scale != nullptr) hv *= row_scale[grow];
+          static_cast<float*>(out)[grow * F + col] = hv;
         } else {
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
@@ -397,7 +410,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(const float* __restr
                                                            const int32_t* __restrict__ offsets,
                                                            int64_t rows, int E, int K, int ldb, int NT,
                                                            float* __restrict__ out,
-                                                           const int32_t* __restrict__ gather) {
+                                                           const int32_t* __restrict__ gather,
+                                                           const float* __restrict__ row_scale) {
   __shared__ float sa[kF32BM][kF32BK + 1];
   __shared__ float sb[kF32BK][kF32BN + 4];
   __shared__ int s_pref[kMaxExpertsLds];
@@ -444,7 +458,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(const float* __restr
       for (int r = 0; r < 16; ++r) {
         const int64_t grow = tm.row0 + wm * 32 + (r / 4) * 8 + (lane / 32) * 4 + (r % 4);
         if (grow >= tm.row_end) continue;
-        const float h = silu(acc[r]) * s_up[wm][r][lane];
+        float h = silu(acc[r]) * s_up[wm][r][lane];
+        if (row_scale != nullptr) h *= row_scale[grow];
         out[grow * F + static_cast<int64_t>(tm.nt) * 32 + lane % 32] = h;
       }
     }
@@ -479,7 +494,7 @@ int device_cus() {
 template <int BM, bool SWIGLU, bool OUT_F32, int WM = 2, int S = 1>
 hipError_t launch_bf16(const bf16_t* A, const bf16_t* B, const int32_t* offsets, int64_t rows, int E,
                        int K, int ldb, int NT, void* out, hipStream_t stream, int ncu = 0,
-                       const int32_t* gather = nullptr, int ksplit = 1) {
+                       const int32_t* gather = nullptr, int ksplit = 1, const float* row_scale = nullptr) {
   constexpr int smem = Bf16Rings<BM>::SMEM;
   auto kern = gemm_bf16_kernel<BM, WM, SWIGLU, OUT_F32, S>;
   // once per instantiation (and never inside a stream capture after the first eager call)
@@ -489,7 +504,7 @@ hipError_t launch_bf16(const bf16_t* A, const bf16_t* B, const int32_t* offsets,
   const int64_t mt = max_tiles<BM>(rows, E, offsets == nullptr);
   const unsigned grid = SWIGLU ? grid_for_any(mt, NT, E, offsets == nullptr, ncu, S) : grid_for(mt, NT, ncu, S);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256 * WM), smem, stream, A, B, offsets, rows, E, K, ldb, NT, out, ncu,
-                     gather, ksplit);
+                     gather, ksplit, row_scale);
   return hipGetLastError();
 }
 
@@ -506,10 +521,11 @@ hipError_t launch_bf16_down(const bf16_t* h, const bf16_t* w2, const int32_t* of
 template <int BM>
 hipError_t launch_bf16_pair(const void* x_perm, const void* w1, const void* w2, const int32_t* offsets,
                             int64_t rows, int E, int H, int F, void* y_perm, int out_dt, void* scratch,
-                            hipStream_t stream, hipEvent_t between, const int32_t* gather) {
+                            hipStream_t stream, hipEvent_t between, const int32_t* gather, const float* row_scale) {
   bf16_t* h = static_cast<bf16_t*>(scratch);
   hipError_t err = launch_bf16<BM, true, false>(static_cast<const bf16_t*>(x_perm), static_cast<const bf16_t*>(w1),
-                                                offsets, rows, E, H, 2 * F, F / 128, h, stream, 0, gather);
+                                                offsets, rows, E, H, 2 * F, F / 128, h, stream, 0, gather, 1,
+                                                row_scale);
   if (err != hipSuccess) return err;
   if (between && (err = hipEventRecord(between, stream)) != hipSuccess) return err;
   const int nt2 = static_cast<int>(ceil_div(H, kBN));
@@ -552,24 +568,26 @@ hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int 
                                  const int32_t* offsets, int64_t rows, int E, int H, int F,
                                  const void* w1, const float* w1_scales, const void* w2,
                                  const float* w2_scales, void* y_perm, int out_dt, void* scratch,
-                                 hipStream_t stream, hipEvent_t between, const int32_t* gather) {
+                                 hipStream_t stream, hipEvent_t between, const int32_t* gather,
+                                 const float* row_scale) {
   if (dt == 2)
     return launch_grouped_swiglu_fp8(x_perm, x_scales, offsets, rows, E, H, F, w1, w1_scales, w2, w2_scales,
-                                     y_perm, out_dt, scratch, stream, between, gather);
+                                     y_perm, out_dt, scratch, stream, between, gather, row_scale);
   if (dt == 0) {
     float* h = static_cast<float*>(scratch);
     const int nt1 = F / 32, nt2 = static_cast<int>(ceil_div(H, kF32BN));
     const unsigned g1 = grid_for(max_tiles<kF32BM>(rows, E, offsets == nullptr), nt1);
     hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(g1), dim3(kThreads), 0, stream,
                        static_cast<const float*>(x_perm), static_cast<const float*>(w1), offsets, rows, E,
-                       H, 2 * F, nt1, h, gather);
+                       H, 2 * F, nt1, h, gather, row_scale);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (between && (err = hipEventRecord(between, stream)) != hipSuccess) return err;
     const unsigned g2 = grid_for(max_tiles<kF32BM>(rows, E, offsets == nullptr), nt2);
     hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(g2), dim3(kThreads), 0, stream, h,
                        static_cast<const float*>(w2), offsets, rows, E, F, H, nt2,
-                       static_cast<float*>(y_perm), static_cast<const int32_t*>(nullptr));
+                       static_cast<float*>(y_perm), static_cast<const int32_t*>(nullptr),
+                       static_cast<const float*>(nullptr));
     return hipGetLastError();
   }
   if (dt == 1) {
@@ -577,9 +595,9 @@ hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int 
     // computes its live 32-row blocks), else 128-row tiles
     const bool big = offsets == nullptr ? rows >= 192 : rows >= 192 * static_cast<int64_t>(E);
     return big ? launch_bf16_pair<256>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream,
-                                       between, gather)
+                                       between, gather, row_scale)
                : launch_bf16_pair<128>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream,
-                                       between, gather);
+                                       between, gather, row_scale);
   }
   return hipErrorNotSupported;
 }

@@ -88,6 +88,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ A_scales, const uint8_t* __restrict__ B,
     const float* __restrict__ B_scales, const int32_t* __restrict__ offsets, int64_t rows, int E, int K,
     int ldb, int NT, void* __restrict__ out, float* __restrict__ out_scales, const int32_t* __restrict__ gather,
+    const float* __restrict__ row_scale,
     const int* __restrict__ mx_flag) {
   using C = F8Cfg<BM>;
   constexpr bool MX = C::MX;
@@ -477,17 +478,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
     for (int pass = 0; pass < BM / 64; ++pass) {
       const int row_t = pass * 64 + tid / 8;
       const f32x4_t* src = reinterpret_cast<const f32x4_t*>(hl + row_t * kHS + seg * 16);
+      const int64_t grow = tm.row0 + row_t;
+      // gate folded into the expert: h of the row scaled by its gate before the block is quantised
+      const float g = row_scale != nullptr ? row_scale[grow < tm.row_end ? grow : tm.row_end - 1] : 1.0f;
       f32x4_t v[4];
       float m = 0.0f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         v[q] = src[q];
+        if (row_scale != nullptr) v[q] *= g;
         m = fmaxf(fmaxf(m, fmaxf(fabsf(v[q][0]), fabsf(v[q][1]))), fmaxf(fabsf(v[q][2]), fabsf(v[q][3])));
       }
       m = fmaxf(m, __shfl_xor(m, 1, kWave));
       m = fmaxf(m, __shfl_xor(m, 2, kWave));
       m = fmaxf(m, __shfl_xor(m, 4, kWave));
-      const int64_t grow = tm.row0 + row_t;
       if (grow < tm.row_end) {
         const float sc = e4m3_block_scale(m);  // a power of two
         const float inv = pow2_inverse(sc);    // exact: x * inv == x / sc
@@ -552,7 +556,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
 template <int BM, bool SWIGLU, bool OUT_F32>
 hipError_t launch_fp8(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, const int32_t* offsets,
                       int64_t rows, int E, int K, int ldb, int NT, void* out, float* out_scales,
-                      hipStream_t stream, const int32_t* gather, const int* mx_flag) {
+                      hipStream_t stream, const int32_t* gather, const int* mx_flag, const float* row_scale) {
   constexpr int smem = F8Cfg<BM>::SMEM;
   auto kern = gemm_fp8_kernel<BM, SWIGLU, OUT_F32>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -561,7 +565,7 @@ hipError_t launch_fp8(const uint8_t* A, const float* As, const uint8_t* B, const
   const int64_t mt = max_tiles<BM>(rows, E, offsets == nullptr);
   const unsigned grid = SWIGLU ? grid_for_any(mt, NT, E, offsets == nullptr) : grid_for(mt, NT);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), smem, stream, A, As, B, Bs, offsets, rows, E, K, ldb,
-                     NT, out, out_scales, gather, mx_flag);
+                     NT, out, out_scales, gather, row_scale, mx_flag);
   return hipGetLastError();
 }
 
@@ -570,12 +574,12 @@ template <bool SWIGLU, bool OUT_F32>
 hipError_t launch_fp8_both(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs,
                            const int32_t* offsets, int64_t rows, int E, int K, int ldb, int NT_mx, int NT_gen,
                            void* out, float* out_scales, hipStream_t stream, const int32_t* gather,
-                           const int* mx_flag) {
+                           const int* mx_flag, const float* row_scale = nullptr) {
   hipError_t err = launch_fp8<192, SWIGLU, OUT_F32>(A, As, B, Bs, offsets, rows, E, K, ldb, NT_mx, out, out_scales,
-                                                    stream, gather, mx_flag);
+                                                    stream, gather, mx_flag, row_scale);
   if (err != hipSuccess) return err;
   return launch_fp8<128, SWIGLU, OUT_F32>(A, As, B, Bs, offsets, rows, E, K, ldb, NT_gen, out, out_scales, stream,
-                                          gather, mx_flag);
+                                          gather, mx_flag, row_scale);
 }
 
 }  // namespace
@@ -587,7 +591,8 @@ size_t fp8_hidden_bytes(int64_t rows, int F) {
 hipError_t launch_grouped_swiglu_fp8(const void* x_perm, const float* x_scales, const int32_t* offsets,
                                      int64_t rows, int E, int H, int F, const void* w1, const float* w1_scales,
                                      const void* w2, const float* w2_scales, void* y_perm, int out_dt,
-                                     void* scratch, hipStream_t stream, hipEvent_t between, const int32_t* gather) {
+                                     void* scratch, hipStream_t stream, hipEvent_t between, const int32_t* gather,
+                                     const float* row_scale) {
   uint8_t* hq = static_cast<uint8_t*>(scratch);
   float* hs = reinterpret_cast<float*>(static_cast<char*>(scratch) + fp8_hidden_bytes(rows, F));
   int* flag = reinterpret_cast<int*>(static_cast<char*>(scratch) + fp8_hidden_bytes(rows, F) +
@@ -606,7 +611,8 @@ hipError_t launch_grouped_swiglu_fp8(const void* x_perm, const float* x_scales, 
   if (err != hipSuccess) return err;
   const int nt1 = F / 128, nt2 = static_cast<int>(ceil_div(H, kBN));
   err = launch_fp8_both<true, false>(static_cast<const uint8_t*>(x_perm), x_scales, static_cast<const uint8_t*>(w1),
-                                     w1_scales, offsets, rows, E, H, 2 * F, nt1, nt1, hq, hs, stream, gather, flag);
+                                     w1_scales, offsets, rows, E, H, 2 * F, nt1, nt1, hq, hs, stream, gather, flag,
+                                     row_scale);
   if (err != hipSuccess) return err;
   if (between && (err = hipEventRecord(between, stream)) != hipSuccess) return err;
   if (out_dt == 0)

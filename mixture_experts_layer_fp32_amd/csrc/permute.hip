@@ -104,16 +104,19 @@ __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(int32_t* __rest
 constexpr int kScatterThreads = 256;
 constexpr int kTokPerBlock = kScatterThreads / kWave;
 
-// Resolve the k permuted rows of token t in lanes 0..k-1 (others: 0) and publish the maps.
+// Resolve the k permuted rows of token t in lanes 0..k-1 (others: 0) and publish the maps; with
+// gate_perm, also each row's gate (gate_perm[row_map[t, j]] = gates[t, j]).
 __device__ __forceinline__ int resolve_row(const int32_t* ids, const int32_t* base,
                                            const int32_t* local_rank, int64_t t, int k, int E, int nblk,
-                                           int lane, int32_t* row_map, int32_t* src_token) {
+                                           int lane, int32_t* row_map, int32_t* src_token, const float* gates,
+                                           float* gate_perm) {
   int row = 0;
   if (lane < k) {
     int e = valid_id(ids[t * k + lane], E);
     row = base[static_cast<int64_t>(e) * nblk + t / kBT] + local_rank[t * k + lane];
     row_map[t * k + lane] = row;
     src_token[row] = static_cast<int32_t>(t);
+    if (gate_perm) gate_perm[row] = gates[t * k + lane];
   }
   return row;
 }
@@ -122,11 +125,12 @@ __device__ __forceinline__ int resolve_row(const int32_t* ids, const int32_t* ba
 __global__ __launch_bounds__(kScatterThreads) void perm_scatter_copy_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ ids, const int32_t* __restrict__ base,
     const int32_t* __restrict__ local_rank, int64_t T, int row_vecs, int k, int E, int nblk,
-    uint4* __restrict__ x_perm, int32_t* __restrict__ row_map, int32_t* __restrict__ src_token) {
+    uint4* __restrict__ x_perm, int32_t* __restrict__ row_map, int32_t* __restrict__ src_token,
+    const float* __restrict__ gates, float* __restrict__ gate_perm) {
   const int lane = threadIdx.x % kWave;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + threadIdx.x / kWave;
   if (t >= T) return;
-  int row = resolve_row(ids, base, local_rank, t, k, E, nblk, lane, row_map, src_token);
+  int row = resolve_row(ids, base, local_rank, t, k, E, nblk, lane, row_map, src_token, gates, gate_perm);
   if (!x_perm) return;
   const uint4* src = x + t * row_vecs;
   // four 16-byte loads in flight per lane before their k stores each
@@ -184,11 +188,11 @@ __global__ __launch_bounds__(kScatterThreads) void perm_scatter_fp8_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ ids, const int32_t* __restrict__ base,
     const int32_t* __restrict__ local_rank, int64_t T, int H, int k, int E, int nblk,
     uint2* __restrict__ x_perm, float* __restrict__ scales, int32_t* __restrict__ row_map,
-    int32_t* __restrict__ src_token) {
+    int32_t* __restrict__ src_token, const float* __restrict__ gates, float* __restrict__ gate_perm) {
   const int lane = threadIdx.x % kWave;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + threadIdx.x / kWave;
   if (t >= T) return;
-  int row = resolve_row(ids, base, local_rank, t, k, E, nblk, lane, row_map, src_token);
+  int row = resolve_row(ids, base, local_rank, t, k, E, nblk, lane, row_map, src_token, gates, gate_perm);
   if (!x_perm) return;
   const int row_vecs = H / 8;
   const int nsb = H / 128;
@@ -262,7 +266,8 @@ size_t permute_scratch_bytes(int64_t T, int E, int k) {
 hipError_t launch_permute(const void* x, int x_dt, const int32_t* ids, int64_t T, int H, int E, int k,
                           void* x_perm, int perm_dt, float* x_perm_scales, int32_t* row_map,
                           int32_t* src_token, int32_t* counts, int32_t* offsets, void* scratch,
-                          hipStream_t stream) {
+                          hipStream_t stream, const float* gates, float* gate_perm) {
+  if ((gates == nullptr) != (gate_perm == nullptr)) return hipErrorInvalidValue;
   const int nblk = static_cast<int>(ceil_div(T, kBT));
   int32_t* blk = static_cast<int32_t*>(scratch);
   size_t a = static_cast<size_t>(E) * nblk * sizeof(int32_t);
@@ -277,13 +282,13 @@ hipError_t launch_permute(const void* x, int x_dt, const int32_t* ids, int64_t T
   if (perm_dt == 2) {
     hipLaunchKernelGGL(perm_scatter_fp8_kernel, grid, dim3(kScatterThreads), 0, stream,
                        static_cast<const uint4*>(x), ids, blk, local_rank, T, H, k, E, nblk,
-                       static_cast<uint2*>(x_perm), x_perm_scales, row_map, src_token);
+                       static_cast<uint2*>(x_perm), x_perm_scales, row_map, src_token, gates, gate_perm);
   } else {
     const int elt = (x_dt == 0) ? 4 : 2;
     const int row_vecs = H * elt / 16;
     hipLaunchKernelGGL(perm_scatter_copy_kernel, grid, dim3(kScatterThreads), 0, stream,
                        static_cast<const uint4*>(x), ids, blk, local_rank, T, row_vecs, k, E, nblk,
-                       static_cast<uint4*>(x_perm), row_map, src_token);
+                       static_cast<uint4*>(x_perm), row_map, src_token, gates, gate_perm);
   }
   return hipGetLastError();
 }

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     for s in range(6):
         assert L.moe_status_str(s).startswith(b"MOE_")
 
@@ -123,12 +123,20 @@ def _layer(**over):
 
 
 @pytest.mark.parametrize("over", [dict(k=9), dict(w_dt=0), dict(x_dt=2), dict(F=100), dict(Fs=256),
-                                  dict(w_dt=2), dict(w1=None), dict(score=3), dict(Fs=-1)])
+                                  dict(w_dt=2), dict(w1=None), dict(score=3), dict(Fs=-1), dict(gate_in_expert=2)])
 def test_forward_rejects_bad_layers(over):
     L = _lib.lib()
     lay = _layer(**over)
     assert L.moe_workspace_size(ctypes.byref(lay), 64) == 0
     assert L.moe_forward(ctypes.byref(lay), P, 64, P, None, P, 1 << 30, None) == INVALID
+
+
+def test_gate_in_expert_needs_a_per_row_gate_buffer():
+    """Folding the gate into the experts carves one fp32 gate per permuted row from the workspace."""
+    L = _lib.lib()
+    plain = L.moe_workspace_size(ctypes.byref(_layer()), 64)
+    folded = L.moe_workspace_size(ctypes.byref(_layer(gate_in_expert=1)), 64)
+    assert folded - plain == 64 * 2 * 4 + (256 - 64 * 2 * 4 % 256) % 256
 
 
 def test_forward_workspace_checks():
