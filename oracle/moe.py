@@ -33,6 +33,11 @@ R6 the shared expert has gate 1 and is added after the routed sum.
 R7 in FP8 mode the oracle runs on the dequantised operands (x quantised per
    token in 1x128 blocks, weights given as 128x128-block codes + scales) and
    keeps the SwiGLU activation h unrounded.
+R8 in MXFP4 mode (oracle/mxfp4.py) both operands of both expert GEMMs are MXFP4:
+   x quantised per token in 1x32 blocks, weights given as 32-element-block codes
+   + E8M0 scales (dequantised by the caller), and the SwiGLU activation h
+   quantised per row in 1x32 blocks before the second GEMM (the operand the
+   second GEMM takes is MXFP4 too); the quantisation decision is taken in fp32.
 
 No stage here is blocked, fused or reordered beyond what its definition states;
 numpy matmul / argsort / bincount are the only library steps.
@@ -45,7 +50,7 @@ import math
 
 import numpy as np
 
-from . import e4m3
+from . import e4m3, mxfp4
 
 SOFTMAX = "softmax"
 SIGMOID = "sigmoid"
@@ -155,11 +160,12 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def swiglu_expert(rows: np.ndarray, w1: np.ndarray, w2: np.ndarray) -> np.ndarray:
+def swiglu_expert(rows: np.ndarray, w1: np.ndarray, w2: np.ndarray, h_quant=None) -> np.ndarray:
     """One SwiGLU expert on a block of rows, float64 (reading R5).
 
     u = rows @ W1 with W1 [H, 2F]; h = SiLU(u[:, :F]) * u[:, F:]; out = h @ W2 with W2 [F, H].
-    h is not rounded.
+    h is not rounded, except by ``h_quant`` when given (MXFP4 mode, reading R8: the second GEMM's
+    operand is h quantised per row).
     """
     r64 = np.asarray(rows, dtype=np.float64)
     w1 = np.asarray(w1, dtype=np.float64)
@@ -169,6 +175,8 @@ def swiglu_expert(rows: np.ndarray, w1: np.ndarray, w2: np.ndarray) -> np.ndarra
         raise ValueError(f"W1 has {w1.shape[1]} columns, expected 2F = {2 * F}")
     u = r64 @ w1
     h = silu(u[:, :F]) * u[:, F:]
+    if h_quant is not None:
+        h = h_quant(h)
     return h @ w2
 
 
@@ -179,12 +187,12 @@ def swiglu_hidden(rows: np.ndarray, w1: np.ndarray) -> np.ndarray:
     return silu(u[:, :F]) * u[:, F:]
 
 
-def grouped_experts(x_perm: np.ndarray, offsets: np.ndarray, w1_of, w2_of) -> np.ndarray:
+def grouped_experts(x_perm: np.ndarray, offsets: np.ndarray, w1_of, w2_of, h_quant=None) -> np.ndarray:
     """Apply expert e to rows offsets[e]:offsets[e+1] of ``x_perm`` for every e (the grouped GEMM).
 
     ``w1_of(e)`` / ``w2_of(e)`` return expert e's [H, 2F] / [F, H] weights (so a caller
-    can widen one expert at a time); experts with no rows are skipped.
-    Returns float64 [R, H].
+    can widen one expert at a time); experts with no rows are skipped; ``h_quant`` as for
+    swiglu_expert.  Returns float64 [R, H].
     """
     x_perm = np.asarray(x_perm)
     R = x_perm.shape[0]
@@ -193,7 +201,7 @@ def grouped_experts(x_perm: np.ndarray, offsets: np.ndarray, w1_of, w2_of) -> np
         a, b = int(offsets[e]), int(offsets[e + 1])
         if b == a:
             continue
-        out = swiglu_expert(x_perm[a:b], w1_of(e), w2_of(e))
+        out = swiglu_expert(x_perm[a:b], w1_of(e), w2_of(e), h_quant)
         if y is None:
             y = np.zeros((R, out.shape[1]), dtype=np.float64)
         y[a:b] = out
@@ -225,12 +233,12 @@ def quantised_input(x: np.ndarray) -> np.ndarray:
 
 
 def forward(x, w_router, w1_of, w2_of, *, E, k, score, norm, bias=None, shared_w1=None,
-            shared_w2=None, fp8=False, logits=None):
+            shared_w2=None, fp8=False, mxfp4_mode=False, logits=None):
     """The whole layer, stage by stage; returns a dict of every intermediate.
 
     ``x`` [T, H] float array; ``w_router`` [H, E]; ``w1_of(e)``/``w2_of(e)`` give expert
-    weights (dequantised values in FP8 mode); ``shared_w1``/``shared_w2`` the shared
-    expert or None.  If ``logits`` is given (fp32 [T, E]) routing is driven from those
+    weights (dequantised values in FP8 / MXFP4 mode); ``shared_w1``/``shared_w2`` the shared
+    expert or None.  ``fp8``: reading R7; ``mxfp4_mode``: reading R8.  If ``logits`` is given (fp32 [T, E]) routing is driven from those
     logits instead of recomputing them -- this is how the GPU's own logits are checked
     bit-exactly for ids / counts / offsets / permutation.
     """
@@ -245,13 +253,21 @@ def forward(x, w_router, w1_of, w2_of, *, E, k, score, norm, bias=None, shared_w
     out["counts"] = expert_counts(out["ids"], E)
     out["offsets"] = expert_offsets(out["counts"])
     out["row_map"], out["src_token"] = permutation(out["ids"])
-    xq = quantised_input(x) if fp8 else np.asarray(x, dtype=np.float64)
+    if fp8 and mxfp4_mode:
+        raise ValueError("one low-precision mode at a time")
+    h_quant = mxfp4.quantised if mxfp4_mode else None
+    if fp8:
+        xq = quantised_input(x)
+    elif mxfp4_mode:
+        xq = mxfp4.quantised(x)
+    else:
+        xq = np.asarray(x, dtype=np.float64)
     out["x_hat"] = xq
     out["x_perm"] = permute_rows(xq, out["src_token"])
-    out["y_perm"] = grouped_experts(out["x_perm"], out["offsets"], w1_of, w2_of)
+    out["y_perm"] = grouped_experts(out["x_perm"], out["offsets"], w1_of, w2_of, h_quant)
     shared = None
     if shared_w1 is not None:
-        shared = swiglu_expert(xq, shared_w1, shared_w2)
+        shared = swiglu_expert(xq, shared_w1, shared_w2, h_quant)
     out["shared"] = shared
     out["y"] = combine(out["y_perm"], out["row_map"], out["gates"], shared)
     return out

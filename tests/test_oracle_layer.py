@@ -140,7 +140,7 @@ def test_driving_routing_from_given_logits():
 # ----------------------------------------------------------------------------------------------
 # Planted mistakes: a plausible bug anywhere in the staged oracle must fail a pin.  Each mutation is
 # monkeypatched into the oracle on the CPU and the brute-force comparison must then disagree.
-def _swap_halves(rows, w1, w2):
+def _swap_halves(rows, w1, w2, h_quant=None):
     F = w2.shape[0]
     w1 = np.asarray(w1)
     return _orig_swiglu(rows, np.concatenate([w1[:, F:], w1[:, :F]], axis=1), w2)
@@ -157,7 +157,7 @@ def _softmax_over_selected(l, i, s, n):
     return _orig_gates(sel, np.tile(np.arange(sel.shape[1]), (sel.shape[0], 1)), s, n)
 
 
-def _rows_reversed_in_w2(r, a, b):
+def _rows_reversed_in_w2(r, a, b, h_quant=None):
     return _orig_swiglu(r, a, np.asarray(b)[::-1])
 
 
