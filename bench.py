@@ -52,7 +52,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer fwd active TFLOPS + tokens/s at 1 GPU; % of MFMA / HBM peak"
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA by operand type
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}  # MI355X dense MFMA by operand type
 PEAK_BF16_TFLOPS = PEAK_TFLOPS["bf16"]
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 STAGES = ["route", "permute", "gemm1_swiglu", "gemm2", "shared_expert", "combine"]
@@ -207,22 +207,32 @@ def algorithmic(cfg, active_experts=None):
     """Useful FLOPs and the bytes each stage of the fused forward must move (unique HBM bytes).
 
     Activations in the config's dtype (bf16 2 B, fp32 4 B); weights and the permuted / hidden
-    rows of the e4m3 path 1 B plus one fp32 scale per 128 values (weights: per 128 x 128 block).
+    rows of the e4m3 path 1 B plus one fp32 scale per 128 values (weights: per 128 x 128 block);
+    of the MXFP4 path half a byte plus one E8M0 byte per 32 values.
     Only experts that received rows are streamed (``active_experts``, default all E).
     """
     T, H, E, k, F, Fs = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
     R = T * k
     Ea = E if active_experts is None else active_experts
     fp8 = cfg.w_dtype == "fp8"
+    fp4 = cfg.w_dtype == "mxfp4"
     a = 4 if cfg.act_dtype == "f32" else 2
-    rowb = (lambda n: n + n // 128 * 4) if fp8 else (lambda n: n * a)   # one row of n values
-    wbytes = (lambda K, N: K * N + (K // 128) * (N // 128) * 4) if fp8 else (lambda K, N: K * N * a)
+    if fp8:
+        rowb = lambda n: n + n // 128 * 4   # noqa: E731 -- one row of n values
+        wbytes = lambda K, N: K * N + (K // 128) * (N // 128) * 4  # noqa: E731
+    elif fp4:
+        rowb = lambda n: n // 2 + n // 32  # noqa: E731
+        wbytes = lambda K, N: K * N // 2 + K * N // 32  # noqa: E731
+    else:
+        rowb = lambda n: n * a  # noqa: E731
+        wbytes = lambda K, N: K * N * a  # noqa: E731
     sh = bool(Fs)
     return {
         "route": dict(flops=2 * T * H * E, bytes=T * H * a + H * E * 4 + R * 8 + (E * 4 if cfg.zipf_bias else 0)),
         # the fused forward writes no permuted copy: dispatch = ids -> maps (+ the e4m3 path's
         # per-token quantisation of x), and GEMM1 gathers the token rows it needs
-        "permute": dict(flops=0, bytes=R * 4 + R * 8 + (2 * E + 1) * 4 + ((T * H * a + T * rowb(H)) if fp8 else 0)),
+        "permute": dict(flops=0, bytes=R * 4 + R * 8 + (2 * E + 1) * 4 + ((T * H * a + T * rowb(H)) if fp8 or fp4
+                                                                          else 0)),
         "gemm1_swiglu": dict(flops=4 * R * H * F,
                              bytes=T * rowb(H) + R * 4 + Ea * wbytes(H, 2 * F) + R * rowb(F) + (E + 1) * 4),
         "gemm2": dict(flops=2 * R * F * H, bytes=R * rowb(F) + Ea * wbytes(F, H) + R * H * a + (E + 1) * 4),
@@ -259,19 +269,22 @@ def cpu_baseline(cfg, d, sample_tokens, min_seconds=10.0):
     apart and left out of the reported rate.
     """
     import torch
-    from oracle import e4m3, moe
+    from oracle import e4m3, moe, mxfp4
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     fp8 = cfg.w_dtype == "fp8"
+    fp4 = cfg.w_dtype == "mxfp4"
     copy_s = [0.0]
 
     def weight(w, scales):
         t0 = time.perf_counter()
         if fp8:
             out = e4m3.dequantise_blocks_128x128(w.view(torch.uint8).cpu().numpy(), scales.cpu().numpy())
+        elif fp4:  # stored [N, K/2] codes + [N, K/32] E8M0 -> the logical [K, N]
+            out = mxfp4.dequantise_packed(w.view(torch.uint8).cpu().numpy(), scales.view(torch.uint8).cpu().numpy()).T
         else:
             out = w.float().cpu().numpy()
         copy_s[0] += time.perf_counter() - t0
@@ -294,7 +307,7 @@ def cpu_baseline(cfg, d, sample_tokens, min_seconds=10.0):
         moe.forward(x, wr, lambda e: weight(d["w1"][e], None if d["w1_scales"] is None else d["w1_scales"][e]),
                     lambda e: weight(d["w2"][e], None if d["w2_scales"] is None else d["w2_scales"][e]),
                     E=cfg.E, k=cfg.k, score=cfg.score, norm=cfg.norm, bias=bias, shared_w1=sw1, shared_w2=sw2,
-                    fp8=fp8)
+                    fp8=fp8, mxfp4_mode=fp4)
         dt += time.perf_counter() - t0 - (copy_s[0] - c0)
         runs += 1
         print(f"[bench] cpu oracle run {runs}: {dt:.1f} s oracle time so far, {copy_s[0]:.1f} s weight "
@@ -839,7 +852,7 @@ def bench_forward(args, cfg, d, layer, torch, _lib, util, moe_gpu):
     ms_per_step = elapsed * 1e3 / K
     tokens_per_s = cfg.T * K / elapsed
     active_tflops = alg["active_flops"] / (ms_per_step * 1e-3) / 1e12
-    mm_dtype = "fp8" if cfg.w_dtype == "fp8" else cfg.act_dtype
+    mm_dtype = {"fp8": "fp8", "mxfp4": "fp4"}.get(cfg.w_dtype, cfg.act_dtype)
     peak_tf = PEAK_TFLOPS[mm_dtype]
 
     def stage_records(ms_lists):
@@ -866,6 +879,7 @@ def bench_forward(args, cfg, d, layer, torch, _lib, util, moe_gpu):
     g1_s = cold_avg["gemm1_swiglu"] * 1e-3
     mfma_bound = g1["flops"] / (peak_tf * 1e12) >= g1["bytes"] / (PEAK_HBM_GBS * 1e9)
     kernel = {"fp8": "gemm_fp8_kernel<swiglu> (grouped e4m3 GEMM1 + fused SwiGLU + 1x128 re-quantisation)",
+              "fp4": "gemm_fp4_kernel<128, true, false> (grouped MXFP4 GEMM1 + fused SwiGLU + 1x32 re-quantisation)",
               "bf16": f"gemm_bf16_kernel<{256 if cfg.T * cfg.k >= 192 * cfg.E else 128}, 2, true, false, 1> "
                       "(routed experts' grouped GEMM1 + fused SwiGLU)",
               "f32": "gemm_f32_kernel<swiglu> (grouped fp32 GEMM1 + fused SwiGLU)"}[mm_dtype]
@@ -875,7 +889,7 @@ def bench_forward(args, cfg, d, layer, torch, _lib, util, moe_gpu):
         achieved, peak, unit = g1["bytes"] / g1_s / 1e9, PEAK_HBM_GBS, "GB/s"
     roofline = {"kernel": kernel, "bound": "mfma" if mfma_bound else "hbm", "achieved": round(achieved, 1),
                 "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
-                "traffic": measured_traffic(args.workload, fp8=mm_dtype == "fp8"),
+                "traffic": measured_traffic(args.workload, fp8=mm_dtype == "fp8") if mm_dtype != "fp4" else None,
                 "flops_per_launch": g1["flops"], "algorithmic_bytes_per_launch": g1["bytes"],
                 "avg_launch_us": round(cold_avg["gemm1_swiglu"] * 1e3, 2),
                 "timing": f"HIP events around the launch on the compute stream, mean of {K} cold steps "
@@ -915,7 +929,7 @@ def bench_forward(args, cfg, d, layer, torch, _lib, util, moe_gpu):
                          "input_sha256": input_hashes(d, cfg), "seed": 0}
     if not args.no_cpu_baseline:
         default_sample = {"mixtral_8x7b": 4096, "qwen3_235b": 256, "deepseek_v3": 128,
-                          "deepseek_v3_fp8_zipf": 128, "tiny_fp32": 256}
+                          "deepseek_v3_fp8_zipf": 128, "deepseek_v3_mxfp4": 128, "tiny_fp32": 256}
         out["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_sample_tokens or default_sample[args.workload])
     print(json.dumps(out), flush=True)
 
@@ -927,7 +941,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="layer shape: deepseek_v3 (default), mixtral_8x7b, qwen3_235b, deepseek_v3_fp8_zipf, "
-                         "tiny_fp32")
+                         "deepseek_v3_mxfp4, tiny_fp32")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None,
                     help="tokens in the CPU oracle sample (default: about 10-30 s of oracle work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

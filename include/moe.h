@@ -60,7 +60,10 @@ typedef enum {
 typedef enum {
   MOE_F32 = 0,
   MOE_BF16 = 1,
-  MOE_FP8_E4M3 = 2 /* OCP E4M3 without infinities ("e4m3fn"), max 448 */
+  MOE_FP8_E4M3 = 2, /* OCP E4M3 without infinities ("e4m3fn"), max 448 */
+  MOE_MXFP4 = 3     /* OCP MXFP4: FP4 E2M1 elements (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6), two per
+                       byte (element 2i in the low nibble), one E8M0 scale byte (2^(e - 127)) per 32
+                       consecutive elements along the contraction; expert GEMMs only */
 } moe_dtype;
 
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
@@ -104,13 +107,17 @@ moe_status moe_route(const void* x, moe_dtype x_dt, const float* w_router, const
  *                  each row in 1x128 blocks: scale = the smallest power of two 2^q with
  *                  448 * 2^q >= amax, q in [-127, 127] (1 for an all-zero block),
  *                  code = e4m3_rne(clamp(x / scale, +-448)); scales go to
- *   x_perm_scales  [T*k, H/128] fp32 out (FP8 only, else ignored).
+ *   x_perm_scales  [T*k, H/128] fp32 out (FP8 only, else ignored).  perm_dt = MOE_MXFP4 (x_dt =
+ *                  MOE_BF16, H % 32 == 0) quantises each row in 1x32 blocks: scale = the smallest
+ *                  power of two 2^q with 6 * 2^q >= amax, q in [-127, 127] (2^0 for an all-zero
+ *                  block), element = the nearest E2M1 value of x / scale (ties to the even-mantissa
+ *                  code); x_perm [T*k, H/2] bytes, x_perm_scales [T*k, H/32] E8M0 bytes.
  *   x_perm may be NULL to build only the maps.
  *   workspace      device scratch of at least moe_permute_workspace_size(T, E, k) bytes.
  * ------------------------------------------------------------------------------------- */
 size_t moe_permute_workspace_size(int64_t T, int32_t E, int32_t k);
 moe_status moe_permute(const void* x, moe_dtype x_dt, const int32_t* topk_ids, int64_t T, int32_t H,
-                       int32_t E, int32_t k, void* x_perm, moe_dtype perm_dt, float* x_perm_scales,
+                       int32_t E, int32_t k, void* x_perm, moe_dtype perm_dt, void* x_perm_scales,
                        int32_t* row_map, int32_t* src_token, int32_t* expert_counts,
                        int32_t* expert_offsets, void* workspace, size_t workspace_bytes,
                        moe_stream_t stream);
@@ -133,15 +140,21 @@ moe_status moe_permute(const void* x, moe_dtype x_dt, const int32_t* topk_ids, i
  *        any positive finite fp32 values; when all of them are powers of two (as the ones
  *        moe_permute writes) the scaled MFMA applies them exactly as exponents, otherwise a
  *        slower path multiplies them in fp32 (chosen on the device, no host sync).
- * Sizes: bf16: H a multiple of 64 and F of 128; e4m3: both multiples of 128; fp32: both of 32.
+ *   dt = MOE_MXFP4: both operands of both GEMMs 4-bit, every matrix stored contraction-contiguous
+ *        with one E8M0 byte per 32 elements: x_perm [rows, H/2] + x_perm_scales [rows, H/32];
+ *        W1[e] (the logical [H, 2F] above) as w1 [E, 2F, H/2] + w1_scales [E, 2F, H/32]; W2[e]
+ *        (logical [F, H]) as w2 [E, H, F/2] + w2_scales [E, H, F/32]; h is re-quantised to MXFP4
+ *        in 1x32 blocks inside the path (the moe_permute rule); y_perm bf16 or fp32.
+ * Sizes: bf16: H a multiple of 64 and F of 128; e4m3: both multiples of 128; MXFP4: both of 256;
+ * fp32: both of 32.
  * workspace: at least moe_grouped_swiglu_workspace_size(rows, F, dt) bytes (holds h).
  * Rows beyond offsets[E] are not written.
  * ------------------------------------------------------------------------------------- */
 size_t moe_grouped_swiglu_workspace_size(int64_t rows, int32_t F, moe_dtype dt);
-moe_status moe_grouped_swiglu(const void* x_perm, const float* x_perm_scales, moe_dtype dt,
+moe_status moe_grouped_swiglu(const void* x_perm, const void* x_perm_scales, moe_dtype dt,
                               const int32_t* expert_offsets, int64_t rows, int32_t E, int32_t H,
-                              int32_t F, const void* w1, const float* w1_scales, const void* w2,
-                              const float* w2_scales, void* y_perm, moe_dtype out_dt,
+                              int32_t F, const void* w1, const void* w1_scales, const void* w2,
+                              const void* w2_scales, void* y_perm, moe_dtype out_dt,
                               void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
@@ -166,7 +179,9 @@ typedef struct {
   int32_t H, E, k, F;
   int32_t Fs;           /* shared expert hidden size, 0 = no shared expert                */
   moe_dtype x_dt;       /* activations x and y: MOE_F32 or MOE_BF16                      */
-  moe_dtype w_dt;       /* expert weights: MOE_F32 (x_dt F32), MOE_BF16, MOE_FP8_E4M3    */
+  moe_dtype w_dt;       /* expert weights: MOE_F32 (x_dt F32), MOE_BF16, MOE_FP8_E4M3,   */
+                        /* MOE_MXFP4 (stored as in moe_grouped_swiglu; shared: ws1       */
+                        /* [2Fs, H/2] + [2Fs, H/32], ws2 [H, Fs/2] + [H, Fs/32])          */
   moe_dtype out_dt;     /* y: MOE_F32 or MOE_BF16                                        */
   moe_score score;
   int32_t norm_topk;
@@ -176,7 +191,8 @@ typedef struct {
   const void* w2;        /* [E, F, H]                                                    */
   const void* ws1;       /* [H, 2Fs] or NULL                                             */
   const void* ws2;       /* [Fs, H] or NULL                                              */
-  const float* w1_scales, *w2_scales, *ws1_scales, *ws2_scales; /* FP8 only, else NULL  */
+  const void* w1_scales, *w2_scales, *ws1_scales, *ws2_scales;  /* FP8: fp32; MXFP4: E8M0 */
+                                                                 /* bytes; else NULL       */
   int32_t gate_in_expert; /* 0: combine weights the expert rows by their gates.  1: the gate  */
                           /* is folded into the experts: the first GEMM's SwiGLU epilogue     */
                           /* multiplies each permuted row's h by its gate before rounding, so */
@@ -205,7 +221,7 @@ typedef struct {
   int32_t* row_map;
   int32_t* src_token;
   void* x_perm;
-  float* x_perm_scales;
+  void* x_perm_scales;
   void* y_perm;
   void* stage_events[MOE_NUM_STAGE_EVENTS];
 } moe_debug;
@@ -230,7 +246,7 @@ moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, co
  *            dx += dlogits W_r^T, dW_r = x^T dlogits
  *   shared   the expert rule on all T rows with gate 1
  *   L        the layer as given to moe_forward; w_dt = x_dt = MOE_F32 or MOE_BF16
- *            (MOE_FP8_E4M3 returns MOE_ERR_UNSUPPORTED).  out_dt is not used.
+ *            (MOE_FP8_E4M3 and MOE_MXFP4 return MOE_ERR_UNSUPPORTED).  out_dt is not used.
  *   x        [T, H] x_dt, the forward's input
  *   dy       [T, H] x_dt
  *   r        the forward's routing, as written through moe_debug: logits [T, E] fp32,

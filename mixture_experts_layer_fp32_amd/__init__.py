@@ -23,7 +23,16 @@ from ._lib import MoeError  # noqa: F401
 __all__ = ["route", "permute", "grouped_swiglu", "unpermute_combine", "forward", "forward_static", "Layer",
            "workspace_size", "MoeError"]
 
-_DT = {torch.float32: _lib.MOE_F32, torch.bfloat16: _lib.MOE_BF16, torch.float8_e4m3fn: _lib.MOE_FP8_E4M3}
+_DT = {torch.float32: _lib.MOE_F32, torch.bfloat16: _lib.MOE_BF16, torch.float8_e4m3fn: _lib.MOE_FP8_E4M3,
+       torch.float4_e2m1fn_x2: _lib.MOE_MXFP4}
+FP4 = torch.float4_e2m1fn_x2  # two E2M1 elements per byte (MXFP4 codes)
+E8M0 = torch.float8_e8m0fnu   # MXFP4 block scales
+
+
+def _bytes(shape, dtype, device):
+    """A tensor of a byte-sized dtype, allocated as uint8 (torch has no fill kernels for the 4-bit and
+    E8M0 dtypes)."""
+    return torch.empty(shape, dtype=torch.uint8, device=device).view(dtype)
 _SCORE = {"softmax": _lib.MOE_SOFTMAX, "sigmoid": _lib.MOE_SIGMOID}
 
 
@@ -75,13 +84,16 @@ def permute(x, ids, E, perm_dtype=None, with_rows=True):
     dev = x.device
     perm_dtype = perm_dtype or x.dtype
     R = T * k
+    fp4 = perm_dtype == FP4
     out = {
         "row_map": torch.empty(T, k, dtype=torch.int32, device=dev),
         "src_token": torch.empty(R, dtype=torch.int32, device=dev),
         "counts": torch.empty(E, dtype=torch.int32, device=dev),
         "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
-        "x_perm": torch.empty(R, H, dtype=perm_dtype, device=dev) if with_rows else None,
-        "x_perm_scales": (torch.empty(R, H // 128, dtype=torch.float32, device=dev)
+        "x_perm": (None if not with_rows else _bytes((R, H // 2), FP4, dev) if fp4
+                   else torch.empty(R, H, dtype=perm_dtype, device=dev)),
+        "x_perm_scales": (_bytes((R, H // 32), E8M0, dev) if with_rows and fp4 else
+                          torch.empty(R, H // 128, dtype=torch.float32, device=dev)
                           if with_rows and perm_dtype == torch.float8_e4m3fn else None),
     }
     L = _lib.lib()
@@ -99,7 +111,11 @@ def grouped_swiglu(x_perm, offsets, w1, w2, x_perm_scales=None, w1_scales=None, 
     """All experts' SwiGLU MLPs over their contiguous rows (one grouped GEMM per matrix).  Returns y_perm."""
     _need_gpu(x_perm, offsets, w1, w2, x_perm_scales, w1_scales, w2_scales)
     rows, H = x_perm.shape
-    E, _, F2 = w1.shape
+    if x_perm.dtype == FP4:  # contraction-contiguous MXFP4: x_perm [rows, H/2], w1 [E, 2F, H/2]
+        H *= 2
+        E, F2, _ = w1.shape
+    else:
+        E, _, F2 = w1.shape
     F = F2 // 2
     dt = _DT[x_perm.dtype]
     if out_dtype is None:
@@ -157,8 +173,12 @@ class Layer:
 
     def c_struct(self, x_dtype) -> _lib.MoeLayerC:
         H, E = self.w_router.shape
-        F = self.w2.shape[1]
-        Fs = 0 if self.ws2 is None else self.ws2.shape[0]
+        if self.w1.dtype == FP4:  # w2 [E, H, F/2], ws2 [H, Fs/2]
+            F = 2 * self.w2.shape[2]
+            Fs = 0 if self.ws2 is None else 2 * self.ws2.shape[1]
+        else:
+            F = self.w2.shape[1]
+            Fs = 0 if self.ws2 is None else self.ws2.shape[0]
         out_dt = self.out_dtype or x_dtype
         return _lib.MoeLayerC(
             H=H, E=E, k=self.k, F=F, Fs=Fs, x_dt=_DT[x_dtype], w_dt=_DT[self.w1.dtype], out_dt=_DT[out_dt],
@@ -200,6 +220,7 @@ def forward(x, layer: Layer, debug: bool = False, workspace=None):
     if debug:
         R = T * k
         fp8 = layer.w1.dtype == torch.float8_e4m3fn
+        fp4 = layer.w1.dtype == FP4
         dbg = {
             "logits": torch.empty(T, E, dtype=torch.float32, device=dev),
             "topk_ids": torch.empty(T, k, dtype=torch.int32, device=dev),
@@ -208,8 +229,9 @@ def forward(x, layer: Layer, debug: bool = False, workspace=None):
             "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
             "row_map": torch.empty(T, k, dtype=torch.int32, device=dev),
             "src_token": torch.empty(R, dtype=torch.int32, device=dev),
-            "x_perm": torch.empty(R, H, dtype=layer.w1.dtype, device=dev),
-            "x_perm_scales": torch.empty(R, H // 128, dtype=torch.float32, device=dev) if fp8 else None,
+            "x_perm": _bytes((R, H // 2), FP4, dev) if fp4 else torch.empty(R, H, dtype=layer.w1.dtype, device=dev),
+            "x_perm_scales": (torch.empty(R, H // 128, dtype=torch.float32, device=dev) if fp8 else
+                              _bytes((R, H // 32), E8M0, dev) if fp4 else None),
             "y_perm": torch.empty(R, H, dtype=x.dtype, device=dev),
         }
         dbg_c = _lib.MoeDebugC(**{name: (None if t is None else t.data_ptr()) for name, t in dbg.items()})

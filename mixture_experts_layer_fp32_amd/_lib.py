@@ -12,7 +12,7 @@ _vp, _i32, _i64, _sz = _c.c_void_p, _c.c_int32, _c.c_int64, _c.c_size_t
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_TOO_LARGE = range(6)
 MOE_STATIC_SCRATCH_BYTES = 64 << 20
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 
 # every function the header declares, with its argument and result types

@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["api.hip", "route.hip", "permute.hip", "gemm.hip", "gemm_fp8.hip", "combine.hip", "backward.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "gemm.hip", "gemm_fp8.hip", "gemm_fp4.hip", "combine.hip",
+           "backward.hip"]
 BENCH_UTIL_SOURCE = "bench_util.hip"
 BENCH_UTIL_NAME = "libmoe_bench_util.so"
 BENCH_UTIL_PATH = os.path.join(PKG, BENCH_UTIL_NAME)

@@ -39,12 +39,15 @@ bool act_dtype_ok(moe_dtype d) { return d == MOE_F32 || d == MOE_BF16; }
 
 size_t elt_bytes(moe_dtype d) { return d == MOE_F32 ? 4 : (d == MOE_BF16 ? 2 : 1); }
 
+bool low_precision(moe_dtype d) { return d == MOE_FP8_E4M3 || d == MOE_MXFP4; }
+
 // grouped-GEMM shape rules per dtype
 moe_status check_gemm_shape(moe_dtype dt, int32_t H, int32_t F) {
   if (H < 1 || F < 1) return MOE_ERR_INVALID_ARG;
   if (dt == MOE_F32) return (H % 32 == 0 && F % 32 == 0) ? MOE_OK : MOE_ERR_INVALID_ARG;
   if (dt == MOE_BF16) return (H % 64 == 0 && F % 128 == 0) ? MOE_OK : MOE_ERR_INVALID_ARG;
   if (dt == MOE_FP8_E4M3) return (H % 128 == 0 && F % 128 == 0) ? MOE_OK : MOE_ERR_INVALID_ARG;
+  if (dt == MOE_MXFP4) return (H % 256 == 0 && F % 256 == 0) ? MOE_OK : MOE_ERR_INVALID_ARG;
   return MOE_ERR_INVALID_ARG;
 }
 
@@ -106,7 +109,7 @@ size_t moe_permute_workspace_size(int64_t T, int32_t E, int32_t k) {
 }
 
 moe_status moe_permute(const void* x, moe_dtype x_dt, const int32_t* topk_ids, int64_t T, int32_t H,
-                       int32_t E, int32_t k, void* x_perm, moe_dtype perm_dt, float* x_perm_scales,
+                       int32_t E, int32_t k, void* x_perm, moe_dtype perm_dt, void* x_perm_scales,
                        int32_t* row_map, int32_t* src_token, int32_t* expert_counts,
                        int32_t* expert_offsets, void* workspace, size_t workspace_bytes,
                        moe_stream_t stream) {
@@ -118,6 +121,8 @@ moe_status moe_permute(const void* x, moe_dtype x_dt, const int32_t* topk_ids, i
     if (!x) return MOE_ERR_INVALID_ARG;
     if (perm_dt == MOE_FP8_E4M3) {
       if (x_dt != MOE_BF16 || H % 128 != 0 || !x_perm_scales) return MOE_ERR_INVALID_ARG;
+    } else if (perm_dt == MOE_MXFP4) {
+      if (x_dt != MOE_BF16 || H % 32 != 0 || !x_perm_scales) return MOE_ERR_INVALID_ARG;
     } else if (perm_dt != x_dt) {
       return MOE_ERR_INVALID_ARG;
     }
@@ -135,10 +140,10 @@ size_t moe_grouped_swiglu_workspace_size(int64_t rows, int32_t F, moe_dtype dt) 
   return align_up(moe::grouped_swiglu_scratch_bytes(rows, F, dt));
 }
 
-moe_status moe_grouped_swiglu(const void* x_perm, const float* x_perm_scales, moe_dtype dt,
+moe_status moe_grouped_swiglu(const void* x_perm, const void* x_perm_scales, moe_dtype dt,
                               const int32_t* expert_offsets, int64_t rows, int32_t E, int32_t H, int32_t F,
-                              const void* w1, const float* w1_scales, const void* w2,
-                              const float* w2_scales, void* y_perm, moe_dtype out_dt, void* workspace,
+                              const void* w1, const void* w1_scales, const void* w2,
+                              const void* w2_scales, void* y_perm, moe_dtype out_dt, void* workspace,
                               size_t workspace_bytes, moe_stream_t stream) {
   if (rows < 0 || rows >= (int64_t{1} << 31) || E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
   moe_status st = check_gemm_shape(dt, H, F);
@@ -147,7 +152,7 @@ moe_status moe_grouped_swiglu(const void* x_perm, const float* x_perm_scales, mo
   if (!act_dtype_ok(out_dt)) return MOE_ERR_INVALID_ARG;
   if (rows == 0) return MOE_OK;  // nothing to do; empty tensors may carry null pointers
   if (!x_perm || !expert_offsets || !w1 || !w2 || !y_perm) return MOE_ERR_INVALID_ARG;
-  if (dt == MOE_FP8_E4M3 && (!x_perm_scales || !w1_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
+  if (low_precision(dt) && (!x_perm_scales || !w1_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
   if (workspace_bytes < moe_grouped_swiglu_workspace_size(rows, F, dt) || !workspace)
     return MOE_ERR_WORKSPACE;
   return from_hip(moe::launch_grouped_swiglu(x_perm, x_perm_scales, dt, expert_offsets, rows, E, H, F,
@@ -186,7 +191,7 @@ moe_status validate_layer(const moe_layer* L) {
   if (L->gate_in_expert != 0 && L->gate_in_expert != 1) return MOE_ERR_INVALID_ARG;
   if (L->w_dt == MOE_F32 && (L->x_dt != MOE_F32)) return MOE_ERR_INVALID_ARG;
   if (L->w_dt == MOE_BF16 && L->x_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (L->w_dt == MOE_FP8_E4M3 && L->x_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (low_precision(L->w_dt) && L->x_dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   st = check_gemm_shape(L->w_dt, L->H, L->F);
   if (st != MOE_OK) return st;
   if (L->Fs < 0) return MOE_ERR_INVALID_ARG;
@@ -196,19 +201,19 @@ moe_status validate_layer(const moe_layer* L) {
     if (!L->ws1 || !L->ws2) return MOE_ERR_INVALID_ARG;
   }
   if (!L->w_router || !L->w1 || !L->w2) return MOE_ERR_INVALID_ARG;
-  if (L->w_dt == MOE_FP8_E4M3 &&
+  if (low_precision(L->w_dt) &&
       (!L->w1_scales || !L->w2_scales || (L->Fs > 0 && (!L->ws1_scales || !L->ws2_scales))))
     return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
 // The first grouped GEMM gathers its rows straight from x (or from x quantised once per token
-// in the e4m3 path) through src_token, so the permuted copy x_perm exists only when the caller
-// asks for it through moe_debug.
+// in the e4m3 / MXFP4 paths) through src_token, so the permuted copy x_perm exists only when the
+// caller asks for it through moe_debug.
 ForwardPlan plan(const moe_layer* L, int64_t T, void* ws, const moe_debug* dbg) {
   const int64_t R = T * L->k;
   const size_t xe = elt_bytes(L->x_dt);
-  const bool fp8 = L->w_dt == MOE_FP8_E4M3;
+  const bool fp8 = L->w_dt == MOE_FP8_E4M3, fp4 = L->w_dt == MOE_MXFP4;
   Carve c(ws);
   ForwardPlan p{};
   auto pick = [&](void* user, size_t n) { void* w = c.take(n); return user ? user : w; };
@@ -223,9 +228,9 @@ ForwardPlan plan(const moe_layer* L, int64_t T, void* ws, const moe_debug* dbg) 
   p.perm_ws = c.take(moe::permute_scratch_bytes(T, L->E, L->k));
   // debug-only outputs with no workspace share (the layout must not depend on dbg)
   p.x_perm = dbg ? dbg->x_perm : nullptr;
-  p.x_scales = (fp8 && p.x_perm) ? dbg->x_perm_scales : nullptr;
-  p.xq = fp8 ? c.take(T * L->H) : nullptr;
-  p.xq_scales = fp8 ? c.take(T * (L->H / 128) * 4) : nullptr;
+  p.x_scales = (low_precision(L->w_dt) && p.x_perm) ? dbg->x_perm_scales : nullptr;
+  p.xq = fp8 ? c.take(T * L->H) : (fp4 ? c.take(T * (L->H / 2)) : nullptr);
+  p.xq_scales = fp8 ? c.take(T * (L->H / 128) * 4) : (fp4 ? c.take(T * (L->H / 32)) : nullptr);
   p.gemm_ws = c.take(moe::grouped_swiglu_scratch_bytes(R, L->F, L->w_dt));
   p.y_perm = pick(dbg ? dbg->y_perm : nullptr, R * L->H * xe);
   if (L->Fs > 0) {
@@ -252,14 +257,14 @@ moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, co
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;  // nothing to do; empty tensors may carry null pointers
   if (!x || !y || !aligned16(x) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
-  if (dbg && dbg->x_perm && (!aligned16(dbg->x_perm) || (L->w_dt == MOE_FP8_E4M3 && !dbg->x_perm_scales)))
-    return MOE_ERR_INVALID_ARG;  // e4m3 rows come with their scales
+  if (dbg && dbg->x_perm && (!aligned16(dbg->x_perm) || (low_precision(L->w_dt) && !dbg->x_perm_scales)))
+    return MOE_ERR_INVALID_ARG;  // e4m3 / MXFP4 rows come with their scales
   const size_t need = plan(L, T, nullptr, nullptr).bytes;
   if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
   ForwardPlan p = plan(L, T, workspace, dbg);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t R = T * L->k;
-  const bool fp8 = L->w_dt == MOE_FP8_E4M3;
+  const bool fp8 = L->w_dt == MOE_FP8_E4M3, fp4 = L->w_dt == MOE_MXFP4;
   auto ev = [&](int i) -> hipEvent_t { return dbg ? static_cast<hipEvent_t>(dbg->stage_events[i]) : nullptr; };
   auto mark = [&](int i) -> hipError_t { return ev(i) ? hipEventRecord(ev(i), s) : hipSuccess; };
 
@@ -274,26 +279,29 @@ moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, co
   // SwiGLU epilogue scales h by it, and combine sums the k rows unweighted
   float* gate_perm = static_cast<float*>(p.gate_perm);
   e = moe::launch_permute(x, L->x_dt, static_cast<int32_t*>(p.ids), T, L->H, L->E, L->k, p.x_perm,
-                          L->w_dt, static_cast<float*>(p.x_scales), static_cast<int32_t*>(p.row_map),
+                          L->w_dt, p.x_scales, static_cast<int32_t*>(p.row_map),
                           static_cast<int32_t*>(p.src), static_cast<int32_t*>(p.counts),
                           static_cast<int32_t*>(p.offsets), p.perm_ws, s,
                           gate_perm ? static_cast<float*>(p.gates) : nullptr, gate_perm);
-  // the e4m3 path quantises each token once (1x128 blocks); the GEMM gathers its rows
+  // the e4m3 and MXFP4 paths quantise each token once (1x128 / 1x32 blocks); the GEMM gathers its rows
   const void* a = x;
   if (e == hipSuccess && fp8) {
     e = moe::launch_quant_rows_fp8(x, L->x_dt, T, L->H, static_cast<uint8_t*>(p.xq),
                                    static_cast<float*>(p.xq_scales), s);
     a = p.xq;
+  } else if (e == hipSuccess && fp4) {
+    e = moe::launch_quant_rows_fp4(x, T, L->H, static_cast<uint8_t*>(p.xq), static_cast<uint8_t*>(p.xq_scales), s);
+    a = p.xq;
   }
   if (e == hipSuccess) e = mark(2);
   if (e != hipSuccess) return from_hip(e);
-  e = moe::launch_grouped_swiglu(a, static_cast<float*>(p.xq_scales), L->w_dt, static_cast<int32_t*>(p.offsets),
+  e = moe::launch_grouped_swiglu(a, p.xq_scales, L->w_dt, static_cast<int32_t*>(p.offsets),
                                  R, L->E, L->H, L->F, L->w1, L->w1_scales, L->w2, L->w2_scales, p.y_perm, L->x_dt,
                                  p.gemm_ws, s, ev(3), static_cast<int32_t*>(p.src), gate_perm);
   if (e == hipSuccess) e = mark(4);
   if (e != hipSuccess) return from_hip(e);
   if (L->Fs > 0) {  // every token, unpermuted (quantised like the routed rows in the e4m3 path)
-    e = moe::launch_grouped_swiglu(a, static_cast<float*>(p.xq_scales), L->w_dt, nullptr, T, 1, L->H, L->Fs,
+    e = moe::launch_grouped_swiglu(a, p.xq_scales, L->w_dt, nullptr, T, 1, L->H, L->Fs,
                                    L->ws1, L->ws1_scales, L->ws2, L->ws2_scales, p.sh_out, L->x_dt, p.sh_ws, s);
     if (e != hipSuccess) return from_hip(e);
   }
@@ -322,7 +330,7 @@ size_t backward_bytes(const moe_layer* L, int64_t T) {
 }  // namespace
 
 size_t moe_backward_workspace_size(const moe_layer* L, int64_t T) {
-  if (validate_layer(L) != MOE_OK || L->w_dt == MOE_FP8_E4M3 || T < 0) return 0;
+  if (validate_layer(L) != MOE_OK || low_precision(L->w_dt) || T < 0) return 0;
   return backward_bytes(L, T);
 }
 
@@ -331,7 +339,7 @@ moe_status moe_backward(const moe_layer* L, const void* x, const void* dy, int64
                         moe_stream_t stream) {
   moe_status st = validate_layer(L);
   if (st != MOE_OK) return st;
-  if (L->w_dt == MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  if (low_precision(L->w_dt)) return MOE_ERR_UNSUPPORTED;
   st = check_common(T, L->H, L->E, L->k);
   if (st != MOE_OK) return st;
   if (!r || !g) return MOE_ERR_INVALID_ARG;

@@ -84,6 +84,35 @@ __device__ __forceinline__ float pow2_inverse(float s) {
 // E8M0 byte of a power-of-two fp32 scale (its biased exponent; 2^-127 -> 0).
 __device__ __forceinline__ int e8m0_of(float s) { return static_cast<int>((__float_as_uint(s) >> 23) & 0xFFu); }
 
+// ---- MXFP4: FP4 E2M1 elements (1 sign, 2 exponent bits with bias 1, 1 mantissa bit; magnitudes
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6) with one E8M0 scale byte (2^(e - 127)) per 32 elements.
+// Code of a scaled value (|v| <= 6): the nearest magnitude, ties to the even-mantissa code; each
+// comparison adds one step, strict where the tie goes down, inclusive where it goes up.
+__device__ __forceinline__ uint32_t f32_to_fp4(float v) {
+  const float m = fabsf(v);
+  const uint32_t code = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) + (m >= 3.5f) +
+                        (m > 5.0f);
+  return (v < 0.0f && code != 0u) ? (code | 8u) : code;  // values rounding to 0 encode as +0
+}
+
+// E8M0 byte of the smallest power of two 2^q with 6 * 2^q >= amax, q in [-127, 127]; 127 (2^0) for
+// an all-zero block.  For a normal amax = 1.m * 2^(E - 127): 6 = 1.5 * 2^2, so q = E - 129, plus
+// one when 1.m > 1.5 (mantissa bits above 0x400000); a subnormal amax needs q = -127.
+__device__ __forceinline__ int fp4_block_e8m0(float amax) {
+  if (!(amax > 0.0f)) return 127;
+  const uint32_t u = __float_as_uint(amax);
+  const int E = static_cast<int>((u >> 23) & 0xFFu);
+  int q = E == 0 ? -127 : E - 129 + ((u & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+  q = q < -127 ? -127 : (q > 127 ? 127 : q);
+  return q + 127;
+}
+
+// 2^(127 - e), the inverse of the E8M0 scale e in [0, 254] (2^-127 is the fp32 subnormal 0x00400000):
+// x * e8m0_inverse(e) is x / 2^(e - 127) rounded once.
+__device__ __forceinline__ float e8m0_inverse(int e) {
+  return e < 254 ? __uint_as_float(static_cast<uint32_t>(254 - e) << 23) : __uint_as_float(0x00400000u);
+}
+
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   uint32_t s = (c & 0x80u) << 24;
   uint32_t e = (c >> 3) & 0xFu;
@@ -113,7 +142,8 @@ __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a
 
 // ------------------------------------------------------------------ launcher interface
 // Every launcher enqueues on `stream` and returns hipGetLastError() of its launches.
-// dtype codes follow moe.h: 0 = fp32, 1 = bf16, 2 = fp8 e4m3.
+// dtype codes follow moe.h: 0 = fp32, 1 = bf16, 2 = fp8 e4m3, 3 = MXFP4.  Scale pointers are
+// fp32 arrays for e4m3 and E8M0 byte arrays for MXFP4.
 
 // scratch: logits (when `logits` is null) followed by the split router weight
 hipError_t launch_route(const void* x, int x_dt, const float* w_router, const float* bias, int64_t T,
@@ -125,7 +155,7 @@ size_t permute_scratch_bytes(int64_t T, int E, int k);
 // With gates [T, k] and gate_perm [T k] (both or neither), also writes each permuted row's gate:
 // gate_perm[row_map[t, j]] = gates[t, j].
 hipError_t launch_permute(const void* x, int x_dt, const int32_t* ids, int64_t T, int H, int E, int k,
-                          void* x_perm, int perm_dt, float* x_perm_scales, int32_t* row_map,
+                          void* x_perm, int perm_dt, void* x_perm_scales, int32_t* row_map,
                           int32_t* src_token, int32_t* counts, int32_t* offsets, void* scratch,
                           hipStream_t stream, const float* gates = nullptr, float* gate_perm = nullptr);
 
@@ -135,10 +165,10 @@ size_t grouped_swiglu_scratch_bytes(int64_t rows, int F, int dt);
 // the dispatch permutation fused into the GEMM's loads, so x_perm can be the unpermuted input.
 // With `row_scale` [rows], the SwiGLU epilogue multiplies row p of h by row_scale[p] before it is
 // rounded (the routing gate folded into the expert), so y_perm row p comes out scaled by it.
-hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int dt,
+hipError_t launch_grouped_swiglu(const void* x_perm, const void* x_scales, int dt,
                                  const int32_t* offsets, int64_t rows, int E, int H, int F,
-                                 const void* w1, const float* w1_scales, const void* w2,
-                                 const float* w2_scales, void* y_perm, int out_dt, void* scratch,
+                                 const void* w1, const void* w1_scales, const void* w2,
+                                 const void* w2_scales, void* y_perm, int out_dt, void* scratch,
                                  hipStream_t stream, hipEvent_t between = nullptr,
                                  const int32_t* gather = nullptr, const float* row_scale = nullptr);
 
@@ -166,6 +196,20 @@ hipError_t launch_grouped_swiglu_fp8(const void* x_perm, const float* x_scales, 
                                      const int32_t* gather, const float* row_scale = nullptr);
 // Per-row 1x128 E4M3 quantisation of a dense [T, H] bf16 / fp32 matrix (shared-expert input).
 hipError_t launch_quant_rows_fp8(const void* x, int x_dt, int64_t T, int H, uint8_t* codes, float* scales,
+                                 hipStream_t stream);
+
+// MXFP4 path: activations [rows, H / 2] codes + [rows, H / 32] E8M0; weights stored contraction-
+// contiguous, W1 [E, 2F, H / 2] + [E, 2F, H / 32] and W2 [E, H, F / 2] + [E, H, F / 32]; h re-quantised
+// to MXFP4 in 1 x 32 blocks in the scratch buffer (fp4_hidden_bytes(rows, F) bytes: codes, then
+// scales, each 256-byte aligned).  H and F multiples of 256.
+size_t fp4_hidden_bytes(int64_t rows, int F);
+hipError_t launch_grouped_swiglu_fp4(const void* x_perm, const void* x_scales, const int32_t* offsets,
+                                     int64_t rows, int E, int H, int F, const void* w1, const void* w1_scales,
+                                     const void* w2, const void* w2_scales, void* y_perm, int out_dt,
+                                     void* scratch, hipStream_t stream, hipEvent_t between,
+                                     const int32_t* gather, const float* row_scale = nullptr);
+// Per-row 1x32 MXFP4 quantisation of a dense [T, H] bf16 matrix (H % 32 == 0).
+hipError_t launch_quant_rows_fp4(const void* x, int64_t T, int H, uint8_t* codes, uint8_t* scales,
                                  hipStream_t stream);
 
 // gates == nullptr: every weight is 1 (rows already scaled by their gates).

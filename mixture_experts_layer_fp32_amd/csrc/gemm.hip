@@ -539,6 +539,7 @@ hipError_t launch_bf16_pair(const void* x_perm, const void* w1, const void* w2, 
 size_t grouped_swiglu_scratch_bytes(int64_t rows, int F, int dt) {
   if (dt == 0) return static_cast<size_t>(rows) * F * 4;
   if (dt == 1) return static_cast<size_t>(rows) * F * 2;
+  if (dt == 3) return fp4_hidden_bytes(rows, F);
   // fp8: h codes + their 1x128 scales + the kernel-variant flag
   return fp8_hidden_bytes(rows, F) + ((static_cast<size_t>(rows) * (F / 128) * 4 + 255) & ~static_cast<size_t>(255)) +
          256;
@@ -564,15 +565,19 @@ hipError_t launch_grouped_gemm_f32out(const void* A, const void* B, const int32_
              : launch_bf16<128, false, true>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather);
 }
 
-hipError_t launch_grouped_swiglu(const void* x_perm, const float* x_scales, int dt,
+hipError_t launch_grouped_swiglu(const void* x_perm, const void* x_scales, int dt,
                                  const int32_t* offsets, int64_t rows, int E, int H, int F,
-                                 const void* w1, const float* w1_scales, const void* w2,
-                                 const float* w2_scales, void* y_perm, int out_dt, void* scratch,
+                                 const void* w1, const void* w1_scales, const void* w2,
+                                 const void* w2_scales, void* y_perm, int out_dt, void* scratch,
                                  hipStream_t stream, hipEvent_t between, const int32_t* gather,
                                  const float* row_scale) {
   if (dt == 2)
-    return launch_grouped_swiglu_fp8(x_perm, x_scales, offsets, rows, E, H, F, w1, w1_scales, w2, w2_scales,
+    return launch_grouped_swiglu_fp8(x_perm, static_cast<const float*>(x_scales), offsets, rows, E, H, F, w1,
+                                     static_cast<const float*>(w1_scales), w2, static_cast<const float*>(w2_scales),
                                      y_perm, out_dt, scratch, stream, between, gather, row_scale);
+  if (dt == 3)
+    return launch_grouped_swiglu_fp4(x_perm, x_scales, offsets, rows, E, H, F, w1, w1_scales, w2, w2_scales, y_perm,
+                                     out_dt, scratch, stream, between, gather, row_scale);
   if (dt == 0) {
     float* h = static_cast<float*>(scratch);
     const int nt1 = F / 32, nt2 = static_cast<int>(ceil_div(H, kF32BN));

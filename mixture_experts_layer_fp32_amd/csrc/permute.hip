@@ -222,6 +222,96 @@ __global__ __launch_bounds__(kScatterThreads) void perm_scatter_fp8_kernel(
   }
 }
 
+// 8 bf16 values of a lane -> 8 E2M1 codes (4 bytes, value i in nibble i), with one E8M0 scale per
+// 32 values shared by the 4 lanes that hold them (lanes 4g .. 4g+3; a group is wholly in or out).
+__device__ __forceinline__ uint32_t quant_fp4_x8(uint4 v, int& e8) {
+  const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(wv[i] << 16);
+    f[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
+    amax = fmaxf(amax, fmaxf(fabsf(f[2 * i]), fabsf(f[2 * i + 1])));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+  e8 = fp4_block_e8m0(amax);
+  const float inv = e8m0_inverse(e8);  // f * inv is f / scale rounded once (exact: a power of two)
+  uint32_t q = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q |= f32_to_fp4(f[i] * inv) << (4 * i);
+  return q;
+}
+
+// bf16 -> MXFP4 rows scattered to their permuted positions (codes [R, H / 2], scales [R, H / 32]).
+__global__ __launch_bounds__(kScatterThreads) void perm_scatter_fp4_kernel(
+    const uint4* __restrict__ x, const int32_t* __restrict__ ids, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ local_rank, int64_t T, int H, int k, int E, int nblk,
+    uint32_t* __restrict__ x_perm, uint8_t* __restrict__ scales, int32_t* __restrict__ row_map,
+    int32_t* __restrict__ src_token, const float* __restrict__ gates, float* __restrict__ gate_perm) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + threadIdx.x / kWave;
+  if (t >= T) return;
+  int row = resolve_row(ids, base, local_rank, t, k, E, nblk, lane, row_map, src_token, gates, gate_perm);
+  if (!x_perm) return;
+  const int row_vecs = H / 8;
+  const int nsb = H / 32;
+  const uint4* src = x + t * row_vecs;
+  for (int c0 = 0; c0 < row_vecs; c0 += 2 * kWave) {
+    uint4 v[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + u * kWave + lane;
+      v[u] = c < row_vecs ? src[c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + u * kWave + lane;
+      int e8;
+      const uint32_t packed = quant_fp4_x8(v[u], e8);
+      for (int j = 0; j < k; ++j) {
+        const int r = __shfl(row, j, kWave);
+        if (c < row_vecs) {
+          x_perm[static_cast<int64_t>(r) * row_vecs + c] = packed;
+          if ((lane & 3) == 0) scales[static_cast<int64_t>(r) * nsb + c / 4] = static_cast<uint8_t>(e8);
+        }
+      }
+    }
+  }
+}
+
+// Dense per-row MXFP4 quantisation (each token once, for the fused forward and the shared expert).
+__global__ __launch_bounds__(kScatterThreads) void quant_rows_fp4_kernel(const uint4* __restrict__ x, int64_t T,
+                                                                          int H, uint32_t* __restrict__ codes,
+                                                                          uint8_t* __restrict__ scales) {
+  constexpr int U = 4;
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + threadIdx.x / kWave;
+  if (t >= T) return;
+  const int row_vecs = H / 8;
+  const int nsb = H / 32;
+  const uint4* src = x + t * row_vecs;
+  for (int c0 = 0; c0 < row_vecs; c0 += U * kWave) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave + lane;
+      v[u] = c < row_vecs ? src[c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave + lane;
+      int e8;
+      const uint32_t packed = quant_fp4_x8(v[u], e8);  // H % 32 == 0: a 4-lane group is wholly in or out
+      if (c < row_vecs) {
+        codes[t * row_vecs + c] = packed;
+        if ((lane & 3) == 0) scales[t * nsb + c / 4] = static_cast<uint8_t>(e8);
+      }
+    }
+  }
+}
+
 // Dense per-row quantisation (each token once, for the fused forward and the shared expert):
 // one wavefront per row, four 16-byte loads per lane in flight before any is quantised.
 __global__ __launch_bounds__(kScatterThreads) void quant_rows_fp8_kernel(const uint4* __restrict__ x, int64_t T,
@@ -264,7 +354,7 @@ size_t permute_scratch_bytes(int64_t T, int E, int k) {
 }
 
 hipError_t launch_permute(const void* x, int x_dt, const int32_t* ids, int64_t T, int H, int E, int k,
-                          void* x_perm, int perm_dt, float* x_perm_scales, int32_t* row_map,
+                          void* x_perm, int perm_dt, void* x_perm_scales, int32_t* row_map,
                           int32_t* src_token, int32_t* counts, int32_t* offsets, void* scratch,
                           hipStream_t stream, const float* gates, float* gate_perm) {
   if ((gates == nullptr) != (gate_perm == nullptr)) return hipErrorInvalidValue;
@@ -282,7 +372,13 @@ hipError_t launch_permute(const void* x, int x_dt, const int32_t* ids, int64_t T
   if (perm_dt == 2) {
     hipLaunchKernelGGL(perm_scatter_fp8_kernel, grid, dim3(kScatterThreads), 0, stream,
                        static_cast<const uint4*>(x), ids, blk, local_rank, T, H, k, E, nblk,
-                       static_cast<uint2*>(x_perm), x_perm_scales, row_map, src_token, gates, gate_perm);
+                       static_cast<uint2*>(x_perm), static_cast<float*>(x_perm_scales), row_map, src_token, gates,
+                       gate_perm);
+  } else if (perm_dt == 3) {
+    hipLaunchKernelGGL(perm_scatter_fp4_kernel, grid, dim3(kScatterThreads), 0, stream,
+                       static_cast<const uint4*>(x), ids, blk, local_rank, T, H, k, E, nblk,
+                       static_cast<uint32_t*>(x_perm), static_cast<uint8_t*>(x_perm_scales), row_map, src_token,
+                       gates, gate_perm);
   } else {
     const int elt = (x_dt == 0) ? 4 : 2;
     const int row_vecs = H * elt / 16;
@@ -300,6 +396,16 @@ hipError_t launch_quant_rows_fp8(const void* x, int x_dt, int64_t T, int H, uint
   hipLaunchKernelGGL(quant_rows_fp8_kernel, dim3(static_cast<unsigned>(ceil_div(T, kTokPerBlock))),
                      dim3(kScatterThreads), 0, stream, static_cast<const uint4*>(x), T, H,
                      reinterpret_cast<uint2*>(codes), scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_fp4(const void* x, int64_t T, int H, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t stream) {
+  if (H % 32 != 0) return hipErrorInvalidValue;
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_rows_fp4_kernel, dim3(static_cast<unsigned>(ceil_div(T, kTokPerBlock))),
+                     dim3(kScatterThreads), 0, stream, static_cast<const uint4*>(x), T, H,
+                     reinterpret_cast<uint32_t*>(codes), scales);
   return hipGetLastError();
 }
 

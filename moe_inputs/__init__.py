@@ -23,6 +23,12 @@ Recipe (all workloads, seed 0 unless stated):
   E4M3 codes with one fp32 scale per 128x128 block (scale = the smallest power
   of two 2^q with 448 * 2^q >= the block's amax, 1 for an all-zero block;
   codes by torch's own float8_e4m3fn cast of w / scale after clamping to +-448);
+* MXFP4 workloads: each weight matrix is drawn in fp32 as above, stored
+  contraction-contiguous (W1[e] as [2F, H/2] bytes, W2[e] as [H, F/2]) as E2M1
+  codes, two per byte (element 2i in the low nibble), with one E8M0 scale per
+  32 consecutive elements along the contraction (the smallest power of two
+  2^q with 6 * 2^q >= the block's amax; codes: nearest E2M1 value of w / 2^q,
+  ties to the even-mantissa code), as torch float4_e2m1fn_x2 / float8_e8m0fnu;
 * the skewed-routing workload adds a per-expert routing bias read from
   ``tests/golden/zipf_bias_deepseek_v3_fp8.txt`` (written by
   ``tests/golden/make_zipf_bias.py``), calibrated so expert loads follow a Zipf
@@ -83,6 +89,10 @@ CONFIGS = {
         "deepseek_v3", T=8192, H=7168, E=256, k=8, F=2048, Fs=2048, score="sigmoid", norm=True,
         act_dtype="bf16", w_dtype="bf16",
         description="DeepSeek-V3-shaped layer: T=8192 H=7168 E=256 top-8 F=2048 + shared expert, sigmoid"),
+    "deepseek_v3_mxfp4": LayerConfig(
+        "deepseek_v3_mxfp4", T=8192, H=7168, E=256, k=8, F=2048, Fs=2048, score="sigmoid", norm=True,
+        act_dtype="bf16", w_dtype="mxfp4",
+        description="DeepSeek-V3-shaped layer with MXFP4 expert GEMMs (E2M1, E8M0 per 32), bf16 activations"),
     "deepseek_v3_fp8_zipf": LayerConfig(
         "deepseek_v3_fp8_zipf", T=8192, H=7168, E=256, k=8, F=2048, Fs=2048, score="sigmoid",
         norm=True, act_dtype="bf16", w_dtype="fp8", zipf_bias=True,
@@ -127,10 +137,36 @@ def _block_fp8(w: torch.Tensor):
     return q.reshape(K, N), s.contiguous()
 
 
+_FP4_MIDS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)  # between consecutive E2M1 magnitudes
+
+
+def _mx_fp4(w: torch.Tensor):
+    """fp32 [K, N] -> (E2M1 codes stored [N, K/2] as float4_e2m1fn_x2, E8M0 scales [N, K/32] as
+    float8_e8m0fnu); input preparation only."""
+    wt = w.t().contiguous()
+    N, K = wt.shape
+    b = wt.reshape(N, K // 32, 32)
+    amax = b.abs().amax(dim=2)
+    # smallest q with 6 * 2^q >= amax: from frexp(amax) = m * 2^e (m in [0.5, 1)), q = e - 2 - (m <= 0.75)
+    m, e = torch.frexp(amax)
+    q = (e - 2 - (m <= 0.75).to(e.dtype)).clamp(-127, 127)
+    q = torch.where(amax > 0, q, torch.zeros_like(q))
+    v = b * torch.ldexp(torch.ones_like(amax), -q)[:, :, None]
+    mag = v.abs().clamp(max=6.0)
+    code = torch.zeros_like(mag, dtype=torch.uint8)
+    for i, mid in enumerate(_FP4_MIDS):  # ties: down at odd steps 0, 2, 4, 6 (strict), up at 1, 3, 5
+        code += (mag > mid if i % 2 == 0 else mag >= mid).to(torch.uint8)
+    code = torch.where((v < 0) & (code != 0), code | 8, code).reshape(N, K)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).contiguous()
+    return packed.view(torch.float4_e2m1fn_x2), (q + 127).to(torch.uint8).view(torch.float8_e8m0fnu)
+
+
 def _draw_matrix(g, rows, cols, std, w_dtype, device):
     w = torch.randn(rows, cols, generator=g, dtype=torch.float32, device=device) * std
     if w_dtype == "fp8":
         return _block_fp8(w)
+    if w_dtype == "mxfp4":
+        return _mx_fp4(w)
     return w.to(_TORCH_DT[w_dtype]), None
 
 
@@ -149,21 +185,33 @@ def make_inputs(cfg: LayerConfig, seed: int = 0, weight_device: str = "cpu", act
     gw = torch.Generator(device=weight_device).manual_seed(seed + 1)
     E, H, F, Fs = cfg.E, cfg.H, cfg.F, cfg.Fs
     fp8 = cfg.w_dtype == "fp8"
-    wdt = torch.float8_e4m3fn if fp8 else _TORCH_DT[cfg.w_dtype]
-    w1 = torch.empty(E, H, 2 * F, dtype=wdt, device=weight_device)
-    w2 = torch.empty(E, F, H, dtype=wdt, device=weight_device)
-    w1s = torch.empty(E, H // 128, 2 * F // 128, device=weight_device) if fp8 else None
-    w2s = torch.empty(E, F // 128, H // 128, device=weight_device) if fp8 else None
+    fp4 = cfg.w_dtype == "mxfp4"
+    if fp4:
+        u8, e8 = torch.uint8, torch.float8_e8m0fnu
+        w1 = torch.empty(E, 2 * F, H // 2, dtype=u8, device=weight_device).view(torch.float4_e2m1fn_x2)
+        w2 = torch.empty(E, H, F // 2, dtype=u8, device=weight_device).view(torch.float4_e2m1fn_x2)
+        w1s = torch.empty(E, 2 * F, H // 32, dtype=u8, device=weight_device).view(e8)
+        w2s = torch.empty(E, H, F // 32, dtype=u8, device=weight_device).view(e8)
+    else:
+        wdt = torch.float8_e4m3fn if fp8 else _TORCH_DT[cfg.w_dtype]
+        w1 = torch.empty(E, H, 2 * F, dtype=wdt, device=weight_device)
+        w2 = torch.empty(E, F, H, dtype=wdt, device=weight_device)
+        w1s = torch.empty(E, H // 128, 2 * F // 128, device=weight_device) if fp8 else None
+        w2s = torch.empty(E, F // 128, H // 128, device=weight_device) if fp8 else None
+
+    def put(dst, src):  # byte copy (torch has no copy kernels for the 4-bit / E8M0 dtypes)
+        dst.view(torch.uint8).copy_(src.view(torch.uint8)) if fp4 else dst.copy_(src)
+
     for e in range(E):
         q, s = _draw_matrix(gw, H, 2 * F, 1.0 / math.sqrt(H), cfg.w_dtype, weight_device)
-        w1[e].copy_(q)
-        if fp8:
-            w1s[e].copy_(s)
+        put(w1[e], q)
+        if fp8 or fp4:
+            put(w1s[e], s)
     for e in range(E):
         q, s = _draw_matrix(gw, F, H, 1.0 / math.sqrt(F), cfg.w_dtype, weight_device)
-        w2[e].copy_(q)
-        if fp8:
-            w2s[e].copy_(s)
+        put(w2[e], q)
+        if fp8 or fp4:
+            put(w2s[e], s)
     ws1 = ws2 = ws1s = ws2s = None
     if Fs:
         ws1, ws1s = _draw_matrix(gw, H, 2 * Fs, 1.0 / math.sqrt(H), cfg.w_dtype, weight_device)

@@ -38,6 +38,10 @@ R8 in MXFP4 mode (oracle/mxfp4.py) both operands of both expert GEMMs are MXFP4:
    + E8M0 scales (dequantised by the caller), and the SwiGLU activation h
    quantised per row in 1x32 blocks before the second GEMM (the operand the
    second GEMM takes is MXFP4 too); the quantisation decision is taken in fp32.
+R9 with the gate folded into the experts (``gate_in_expert``, memory-efficient permutation),
+   h of each permuted row is multiplied by that row's gate before it is rounded, and
+   combine adds the k rows with weight 1: in exact arithmetic the same layer; where h is
+   quantised (R8) the quantiser sees g h.
 
 No stage here is blocked, fused or reordered beyond what its definition states;
 numpy matmul / argsort / bincount are the only library steps.
@@ -160,12 +164,12 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def swiglu_expert(rows: np.ndarray, w1: np.ndarray, w2: np.ndarray, h_quant=None) -> np.ndarray:
+def swiglu_expert(rows: np.ndarray, w1: np.ndarray, w2: np.ndarray, h_quant=None, row_scale=None) -> np.ndarray:
     """One SwiGLU expert on a block of rows, float64 (reading R5).
 
     u = rows @ W1 with W1 [H, 2F]; h = SiLU(u[:, :F]) * u[:, F:]; out = h @ W2 with W2 [F, H].
     h is not rounded, except by ``h_quant`` when given (MXFP4 mode, reading R8: the second GEMM's
-    operand is h quantised per row).
+    operand is h quantised per row); ``row_scale`` [n] multiplies h row by row first (R9).
     """
     r64 = np.asarray(rows, dtype=np.float64)
     w1 = np.asarray(w1, dtype=np.float64)
@@ -175,6 +179,8 @@ def swiglu_expert(rows: np.ndarray, w1: np.ndarray, w2: np.ndarray, h_quant=None
         raise ValueError(f"W1 has {w1.shape[1]} columns, expected 2F = {2 * F}")
     u = r64 @ w1
     h = silu(u[:, :F]) * u[:, F:]
+    if row_scale is not None:
+        h = h * np.asarray(row_scale, dtype=np.float64)[:, None]
     if h_quant is not None:
         h = h_quant(h)
     return h @ w2
@@ -187,12 +193,13 @@ def swiglu_hidden(rows: np.ndarray, w1: np.ndarray) -> np.ndarray:
     return silu(u[:, :F]) * u[:, F:]
 
 
-def grouped_experts(x_perm: np.ndarray, offsets: np.ndarray, w1_of, w2_of, h_quant=None) -> np.ndarray:
+def grouped_experts(x_perm: np.ndarray, offsets: np.ndarray, w1_of, w2_of, h_quant=None,
+                    row_scale=None) -> np.ndarray:
     """Apply expert e to rows offsets[e]:offsets[e+1] of ``x_perm`` for every e (the grouped GEMM).
 
     ``w1_of(e)`` / ``w2_of(e)`` return expert e's [H, 2F] / [F, H] weights (so a caller
-    can widen one expert at a time); experts with no rows are skipped; ``h_quant`` as for
-    swiglu_expert.  Returns float64 [R, H].
+    can widen one expert at a time); experts with no rows are skipped; ``h_quant`` and
+    ``row_scale`` ([R], one per permuted row) as for swiglu_expert.  Returns float64 [R, H].
     """
     x_perm = np.asarray(x_perm)
     R = x_perm.shape[0]
@@ -201,7 +208,8 @@ def grouped_experts(x_perm: np.ndarray, offsets: np.ndarray, w1_of, w2_of, h_qua
         a, b = int(offsets[e]), int(offsets[e + 1])
         if b == a:
             continue
-        out = swiglu_expert(x_perm[a:b], w1_of(e), w2_of(e), h_quant)
+        out = swiglu_expert(x_perm[a:b], w1_of(e), w2_of(e), h_quant,
+                            None if row_scale is None else np.asarray(row_scale)[a:b])
         if y is None:
             y = np.zeros((R, out.shape[1]), dtype=np.float64)
         y[a:b] = out
@@ -233,12 +241,13 @@ def quantised_input(x: np.ndarray) -> np.ndarray:
 
 
 def forward(x, w_router, w1_of, w2_of, *, E, k, score, norm, bias=None, shared_w1=None,
-            shared_w2=None, fp8=False, mxfp4_mode=False, logits=None):
+            shared_w2=None, fp8=False, mxfp4_mode=False, logits=None, gate_in_expert=False):
     """The whole layer, stage by stage; returns a dict of every intermediate.
 
     ``x`` [T, H] float array; ``w_router`` [H, E]; ``w1_of(e)``/``w2_of(e)`` give expert
     weights (dequantised values in FP8 / MXFP4 mode); ``shared_w1``/``shared_w2`` the shared
-    expert or None.  ``fp8``: reading R7; ``mxfp4_mode``: reading R8.  If ``logits`` is given (fp32 [T, E]) routing is driven from those
+    expert or None.  ``fp8``: reading R7; ``mxfp4_mode``: reading R8; ``gate_in_expert``: R9
+    (then ``y_perm`` holds the gate-weighted rows).  If ``logits`` is given (fp32 [T, E]) routing is driven from those
     logits instead of recomputing them -- this is how the GPU's own logits are checked
     bit-exactly for ids / counts / offsets / permutation.
     """
@@ -264,12 +273,17 @@ def forward(x, w_router, w1_of, w2_of, *, E, k, score, norm, bias=None, shared_w
         xq = np.asarray(x, dtype=np.float64)
     out["x_hat"] = xq
     out["x_perm"] = permute_rows(xq, out["src_token"])
-    out["y_perm"] = grouped_experts(out["x_perm"], out["offsets"], w1_of, w2_of, h_quant)
+    g_perm = None
+    if gate_in_expert:  # each permuted row's gate: g_perm[row_map[t, j]] = gates[t, j]
+        g_perm = np.empty(out["row_map"].size, dtype=np.float64)
+        g_perm[out["row_map"].ravel()] = out["gates"].ravel()
+    out["y_perm"] = grouped_experts(out["x_perm"], out["offsets"], w1_of, w2_of, h_quant, g_perm)
     shared = None
     if shared_w1 is not None:
         shared = swiglu_expert(xq, shared_w1, shared_w2, h_quant)
     out["shared"] = shared
-    out["y"] = combine(out["y_perm"], out["row_map"], out["gates"], shared)
+    weights = np.ones_like(out["gates"]) if gate_in_expert else out["gates"]
+    out["y"] = combine(out["y_perm"], out["row_map"], weights, shared)
     return out
 
 

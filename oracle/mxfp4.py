@@ -123,9 +123,21 @@ def unpack(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+# decode_fp4 of both nibbles of every byte, so large stored matrices decode by one table lookup
+# (the same values as decode_fp4 element by element).
+_PAIR_TABLE = None
+
+
 def dequantise_packed(packed: np.ndarray, scales: np.ndarray, block: int = BLOCK) -> np.ndarray:
     """Stored MXFP4 rows ([n, K / 2] packed bytes + [n, K / block] E8M0) -> float64 [n, K]."""
-    return dequantise_rows(unpack(packed), scales, block)
+    global _PAIR_TABLE
+    if _PAIR_TABLE is None:
+        b = np.arange(256, dtype=np.uint8)
+        _PAIR_TABLE = np.stack([decode_fp4(b & 0xF), decode_fp4(b >> 4)], axis=1)  # [256, 2]
+    p = np.asarray(packed, dtype=np.uint8)
+    n, half = p.shape
+    d = _PAIR_TABLE[p].reshape(n, half * 2 // block, block)
+    return (d * decode_e8m0(scales)[:, :, None]).reshape(n, half * 2)
 
 
 def quantised(x: np.ndarray) -> np.ndarray:

@@ -123,12 +123,23 @@ def _layer(**over):
 
 
 @pytest.mark.parametrize("over", [dict(k=9), dict(w_dt=0), dict(x_dt=2), dict(F=100), dict(Fs=256),
-                                  dict(w_dt=2), dict(w1=None), dict(score=3), dict(Fs=-1), dict(gate_in_expert=2)])
+                                  dict(w_dt=2), dict(w1=None), dict(score=3), dict(Fs=-1), dict(gate_in_expert=2),
+                                  dict(w_dt=3), dict(w_dt=3, w1_scales=16384, w2_scales=16384, F=384),
+                                  dict(w_dt=3, w1_scales=16384, w2_scales=16384, H=384), dict(w_dt=4)])
 def test_forward_rejects_bad_layers(over):
     L = _lib.lib()
     lay = _layer(**over)
     assert L.moe_workspace_size(ctypes.byref(lay), 64) == 0
     assert L.moe_forward(ctypes.byref(lay), P, 64, P, None, P, 1 << 30, None) == INVALID
+
+
+def test_mxfp4_layers_need_their_scales_and_have_no_backward():
+    L = _lib.lib()
+    lay = _layer(w_dt=3, w1_scales=16384, w2_scales=16384)
+    need = L.moe_workspace_size(ctypes.byref(lay), 64)
+    assert need > 0
+    assert L.moe_backward_workspace_size(ctypes.byref(lay), 64) == 0
+    assert L.moe_backward(ctypes.byref(lay), P, P, 64, None, None, None, P, 1 << 30, None) == UNSUP
 
 
 def test_gate_in_expert_needs_a_per_row_gate_buffer():

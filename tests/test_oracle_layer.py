@@ -140,7 +140,7 @@ def test_driving_routing_from_given_logits():
 # ----------------------------------------------------------------------------------------------
 # Planted mistakes: a plausible bug anywhere in the staged oracle must fail a pin.  Each mutation is
 # monkeypatched into the oracle on the CPU and the brute-force comparison must then disagree.
-def _swap_halves(rows, w1, w2, h_quant=None):
+def _swap_halves(rows, w1, w2, h_quant=None, row_scale=None):
     F = w2.shape[0]
     w1 = np.asarray(w1)
     return _orig_swiglu(rows, np.concatenate([w1[:, F:], w1[:, :F]], axis=1), w2)
@@ -157,7 +157,7 @@ def _softmax_over_selected(l, i, s, n):
     return _orig_gates(sel, np.tile(np.arange(sel.shape[1]), (sel.shape[0], 1)), s, n)
 
 
-def _rows_reversed_in_w2(r, a, b, h_quant=None):
+def _rows_reversed_in_w2(r, a, b, h_quant=None, row_scale=None):
     return _orig_swiglu(r, a, np.asarray(b)[::-1])
 
 
@@ -209,3 +209,24 @@ def test_swiglu_hidden_pins():
     assert rel_frobenius(h @ w2, moe.swiglu_expert(rows, w1, w2)) <= 1e-14
     swapped = np.concatenate([w1[:, F:], w1[:, :F]], axis=1)
     assert rel_frobenius(moe.swiglu_hidden(rows, swapped), loop) > 0.1
+
+
+def test_gate_folded_form_is_the_same_layer_in_exact_arithmetic():
+    """Reading R9: with the gate multiplied into h and combine weights 1, y is unchanged (1e-12) and
+    y_perm is gate x the plain expert rows; in MXFP4 mode the quantiser sees g h, which differs."""
+    from oracle import mxfp4
+    x, wr, w1, w2, ws1, ws2 = _tiny(31, T=10, H=64, E=4, F=32, Fs=32)
+    kw = dict(E=4, k=2, score="sigmoid", norm=True)
+    a = _forward(x, wr, w1, w2, ws1, ws2, **kw)
+    b = _forward(x, wr, w1, w2, ws1, ws2, gate_in_expert=True, **kw)
+    assert rel_frobenius(b["y"], a["y"]) <= 1e-12
+    g = np.empty(a["row_map"].size)
+    g[a["row_map"].ravel()] = a["gates"].ravel()
+    assert rel_frobenius(b["y_perm"], g[:, None] * a["y_perm"]) <= 1e-12
+    c = _forward(x, wr, w1, w2, ws1, ws2, mxfp4_mode=True, gate_in_expert=True, **kw)
+    d = _forward(x, wr, w1, w2, ws1, ws2, mxfp4_mode=True, **kw)
+    assert rel_frobenius(c["y_perm"], g[:, None] * d["y_perm"]) > 1e-3
+    rows = c["x_perm"][c["offsets"][0]:c["offsets"][1]]
+    u = rows @ w1[0]
+    hq = mxfp4.quantised(g[c["offsets"][0]:c["offsets"][1], None] * moe.silu(u[:, :32]) * u[:, 32:])
+    assert rel_frobenius(c["y_perm"][c["offsets"][0]:c["offsets"][1]], hq @ w2[0]) <= 1e-12

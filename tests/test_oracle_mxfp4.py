@@ -162,3 +162,10 @@ def test_mxfp4_layer_mode_quantises_x_and_h():
     # quantising h matters: the unrounded-h layer differs by the 4-bit rounding of h
     plain = moe.forward(xq, wr, lambda e: w1[e], lambda e: w2[e], E=E, k=k, score="softmax", norm=True)
     assert 0.02 < np.linalg.norm(plain["y"] - o["y"]) / np.linalg.norm(plain["y"]) < 0.5
+
+
+def test_packed_table_decode_equals_the_element_decode():
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 16, (7, 64)).astype(np.uint8)
+    scales = rng.integers(100, 150, (7, 2)).astype(np.uint8)
+    assert np.array_equal(mxfp4.dequantise_packed(mxfp4.pack(codes), scales), mxfp4.dequantise_rows(codes, scales))

@@ -20,6 +20,7 @@ REDUCED = {
     "e4m3": moe_inputs.CONFIGS["deepseek_v3_fp8_zipf"].replace(T=300, H=512, E=32, k=8, F=256, Fs=128,
                                                                zipf_bias=False),
     "fp32": moe_inputs.CONFIGS["tiny_fp32"],
+    "mxfp4": moe_inputs.CONFIGS["deepseek_v3_mxfp4"].replace(T=300, H=512, E=32, k=8, F=256, Fs=256),
 }
 
 
