@@ -10,8 +10,9 @@
 //     set with 64-bit LDS atomic OR, which is order-independent).  A (t, j) pair's rank
 //     inside its expert and block is the popcount of the bits below t; the block's count
 //     for expert e is the popcount of e's bitmap.
-//  2. perm_scan: one workgroup scans the [E][B] count table in expert-major order, giving
-//     each (expert, block) its first permuted row, expert_offsets and expert_counts.
+//  2. perm_scan: one workgroup scans the [E][B] count table in expert-major order (each thread a
+//     run of it, the run totals by wave shuffles), giving each (expert, block) its first
+//     permuted row, expert_offsets and expert_counts.
 //  3. perm_scatter: one wavefront per token resolves its k rows, writes row_map/src_token,
 //     reads the token's row once (16 B per lane) and writes it to its k permuted rows,
 //     optionally quantising bf16 -> e4m3 in 1x128 blocks on the way.
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(kBT) void perm_count_kernel(const int32_t* __restri
 __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(int32_t* __restrict__ base, int E,
                                                                  int nblk, int32_t* __restrict__ offsets,
                                                                  int32_t* __restrict__ counts) {
-  __shared__ int32_t part[kScanThreads];
+  __shared__ int32_t part[kScanThreads / kWave];
   const int tid = threadIdx.x;
   const int64_t n = static_cast<int64_t>(E) * nblk;
   const int64_t per = ceil_div(n, kScanThreads);
@@ -74,23 +75,36 @@ __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(int32_t* __rest
   const int64_t hi = lo + per < n ? lo + per : n;
   int32_t s = 0;
   for (int64_t i = lo; i < hi; ++i) s += base[i];
-  part[tid] = s;
-  __syncthreads();
-  // Hillis-Steele inclusive scan of the 1024 partial sums
-  for (int o = 1; o < kScanThreads; o <<= 1) {
-    int32_t v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  // inclusive scan of the 1024 partial sums: within each wave by shuffles, then across the 16 wave
+  // totals by wave 0, then each thread adds the totals of the waves before it
+  const int lane = tid % kWave, wave = tid / kWave;
+  constexpr int NW = kScanThreads / kWave;
+  int32_t v = s;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
   }
-  int32_t run = part[tid] - s;  // exclusive prefix of this thread's chunk
+  if (lane == kWave - 1) part[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int32_t w = lane < NW ? part[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < NW; o <<= 1) {
+      const int32_t u = __shfl_up(w, o, kWave);
+      if (lane >= o) w += u;
+    }
+    if (lane < NW) part[lane] = w;
+  }
+  __syncthreads();
+  int32_t run = v - s + (wave > 0 ? part[wave - 1] : 0);  // exclusive prefix of this thread's chunk
   for (int64_t i = lo; i < hi; ++i) {
     int32_t c = base[i];
     base[i] = run;
     run += c;
   }
   __syncthreads();
-  const int32_t total = part[kScanThreads - 1];
+  const int32_t total = part[NW - 1];
   for (int e = tid; e <= E; e += kScanThreads) {
     int32_t o = e < E ? base[static_cast<int64_t>(e) * nblk] : total;
     offsets[e] = o;
@@ -146,6 +160,7 @@ __global__ __launch_bounds__(kScatterThreads) void perm_scatter_copy_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u)  // keep the loaded values: no re-load inside the store loop
       asm volatile("" : "+v"(v[u].x), "+v"(v[u].y), "+v"(v[u].z), "+v"(v[u].w));
+    // (non-temporal stores here measured slower: 247 -> 263 us for the DeepSeek-V3-shaped rows)
     for (int j = 0; j < k; ++j) {
       uint4* dst = x_perm + static_cast<int64_t>(__shfl(row, j, kWave)) * row_vecs;
 #pragma unroll
