@@ -173,11 +173,11 @@ hipError_t launch_grouped_swiglu(const void* x_perm, const void* x_scales, int d
                                  const int32_t* gather = nullptr, const float* row_scale = nullptr);
 
 // Dense out[rows, N] (fp32) = A[rows, K] . B[K, N] with bf16 A and B (B N-contiguous),
-// K % 64 == 0, N % 8 == 0: the grouped-GEMM kernel with one expert.  With ksplit > 1 (K / 64 a
-// multiple of ksplit) K is cut into ksplit equal slices and out[s] (at out + s * rows * N) gets
-// slice s's partial product; the caller sums them.
+// K % 64 == 0, N % 8 == 0: the grouped-GEMM kernel with one expert, on bm-row tiles (128 or 256).
+// With ksplit > 1 (K / 64 a multiple of ksplit) K is cut into ksplit equal slices and out[s] (at
+// out + s * rows * N) gets slice s's partial product; the caller sums them.
 hipError_t launch_dense_gemm_f32out(const void* A, const void* B, int64_t rows, int K, int N, float* out,
-                                    hipStream_t stream, int ksplit = 1);
+                                    hipStream_t stream, int ksplit = 1, int bm = 128);
 
 // Grouped out[p, :] (fp32) = A[gather ? gather[p] : p] . B_e over the rows of each expert, bf16
 // operands (B [E, K, N] N-contiguous, K % 64 == 0, N % 256 == 0): the grouped-GEMM kernel without

@@ -546,12 +546,14 @@ size_t grouped_swiglu_scratch_bytes(int64_t rows, int F, int dt) {
 }
 
 hipError_t launch_dense_gemm_f32out(const void* A, const void* B, int64_t rows, int K, int N, float* out,
-                                    hipStream_t stream, int ksplit) {
+                                    hipStream_t stream, int ksplit, int bm) {
   if (rows <= 0) return hipSuccess;
-  if (ksplit < 1 || (K / kBKT) % ksplit != 0) return hipErrorInvalidValue;
-  return launch_bf16<128, false, true>(static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B), nullptr, rows,
-                                       1, K, N, static_cast<int>(ceil_div(N, kBN)) * ksplit, out, stream, 0, nullptr,
-                                       ksplit);
+  if (ksplit < 1 || (K / kBKT) % ksplit != 0 || (bm != 128 && bm != 256)) return hipErrorInvalidValue;
+  const int nt = static_cast<int>(ceil_div(N, kBN)) * ksplit;
+  const bf16_t* a = static_cast<const bf16_t*>(A);
+  const bf16_t* b = static_cast<const bf16_t*>(B);
+  return bm == 256 ? launch_bf16<256, false, true>(a, b, nullptr, rows, 1, K, N, nt, out, stream, 0, nullptr, ksplit)
+                   : launch_bf16<128, false, true>(a, b, nullptr, rows, 1, K, N, nt, out, stream, 0, nullptr, ksplit);
 }
 
 hipError_t launch_grouped_gemm_f32out(const void* A, const void* B, const int32_t* offsets, int64_t rows, int E,

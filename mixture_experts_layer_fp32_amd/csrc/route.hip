@@ -28,6 +28,11 @@ namespace moe {
 namespace {
 
 constexpr int kRouteThreads = 256;
+
+struct RouterGemmPlan {
+  int bm;      // tile rows of the router GEMM (128 or 256)
+  int ksplit;  // K slices
+};
 constexpr int kKC = 32;  // H chunk staged per iteration
 
 template <typename XT>
@@ -520,26 +525,34 @@ size_t split_bytes(int H, int E) { return static_cast<size_t>(3) * padded_expert
 // grouped-GEMM kernel (fp32 output, one row band per 128 tokens), summed per expert by top-k.
 bool logits_by_gemm(int H, int E) { return padded_experts(E) >= 64 && H % 64 == 0; }
 
-// K slices of the router GEMM.  With few output tiles (T/128 x 3Ep/256 of them) the projection
-// leaves CUs idle, but every slice writes a [T][3Ep] fp32 partial product that the top-k kernel
-// reads back.  Estimated cost, in 64-deep K steps of one tile: rounds of 256 single-workgroup
-// CUs x K steps per slice, plus the partial products at about 4 MB of HBM traffic per K step
-// (measured on the DeepSeek- and Qwen3-shaped routers: 1 and 2 slices, against 4 from a rule
-// that only filled two rounds of CUs: 169 -> 164 us and 98 -> 85 us).  Powers of two up to 8
-// that keep >= 8 K steps per slice; ties go to fewer slices.  A pure function of (T, H, E): the
-// workspace size and the launch must agree.
-int router_ksplit(int64_t T, int H, int E) {
-  const int64_t tiles = ceil_div(T, 128) * ceil_div(3 * padded_experts(E), 256);
+// Tile height and K slices of the router GEMM.  With few output tiles (T/bm x 3Ep/256 of them)
+// the projection leaves CUs idle, but every slice writes a [T][3Ep] fp32 partial product that the
+// top-k kernel reads back.  Estimated cost, in 64-deep K steps of a 128-row tile: rounds of 256
+// single-workgroup CUs x K steps per slice x the tile's step cost (a 256-row step costs 1.3
+// 128-row steps: its weight loads and fragment reads serve twice the rows), plus the partial
+// products at about 8 MB of HBM traffic per K step.  Measured GEMM times of the candidates
+// (DeepSeek-V3-shaped router, T=8192 H=7168 3Ep=768: 128-row tiles 1 slice 132 us, 2 slices
+// 131, 4 slices 130; 256-row tiles 1 slice 169, 2 slices 114, 4 slices 119.  Qwen3-235B-shaped,
+// T=8192 H=4096 3Ep=384: 128-row 1/2/4 slices 74/52/55 us, 256-row 2/4 slices 63/46 us).  Powers
+// of two up to 8 that keep >= 8 K steps per slice; ties go to 128-row tiles, then fewer slices.
+// A pure function of (T, H, E): the workspace size and the launch must agree.
+RouterGemmPlan router_gemm_plan(int64_t T, int H, int E) {
+  const int64_t ntiles = ceil_div(3 * padded_experts(E), 256);
   const int nk = H / 64;
-  const double slice_steps = static_cast<double>(T) * 3 * padded_experts(E) * 8 / 4.0e6;
-  int best = 1;
-  double best_cost = 0.0;
-  for (int ks = 1; ks <= 8; ks *= 2) {
-    if (nk % ks != 0 || (ks > 1 && nk / ks < 8)) break;
-    const double cost = static_cast<double>(ceil_div(tiles * ks, 256)) * (nk / ks) + ks * slice_steps;
-    if (ks == 1 || cost < best_cost) {
-      best = ks;
-      best_cost = cost;
+  const double slice_steps = static_cast<double>(T) * 3 * padded_experts(E) * 8 / 8.0e6;
+  RouterGemmPlan best{128, 1};
+  double best_cost = -1.0;
+  for (int bm : {128, 256}) {
+    const int64_t tiles = ceil_div(T, bm) * ntiles;
+    const double step = bm == 256 ? 1.3 : 1.0;
+    for (int ks = 1; ks <= 8; ks *= 2) {
+      if (nk % ks != 0 || (ks > 1 && nk / ks < 8)) break;
+      const double cost =
+          static_cast<double>(ceil_div(tiles * ks, 256)) * (nk / ks) * step + ks * slice_steps;
+      if (best_cost < 0.0 || cost < best_cost) {
+        best = RouterGemmPlan{bm, ks};
+        best_cost = cost;
+      }
     }
   }
   return best;
@@ -583,7 +596,7 @@ size_t hslice_bytes(int64_t T, int H, int E) {
 }
 
 size_t parts_bytes(int64_t T, int H, int E) {
-  return (static_cast<size_t>(router_ksplit(T, H, E)) * T * 3 * padded_experts(E) * sizeof(float) + 255) &
+  return (static_cast<size_t>(router_gemm_plan(T, H, E).ksplit) * T * 3 * padded_experts(E) * sizeof(float) + 255) &
          ~static_cast<size_t>(255);
 }
 
@@ -596,7 +609,8 @@ hipError_t launch_logits_bf16(const bf16_t* x, const float* w, float* logits, fl
     hipLaunchKernelGGL(route_split_kn_kernel, dim3(gs), dim3(kRouteThreads), 0, stream, w, H, E, Ep, wsplit);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return launch_dense_gemm_f32out(x, wsplit, T, H, 3 * Ep, parts, stream, router_ksplit(T, H, E));
+    const RouterGemmPlan plan = router_gemm_plan(T, H, E);
+    return launch_dense_gemm_f32out(x, wsplit, T, H, 3 * Ep, parts, stream, plan.ksplit, plan.bm);
   }
   hipLaunchKernelGGL(route_split_kernel, dim3(gs), dim3(kRouteThreads), 0, stream, w, H, E, Ep, wsplit);
   if (Ep <= 16) {
@@ -663,7 +677,7 @@ hipError_t launch_route(const void* x, int x_dt, const float* w_router, const fl
   if (err != hipSuccess) return err;
   dim3 grid(static_cast<unsigned>(ceil_div(T, kRouteThreads / kWave)));
   hipLaunchKernelGGL(route_topk_kernel, grid, dim3(kRouteThreads), 0, stream, lg, hs > 1 ? hparts : parts,
-                     padded_experts(E), parts ? router_ksplit(T, H, E) : 1, hs, bias, T, E, k, score, norm, ids,
+                     padded_experts(E), parts ? router_gemm_plan(T, H, E).ksplit : 1, hs, bias, T, E, k, score, norm, ids,
                      gates);
   return hipGetLastError();
 }
