@@ -672,10 +672,15 @@ hipError_t expert_group_backward(const WT* x, const WT* dy, const WT* w1, const 
                                   2 * F, H, u, 2 * F, 0),
                              s);
   if (e == hipSuccess) e = mark(1);
-  if (e == hipSuccess)
-    e = launch_bwd_gemm<kNT>(args(dy, H, src, gx, w2, H, int64_t{F} * H, nullptr, 0, offsets, rows, G, 0, F, H, dhp,
-                                  F, 0),
-                             s);
+  // dh' = dy[src] W2^T: bf16 on the forward's kernel with the weight read as stored ([F, H] = [N, K])
+  if (e == hipSuccess) {
+    if constexpr (std::is_same<WT, bf16_t>::value)
+      e = launch_grouped_gemm_nt_f32out(dy, w2, offsets, rows, G, H, F, dhp, s, src);
+    else
+      e = launch_bwd_gemm<kNT>(args(dy, H, src, gx, w2, H, int64_t{F} * H, nullptr, 0, offsets, rows, G, 0, F, H,
+                                    dhp, F, 0),
+                               s);
+  }
   if (e == hipSuccess) e = mark(2);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_swiglu_kernel<WT>, dim3(static_cast<unsigned>(rows)), dim3(256), 0, s, u, dhp, gates,
@@ -687,10 +692,16 @@ hipError_t expert_group_backward(const WT* x, const WT* dy, const WT* w1, const 
                                   G, F, H, 0, dw2, H, int64_t{F} * H),
                              s);
   if (e == hipSuccess) e = mark(4);
-  if (e == hipSuccess)
-    e = launch_bwd_gemm<kNT>(args(static_cast<const WT*>(du), 2 * F, static_cast<const int32_t*>(nullptr), rows, w1,
-                                  2 * F, int64_t{H} * 2 * F, nullptr, 0, offsets, rows, G, 0, H, 2 * F, dxp, H, 0),
-                             s);
+  // dx_perm = du W1^T (W1 [H, 2F] = [N, K] as stored)
+  if (e == hipSuccess) {
+    if constexpr (std::is_same<WT, bf16_t>::value)
+      e = launch_grouped_gemm_nt_f32out(du, w1, offsets, rows, G, 2 * F, H, dxp, s, nullptr);
+    else
+      e = launch_bwd_gemm<kNT>(args(static_cast<const WT*>(du), 2 * F, static_cast<const int32_t*>(nullptr), rows,
+                                    w1, 2 * F, int64_t{H} * 2 * F, nullptr, 0, offsets, rows, G, 0, H, 2 * F, dxp, H,
+                                    0),
+                               s);
+  }
   if (e == hipSuccess) e = mark(5);
   if (e == hipSuccess)
     e = launch_bwd_gemm<kTN>(args(x, H, src, gx, static_cast<const WT*>(du), 2 * F, 0, static_cast<const int32_t*>(nullptr),

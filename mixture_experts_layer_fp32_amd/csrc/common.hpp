@@ -185,6 +185,12 @@ hipError_t launch_dense_gemm_f32out(const void* A, const void* B, int64_t rows, 
 hipError_t launch_grouped_gemm_f32out(const void* A, const void* B, const int32_t* offsets, int64_t rows, int E,
                                       int K, int N, float* out, hipStream_t stream, const int32_t* gather);
 
+// The same with the weight read transposed: out[p, n] = sum_k A[gather ? gather[p] : p, k] B_e[n, k],
+// B [E, N, K] K-contiguous (the stored W2 [F, H] and W1 [H, 2F] of an expert read as W2^T, W1^T),
+// bf16 operands, K % 64 == 0, N % 8 == 0, fp32 out.
+hipError_t launch_grouped_gemm_nt_f32out(const void* A, const void* B, const int32_t* offsets, int64_t rows, int E,
+                                         int K, int N, float* out, hipStream_t stream, const int32_t* gather);
+
 // FP8 (E4M3) path: x_perm codes + [rows, H/128] scales, weights as codes + 128x128-block scales;
 // the SwiGLU output h is re-quantised to E4M3 in 1x128 blocks in the scratch buffer
 // (fp8_hidden_bytes(rows, F) bytes of codes, then [rows, F/128] fp32 scales).

@@ -33,7 +33,8 @@ constexpr int kThreads = 256;  // fp32 path
 
 // ------------------------------------------------------------------------------ bf16 path
 // A: [rows, K] bf16 row-major (x_perm or h).  B: per expert [K, N] bf16 (N-contiguous, the
-// layout the weights arrive in).
+// layout the weights arrive in), or with BNK per expert [N, K] (K-contiguous: the transposed
+// weight products of the backward, dh' = dy W2^T and dx_perm = du W1^T, read W2 and W1 as stored).
 // SWIGLU: out h [rows, F] (F = N / 2), tile n covers gate cols n*128.. and up cols F + n*128..
 // else:   out [rows, N], tile n covers cols n*256..
 //
@@ -52,6 +53,8 @@ constexpr int kThreads = 256;  // fp32 path
 // lane s addresses k-row 8 (s / 32) + 4 r + (s % 16) / 4 at column 16 ((s / 16) % 2) +
 // 4 (s % 4) of the fragment and destination lane d collects column d % 32 for 4 consecutive k.
 // The swizzles spread every fragment read of a 16-lane group over distinct banks.
+// BNK: a B stage is BN rows (columns n) x 128 B laid out, loaded and read exactly like an A
+// stage (chunk c of row n at c ^ ((n >> 1) & 7), one ds_read_b128 per fragment).
 //
 // Iteration kt (four 16-deep k-steps): each MFMA of k-step s is followed by one LDS read of the
 // fragments of k-step s + 1 (in the order the MFMAs consume them) and, in some slots, one direct
@@ -77,7 +80,7 @@ struct Bf16Rings {
   static constexpr int SMEM = NA * A_BYTES + NB * B_BYTES;
 };
 
-template <int BM, int WM, bool SWIGLU, bool OUT_F32, int S>
+template <int BM, int WM, bool SWIGLU, bool OUT_F32, int S, bool BNK = false>
 __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const int32_t* __restrict__ offsets,
     int64_t rows, int E, int K, int ldb, int NT, void* __restrict__ out, int ncu,
@@ -141,8 +144,20 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
   }
   // B round p of wave w covers k-rows 2 (8p + w) + lane / 32 (1 KB = 2 k-rows x 512 B); stored
   // chunk lane % 32 holds logical chunk (lane % 32) ^ 4 ((2w + lane / 32) & 3).
-  const bf16_t* b_src;
-  {
+  // BNK: round p of wave w covers B rows (columns) (8p + w) * 8 + lane / 8, as for A.
+  const bf16_t* b_src = nullptr;
+  const bf16_t* b_nk[BNK ? B_ROUNDS : 1];
+  if constexpr (BNK) {
+#pragma unroll
+    for (int p = 0; p < B_ROUNDS; ++p) {
+      const int r = (NWAVE * p + wave) * 8 + lane / 8;
+      int64_t n = SWIGLU ? (r < 128 ? static_cast<int64_t>(tm.nt) * 128 + r
+                                    : ldb / 2 + static_cast<int64_t>(tm.nt) * 128 + (r - 128))
+                         : static_cast<int64_t>(tm.nt) * kBN + r;
+      if (n >= ldb) n = 0;  // columns past the matrix edge re-read column 0 (never stored)
+      b_nk[p] = B + (static_cast<int64_t>(tm.expert) * ldb + n) * K + k_first + (((lane % 8) ^ ((r >> 1) & 7)) * 8);
+    }
+  } else {
     const int b_lchunk = (lane % 32) ^ (4 * ((2 * wave + lane / 32) & 3));
     int64_t b_col;
     if (SWIGLU) {
@@ -175,7 +190,12 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
       const uint32_t bbase = b_stage(tb);
       const bf16_t* bs = b_src + static_cast<int64_t>(tb) * b_kstep;
 #pragma unroll
-      for (int p = 0; p < B_ROUNDS; ++p) lds_dma16(bs + p * b_round, bbase + (NWAVE * p + wave) * 1024);
+      for (int p = 0; p < B_ROUNDS; ++p) {
+        if constexpr (BNK)
+          lds_dma16(b_nk[p] + static_cast<int64_t>(tb) * kBKT, bbase + (NWAVE * p + wave) * 1024);
+        else
+          lds_dma16(bs + p * b_round, bbase + (NWAVE * p + wave) * 1024);
+      }
     }
   };
   // Loads issued after both A and B tile t + 1 by the time iteration t waits (load group j: A
@@ -196,8 +216,16 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     a_row_off[i] = r * 128;
     a_sw[i] = (r >> 1) & 7;
   }
-  uint32_t b_off[FN][2];
-  {
+  uint32_t b_off[BNK ? 1 : FN][2];
+  uint32_t b_row_off[BNK ? FN : 1], b_sw[BNK ? FN : 1];
+  if constexpr (BNK) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = (SWIGLU ? j * 128 + wn * 32 : wn * 64 + j * 32) + lane % 32;
+      b_row_off[j] = r * 128;
+      b_sw[j] = (r >> 1) & 7;
+    }
+  } else {
     const int g = lane / 16, h = lane / 32, a4 = lane % 4, e = (lane % 16) / 4;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -232,13 +260,19 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     constexpr int NLA = NL > 0 ? NL : 1;
     bf16x8_t af[2][NLA], bfr[2][FN];
     auto read_b = [&](uint32_t bbase, int ks, int buf, int j) {
-      v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          reinterpret_cast<lds_v4i16_t*>(static_cast<uintptr_t>(bbase + b_off[j][0] + ks * 16 * kBRow)));
-      v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          reinterpret_cast<lds_v4i16_t*>(static_cast<uintptr_t>(bbase + b_off[j][1] + ks * 16 * kBRow)));
-      typedef short v8i16_t __attribute__((ext_vector_type(8)));
-      v8i16_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      bfr[buf][j] = __builtin_bit_cast(bf16x8_t, both);
+      if constexpr (BNK) {
+        const uint32_t chunk = ks * 2 + khalf;
+        bfr[buf][j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
+            static_cast<uintptr_t>(bbase + b_row_off[j] + ((chunk ^ b_sw[j]) << 4)));
+      } else {
+        v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_v4i16_t*>(static_cast<uintptr_t>(bbase + b_off[j][0] + ks * 16 * kBRow)));
+        v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_v4i16_t*>(static_cast<uintptr_t>(bbase + b_off[j][1] + ks * 16 * kBRow)));
+        typedef short v8i16_t __attribute__((ext_vector_type(8)));
+        v8i16_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        bfr[buf][j] = __builtin_bit_cast(bf16x8_t, both);
+      }
     };
     auto read_a = [&](uint32_t abase, int ks, int buf, int i) {
       const uint32_t chunk = ks * 2 + khalf;
@@ -275,7 +309,12 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks % 2][i], bfr[ks % 2][j], acc[i][j], 0, 0, 0);
         }
         if (q < NR) read_unit(kt, ks + 1, (ks + 1) % 2, q);
-        if (q < BL && do_b) lds_dma16(bs + (B0 + q) * b_round, bbase + (NWAVE * (B0 + q) + wave) * 1024);
+        if (q < BL && do_b) {
+          if constexpr (BNK)
+            lds_dma16(b_nk[B0 + q] + static_cast<int64_t>(tb) * kBKT, bbase + (NWAVE * (B0 + q) + wave) * 1024);
+          else
+            lds_dma16(bs + (B0 + q) * b_round, bbase + (NWAVE * (B0 + q) + wave) * 1024);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -491,12 +530,12 @@ int device_cus() {
   return cached[dev];
 }
 
-template <int BM, bool SWIGLU, bool OUT_F32, int WM = 2, int S = 1>
+template <int BM, bool SWIGLU, bool OUT_F32, int WM = 2, int S = 1, bool BNK = false>
 hipError_t launch_bf16(const bf16_t* A, const bf16_t* B, const int32_t* offsets, int64_t rows, int E,
                        int K, int ldb, int NT, void* out, hipStream_t stream, int ncu = 0,
                        const int32_t* gather = nullptr, int ksplit = 1, const float* row_scale = nullptr) {
   constexpr int smem = Bf16Rings<BM>::SMEM;
-  auto kern = gemm_bf16_kernel<BM, WM, SWIGLU, OUT_F32, S>;
+  auto kern = gemm_bf16_kernel<BM, WM, SWIGLU, OUT_F32, S, BNK>;
   // once per instantiation (and never inside a stream capture after the first eager call)
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, smem);
@@ -565,6 +604,17 @@ hipError_t launch_grouped_gemm_f32out(const void* A, const void* B, const int32_
   const bf16_t* b = static_cast<const bf16_t*>(B);
   return big ? launch_bf16<256, false, true>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather)
              : launch_bf16<128, false, true>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather);
+}
+
+hipError_t launch_grouped_gemm_nt_f32out(const void* A, const void* B, const int32_t* offsets, int64_t rows, int E,
+                                         int K, int N, float* out, hipStream_t stream, const int32_t* gather) {
+  if (rows <= 0) return hipSuccess;
+  const bool big = offsets == nullptr ? rows >= 192 : rows >= 192 * static_cast<int64_t>(E);
+  const int nt = static_cast<int>(ceil_div(N, kBN));
+  const bf16_t* a = static_cast<const bf16_t*>(A);
+  const bf16_t* b = static_cast<const bf16_t*>(B);
+  return big ? launch_bf16<256, false, true, 2, 1, true>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather)
+             : launch_bf16<128, false, true, 2, 1, true>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather);
 }
 
 hipError_t launch_grouped_swiglu(const void* x_perm, const void* x_scales, int dt,
