@@ -27,6 +27,11 @@
 //  * bwd_swiglu_kernel: per permuted row, the SwiGLU backward and the gate gradient dg_p.
 //  * bwd_gate_kernel: per token, the softmax / sigmoid (+ renormalisation) Jacobian.
 //  * bwd_dx_kernel: per token, dx = sum_j dxp[row_map(t, j)] + shared expert + router terms.
+// With bf16 operands the expert GEMMs run on the forward's grouped-GEMM kernel instead (gemm.hip):
+// u as there, dh' and dxp with the weight read as stored ([N, K]), and dW1, dW2 as independent
+// per-expert products over the expert's rows padded to a multiple of 64: dW1_e = (x[src]^T)_e du_e
+// and dW2_e = ((g h)^T)_e dy[src]_e, the transposed operands written by bwd_transpose_pad_kernel
+// (zeros in the padding columns) and dy gathered into row order by bwd_gather_rows_kernel.
 #include "gemm_common.hpp"
 
 namespace moe {
@@ -642,12 +647,116 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
   }
 }
 
+// The padded contraction table of the per-expert weight-gradient products: kinfo[0 .. E] the
+// exclusive prefix of the experts' row counts rounded up to 64, kinfo[E + 1 .. 2E + 1] the
+// experts' row offsets (clamped like the forward's tile map; offsets null: one group of `rows`).
+// One workgroup of 256 threads, E <= 512.
+__global__ __launch_bounds__(256) void bwd_kinfo_kernel(const int32_t* __restrict__ offsets, int64_t rows, int E,
+                                                        int32_t* __restrict__ kinfo) {
+  __shared__ int s[kMaxExpertsLds];
+  for (int e = static_cast<int>(threadIdx.x); e < E; e += static_cast<int>(blockDim.x)) {
+    int64_t base = 0, M = rows;
+    if (offsets) expert_rows(offsets, e, rows, base, M);
+    s[e + 1] = static_cast<int>((M + 63) / 64 * 64);
+    kinfo[E + 1 + e] = static_cast<int32_t>(base);
+    if (e == E - 1) kinfo[2 * E + 1] = static_cast<int32_t>(base + M);
+  }
+  scan_prefix(s, E);
+  for (int e = static_cast<int>(threadIdx.x); e <= E; e += static_cast<int>(blockDim.x)) kinfo[e] = s[e];
+}
+
+// dst [C, ld] (bf16) = the per-expert transposes of the rows of src [*, C]: padded column
+// kinfo[e] + i holds row kinfo[E + 1 + e] + i of expert e (read at gather[row] when gather is
+// given), the padding columns up to kinfo[e + 1] hold zeros; columns past kinfo[E] are not
+// written.  Tiles of 64 columns x 64 rows of dst staged through LDS; grid (ld / 64, C / 64),
+// C % 64 == 0.
+__global__ __launch_bounds__(256) void bwd_transpose_pad_kernel(const bf16_t* __restrict__ src,
+                                                                const int32_t* __restrict__ gather, int C,
+                                                                const int32_t* __restrict__ kinfo, int E,
+                                                                bf16_t* __restrict__ dst, int64_t ld) {
+  __shared__ uint32_t tile[64][33];  // [padded column q][pairs of source columns], odd pitch
+  const int64_t q0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int c0 = static_cast<int>(blockIdx.y) * 64;
+  if (q0 >= kinfo[E]) return;
+  int lo = 0, hi = E - 1;  // the expert whose padded range holds q0 (ranges are multiples of 64)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (kinfo[mid] <= q0) lo = mid; else hi = mid - 1;
+  }
+  const int64_t off = q0 - kinfo[lo];
+  const int64_t first = kinfo[E + 1 + lo] + off;
+  const int64_t valid = kinfo[E + 2 + lo] - kinfo[E + 1 + lo] - off;  // >= 1
+  const int tid = static_cast<int>(threadIdx.x);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid / 8 + 32 * j, cc = (tid % 8) * 8;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (i < valid) {
+      int64_t r = first + i;
+      if (gather) r = gather[r];
+      v = *reinterpret_cast<const u32x4_t*>(src + r * C + c0 + cc);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) tile[i][cc / 2 + t] = v[t];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int ci = tid / 8 + 32 * j, qq = (tid % 8) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t a = tile[qq + 2 * t][ci / 2], b = tile[qq + 2 * t + 1][ci / 2];
+      w[t] = (ci % 2) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+    *reinterpret_cast<u32x4_t*>(dst + static_cast<int64_t>(c0 + ci) * ld + q0 + qq) = u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// dst [rows + pad, C] (bf16): row p = src[gather ? gather[p] : p] for p < rows, zeros after.
+// One workgroup per row, C % 8 == 0.
+__global__ __launch_bounds__(256) void bwd_gather_rows_kernel(const bf16_t* __restrict__ src,
+                                                              const int32_t* __restrict__ gather, int64_t rows, int C,
+                                                              bf16_t* __restrict__ dst) {
+  const int64_t p = blockIdx.x;
+  u32x4_t* d = reinterpret_cast<u32x4_t*>(dst + p * C);
+  if (p < rows) {
+    const u32x4_t* sp = reinterpret_cast<const u32x4_t*>(src + (gather ? static_cast<int64_t>(gather[p]) : p) * C);
+    for (int c = static_cast<int>(threadIdx.x); c < C / 8; c += 256) d[c] = sp[c];
+  } else {
+    for (int c = static_cast<int>(threadIdx.x); c < C / 8; c += 256) d[c] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
+// Rows a per-expert product's B operand may read past the group's last row (its padding).
+constexpr int kPadRows = 64;
+
+// Padded contraction columns of the weight-gradient products: sum_e roundup(M_e, 64) <= rows + 64 E.
+int64_t padded_cols(int64_t rows, int E) { return rows + static_cast<int64_t>(kPadRows) * E; }
+
+// dW_e = (A^T)_e B_e for the groups of offsets (null: one group): the padded table, the transposed
+// activation, the product.  B holds rows + kPadRows rows (the last kPadRows finite).
+hipError_t wgrad_bf16(const bf16_t* act, const int32_t* act_gather, int C, const bf16_t* B, int N,
+                      const int32_t* offsets, int64_t rows, int G, int32_t* kinfo, bf16_t* at, int64_t ld_t,
+                      float* dw, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_kinfo_kernel, dim3(1), dim3(256), 0, s, offsets, rows, G, kinfo);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t ld = padded_cols(rows, G);
+  if (ld > ld_t) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_transpose_pad_kernel, dim3(static_cast<unsigned>(ceil_div(ld, 64)), C / 64), dim3(256), 0,
+                     s, act, act_gather, C, kinfo, G, at, ld_t);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return launch_batched_gemm_f32out(at, ld_t, B, kinfo, G, C, N, dw, s);
+}
+
 // The backward of one SwiGLU expert group (routed: offsets/src/gates given; shared: all null).
 template <typename WT>
 hipError_t expert_group_backward(const WT* x, const WT* dy, const WT* w1, const WT* w2, const int32_t* offsets,
                                  const int32_t* src, const float* gates, const int32_t* row_map, int64_t T, int k,
                                  int64_t rows, int G, int H, int F, float* u, float* dhp, WT* du, WT* gh, float* dg,
-                                 float* dxp, float* dw1, float* dw2, hipStream_t s, hipEvent_t const* ev) {
+                                 float* dxp, float* dw1, float* dw2, int32_t* kinfo, void* xt, void* dyp,
+                                 int64_t ld_t, hipStream_t s, hipEvent_t const* ev) {
   auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord(ev[i], s) : hipSuccess; };
   const int64_t gx = src ? T : rows;
   if (rows == 0) {  // no rows: every weight gradient is zero (TN tiles without K steps), nothing else runs
@@ -687,10 +796,21 @@ hipError_t expert_group_backward(const WT* x, const WT* dy, const WT* w1, const 
                      row_map, src, T, k, F, du, gh, dg);
   e = hipGetLastError();
   if (e == hipSuccess) e = mark(3);
-  if (e == hipSuccess)
-    e = launch_bwd_gemm<kTN>(args(gh, F, static_cast<const int32_t*>(nullptr), rows, dy, H, 0, src, gx, offsets, rows,
-                                  G, F, H, 0, dw2, H, int64_t{F} * H),
-                             s);
+  // dW2 = (g h)^T dy[src]: bf16 per expert on the forward's kernel (dy gathered into row order first)
+  if (e == hipSuccess) {
+    if constexpr (std::is_same<WT, bf16_t>::value) {
+      hipLaunchKernelGGL(bwd_gather_rows_kernel, dim3(static_cast<unsigned>(rows + kPadRows)), dim3(256), 0, s, dy,
+                         src, rows, H, static_cast<bf16_t*>(dyp));
+      e = hipGetLastError();
+      if (e == hipSuccess)
+        e = wgrad_bf16(gh, nullptr, F, static_cast<const bf16_t*>(dyp), H, offsets, rows, G, kinfo,
+                       static_cast<bf16_t*>(xt), ld_t, dw2, s);
+    } else {
+      e = launch_bwd_gemm<kTN>(args(gh, F, static_cast<const int32_t*>(nullptr), rows, dy, H, 0, src, gx, offsets,
+                                    rows, G, F, H, 0, dw2, H, int64_t{F} * H),
+                               s);
+    }
+  }
   if (e == hipSuccess) e = mark(4);
   // dx_perm = du W1^T (W1 [H, 2F] = [N, K] as stored)
   if (e == hipSuccess) {
@@ -703,10 +823,21 @@ hipError_t expert_group_backward(const WT* x, const WT* dy, const WT* w1, const 
                                s);
   }
   if (e == hipSuccess) e = mark(5);
-  if (e == hipSuccess)
-    e = launch_bwd_gemm<kTN>(args(x, H, src, gx, static_cast<const WT*>(du), 2 * F, 0, static_cast<const int32_t*>(nullptr),
-                                  rows, offsets, rows, G, H, 2 * F, 0, dw1, 2 * F, int64_t{H} * 2 * F),
-                             s);
+  // dW1 = x[src]^T du: bf16 per expert on the forward's kernel (du's kPadRows rows after its end zeroed)
+  if (e == hipSuccess) {
+    if constexpr (std::is_same<WT, bf16_t>::value) {
+      hipLaunchKernelGGL(bwd_gather_rows_kernel, dim3(kPadRows), dim3(256), 0, s, du, nullptr, int64_t{0}, 2 * F,
+                         du + rows * 2 * F);
+      e = hipGetLastError();
+      if (e == hipSuccess)
+        e = wgrad_bf16(x, src, H, du, 2 * F, offsets, rows, G, kinfo, static_cast<bf16_t*>(xt), ld_t, dw1, s);
+    } else {
+      e = launch_bwd_gemm<kTN>(args(x, H, src, gx, static_cast<const WT*>(du), 2 * F, 0,
+                                    static_cast<const int32_t*>(nullptr), rows, offsets, rows, G, H, 2 * F, 0, dw1,
+                                    2 * F, int64_t{H} * 2 * F),
+                               s);
+    }
+  }
   if (e == hipSuccess) e = mark(6);
   return e;
 }
@@ -722,13 +853,13 @@ hipError_t layer_backward(const BackwardShape& sh, const BackwardIO& io, const B
   if (e == hipSuccess)
     e = expert_group_backward<WT>(x, dy, static_cast<const WT*>(io.w1), static_cast<const WT*>(io.w2), io.offsets,
                                   io.src_token, io.gates, io.row_map, T, sh.k, R, sh.E, sh.H, sh.F, ws.u, ws.dhp,
-                                  static_cast<WT*>(ws.du), static_cast<WT*>(ws.gh), ws.dg, ws.dxp, io.dw1, io.dw2, s,
-                                  ev);
+                                  static_cast<WT*>(ws.du), static_cast<WT*>(ws.gh), ws.dg, ws.dxp, io.dw1, io.dw2,
+                                  ws.kinfo, ws.xt, ws.dyp, ws.ld_t, s, ev);
   if (e == hipSuccess && sh.Fs > 0)
     e = expert_group_backward<WT>(x, dy, static_cast<const WT*>(io.ws1), static_cast<const WT*>(io.ws2), nullptr,
                                   nullptr, nullptr, nullptr, T, 1, T, 1, sh.H, sh.Fs, ws.us, ws.dhs,
                                   static_cast<WT*>(ws.dus), static_cast<WT*>(ws.ghs), nullptr, ws.dxs, io.dws1,
-                                  io.dws2, s, nullptr);
+                                  io.dws2, ws.kinfo_s, ws.xt, ws.dyp, ws.ld_t, s, nullptr);
   if (e == hipSuccess) e = mark(7);
   if (e != hipSuccess) return e;
   if (T > 0) {
@@ -787,9 +918,11 @@ BackwardScratch carve_backward(const BackwardShape& sh, int dt, void* base, size
   BackwardScratch w{};
   const int S = router_slices(T, sh.H, sh.E);
   w.dwr_part = S > 1 ? static_cast<float*>(take(static_cast<size_t>(S) * sh.H * sh.E * 4)) : nullptr;
+  const bool bf16 = dt != 0;
+  const int64_t pad = bf16 ? kPadRows : 0;  // zero rows after du and dy's row-order copy (bf16 weight gradients)
   w.u = static_cast<float*>(take(R * 2 * sh.F * 4));
   w.dhp = static_cast<float*>(take(R * sh.F * 4));
-  w.du = take(R * 2 * sh.F * cts);
+  w.du = take((R + pad) * 2 * sh.F * cts);
   w.gh = take(R * sh.F * cts);
   w.dg = static_cast<float*>(take(R * 4));
   w.dxp = static_cast<float*>(take(R * sh.H * 4));
@@ -798,9 +931,19 @@ BackwardScratch carve_backward(const BackwardShape& sh, int dt, void* base, size
   if (sh.Fs > 0) {
     w.us = static_cast<float*>(take(T * 2 * sh.Fs * 4));
     w.dhs = static_cast<float*>(take(T * sh.Fs * 4));
-    w.dus = take(T * 2 * sh.Fs * cts);
+    w.dus = take((T + pad) * 2 * sh.Fs * cts);
     w.ghs = take(T * sh.Fs * cts);
     w.dxs = static_cast<float*>(take(T * sh.H * 4));
+  }
+  if (bf16) {
+    // one transposed activation at a time ([H or F or Fs][ld_t]); ld_t covers both groups' padding
+    const int64_t ld_r = padded_cols(R, sh.E), ld_s = sh.Fs > 0 ? padded_cols(T, 1) : 0;
+    w.ld_t = ((ld_r > ld_s ? ld_r : ld_s) + 63) / 64 * 64;
+    const int64_t cmax_ = sh.H > sh.F ? (sh.H > sh.Fs ? sh.H : sh.Fs) : (sh.F > sh.Fs ? sh.F : sh.Fs);
+    w.kinfo = static_cast<int32_t*>(take(static_cast<size_t>(2 * (sh.E + 1)) * 4));
+    w.kinfo_s = static_cast<int32_t*>(take(4 * 4));
+    w.xt = take(static_cast<size_t>(cmax_) * w.ld_t * 2);
+    w.dyp = take(static_cast<size_t>((R > T ? R : T) + pad) * sh.H * 2);
   }
   if (bytes) *bytes = used;
   return w;

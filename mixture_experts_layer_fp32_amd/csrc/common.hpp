@@ -191,6 +191,13 @@ hipError_t launch_grouped_gemm_f32out(const void* A, const void* B, const int32_
 hipError_t launch_grouped_gemm_nt_f32out(const void* A, const void* B, const int32_t* offsets, int64_t rows, int E,
                                          int K, int N, float* out, hipStream_t stream, const int32_t* gather);
 
+// E independent products out_e [M, N] (fp32, out_e at out + e M N) = A_e . B_e, bf16 operands:
+// A_e is columns [P_e, P_{e+1}) of A [M, lda] (P = kinfo[0 .. E], multiples of 64; A's columns
+// past an expert's own rows hold zeros) and B_e is P_{e+1} - P_e rows of B [*, N] from row
+// kinfo[E + 1 + e] on (rows that B must hold, finite).  lda % 8 == 0, N % 8 == 0.
+hipError_t launch_batched_gemm_f32out(const void* A, int64_t lda, const void* B, const int32_t* kinfo, int E, int M,
+                                      int N, float* out, hipStream_t stream);
+
 // FP8 (E4M3) path: x_perm codes + [rows, H/128] scales, weights as codes + 128x128-block scales;
 // the SwiGLU output h is re-quantised to E4M3 in 1x128 blocks in the scratch buffer
 // (fp8_hidden_bytes(rows, F) bytes of codes, then [rows, F/128] fp32 scales).
@@ -253,6 +260,12 @@ struct BackwardScratch {
   float *us, *dhs;
   void *dus, *ghs;
   float* dxs;
+  // bf16 weight gradients as per-expert products (launch_batched_gemm_f32out): the padded
+  // contraction table (2 (E + 1) ints, routed and shared), the transposed zero-padded activations
+  // ([H or F][ld_t]) and dy gathered into expert-row order with 64 zero rows after the end
+  int32_t *kinfo, *kinfo_s;
+  void *xt, *dyp;
+  int64_t ld_t;
 };
 // Row slices of the router-weight gradient x^T dlogits (its [H, E] output has few tiles).
 int router_slices(int64_t T, int H, int E);

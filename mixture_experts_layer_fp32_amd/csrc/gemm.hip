@@ -53,8 +53,14 @@ constexpr int kThreads = 256;  // fp32 path
 // lane s addresses k-row 8 (s / 32) + 4 r + (s % 16) / 4 at column 16 ((s / 16) % 2) +
 // 4 (s % 4) of the fragment and destination lane d collects column d % 32 for 4 consecutive k.
 // The swizzles spread every fragment read of a 16-lane group over distinct banks.
-// BNK: a B stage is BN rows (columns n) x 128 B laid out, loaded and read exactly like an A
-// stage (chunk c of row n at c ^ ((n >> 1) & 7), one ds_read_b128 per fragment).
+// MODE kModeNT: B is [N, K]; a B stage is BN rows (columns n) x 128 B laid out, loaded and read
+// exactly like an A stage (chunk c of row n at c ^ ((n >> 1) & 7), one ds_read_b128 per fragment).
+// MODE kModeBatchK: independent per-expert GEMMs out_e [M, N] = A_e [M, K_e] . B_e [K_e, N] (the
+// weight gradients of the backward) with a contraction of its own per expert, padded to a multiple
+// of 64; `offsets` points at 2 (E + 1) ints: the padded contraction prefix P (A_e is columns
+// [P_e, P_{e+1}) of A, whose row stride is the K argument; its padding columns hold zeros) and
+// then the first B row of every expert (B_e is rows offsets[E + 1 + e] .. + P_{e+1} - P_e of B;
+// the rows past the expert's own meet A's zero columns).  `rows` is M; out_e starts at e M N.
 //
 // Iteration kt (four 16-deep k-steps): each MFMA of k-step s is followed by one LDS read of the
 // fragments of k-step s + 1 (in the order the MFMAs consume them) and, in some slots, one direct
@@ -80,7 +86,7 @@ struct Bf16Rings {
   static constexpr int SMEM = NA * A_BYTES + NB * B_BYTES;
 };
 
-template <int BM, int WM, bool SWIGLU, bool OUT_F32, int S, bool BNK = false>
+template <int BM, int WM, bool SWIGLU, bool OUT_F32, int S, int MODE = kModeNN>
 __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, const int32_t* __restrict__ offsets,
     int64_t rows, int E, int K, int ldb, int NT, void* __restrict__ out, int ncu,
@@ -99,6 +105,8 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
   constexpr int RPT = A_ROUNDS + B_ROUNDS;
   static_assert(NA >= 2 && NB >= NA, "ring depths");
   static_assert(kMaxExpertsLds * 4 <= B_BYTES, "tile-map prefix fits in the first B stage");
+  static_assert(MODE != kModeBatchK || (OUT_F32 && !SWIGLU && S == 1), "batched mode: plain fp32 out");
+  constexpr bool BNK = MODE == kModeNT;
 
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   // The per-expert m-tile prefix of the tile map lives in the first B stage until the first loads.
@@ -106,9 +114,13 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
   // skewed loads: SwiGLU GEMMs spread every expert over the XCDs (measured: the second GEMM,
   // whose activation rows are as large as its weights, runs better on the contiguous map)
   int* s_pref = reinterpret_cast<int*>(smem + B_RING);
-  if (SWIGLU ? !map_tile_auto<BM>(offsets, rows, E, NT, s_pref, tm, ncu, S)
-             : !map_tile<BM>(offsets, rows, E, NT, s_pref, tm, ncu, S))
-    return;
+  if constexpr (MODE == kModeBatchK) {
+    if (!map_tile_batched<BM>(rows, E, NT, tm)) return;
+  } else {
+    if (SWIGLU ? !map_tile_auto<BM>(offsets, rows, E, NT, s_pref, tm, ncu, S)
+               : !map_tile<BM>(offsets, rows, E, NT, s_pref, tm, ncu, S))
+      return;
+  }
   __syncthreads();
   // Split K (one dense matrix, fp32 out): n-tile index ks * NT / ksplit + n covers n-tile n over
   // the ks-th 1/ksplit of K and writes its partial product to out + ks * rows * ldb.
@@ -121,6 +133,13 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     nk /= ksplit;
     k_first = static_cast<int64_t>(ks) * nk * kBKT;
     out = static_cast<float*>(out) + static_cast<int64_t>(ks) * rows * ldb;
+  }
+  int64_t a_col0 = 0, b_row0 = static_cast<int64_t>(tm.expert) * K;  // batched: A column, B row of the expert
+  if constexpr (MODE == kModeBatchK) {
+    const int64_t p0 = offsets[tm.expert], p1 = offsets[tm.expert + 1];
+    nk = static_cast<int>((p1 - p0) / kBKT);
+    a_col0 = p0;
+    b_row0 = offsets[E + 1 + tm.expert];
   }
 
   const int tid = threadIdx.x;
@@ -139,8 +158,12 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     const int r = (NWAVE * p + wave) * 8 + lane / 8;
     int64_t grow = tm.row0 + r;
     if (grow >= tm.row_end) grow = tm.row_end - 1;
-    if (gather) grow = gather[grow];  // fused dispatch: row p of the tile is token gather[p]
-    a_src[p] = A + grow * K + k_first + (((lane % 8) ^ ((r >> 1) & 7)) * 8);
+    if constexpr (MODE == kModeBatchK) {
+      grow -= static_cast<int64_t>(tm.expert) * rows;  // row of A_e
+    } else {
+      if (gather) grow = gather[grow];  // fused dispatch: row p of the tile is token gather[p]
+    }
+    a_src[p] = A + grow * K + a_col0 + k_first + (((lane % 8) ^ ((r >> 1) & 7)) * 8);
   }
   // B round p of wave w covers k-rows 2 (8p + w) + lane / 32 (1 KB = 2 k-rows x 512 B); stored
   // chunk lane % 32 holds logical chunk (lane % 32) ^ 4 ((2w + lane / 32) & 3).
@@ -168,7 +191,7 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
       b_col = static_cast<int64_t>(tm.nt) * kBN + b_lchunk * 8;
     }
     if (b_col >= ldb) b_col = 0;  // ldb % 8 == 0: an 8-column group is wholly in or out
-    b_src = B + static_cast<int64_t>(tm.expert) * K * ldb + (k_first + 2 * wave + lane / 32) * ldb + b_col;
+    b_src = B + b_row0 * ldb + (k_first + 2 * wave + lane / 32) * ldb + b_col;
   }
   const int64_t b_round = static_cast<int64_t>(2 * NWAVE) * ldb;
   const int64_t b_kstep = static_cast<int64_t>(kBKT) * ldb;
@@ -530,18 +553,20 @@ int device_cus() {
   return cached[dev];
 }
 
-template <int BM, bool SWIGLU, bool OUT_F32, int WM = 2, int S = 1, bool BNK = false>
+template <int BM, bool SWIGLU, bool OUT_F32, int WM = 2, int S = 1, int MODE = kModeNN>
 hipError_t launch_bf16(const bf16_t* A, const bf16_t* B, const int32_t* offsets, int64_t rows, int E,
                        int K, int ldb, int NT, void* out, hipStream_t stream, int ncu = 0,
                        const int32_t* gather = nullptr, int ksplit = 1, const float* row_scale = nullptr) {
   constexpr int smem = Bf16Rings<BM>::SMEM;
-  auto kern = gemm_bf16_kernel<BM, WM, SWIGLU, OUT_F32, S, BNK>;
+  auto kern = gemm_bf16_kernel<BM, WM, SWIGLU, OUT_F32, S, MODE>;
   // once per instantiation (and never inside a stream capture after the first eager call)
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (attr != hipSuccess) return attr;
-  const int64_t mt = max_tiles<BM>(rows, E, offsets == nullptr);
-  const unsigned grid = SWIGLU ? grid_for_any(mt, NT, E, offsets == nullptr, ncu, S) : grid_for(mt, NT, ncu, S);
+  const int64_t mt = MODE == kModeBatchK ? ceil_div(rows, BM) * E : max_tiles<BM>(rows, E, offsets == nullptr);
+  const unsigned grid = MODE == kModeBatchK ? static_cast<unsigned>(8 * ceil_div(mt * NT, 8))
+                        : SWIGLU            ? grid_for_any(mt, NT, E, offsets == nullptr, ncu, S)
+                                            : grid_for(mt, NT, ncu, S);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256 * WM), smem, stream, A, B, offsets, rows, E, K, ldb, NT, out, ncu,
                      gather, ksplit, row_scale);
   return hipGetLastError();
@@ -613,8 +638,20 @@ hipError_t launch_grouped_gemm_nt_f32out(const void* A, const void* B, const int
   const int nt = static_cast<int>(ceil_div(N, kBN));
   const bf16_t* a = static_cast<const bf16_t*>(A);
   const bf16_t* b = static_cast<const bf16_t*>(B);
-  return big ? launch_bf16<256, false, true, 2, 1, true>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather)
-             : launch_bf16<128, false, true, 2, 1, true>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather);
+  return big ? launch_bf16<256, false, true, 2, 1, kModeNT>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather)
+             : launch_bf16<128, false, true, 2, 1, kModeNT>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather);
+}
+
+hipError_t launch_batched_gemm_f32out(const void* A, int64_t lda, const void* B, const int32_t* kinfo, int E, int M,
+                                      int N, float* out, hipStream_t stream) {
+  if (E <= 0 || M <= 0 || N <= 0) return hipSuccess;
+  if (lda % 8 != 0 || N % 8 != 0 || lda > INT32_MAX) return hipErrorInvalidValue;
+  const int nt = static_cast<int>(ceil_div(N, kBN));
+  const bf16_t* a = static_cast<const bf16_t*>(A);
+  const bf16_t* b = static_cast<const bf16_t*>(B);
+  const int K = static_cast<int>(lda);
+  return M >= 256 ? launch_bf16<256, false, true, 2, 1, kModeBatchK>(a, b, kinfo, M, E, K, N, nt, out, stream)
+                  : launch_bf16<128, false, true, 2, 1, kModeBatchK>(a, b, kinfo, M, E, K, N, nt, out, stream);
 }
 
 hipError_t launch_grouped_swiglu(const void* x_perm, const void* x_scales, int dt,

@@ -238,6 +238,36 @@ __device__ bool map_tile_auto(const int32_t* offsets, int64_t rows, int E, int N
   return map_tile_counted<BM>(offsets, rows, E, NT, s_pref, total, tm, ncu, S);
 }
 
+// Operand modes of the bf16 grouped GEMM (gemm.hip): weights [K, N]; weights [N, K]; independent
+// per-expert GEMMs with contractions of their own (the weight gradients).
+constexpr int kModeNN = 0, kModeNT = 1, kModeBatchK = 2;
+
+// Tile map of the batched mode: E independent [M, N] outputs of MT x NT tiles each.  The tiles of
+// one expert are walked in groups of 8 m-tiles, n-major inside a group (the tiles running together
+// then share 8 row blocks of A and a few column blocks of B in L2), and every XCD takes a
+// contiguous range of this order (workgroup w runs on XCD w % 8).  The launch has
+// 8 ceil(E MT NT / 8) workgroups.
+template <int BM>
+__device__ bool map_tile_batched(int64_t M, int E, int NT, TileMap& tm) {
+  const int MT = static_cast<int>(ceil_div(M, BM));
+  const int per_e = MT * NT;
+  const int total = E * per_e;
+  const int per = (total + 7) / 8;
+  const int w = blockIdx.x;
+  const int L = (w % 8) * per + w / 8;
+  if (L >= total) return false;
+  const int e = L / per_e, idx = L % per_e;
+  const int g = idx / (8 * NT);
+  const int gm = MT - 8 * g < 8 ? MT - 8 * g : 8;
+  const int r = idx - g * 8 * NT;
+  tm.expert = e;
+  tm.nt = r / gm;
+  tm.mt = 8 * g + r % gm;
+  tm.row0 = static_cast<int64_t>(e) * M + static_cast<int64_t>(tm.mt) * BM;
+  tm.row_end = static_cast<int64_t>(e) * M + M;
+  return true;
+}
+
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
