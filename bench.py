@@ -6,7 +6,8 @@ bf16 activations and weights), synthetic seeded inputs resident in HBM: the larg
 layer shapes that fits one GPU.  One step = one full layer forward through the library's fused
 entry point (route -> permute -> grouped SwiGLU GEMMs -> shared expert -> combine).
 ``--workload`` selects another layer shape (Mixtral-8x7B, Qwen3-235B, DeepSeek-V3 with Zipf loads
-and e4m3 experts, the tiny fp32 layer) for the same measurement.
+and e4m3 experts, DeepSeek-V3 with MXFP4 experts, the tiny fp32 layer) for the same measurement;
+``--gate-in-expert`` folds the gates into the experts' SwiGLU epilogue.
 
 Measurement:
   * warm-up W steps, then K steps back to back bracketed by torch.cuda.synchronize(): `value`
@@ -75,7 +76,7 @@ PHASES = {1: "forward warm-up", 2: "forward timed (back to back)", 3: "forward c
 # these files' code lines (// comments and blank lines removed) hash as they did when it was taken.
 GEMM_SOURCES = [os.path.join(CSRC, f) for f in ("gemm.hip", "gemm_common.hpp", "common.hpp")]
 FP8_GEMM_SOURCES = [os.path.join(CSRC, f) for f in ("gemm_fp8.hip", "gemm_common.hpp", "common.hpp")]
-BWD_SOURCES = [os.path.join(CSRC, f) for f in ("backward.hip", "gemm_common.hpp", "common.hpp")]
+BWD_SOURCES = [os.path.join(CSRC, f) for f in ("backward.hip", "gemm.hip", "gemm_common.hpp", "common.hpp")]
 
 
 def code_sha256(files):
@@ -468,12 +469,24 @@ def bench_backward(args, cfg, d, layer, torch, moe_gpu, _lib, util):
     a_s = alg[dom]
     t_s = avg_ms[dom] * 1e-3
     mfma_bound = a_s["flops"] / (peak_tf * 1e12) >= a_s["bytes"] / (PEAK_HBM_GBS * 1e9)
-    layout = {"recompute_u": "NN", "dgrad_h": "NT", "dgrad_x": "NT", "wgrad_w2": "TN", "wgrad_w1": "TN"}[dom]
+    if mm_dtype == "bf16":
+        # bf16 expert GEMMs run on the forward's grouped-GEMM kernel (operand mode: 0 weights [K, N],
+        # 1 weights [N, K], 2 per-expert products); the weight-gradient stages include the transposes
+        bm = {"recompute_u": 256 if cfg.T * cfg.k >= 192 * cfg.E else 128,
+              "dgrad_h": 256 if cfg.T * cfg.k >= 192 * cfg.E else 128,
+              "dgrad_x": 256 if cfg.T * cfg.k >= 192 * cfg.E else 128,
+              "wgrad_w2": 256 if cfg.F >= 256 else 128, "wgrad_w1": 256 if cfg.H >= 256 else 128}[dom]
+        mode = {"recompute_u": 0, "dgrad_h": 1, "dgrad_x": 1, "wgrad_w2": 2, "wgrad_w1": 2}[dom]
+        kname = f"gemm_bf16_kernel<{bm}, 2, false, true, 1, {mode}> ({dom}" + \
+                (", with its operand transpose)" if mode == 2 else ")")
+    else:
+        layout = {"recompute_u": "NN", "dgrad_h": "NT", "dgrad_x": "NT", "wgrad_w2": "TN", "wgrad_w1": "TN"}[dom]
+        kname = f"bwd_gemm_kernel<{layout}> ({dom})"
     if mfma_bound:
         achieved, peak, unit = a_s["flops"] / t_s / 1e12, peak_tf, "TFLOP/s"
     else:
         achieved, peak, unit = a_s["bytes"] / t_s / 1e9, PEAK_HBM_GBS, "GB/s"
-    roofline = {"kernel": f"bwd_gemm_kernel<{layout}> ({dom})", "bound": "mfma" if mfma_bound else "hbm",
+    roofline = {"kernel": kname, "bound": "mfma" if mfma_bound else "hbm",
                 "achieved": round(achieved, 1), "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                 "traffic": measured_backward_traffic(args.workload) if dom == "wgrad_w1" else None,
                 "flops_per_launch": a_s["flops"], "algorithmic_bytes_per_launch": a_s["bytes"],
@@ -599,8 +612,8 @@ def input_hashes(d, cfg):
 
 # ------------------------------------------------------------------------ rocprofv3 summaries
 def short_kernel_name(name):
-    """'void moe::(anonymous namespace)::gemm_bf16_kernel<256, 2, true, false, 1>(...)' ->
-    'gemm_bf16_kernel<256, 2, true, false, 1>'."""
+    """'void moe::(anonymous namespace)::gemm_bf16_kernel<256, 2, true, false, 1, 0>(...)' ->
+    'gemm_bf16_kernel<256, 2, true, false, 1, 0>'."""
     name = name.strip().strip('"').replace("(anonymous namespace)::", "")
     if name.startswith("void "):
         name = name[5:]
@@ -880,7 +893,7 @@ def bench_forward(args, cfg, d, layer, torch, _lib, util, moe_gpu):
     mfma_bound = g1["flops"] / (peak_tf * 1e12) >= g1["bytes"] / (PEAK_HBM_GBS * 1e9)
     kernel = {"fp8": "gemm_fp8_kernel<swiglu> (grouped e4m3 GEMM1 + fused SwiGLU + 1x128 re-quantisation)",
               "fp4": "gemm_fp4_kernel<128, true, false> (grouped MXFP4 GEMM1 + fused SwiGLU + 1x32 re-quantisation)",
-              "bf16": f"gemm_bf16_kernel<{256 if cfg.T * cfg.k >= 192 * cfg.E else 128}, 2, true, false, 1> "
+              "bf16": f"gemm_bf16_kernel<{256 if cfg.T * cfg.k >= 192 * cfg.E else 128}, 2, true, false, 1, 0> "
                       "(routed experts' grouped GEMM1 + fused SwiGLU)",
               "f32": "gemm_f32_kernel<swiglu> (grouped fp32 GEMM1 + fused SwiGLU)"}[mm_dtype]
     if mfma_bound:
@@ -958,7 +971,7 @@ def main():
     ap.add_argument("--traffic-report", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
                     help="HBM traffic summary of one launch position from FETCH_SIZE / WRITE_SIZE runs")
     ap.add_argument("--traffic-phase", type=int, default=PH_COLD)
-    ap.add_argument("--traffic-label", default="gemm_bf16_kernel<256, 2, true, false, 1> #0")
+    ap.add_argument("--traffic-label", default="gemm_bf16_kernel<256, 2, true, false, 1, 0> #0")
     ap.add_argument("--traffic-alg-bytes", type=int, default=0)
     args = ap.parse_args()
     if args.summarize_trace:
