@@ -891,7 +891,9 @@ def bench_forward(args, cfg, d, layer, torch, _lib, util, moe_gpu):
     g1 = alg["gemm1_swiglu"]
     g1_s = cold_avg["gemm1_swiglu"] * 1e-3
     mfma_bound = g1["flops"] / (peak_tf * 1e12) >= g1["bytes"] / (PEAK_HBM_GBS * 1e9)
-    kernel = {"fp8": "gemm_fp8_kernel<swiglu> (grouped e4m3 GEMM1 + fused SwiGLU + 1x128 re-quantisation)",
+    kernel = {"fp8": "gemm_fp8_kernel<192, true, false> (grouped e4m3 GEMM1 + fused SwiGLU + 1x128 re-quantisation, "
+                     "E8M0 variant; the events include the fp32-scale variant <128, true, false> launched beside it, "
+                     "which exits at once when every scale is a power of two)",
               "fp4": "gemm_fp4_kernel<128, true, false> (grouped MXFP4 GEMM1 + fused SwiGLU + 1x32 re-quantisation)",
               "bf16": f"gemm_bf16_kernel<{256 if cfg.T * cfg.k >= 192 * cfg.E else 128}, 2, true, false, 1, 0> "
                       "(routed experts' grouped GEMM1 + fused SwiGLU)",
