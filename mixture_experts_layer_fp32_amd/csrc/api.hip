@@ -152,6 +152,7 @@ moe_status moe_grouped_swiglu(const void* x_perm, const void* x_perm_scales, moe
   if (!act_dtype_ok(out_dt)) return MOE_ERR_INVALID_ARG;
   if (rows == 0) return MOE_OK;  // nothing to do; empty tensors may carry null pointers
   if (!x_perm || !expert_offsets || !w1 || !w2 || !y_perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_perm) || !aligned16(y_perm)) return MOE_ERR_INVALID_ARG;  // 16-byte row pieces
   if (low_precision(dt) && (!x_perm_scales || !w1_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
   if (workspace_bytes < moe_grouped_swiglu_workspace_size(rows, F, dt) || !workspace)
     return MOE_ERR_WORKSPACE;

@@ -435,7 +435,7 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
               *reinterpret_cast<const u32x4_t*>(st + row_t * LS + seg * 8);
       }
     }
-  } else {
+  } else if constexpr (SWIGLU) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -443,20 +443,44 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
         const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
         const int64_t grow = tm.row0 + row_t;
         if (grow >= tm.row_end) continue;
-        if (SWIGLU) {
-          const int F = ldb / 2;
-          const int64_t col = static_cast<int64_t>(tm.nt) * 128 + wn * 32 + lane % 32;
-          float hv = silu_fast(acc[i][0][r]) * acc[i][1][r];
-          if (row_scale != nullptr) hv *= row_scale[grow];
-          static_cast<float*>(out)[grow * F + col] = hv;
-        } else {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int64_t col = static_cast<int64_t>(tm.nt) * kBN + wn * 64 + j * 32 + lane % 32;
-            if (col < ldb) static_cast<float*>(out)[grow * ldb + col] = acc[i][j][r];
-          }
-        }
+        const int F = ldb / 2;
+        const int64_t col = static_cast<int64_t>(tm.nt) * 128 + wn * 32 + lane % 32;
+        float hv = silu_fast(acc[i][0][r]) * acc[i][1][r];
+        if (row_scale != nullptr) hv *= row_scale[grow];
+        static_cast<float*>(out)[grow * F + col] = hv;
       }
+    }
+  } else {
+    // fp32 results staged through LDS one wave row group (WROWS rows) at a time, then written a
+    // whole row per wave instruction (16 bytes per lane, the tile row's 256 columns contiguous):
+    // with one 4-byte store per accumulator slot every instruction wrote 128-byte pieces of two
+    // rows, and the weight gradients of the backward write gigabytes of fp32 this way.
+    constexpr int LSF = kBN + 8;  // fp32 row stride: the two lane halves (rows 4 apart) 32 banks apart
+    static_assert(WROWS * LSF * 4 <= R::SMEM, "one row group of fp32 results fits in the rings");
+    float* st = reinterpret_cast<float*>(smem);
+    wait_lgkm0();
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < WM; ++g) {
+      if (wm == g) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row_l = i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) st[row_l * LSF + wn * 64 + j * 32 + lane % 32] = acc[i][j][r];
+          }
+      }
+      __syncthreads();
+      const int64_t col = static_cast<int64_t>(tm.nt) * kBN + lane * 4;
+      for (int row_l = wave; row_l < WROWS; row_l += NWAVE) {
+        const int64_t grow = tm.row0 + g * WROWS + row_l;
+        if (grow < tm.row_end && col < ldb)  // ldb % 4 == 0: a 4-column group is wholly in or out
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + grow * ldb + col) =
+              *reinterpret_cast<const f32x4_t*>(st + row_l * LSF + lane * 4);
+      }
+      __syncthreads();
     }
   }
 }

@@ -98,7 +98,8 @@ def _gemm(L, **over):
     (dict(off=None), INVALID), (dict(F=192), INVALID), (dict(H=96), INVALID), (dict(dt=0, odt=1), INVALID),
     (dict(dt=2), INVALID), (dict(dt=2, sc=P, w1s=P, w2s=P, H=192), INVALID), (dict(E=0), INVALID),
     (dict(E=600), INVALID), (dict(odt=2), INVALID), (dict(wsb=1024), WS), (dict(rows=0), _lib.MOE_OK),
-    (dict(rows=0, xp=None, y=None), _lib.MOE_OK)])
+    (dict(rows=0, xp=None, y=None), _lib.MOE_OK), (dict(xp=ctypes.c_void_p(16 * 1024 + 4)), INVALID),
+    (dict(y=ctypes.c_void_p(16 * 1024 + 8), odt=0), INVALID)])
 def test_grouped_swiglu_rejects(over, code):
     assert _gemm(_lib.lib(), **over) == code
 
