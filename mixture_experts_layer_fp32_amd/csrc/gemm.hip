@@ -165,6 +165,19 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     }
     a_src[p] = A + grow * K + a_col0 + k_first + (((lane % 8) ^ ((r >> 1) & 7)) * 8);
   }
+  // A rounds wholly past the tile's last live 32-row block carry rows no fragment read uses (each
+  // wave computes only its live blocks), so they are not loaded: the load path into LDS, busy most
+  // of the time under these GEMMs, costs per instruction.  The waits below count the skipped loads.
+  uint32_t a_dead = 0;
+  {
+    const int64_t live = tm.row_end - tm.row0 < BM ? tm.row_end - tm.row0 : BM;
+    const int used = static_cast<int>((live + 31) / 32 * 32);
+#pragma unroll
+    for (int p = 0; p < A_ROUNDS; ++p)
+      if ((NWAVE * p + wave) * 8 >= used) a_dead |= 1u << p;
+  }
+  a_dead = __builtin_amdgcn_readfirstlane(a_dead);
+  const int n_dead = __builtin_popcount(a_dead);  // A loads this wave skips per A tile
   // B round p of wave w covers k-rows 2 (8p + w) + lane / 32 (1 KB = 2 k-rows x 512 B); stored
   // chunk lane % 32 holds logical chunk (lane % 32) ^ 4 ((2w + lane / 32) & 3).
   // BNK: round p of wave w covers B rows (columns) (8p + w) * 8 + lane / 8, as for A.
@@ -207,7 +220,8 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
       const uint32_t abase = a_stage(ta);
 #pragma unroll
       for (int p = 0; p < A_ROUNDS; ++p)
-        lds_dma16(a_src[p] + static_cast<int64_t>(ta) * kBKT, abase + (NWAVE * p + wave) * 1024);
+        if (!((a_dead >> p) & 1u))
+          lds_dma16(a_src[p] + static_cast<int64_t>(ta) * kBKT, abase + (NWAVE * p + wave) * 1024);
     }
     if (tb < nk) {
       const uint32_t bbase = b_stage(tb);
@@ -224,10 +238,10 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
   // Loads issued after both A and B tile t + 1 by the time iteration t waits (load group j: A
   // tile j + NA at the end of iteration j, B tile j + NB at the start of iteration j + 1), when
   // every tile they name exists (t + NB <= nk): B tile t + 2 when NB > NA (its A partner came
-  // earlier), then NA - 2 whole groups.  Otherwise wait for all.
+  // earlier), then NA - 2 whole groups, each n_dead A loads short.  Otherwise wait for all.
   constexpr int B_AFTER_A = NB > NA ? B_ROUNDS : 0;
   auto wait_tile_next = [&](int t) {
-    if (t + NB <= nk) wait_vmcnt<B_AFTER_A + (NA - 2) * RPT>();
+    if (t + NB <= nk) wait_vmcnt_less<B_AFTER_A + (NA - 2) * RPT, NA - 2, A_ROUNDS>(n_dead);
     else wait_vmcnt<0>();
   };
 
@@ -344,7 +358,7 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
 
     for (int j = -NB; j < 0; ++j) issue_group(j);
     // tile 0: groups -NA + 1 .. -1 (and B(NB - NA) when NB > NA) may still be in flight
-    if (NB <= nk) wait_vmcnt<B_AFTER_A + (NA - 1) * RPT>(); else wait_vmcnt<0>();
+    if (NB <= nk) wait_vmcnt_less<B_AFTER_A + (NA - 1) * RPT, NA - 1, A_ROUNDS>(n_dead); else wait_vmcnt<0>();
     lds_barrier();
 #pragma unroll
     for (int q = 0; q < NR; ++q) read_unit(0, 0, 0, q);
@@ -376,7 +390,7 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
           // unconditional: past the last tile this reads a stale stage (in bounds, never used); a
           // branch here would make the compiler wait for these reads before the next MFMAs
           if (q < NR) read_unit(kt + 1, 0, 0, q);
-          if (q >= AQ && do_a)
+          if (q >= AQ && do_a && !((a_dead >> (q - AQ)) & 1u))
             lds_dma16(a_src[q - AQ] + static_cast<int64_t>(ta) * kBKT, abase + (NWAVE * (q - AQ) + wave) * 1024);
           __builtin_amdgcn_sched_barrier(0);
         }

@@ -293,6 +293,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   // gfx9 s_waitcnt encoding: vmcnt [3:0] + [15:14], expcnt [6:4] (7 = no wait), lgkmcnt [11:8] (15)
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// Wait (vmcnt) until at most N - STEP * d loads are still in flight, d in [0, D] (wave-uniform):
+// the count of a wave that skips d loads in each of STEP load groups issued after the awaited one.
+template <int N, int STEP, int D>
+__device__ __forceinline__ void wait_vmcnt_less(int d) {
+  if constexpr (STEP == 0 || D == 0) {
+    wait_vmcnt<N>();
+  } else {
+    if (d >= D) wait_vmcnt<N - STEP * D>();
+    else wait_vmcnt_less<N, STEP, D - 1>(d);
+  }
+}
+
 // Wait (vmcnt) until at most `tiles` (<= MAXT) tiles of RPT loads each are still in flight.
 template <int RPT, int MAXT>
 __device__ __forceinline__ void wait_tiles(int tiles) {

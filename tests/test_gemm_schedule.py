@@ -18,10 +18,11 @@ import pytest
 
 
 class Wave:
-    def __init__(self, NA, NB, nk):
+    def __init__(self, NA, NB, nk, loads_a=True):
         self.NA, self.NB, self.nk = NA, NB, nk
         self.issued = []          # (operand, tile) per load, in issue order
         self.last_barrier = -1    # iteration whose barrier was passed last (-1: the prologue's)
+        self.needs = {"A", "B"} if loads_a else {"B"}  # operands this wave loads for every tile
 
     def load(self, op, tile, count):
         ring = self.NA if op == "A" else self.NB
@@ -38,20 +39,23 @@ class Wave:
             if t == tile:
                 assert i < done, ("tile in flight", tile, op, n)
                 ops.add(op)
-        assert ops == {"A", "B"}, ("tile never loaded", tile, ops)
+        assert ops == self.needs, ("tile never loaded", tile, ops)
 
 
-def bf16_kernel(NA, NB, AR, BR, nk):
+def bf16_kernel(NA, NB, AR, BR, nk, dead=0):
     """gemm_bf16_kernel: prologue groups -NB..-1 (A tile j+NA, B tile j+NB); in iteration kt the
     B loads of tile kt-1+NB go out in k-steps 1 and 2, the wait for tile kt+1 and the barrier
-    follow k-step 2, and the A loads of tile kt+NA take the last slots of the last k-step."""
-    w = Wave(NA, NB, nk)
-    RPT = AR + BR
+    follow k-step 2, and the A loads of tile kt+NA take the last slots of the last k-step.  A wave
+    skips `dead` of its AR A loads per tile (the rounds past the tile's last live row block); its
+    waits allow (NA - 1) and (NA - 2) groups of AR - dead + BR loads."""
+    ar = AR - dead
+    w = Wave(NA, NB, nk, loads_a=ar > 0)
+    RPT = ar + BR
     after = BR if NB > NA else 0
 
     def group(j):
-        if 0 <= j + NA < nk:
-            w.load("A", j + NA, AR)
+        if 0 <= j + NA < nk and ar:
+            w.load("A", j + NA, ar)
         if j + NB < nk:
             w.load("B", j + NB, BR)
 
@@ -67,8 +71,8 @@ def bf16_kernel(NA, NB, AR, BR, nk):
         if kt + 1 < nk:
             w.wait(after + (NA - 2) * RPT if kt + NB <= nk else 0, kt + 1)
             w.last_barrier = kt
-        if kt + 1 < nk and kt + NA < nk:
-            w.load("A", kt + NA, AR)           # last k-step
+        if kt + 1 < nk and kt + NA < nk and ar:
+            w.load("A", kt + NA, ar)           # last k-step
     return w
 
 
@@ -122,8 +126,24 @@ FP8 = {"MX, BM 192": (2, 3, 3, 4, True), "general, BM 128": (3, 3, 2, 4, False)}
 @pytest.mark.parametrize("name", list(BF16))
 def test_bf16_ring_protocol(name):
     NA, NB, AR, BR = BF16[name]
-    for nk in range(1, 80):
-        bf16_kernel(NA, NB, AR, BR, nk)
+    for nk, dead in itertools.product(range(1, 80), range(AR + 1)):
+        bf16_kernel(NA, NB, AR, BR, nk, dead)
+
+
+def test_dead_rounds_need_the_reduced_counts():
+    """With skipped A loads the unreduced wait count is too permissive for the deeper A ring (the
+    tile's B loads may still be in flight), so the reduction is what keeps the protocol correct."""
+    NA, NB, AR, BR = BF16["BM 128"]
+    nk, dead = 8, 1
+    w = Wave(NA, NB, nk)
+    ar = AR - dead
+    for j in range(-NB, 0):
+        if 0 <= j + NA < nk:
+            w.load("A", j + NA, ar)
+        w.load("B", j + NB, BR)
+    with pytest.raises(AssertionError):
+        w.wait((NA - 1) * (AR + BR), 0)   # the count without the skipped loads
+    w.wait((NA - 1) * (ar + BR), 0)
 
 
 @pytest.mark.parametrize("name", list(FP8))
