@@ -262,15 +262,17 @@ moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, co
  *            dh (2), SwiGLU backward (3), dW2 (4), dx_perm (5) and dW1 (6); after the shared
  *            expert (7); at the end (8).
  *   workspace at least moe_backward_workspace_size(L, T) bytes: u [T*k, 2F] and
- *            dy W2^T [T*k, F] fp32, du [T*k + 64, 2F] and g h [T*k, F] in x_dt, dg [T*k],
- *            dx_perm [T*k, H], dlogits [T, E], dlogits W_r^T [T, H] fp32, and the shared
+ *            dy W2^T [T*k, F] fp32, du [T*k + 64, 2F], g h [T*k, F] and dx_perm [T*k, H] in
+ *            x_dt, dg [T*k], dlogits [T, E], dlogits W_r^T [T, H] fp32, and the shared
  *            expert's counterparts, and with many tokens per router-gradient tile up to 32
  *            row slices of partial router-weight gradients [slices, H, E] fp32; for bf16
  *            also the weight gradients' operands: one activation transposed per expert with
  *            each expert's rows padded to a multiple of 64 ([max(H, F, Fs), T*k + 64 E] bf16),
  *            dy in expert-row order ([T*k + 64, H] bf16) and two small index tables.
  * Accumulation is fp32 throughout (fp32 MFMA for fp32 operands, bf16 MFMA with fp32 accumulate
- * for bf16 ones); du and g h are rounded to x_dt before their GEMMs.  Sizes as for moe_forward.
+ * for bf16 ones); du and g h are rounded to x_dt before their GEMMs, and the per-row input
+ * gradients dx_perm (and the shared expert's) to x_dt before dx sums them in fp32, as the forward
+ * rounds y_perm before combine.  Sizes as for moe_forward.
  * ------------------------------------------------------------------------------------- */
 #define MOE_NUM_BWD_STAGE_EVENTS 9
 typedef struct {

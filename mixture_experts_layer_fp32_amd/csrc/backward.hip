@@ -629,10 +629,24 @@ __global__ __launch_bounds__(256) void bwd_sum_slices_kernel(const float* __rest
   out[i] = acc;
 }
 
-// One workgroup per token: dx[t] = sum_j dxp[row_map(t, j)] (j ascending) + extra0[t] + extra1[t].
+// 4 consecutive values as fp32 (fp32 or bf16 storage, 16- or 8-byte aligned).
+template <typename T>
+__device__ __forceinline__ f32x4_t load4(const T* p) {
+  if constexpr (std::is_same<T, float>::value) {
+    return *reinterpret_cast<const f32x4_t*>(p);
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    return f32x4_t{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+                   __uint_as_float(v.y & 0xffff0000u)};
+  }
+}
+
+// One workgroup per token: dx[t] = sum_j dxp[row_map(t, j)] (j ascending) + extra0[t] + extra1[t], in
+// fp32; dxp and extra0 (the shared expert's term) are stored in the layer's dtype, as the forward
+// keeps y_perm and sums it in fp32 in combine.
 template <typename XT>
-__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dxp, const int32_t* __restrict__ row_map,
-                                                     int64_t R, int k, const float* __restrict__ extra0,
+__global__ __launch_bounds__(256) void bwd_dx_kernel(const XT* __restrict__ dxp, const int32_t* __restrict__ row_map,
+                                                     int64_t R, int k, const XT* __restrict__ extra0,
                                                      const float* __restrict__ extra1, int H, XT* __restrict__ dx) {
   __shared__ int64_t s_rows[kMaxTopk];
   const int64_t t = blockIdx.x;
@@ -640,8 +654,8 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
   __syncthreads();
   for (int h = threadIdx.x * 4; h < H; h += 256 * 4) {
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int j = 0; j < k; ++j) acc += *reinterpret_cast<const f32x4_t*>(dxp + s_rows[j] * H + h);
-    if (extra0) acc += *reinterpret_cast<const f32x4_t*>(extra0 + t * H + h);
+    for (int j = 0; j < k; ++j) acc += load4(dxp + s_rows[j] * H + h);
+    if (extra0) acc += load4(extra0 + t * H + h);
     if (extra1) acc += *reinterpret_cast<const f32x4_t*>(extra1 + t * H + h);
     store4(dx + t * H + h, acc[0], acc[1], acc[2], acc[3]);
   }
@@ -755,7 +769,7 @@ template <typename WT>
 hipError_t expert_group_backward(const WT* x, const WT* dy, const WT* w1, const WT* w2, const int32_t* offsets,
                                  const int32_t* src, const float* gates, const int32_t* row_map, int64_t T, int k,
                                  int64_t rows, int G, int H, int F, float* u, float* dhp, WT* du, WT* gh, float* dg,
-                                 float* dxp, float* dw1, float* dw2, int32_t* kinfo, void* xt, void* dyp,
+                                 WT* dxp, float* dw1, float* dw2, int32_t* kinfo, void* xt, void* dyp,
                                  int64_t ld_t, hipStream_t s, hipEvent_t const* ev) {
   auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord(ev[i], s) : hipSuccess; };
   const int64_t gx = src ? T : rows;
@@ -812,10 +826,10 @@ hipError_t expert_group_backward(const WT* x, const WT* dy, const WT* w1, const 
     }
   }
   if (e == hipSuccess) e = mark(4);
-  // dx_perm = du W1^T (W1 [H, 2F] = [N, K] as stored)
+  // dx_perm = du W1^T (W1 [H, 2F] = [N, K] as stored); bf16 rows, like the forward's y_perm
   if (e == hipSuccess) {
     if constexpr (std::is_same<WT, bf16_t>::value)
-      e = launch_grouped_gemm_nt_f32out(du, w1, offsets, rows, G, 2 * F, H, dxp, s, nullptr);
+      e = launch_grouped_gemm_nt_bf16out(du, w1, offsets, rows, G, 2 * F, H, dxp, s, nullptr);
     else
       e = launch_bwd_gemm<kNT>(args(static_cast<const WT*>(du), 2 * F, static_cast<const int32_t*>(nullptr), rows,
                                     w1, 2 * F, int64_t{H} * 2 * F, nullptr, 0, offsets, rows, G, 0, H, 2 * F, dxp, H,
@@ -853,12 +867,14 @@ hipError_t layer_backward(const BackwardShape& sh, const BackwardIO& io, const B
   if (e == hipSuccess)
     e = expert_group_backward<WT>(x, dy, static_cast<const WT*>(io.w1), static_cast<const WT*>(io.w2), io.offsets,
                                   io.src_token, io.gates, io.row_map, T, sh.k, R, sh.E, sh.H, sh.F, ws.u, ws.dhp,
-                                  static_cast<WT*>(ws.du), static_cast<WT*>(ws.gh), ws.dg, ws.dxp, io.dw1, io.dw2,
+                                  static_cast<WT*>(ws.du), static_cast<WT*>(ws.gh), ws.dg, static_cast<WT*>(ws.dxp),
+                                  io.dw1, io.dw2,
                                   ws.kinfo, ws.xt, ws.dyp, ws.ld_t, s, ev);
   if (e == hipSuccess && sh.Fs > 0)
     e = expert_group_backward<WT>(x, dy, static_cast<const WT*>(io.ws1), static_cast<const WT*>(io.ws2), nullptr,
                                   nullptr, nullptr, nullptr, T, 1, T, 1, sh.H, sh.Fs, ws.us, ws.dhs,
-                                  static_cast<WT*>(ws.dus), static_cast<WT*>(ws.ghs), nullptr, ws.dxs, io.dws1,
+                                  static_cast<WT*>(ws.dus), static_cast<WT*>(ws.ghs), nullptr, static_cast<WT*>(ws.dxs),
+                                  io.dws1,
                                   io.dws2, ws.kinfo_s, ws.xt, ws.dyp, ws.ld_t, s, nullptr);
   if (e == hipSuccess) e = mark(7);
   if (e != hipSuccess) return e;
@@ -885,8 +901,9 @@ hipError_t layer_backward(const BackwardShape& sh, const BackwardIO& io, const B
     e = hipGetLastError();
   }
   if (e == hipSuccess && T > 0) {
-    hipLaunchKernelGGL(bwd_dx_kernel<WT>, dim3(static_cast<unsigned>(T)), dim3(256), 0, s, ws.dxp, io.row_map, R,
-                       sh.k, sh.Fs > 0 ? static_cast<const float*>(ws.dxs) : nullptr,
+    hipLaunchKernelGGL(bwd_dx_kernel<WT>, dim3(static_cast<unsigned>(T)), dim3(256), 0, s,
+                       static_cast<const WT*>(ws.dxp), io.row_map, R, sh.k,
+                       sh.Fs > 0 ? static_cast<const WT*>(ws.dxs) : nullptr,
                        static_cast<const float*>(ws.dxr), sh.H, static_cast<WT*>(io.dx));
     e = hipGetLastError();
   }
@@ -925,7 +942,7 @@ BackwardScratch carve_backward(const BackwardShape& sh, int dt, void* base, size
   w.du = take((R + pad) * 2 * sh.F * cts);
   w.gh = take(R * sh.F * cts);
   w.dg = static_cast<float*>(take(R * 4));
-  w.dxp = static_cast<float*>(take(R * sh.H * 4));
+  w.dxp = take(R * sh.H * cts);
   w.dl = static_cast<float*>(take(T * sh.E * 4));
   w.dxr = static_cast<float*>(take(T * sh.H * 4));
   if (sh.Fs > 0) {
@@ -933,7 +950,7 @@ BackwardScratch carve_backward(const BackwardShape& sh, int dt, void* base, size
     w.dhs = static_cast<float*>(take(T * sh.Fs * 4));
     w.dus = take((T + pad) * 2 * sh.Fs * cts);
     w.ghs = take(T * sh.Fs * cts);
-    w.dxs = static_cast<float*>(take(T * sh.H * 4));
+    w.dxs = take(T * sh.H * cts);
   }
   if (bf16) {
     // one transposed activation at a time ([H or F or Fs][ld_t]); ld_t covers both groups' padding

@@ -191,6 +191,10 @@ hipError_t launch_grouped_gemm_f32out(const void* A, const void* B, const int32_
 hipError_t launch_grouped_gemm_nt_f32out(const void* A, const void* B, const int32_t* offsets, int64_t rows, int E,
                                          int K, int N, float* out, hipStream_t stream, const int32_t* gather);
 
+// The same with bf16 output (fp32 accumulation, one rounding per element), N % 8 == 0.
+hipError_t launch_grouped_gemm_nt_bf16out(const void* A, const void* B, const int32_t* offsets, int64_t rows, int E,
+                                          int K, int N, void* out, hipStream_t stream, const int32_t* gather);
+
 // E independent products out_e [M, N] (fp32, out_e at out + e M N) = A_e . B_e, bf16 operands:
 // A_e is columns [P_e, P_{e+1}) of A [M, lda] (P = kinfo[0 .. E], multiples of 64; A's columns
 // past an expert's own rows hold zeros) and B_e is P_{e+1} - P_e rows of B [*, N] from row
@@ -256,10 +260,12 @@ struct BackwardScratch {
   float* dwr_part;  // [router_slices, H, E] partial router-weight gradients (null for one slice)
   float *u, *dhp;
   void *du, *gh;
-  float *dg, *dxp, *dl, *dxr;
+  float *dg;
+  void* dxp;  // [T*k, H] row gradients in the layer's dtype (bf16 rows are summed in fp32)
+  float *dl, *dxr;
   float *us, *dhs;
   void *dus, *ghs;
-  float* dxs;
+  void* dxs;  // the shared expert's [T, H] input gradient, in the layer's dtype
   // bf16 weight gradients as per-expert products (launch_batched_gemm_f32out): the padded
   // contraction table (2 (E + 1) ints, routed and shared), the transposed zero-padded activations
   // ([H or F][ld_t]) and dy gathered into expert-row order with 64 zero rows after the end

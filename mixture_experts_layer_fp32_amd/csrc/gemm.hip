@@ -680,6 +680,17 @@ hipError_t launch_grouped_gemm_nt_f32out(const void* A, const void* B, const int
              : launch_bf16<128, false, true, 2, 1, kModeNT>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather);
 }
 
+hipError_t launch_grouped_gemm_nt_bf16out(const void* A, const void* B, const int32_t* offsets, int64_t rows, int E,
+                                          int K, int N, void* out, hipStream_t stream, const int32_t* gather) {
+  if (rows <= 0) return hipSuccess;
+  const bool big = offsets == nullptr ? rows >= 192 : rows >= 192 * static_cast<int64_t>(E);
+  const int nt = static_cast<int>(ceil_div(N, kBN));
+  const bf16_t* a = static_cast<const bf16_t*>(A);
+  const bf16_t* b = static_cast<const bf16_t*>(B);
+  return big ? launch_bf16<256, false, false, 2, 1, kModeNT>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather)
+             : launch_bf16<128, false, false, 2, 1, kModeNT>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather);
+}
+
 hipError_t launch_batched_gemm_f32out(const void* A, int64_t lda, const void* B, const int32_t* kinfo, int E, int M,
                                       int N, float* out, hipStream_t stream) {
   if (E <= 0 || M <= 0 || N <= 0) return hipSuccess;

@@ -191,8 +191,8 @@ def _routing(**over):
 
 
 def test_backward_workspace_size():
-    """u, dh' (fp32), du (bf16, 64 zero rows after its end), g h (bf16), dg, dx_perm, dlogits and the
-    router's dx term; with bf16 also the weight-gradient products' padded contraction tables, one
+    """u, dh' (fp32), du (bf16, 64 zero rows after its end), g h (bf16), dg, dx_perm (bf16), dlogits
+    and the router's dx term; with bf16 also the weight-gradient products' padded contraction tables, one
     transposed activation [max(H, F)][ld] (ld = rows + 64 E rounded up to 64) and dy in row order
     (+ 64 rows); each piece 256-byte aligned."""
     L = _lib.lib()
@@ -203,7 +203,7 @@ def test_backward_workspace_size():
     def a(n):
         return (n + 255) // 256 * 256
     ld = (R + 64 * E + 63) // 64 * 64
-    want = (a(R * 2 * F * 4) + a(R * F * 4) + a((R + 64) * 2 * F * 2) + a(R * F * 2) + a(R * 4) + a(R * H * 4)
+    want = (a(R * 2 * F * 4) + a(R * F * 4) + a((R + 64) * 2 * F * 2) + a(R * F * 2) + a(R * 4) + a(R * H * 2)
             + a(T * E * 4) + a(T * H * 4) + a(2 * (E + 1) * 4) + a(16) + a(max(H, F) * ld * 2)
             + a((R + 64) * H * 2))
     assert L.moe_backward_workspace_size(ctypes.byref(lay), T) == want
