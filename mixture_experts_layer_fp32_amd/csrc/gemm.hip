@@ -490,9 +490,16 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
       const int64_t col = static_cast<int64_t>(tm.nt) * kBN + lane * 4;
       for (int row_l = wave; row_l < WROWS; row_l += NWAVE) {
         const int64_t grow = tm.row0 + g * WROWS + row_l;
-        if (grow < tm.row_end && col < ldb)  // ldb % 4 == 0: a 4-column group is wholly in or out
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + grow * ldb + col) =
-              *reinterpret_cast<const f32x4_t*>(st + row_l * LSF + lane * 4);
+        if (grow < tm.row_end && col < ldb) {  // ldb % 4 == 0: a 4-column group is wholly in or out
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(st + row_l * LSF + lane * 4);
+          f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + grow * ldb + col);
+          // the backward's products (weights read as stored, per-expert weight gradients: up to tens
+          // of GB of fp32) stream past the caches (DeepSeek-V3-shaped dW1 10.6 -> 9.7 ms); the
+          // router's partial products are read back at once and keep the cached store (route
+          // 147 -> 158 us when streamed)
+          if constexpr (MODE != kModeNN) __builtin_nontemporal_store(v, dst);
+          else *dst = v;
+        }
       }
       __syncthreads();
     }
