@@ -118,6 +118,15 @@ def git_head():
         return None
 
 
+def bf16_tile_rows(rows, E):
+    """Row height of the bf16 grouped GEMM tiles the library picks for `rows` permuted rows over E
+    experts (the rule in gemm.hip: 128 below 192 rows per expert on average, 320 from 232 to 304,
+    else 256)."""
+    if rows < 192 * E:
+        return 128
+    return 320 if 232 * E <= rows <= 304 * E else 256
+
+
 def traffic_file(kernel_tag, workload):
     return os.path.join(ROOT, "profiles", f"{kernel_tag}_{workload}_hbm_traffic.txt")
 
@@ -895,7 +904,7 @@ def bench_forward(args, cfg, d, layer, torch, _lib, util, moe_gpu):
                      "E8M0 variant; the events include the fp32-scale variant <128, true, false> launched beside it, "
                      "which exits at once when every scale is a power of two)",
               "fp4": "gemm_fp4_kernel<128, true, false> (grouped MXFP4 GEMM1 + fused SwiGLU + 1x32 re-quantisation)",
-              "bf16": f"gemm_bf16_kernel<{256 if cfg.T * cfg.k >= 192 * cfg.E else 128}, 2, true, false, 1, 0> "
+              "bf16": f"gemm_bf16_kernel<{bf16_tile_rows(cfg.T * cfg.k, cfg.E)}, 2, true, false, 1, 0> "
                       "(routed experts' grouped GEMM1 + fused SwiGLU)",
               "f32": "gemm_f32_kernel<swiglu> (grouped fp32 GEMM1 + fused SwiGLU)"}[mm_dtype]
     if mfma_bound:
@@ -973,7 +982,7 @@ def main():
     ap.add_argument("--traffic-report", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
                     help="HBM traffic summary of one launch position from FETCH_SIZE / WRITE_SIZE runs")
     ap.add_argument("--traffic-phase", type=int, default=PH_COLD)
-    ap.add_argument("--traffic-label", default="gemm_bf16_kernel<256, 2, true, false, 1, 0> #0")
+    ap.add_argument("--traffic-label", default="gemm_bf16_kernel<320, 2, true, false, 1, 0> #0")
     ap.add_argument("--traffic-alg-bytes", type=int, default=0)
     args = ap.parse_args()
     if args.summarize_trace:

@@ -68,10 +68,12 @@ constexpr int kThreads = 256;  // fp32 path
 // tile kt + 1 and meets the other waves at the single barrier of the iteration; the last k-step
 // then reads tile kt + 1's first fragments, so the MFMA pipe restarts right after the barrier,
 // and in its last slots loads A tile kt + NA into the stage tile kt used.  The loads of B tile
-// kt + NB follow in k-steps 1 and 2 of iteration kt + 1.  Loads go out after the reads and away
-// from the barrier: a direct load issued ahead of a wave's LDS reads delays them (measured: the
-// GEMMs ran 6-9% slower with each load issued right after the barrier, before its read).  A
-// loads have most of an iteration to land, B loads more than NB - 2.
+// kt + NB follow in k-steps 1 and 2 of iteration kt + 1 -- or, with two B stages (320-row tiles,
+// whose two 40 KB A stages leave room for only two), right after the A loads.  Loads go out
+// after the reads and away from the barrier: a direct load issued ahead of a wave's LDS reads
+// delays them (measured: the GEMMs ran 6-9% slower with each load issued right after the
+// barrier, before its read).  A loads have most of an iteration to land, B loads more than
+// NB - 2 (with two stages, most of one).
 // Loads are unconditional: rows past the expert's end re-read its last row and column groups
 // past the matrix edge re-read column 0; those results are never stored.
 constexpr int kBKT = 64;        // K per iteration / stage
@@ -79,8 +81,14 @@ constexpr int kBRow = kBN * 2;  // bytes per [K, N] B k-row
 
 template <int BM>
 struct Bf16Rings {
-  static constexpr int NA = BM == 256 ? 2 : 3;  // LDS: 2 x 32 + 3 x 32 KB or 3 x 16 + 3 x 32 KB
-  static constexpr int NB = 3;
+  // LDS: 2 x 40 + 2 x 32 KB (BM 320), 2 x 32 + 3 x 32 KB (BM 256), 3 x 16 + 3 x 32 KB (BM 128)
+  static constexpr int NA = BM >= 256 ? 2 : 3;
+  static constexpr int NB = BM == 320 ? 2 : 3;
+  // Where the loads of B tile j + NB go out: 0 = k-steps 1 and 2 of iteration j + 1, 2 = the last
+  // k-step of iteration j, after its A loads: the earliest slot a two-stage B ring allows (the
+  // latest, k-steps 1 and 2, made the DeepSeek-V3-shaped GEMM1 6% slower; B loads ahead of the A
+  // loads in that k-step 3% slower; the A loads moved to k-step 0 of the next iteration: equal).
+  static constexpr int B_PLACE = NB == 2 ? 2 : 0;
   static constexpr int A_BYTES = BM * kBKT * 2;
   static constexpr int B_BYTES = kBN * kBKT * 2;
   static constexpr int SMEM = NA * A_BYTES + NB * B_BYTES;
@@ -104,6 +112,7 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
   constexpr int B_ROUNDS = B_BYTES / 1024 / NWAVE;
   constexpr int RPT = A_ROUNDS + B_ROUNDS;
   static_assert(NA >= 2 && NB >= NA, "ring depths");
+  static_assert(R::B_PLACE == 0 || NA == NB, "B loads beside the A loads: equal ring depths");
   static_assert(kMaxExpertsLds * 4 <= B_BYTES, "tile-map prefix fits in the first B stage");
   static_assert(MODE != kModeBatchK || (OUT_F32 && !SWIGLU && S == 1), "batched mode: plain fp32 out");
   constexpr bool BNK = MODE == kModeNT;
@@ -333,7 +342,7 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     // stage freed at the previous iteration's barrier)
     auto kstep = [&](auto ks_c, int kt) {
       constexpr int ks = decltype(ks_c)::value;
-      constexpr int BL = ks == 0 ? 0 : B_ROUNDS / 2, B0 = ks == 2 ? B_ROUNDS / 2 : 0;
+      constexpr int BL = (ks == 0 || R::B_PLACE != 0) ? 0 : B_ROUNDS / 2, B0 = ks == 2 ? B_ROUNDS / 2 : 0;
       constexpr int NQ = cmax(cmax(NL * FN, NR), BL);
       const int tb = kt - 1 + NB;
       const bool do_b = kt >= 1 && tb < nk;
@@ -376,11 +385,15 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
       // the barrier), and in its last slots the loads of A tile kt + NA (the A part of load group
       // kt, into the stage tile kt just left)
       {
-        const int ta = kt + NA;
+        const int ta = kt + NA, tb = kt + NB;
         const bool do_a = kt + 1 < nk && ta < nk;
-        const uint32_t abase = a_stage(ta);
-        constexpr int NQ = cmax(cmax(NL * FN, NR), A_ROUNDS);
-        constexpr int AQ = NQ - A_ROUNDS;  // first slot with an A load
+        const bool do_b = R::B_PLACE == 2 && kt + 1 < nk && tb < nk;
+        const uint32_t abase = a_stage(ta), bbase = b_stage(tb);
+        const bf16_t* bs = b_src + static_cast<int64_t>(tb) * b_kstep;
+        constexpr int BLL = R::B_PLACE == 2 ? B_ROUNDS : 0;  // B loads in this k-step
+        constexpr int NQ = cmax(cmax(NL * FN, NR), A_ROUNDS + BLL);
+        constexpr int AQ = NQ - A_ROUNDS - BLL;              // first slot with an A load
+        constexpr int BQ = NQ - BLL;                         // first slot with a B load
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
           if (q < NL * FN) {
@@ -390,8 +403,14 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
           // unconditional: past the last tile this reads a stale stage (in bounds, never used); a
           // branch here would make the compiler wait for these reads before the next MFMAs
           if (q < NR) read_unit(kt + 1, 0, 0, q);
-          if (q >= AQ && do_a && !((a_dead >> (q - AQ)) & 1u))
+          if (q >= AQ && q < BQ && do_a && !((a_dead >> (q - AQ)) & 1u))
             lds_dma16(a_src[q - AQ] + static_cast<int64_t>(ta) * kBKT, abase + (NWAVE * (q - AQ) + wave) * 1024);
+          if (q >= BQ && do_b) {
+            if constexpr (BNK)
+              lds_dma16(b_nk[q - BQ] + static_cast<int64_t>(tb) * kBKT, bbase + (NWAVE * (q - BQ) + wave) * 1024);
+            else
+              lds_dma16(bs + (q - BQ) * b_round, bbase + (NWAVE * (q - BQ) + wave) * 1024);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -403,16 +422,20 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
   //      row (r / 4) * 8 + (l / 32) * 4 + (r % 4), column l % 32.
   if constexpr (!OUT_F32) {
     // bf16 results (SwiGLU: h = SiLU(gate) * up) staged through LDS -- the operand rings are free
-    // once every wave is past its last reads -- then stored 16 bytes (8 columns) per lane.
+    // once every wave is past its last reads -- then stored 16 bytes (8 columns) per lane.  The
+    // whole tile is staged at once, or one wave row group (WROWS rows) at a time where the tile
+    // does not fit (BM 320 without SwiGLU).
     constexpr int NTH = NWAVE * kWave;
     constexpr int COLS = SWIGLU ? 128 : kBN;  // output columns of the tile
     constexpr int LS = COLS + 8;              // row stride in bf16: rows 4 apart start 16 banks apart
-    static_assert(BM * LS * 2 + BM * 4 <= R::SMEM, "output staging and row gates fit in the operand rings");
+    constexpr int GROUPS = BM * LS * 2 + BM * 4 <= R::SMEM ? 1 : WM;
+    constexpr int GROWS = BM / GROUPS;        // rows staged at once
+    static_assert(GROWS * LS * 2 + BM * 4 <= R::SMEM, "output staging and row gates fit in the operand rings");
     wait_lgkm0();
     __syncthreads();
     bf16_t* st = reinterpret_cast<bf16_t*>(smem);
     // gate folded into the expert: the tile's row gates, staged after the output rows
-    float* s_gate = reinterpret_cast<float*>(smem + BM * LS * 2);
+    float* s_gate = reinterpret_cast<float*>(smem + GROWS * LS * 2);
     if (SWIGLU && row_scale != nullptr) {
       if (tid < BM) {
         const int64_t g = tm.row0 + tid;
@@ -420,34 +443,42 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
       }
       __syncthreads();
     }
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
-        if (SWIGLU) {
-          float hv = silu_fast(acc[i][0][r]) * acc[i][1][r];
-          if (row_scale != nullptr) hv *= s_gate[row_t];
-          st[row_t * LS + wn * 32 + lane % 32] = f32_to_bf16(hv);
-        } else {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) st[row_t * LS + wn * 64 + j * 32 + lane % 32] = f32_to_bf16(acc[i][j][r]);
-        }
-      }
-    __syncthreads();
     constexpr int SEGS = COLS / 8, RPP = NTH / SEGS;  // lanes per row, rows per pass
+    static_assert(GROWS % RPP == 0, "whole passes per staged group");
     const int seg = tid % SEGS;
     const int64_t ldo = SWIGLU ? ldb / 2 : ldb;
     const int64_t col = static_cast<int64_t>(tm.nt) * COLS + seg * 8;
-    if (col < ldo) {  // ldo % 8 == 0: an 8-column group is wholly in or out
 #pragma unroll
-      for (int pass = 0; pass < BM / RPP; ++pass) {
-        const int row_t = pass * RPP + tid / SEGS;
-        const int64_t grow = tm.row0 + row_t;
-        if (grow < tm.row_end)
-          *reinterpret_cast<u32x4_t*>(static_cast<bf16_t*>(out) + grow * ldo + col) =
-              *reinterpret_cast<const u32x4_t*>(st + row_t * LS + seg * 8);
+    for (int g = 0; g < GROUPS; ++g) {
+      if (GROUPS == 1 || wm == g) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
+            const int row_s = row_t - g * GROWS;  // row in the staging buffer
+            if (SWIGLU) {
+              float hv = silu_fast(acc[i][0][r]) * acc[i][1][r];
+              if (row_scale != nullptr) hv *= s_gate[row_t];
+              st[row_s * LS + wn * 32 + lane % 32] = f32_to_bf16(hv);
+            } else {
+#pragma unroll
+              for (int j = 0; j < FN; ++j) st[row_s * LS + wn * 64 + j * 32 + lane % 32] = f32_to_bf16(acc[i][j][r]);
+            }
+          }
       }
+      __syncthreads();
+      if (col < ldo) {  // ldo % 8 == 0: an 8-column group is wholly in or out
+#pragma unroll
+        for (int pass = 0; pass < GROWS / RPP; ++pass) {
+          const int row_s = pass * RPP + tid / SEGS;
+          const int64_t grow = tm.row0 + g * GROWS + row_s;
+          if (grow < tm.row_end)
+            *reinterpret_cast<u32x4_t*>(static_cast<bf16_t*>(out) + grow * ldo + col) =
+                *reinterpret_cast<const u32x4_t*>(st + row_s * LS + seg * 8);
+        }
+      }
+      if (GROUPS > 1) __syncthreads();
     }
   } else if constexpr (SWIGLU) {
 #pragma unroll
@@ -465,31 +496,37 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
       }
     }
   } else {
-    // fp32 results staged through LDS one wave row group (WROWS rows) at a time, then written a
-    // whole row per wave instruction (16 bytes per lane, the tile row's 256 columns contiguous):
-    // with one 4-byte store per accumulator slot every instruction wrote 128-byte pieces of two
-    // rows, and the weight gradients of the backward write gigabytes of fp32 this way.
+    // fp32 results staged through LDS one wave row group (WROWS rows) at a time -- or one 32-row
+    // block of it where the group does not fit (BM 320) -- then written a whole row per wave
+    // instruction (16 bytes per lane, the tile row's 256 columns contiguous): with one 4-byte store
+    // per accumulator slot every instruction wrote 128-byte pieces of two rows, and the weight
+    // gradients of the backward write gigabytes of fp32 this way.
     constexpr int LSF = kBN + 8;  // fp32 row stride: the two lane halves (rows 4 apart) 32 banks apart
-    static_assert(WROWS * LSF * 4 <= R::SMEM, "one row group of fp32 results fits in the rings");
+    constexpr int FMC = FM * 32 * LSF * 4 <= R::SMEM ? FM : 1;  // 32-row blocks staged at once
+    constexpr int CROWS = FMC * 32;
+    static_assert(CROWS * LSF * 4 <= R::SMEM, "one staged chunk of fp32 results fits in the rings");
     float* st = reinterpret_cast<float*>(smem);
     wait_lgkm0();
     __syncthreads();
 #pragma unroll
-    for (int g = 0; g < WM; ++g) {
+    for (int gc = 0; gc < WM * (FM / FMC); ++gc) {
+      const int g = gc / (FM / FMC), c = gc % (FM / FMC);  // wave row group, chunk of its blocks
       if (wm == g) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i) {
+          if (i / FMC != c) continue;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int row_l = i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
+            const int row_l = (i % FMC) * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
 #pragma unroll
             for (int j = 0; j < FN; ++j) st[row_l * LSF + wn * 64 + j * 32 + lane % 32] = acc[i][j][r];
           }
+        }
       }
       __syncthreads();
       const int64_t col = static_cast<int64_t>(tm.nt) * kBN + lane * 4;
-      for (int row_l = wave; row_l < WROWS; row_l += NWAVE) {
-        const int64_t grow = tm.row0 + g * WROWS + row_l;
+      for (int row_l = wave; row_l < CROWS; row_l += NWAVE) {
+        const int64_t grow = tm.row0 + g * WROWS + c * CROWS + row_l;
         if (grow < tm.row_end && col < ldb) {  // ldb % 4 == 0: a 4-column group is wholly in or out
           const f32x4_t v = *reinterpret_cast<const f32x4_t*>(st + row_l * LSF + lane * 4);
           f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + grow * ldb + col);
@@ -741,13 +778,22 @@ hipError_t launch_grouped_swiglu(const void* x_perm, const void* x_scales, int d
     return hipGetLastError();
   }
   if (dt == 1) {
-    // 256-row tiles when experts average >= 192 rows (the last, partial m-tile of an expert only
-    // computes its live 32-row blocks), else 128-row tiles
-    const bool big = offsets == nullptr ? rows >= 192 : rows >= 192 * static_cast<int64_t>(E);
-    return big ? launch_bf16_pair<256>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream,
-                                       between, gather, row_scale)
-               : launch_bf16_pair<128>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream,
-                                       between, gather, row_scale);
+    // 128-row tiles when experts average < 192 rows; 320-row tiles when they average 232 to 304
+    // rows, so that an expert of up to 320 rows (most of them, with the spread of a balanced
+    // router) streams each weight tile through LDS once instead of twice; else 256-row tiles (the
+    // last, partial m-tile of an expert only computes its live 32-row blocks).  DeepSeek-V3-shaped
+    // routing (211-304 rows per expert): GEMM1 4.31 -> 3.87 ms, GEMM2 2.42 -> 2.34 ms; with exactly
+    // 224 rows per expert (one tile either way) the 256-row tiles and their three B stages are 5%
+    // faster, with exactly 288 rows the 320-row tiles 12%.
+    const int64_t e = offsets == nullptr ? 1 : E;
+    if (rows < 192 * e)
+      return launch_bf16_pair<128>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream,
+                                   between, gather, row_scale);
+    if (offsets != nullptr && rows >= 232 * e && rows <= 304 * e)
+      return launch_bf16_pair<320>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream,
+                                   between, gather, row_scale);
+    return launch_bf16_pair<256>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream,
+                                 between, gather, row_scale);
   }
   return hipErrorNotSupported;
 }

@@ -7,7 +7,7 @@ import torch
 import moe_inputs
 import mixture_experts_layer_fp32_amd as moe_gpu
 from oracle import moe
-from tests.checks import check_permutation, rel_frobenius
+from tests.checks import check_permutation, max_row_rel, rel_frobenius
 from tests.gpu_oracle import TOL, TOL_GATES, TOL_LOGITS, host, routing_from_logits, weights_of
 
 pytestmark = pytest.mark.gpu
@@ -265,6 +265,28 @@ def test_offsets_past_rows_are_clamped():
     torch.cuda.synchronize()
     ref = moe.grouped_experts(host(x), np.array([0, 120, rows]), lambda e: host(w1[e]), lambda e: host(w2[e]))
     assert rel_frobenius(host(yp), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_320_row_tiles(out_dtype):
+    """Experts averaging 192-288 rows take 320-row tiles: one m-tile for experts of up to 320 rows
+    (300 and 215 here: 10 and 7 live 32-row blocks), two for 330 rows; the second GEMM stages its
+    output per row group (bf16) or per 32-row block (fp32).  H = 640 leaves a half N tile."""
+    counts = [300, 215, 330]
+    rows, H, F, E = sum(counts), 640, 384, 3
+    gen = torch.Generator().manual_seed(13)
+    x = (torch.randn(rows, H, generator=gen)).to(torch.bfloat16).to(DEV)
+    w1 = (torch.randn(E, H, 2 * F, generator=gen) * H ** -0.5).to(torch.bfloat16).to(DEV)
+    w2 = (torch.randn(E, F, H, generator=gen) * F ** -0.5).to(torch.bfloat16).to(DEV)
+    off_h = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    off = torch.from_numpy(off_h).to(DEV)
+    yp = moe_gpu.grouped_swiglu(x, off, w1, w2, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref = moe.grouped_experts(host(x), off_h.astype(np.int64), lambda e: host(w1[e]), lambda e: host(w2[e]))
+    got = host(yp)
+    print(f"[edge] 320-row tiles {out_dtype}: rel {rel_frobenius(got, ref):.3e} worst row {max_row_rel(got, ref):.3e}",
+          flush=True)
+    assert rel_frobenius(got, ref) <= TOL["bf16"] and max_row_rel(got, ref) <= TOL["bf16"]
 
 
 def test_row_map_outside_range_reads_row_zero():

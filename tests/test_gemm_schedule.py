@@ -42,12 +42,13 @@ class Wave:
         assert ops == self.needs, ("tile never loaded", tile, ops)
 
 
-def bf16_kernel(NA, NB, AR, BR, nk, dead=0):
+def bf16_kernel(NA, NB, AR, BR, nk, dead=0, place=0):
     """gemm_bf16_kernel: prologue groups -NB..-1 (A tile j+NA, B tile j+NB); in iteration kt the
-    B loads of tile kt-1+NB go out in k-steps 1 and 2, the wait for tile kt+1 and the barrier
-    follow k-step 2, and the A loads of tile kt+NA take the last slots of the last k-step.  A wave
-    skips `dead` of its AR A loads per tile (the rounds past the tile's last live row block); its
-    waits allow (NA - 1) and (NA - 2) groups of AR - dead + BR loads."""
+    B loads of tile kt-1+NB go out in k-steps 1 and 2 (place 0), the wait for tile kt+1 and the
+    barrier follow k-step 2, and the A loads of tile kt+NA take the last slots of the last k-step,
+    followed there by the B loads of tile kt+NB with place 2.  A wave skips `dead` of its AR A
+    loads per tile (the rounds past the tile's last live row block); its waits allow (NA - 1) and
+    (NA - 2) groups of AR - dead + BR loads."""
     ar = AR - dead
     w = Wave(NA, NB, nk, loads_a=ar > 0)
     RPT = ar + BR
@@ -65,7 +66,7 @@ def bf16_kernel(NA, NB, AR, BR, nk, dead=0):
     w.last_barrier = -1
     for kt in range(nk):
         tb = kt - 1 + NB
-        if kt >= 1 and tb < nk:
+        if place == 0 and kt >= 1 and tb < nk:
             w.load("B", tb, BR // 2)           # k-step 1
             w.load("B", tb, BR - BR // 2)      # k-step 2
         if kt + 1 < nk:
@@ -73,6 +74,8 @@ def bf16_kernel(NA, NB, AR, BR, nk, dead=0):
             w.last_barrier = kt
         if kt + 1 < nk and kt + NA < nk and ar:
             w.load("A", kt + NA, ar)           # last k-step
+        if place == 2 and kt + 1 < nk and kt + NB < nk:
+            w.load("B", kt + NB, BR)           # last k-step, after the A loads
     return w
 
 
@@ -119,21 +122,22 @@ def fp8_kernel(NA, NB, AR, BR, nk, scale_load, mx):
 
 
 # ring depths and loads per wave per tile of the instantiated kernels
-BF16 = {"BM 256": (2, 3, 4, 4), "BM 128": (3, 3, 2, 4)}
+BF16 = {"BM 320": (2, 2, 5, 4, 2), "BM 256": (2, 3, 4, 4, 0), "BM 128": (3, 3, 2, 4, 0)}
 FP8 = {"MX, BM 192": (2, 3, 3, 4, True), "general, BM 128": (3, 3, 2, 4, False)}
 
 
 @pytest.mark.parametrize("name", list(BF16))
 def test_bf16_ring_protocol(name):
-    NA, NB, AR, BR = BF16[name]
+    NA, NB, AR, BR, place = BF16[name]
     for nk, dead in itertools.product(range(1, 80), range(AR + 1)):
-        bf16_kernel(NA, NB, AR, BR, nk, dead)
+        bf16_kernel(NA, NB, AR, BR, nk, dead, place)
+
 
 
 def test_dead_rounds_need_the_reduced_counts():
     """With skipped A loads the unreduced wait count is too permissive for the deeper A ring (the
     tile's B loads may still be in flight), so the reduction is what keeps the protocol correct."""
-    NA, NB, AR, BR = BF16["BM 128"]
+    NA, NB, AR, BR, _ = BF16["BM 128"]
     nk, dead = 8, 1
     w = Wave(NA, NB, nk)
     ar = AR - dead
@@ -155,7 +159,7 @@ def test_fp8_ring_protocol(name):
 
 def test_model_catches_a_short_wait():
     """The model is not vacuous: one load fewer allowed in flight passes, one more fails."""
-    NA, NB, AR, BR = BF16["BM 256"]
+    NA, NB, AR, BR, _ = BF16["BM 256"]
     w = Wave(NA, NB, 10)
     w.load("A", 0, AR)
     w.load("B", 0, BR)

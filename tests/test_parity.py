@@ -30,6 +30,9 @@ SMALL = {
     "mixtral_small": _small("mixtral_8x7b", T=300, H=256, F=384),
     "qwen3_small": _small("qwen3_235b", T=333, H=320, E=16, k=4, F=256),
     "deepseek_small": _small("deepseek_v3", T=257, H=512, E=32, k=8, F=256, Fs=384),
+    # experts averaging 192-288 rows: the 320-row GEMM tiles (two B stages; the second GEMM's
+    # output staged per row group); H = 384 leaves a half N tile
+    "deepseek_bm320": _small("deepseek_v3", T=520, H=384, E=8, k=4, F=256, Fs=256),
     # >= 768 rows per expert: the 256-row GEMM tiles; H not a multiple of 256 (ragged N tile)
     "mixtral_bigtile": _small("mixtral_8x7b", T=1700, H=320, E=3, k=2, F=384),
     # >= 64 experts: router logits through the dense GEMM kernel (3 x 96 columns: a ragged N tile)

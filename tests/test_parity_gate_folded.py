@@ -23,6 +23,7 @@ DEV = "cuda"
 CASES = {
     "fp32_ragged": moe_inputs.CONFIGS["tiny_fp32"].replace(T=97, E=6, k=3, H=96, F=160),
     "bf16_deepseek_small": moe_inputs.CONFIGS["deepseek_v3"].replace(T=257, H=512, E=32, k=8, F=256, Fs=384),
+    "bf16_bm320": moe_inputs.CONFIGS["deepseek_v3"].replace(T=520, H=384, E=8, k=4, F=256, Fs=256),
     "bf16_mixtral_bigtile": moe_inputs.CONFIGS["mixtral_8x7b"].replace(T=1700, H=320, E=3, k=2, F=384),
     "e4m3_small": moe_inputs.CONFIGS["deepseek_v3_fp8_zipf"].replace(T=300, H=640, E=16, k=4, F=384, Fs=256,
                                                                       zipf_bias=False),
