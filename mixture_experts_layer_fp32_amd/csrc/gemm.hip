@@ -352,7 +352,7 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
       for (int q = 0; q < NQ; ++q) {
         if (q < NL * FN) {
           const int i = q / FN, j = q % FN;
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks % 2][i], bfr[ks % 2][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks % 2][j], af[ks % 2][i], acc[i][j], 0, 0, 0);
         }
         if (q < NR) read_unit(kt, ks + 1, (ks + 1) % 2, q);
         if (q < BL && do_b) {
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
         for (int q = 0; q < NQ; ++q) {
           if (q < NL * FN) {
             const int i = q / FN, j = q % FN;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bfr[1][j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[1][j], af[1][i], acc[i][j], 0, 0, 0);
           }
           // unconditional: past the last tile this reads a stale stage (in bounds, never used); a
           // branch here would make the compiler wait for these reads before the next MFMAs
@@ -418,31 +418,28 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
   };
   dispatch_live<FM>(nlive, run);
 
-  // ---- epilogue.  32x32 accumulator layout: slot r of lane l is
-  //      row (r / 4) * 8 + (l / 32) * 4 + (r % 4), column l % 32.
+  // ---- epilogue.  The MFMAs take the weight fragment as their first operand, so each computes a
+  //      transposed 32x32 block: slot r of lane l of acc[i][j] is the wave's row i * 32 + l % 32
+  //      and column j * 32 + (r / 4) * 8 + (l / 32) * 4 + (r % 4) of block j, so every lane holds
+  //      4 adjacent columns of one row per group of 4 slots.
   if constexpr (!OUT_F32) {
     // bf16 results (SwiGLU: h = SiLU(gate) * up) staged through LDS -- the operand rings are free
-    // once every wave is past its last reads -- then stored 16 bytes (8 columns) per lane.  The
-    // whole tile is staged at once, or one wave row group (WROWS rows) at a time where the tile
-    // does not fit (BM 320 without SwiGLU).
+    // once every wave is past its last reads -- 4 adjacent columns (8 bytes) per lane and LDS
+    // write, then stored 16 bytes (8 columns) per lane, whole tile rows per wave instruction.  The
+    // whole tile is staged at once, or one wave row group (WROWS rows) at a time where it does not
+    // fit (BM 320 without SwiGLU).  (With one column per lane -- the other operand order -- the
+    // staging took one 2-byte LDS write per value: 9% of the DeepSeek-V3-shaped GEMM2.  Storing
+    // the 8-byte pieces straight to global memory instead, 32 rows per instruction, was slower.)
     constexpr int NTH = NWAVE * kWave;
     constexpr int COLS = SWIGLU ? 128 : kBN;  // output columns of the tile
-    constexpr int LS = COLS + 8;              // row stride in bf16: rows 4 apart start 16 banks apart
-    constexpr int GROUPS = BM * LS * 2 + BM * 4 <= R::SMEM ? 1 : WM;
+    constexpr int LS = COLS + 8;              // row stride in bf16 (rows 16-byte aligned)
+    constexpr int GROUPS = BM * LS * 2 <= R::SMEM ? 1 : WM;
     constexpr int GROWS = BM / GROUPS;        // rows staged at once
-    static_assert(GROWS * LS * 2 + BM * 4 <= R::SMEM, "output staging and row gates fit in the operand rings");
+    static_assert(GROWS * LS * 2 <= R::SMEM, "output staging fits in the operand rings");
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
     wait_lgkm0();
     __syncthreads();
     bf16_t* st = reinterpret_cast<bf16_t*>(smem);
-    // gate folded into the expert: the tile's row gates, staged after the output rows
-    float* s_gate = reinterpret_cast<float*>(smem + GROWS * LS * 2);
-    if (SWIGLU && row_scale != nullptr) {
-      if (tid < BM) {
-        const int64_t g = tm.row0 + tid;
-        s_gate[tid] = row_scale[g < tm.row_end ? g : tm.row_end - 1];
-      }
-      __syncthreads();
-    }
     constexpr int SEGS = COLS / 8, RPP = NTH / SEGS;  // lanes per row, rows per pass
     static_assert(GROWS % RPP == 0, "whole passes per staged group");
     const int seg = tid % SEGS;
@@ -452,20 +449,29 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     for (int g = 0; g < GROUPS; ++g) {
       if (GROUPS == 1 || wm == g) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
-            const int row_s = row_t - g * GROWS;  // row in the staging buffer
-            if (SWIGLU) {
-              float hv = silu_fast(acc[i][0][r]) * acc[i][1][r];
-              if (row_scale != nullptr) hv *= s_gate[row_t];
-              st[row_s * LS + wn * 32 + lane % 32] = f32_to_bf16(hv);
-            } else {
-#pragma unroll
-              for (int j = 0; j < FN; ++j) st[row_s * LS + wn * 64 + j * 32 + lane % 32] = f32_to_bf16(acc[i][j][r]);
-            }
+        for (int i = 0; i < FM; ++i) {
+          if (i * 32 >= nl_rows) continue;  // no row of this block is live (wave-uniform)
+          const int row_t = wm * WROWS + i * 32 + lane % 32;
+          const int row_s = row_t - g * GROWS;  // row in the staging buffer
+          float gate = 1.0f;  // gate folded into the expert: h scaled by the row's gate before rounding
+          if (SWIGLU && row_scale != nullptr) {
+            const int64_t gr = tm.row0 + row_t;
+            gate = row_scale[gr < tm.row_end ? gr : tm.row_end - 1];
           }
+          constexpr int NJ = SWIGLU ? 1 : FN;  // output column blocks (SwiGLU: gate 0 with up 1)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int c = (SWIGLU ? wn * 32 : wn * 64 + j * 32) + q * 8 + khalf * 4;
+              float v[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                v[t] = SWIGLU ? silu_fast(acc[i][0][4 * q + t]) * acc[i][1][4 * q + t] * gate : acc[i][j][4 * q + t];
+              const u32x2_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+              *reinterpret_cast<u32x2_t*>(st + row_s * LS + c) = w;
+            }
+        }
       }
       __syncthreads();
       if (col < ldo) {  // ldo % 8 == 0: an 8-column group is wholly in or out
@@ -481,18 +487,20 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
       if (GROUPS > 1) __syncthreads();
     }
   } else if constexpr (SWIGLU) {
+    // fp32 h straight from the registers, 16 bytes (4 adjacent columns) per lane
+    const int64_t ldo = ldb / 2;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      const int64_t grow = tm.row0 + wm * WROWS + i * 32 + lane % 32;
+      if (grow >= tm.row_end) continue;
+      const float gate = row_scale != nullptr ? row_scale[grow] : 1.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
-        const int64_t grow = tm.row0 + row_t;
-        if (grow >= tm.row_end) continue;
-        const int F = ldb / 2;
-        const int64_t col = static_cast<int64_t>(tm.nt) * 128 + wn * 32 + lane % 32;
-        float hv = silu_fast(acc[i][0][r]) * acc[i][1][r];
-        if (row_scale != nullptr) hv *= row_scale[grow];
-        static_cast<float*>(out)[grow * F + col] = hv;
+      for (int q = 0; q < 4; ++q) {
+        const int64_t c = static_cast<int64_t>(tm.nt) * 128 + wn * 32 + q * 8 + khalf * 4;
+        f32x4_t w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w[t] = silu_fast(acc[i][0][4 * q + t]) * acc[i][1][4 * q + t] * gate;
+        *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + grow * ldo + c) = w;
       }
     }
   } else {
@@ -501,7 +509,7 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
     // instruction (16 bytes per lane, the tile row's 256 columns contiguous): with one 4-byte store
     // per accumulator slot every instruction wrote 128-byte pieces of two rows, and the weight
     // gradients of the backward write gigabytes of fp32 this way.
-    constexpr int LSF = kBN + 8;  // fp32 row stride: the two lane halves (rows 4 apart) 32 banks apart
+    constexpr int LSF = kBN + 4;  // fp32 row stride: 16 consecutive rows start 4 banks apart
     constexpr int FMC = FM * 32 * LSF * 4 <= R::SMEM ? FM : 1;  // 32-row blocks staged at once
     constexpr int CROWS = FMC * 32;
     static_assert(CROWS * LSF * 4 <= R::SMEM, "one staged chunk of fp32 results fits in the rings");
@@ -515,12 +523,14 @@ __global__ __launch_bounds__(256 * WM) void gemm_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           if (i / FMC != c) continue;
+          const int row_l = (i % FMC) * 32 + lane % 32;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row_l = (i % FMC) * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
+          for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) st[row_l * LSF + wn * 64 + j * 32 + lane % 32] = acc[i][j][r];
-          }
+            for (int q = 0; q < 4; ++q) {
+              const f32x4_t w = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+              *reinterpret_cast<f32x4_t*>(st + row_l * LSF + wn * 64 + j * 32 + q * 8 + khalf * 4) = w;
+            }
         }
       }
       __syncthreads();
