@@ -229,8 +229,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp4_kernel(
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int eb = static_cast<int>((s < 2 ? sb[j][0] : sb[j][1]) >> sh);
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[buf][i], bf[buf][j], acc[i][j], 4, 4, 0, ea,
-                                                                       0, eb);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[buf][j], af[buf][i], acc[i][j], 4, 4, 0, eb,
+                                                                       0, ea);
         }
       }
     };
@@ -256,24 +256,31 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp4_kernel(
   };
   dispatch_live<FM>(nlive, run);
 
-  // ---- epilogue.  32x32 accumulator layout: slot r of lane l is row (r / 4) * 8 + (l / 32) * 4 +
-  //      (r % 4), column l % 32.
+  // ---- epilogue.  The MFMAs take the weight fragment as their first operand, so each computes a
+  //      transposed 32x32 block: slot r of lane l of acc[i][j] is the wave's row i * 32 + l % 32
+  //      and column j * 32 + (r / 4) * 8 + (l / 32) * 4 + (r % 4) of block j -- 4 adjacent
+  //      columns of one row per group of 4 slots, written 16 (fp32) or 8 (bf16) bytes at a time.
   __syncthreads();  // every wave is done with the ring
   if constexpr (SWIGLU) {
     // h = SiLU(gate) * up (x the row's gate when folded), staged as fp32 [BM][128 + 8]; then 8 lanes
     // per row, 16 columns each: a 32-column block is 2 lanes (amax: 1 shuffle), each lane packs
     // its 16 codes into 8 bytes and even lanes write the block's E8M0 byte.
-    constexpr int kHS = 136;
+    constexpr int kHS = 132;  // row stride in floats: 16 consecutive rows start 4 banks apart
     static_assert(BM * kHS * 4 <= C::SMEM, "h staging fits in the ring");
     const int F = N / 2;
     float* hl = reinterpret_cast<float*>(smem);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      if (i * 32 >= nl_rows) continue;  // no row of this block is live (wave-uniform)
+      const int row_t = wm * WROWS + i * 32 + lane % 32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
-        hl[row_t * kHS + wn * 32 + lane % 32] = silu_fast(acc[i][0][r]) * acc[i][1][r];
+      for (int q = 0; q < 4; ++q) {
+        f32x4_t w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w[t] = silu_fast(acc[i][0][4 * q + t]) * acc[i][1][4 * q + t];
+        *reinterpret_cast<f32x4_t*>(hl + row_t * kHS + wn * 32 + q * 8 + khalf * 4) = w;
       }
+    }
     __syncthreads();
     uint8_t* hq = static_cast<uint8_t*>(out);
     const int seg = tid % 8;
@@ -307,17 +314,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp4_kernel(
       }
     }
   } else if constexpr (!OUT_F32) {
-    constexpr int kYS = 264;  // bf16 row stride: rows 4 apart (the two lane halves) 16 banks apart
+    constexpr int kYS = 264;  // bf16 row stride: rows 16-byte aligned
     static_assert(BM * kYS * 2 <= C::SMEM, "y staging fits in the ring");
     bf16_t* yl = reinterpret_cast<bf16_t*>(smem);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      if (i * 32 >= nl_rows) continue;  // no row of this block is live (wave-uniform)
+      const int row_t = wm * WROWS + i * 32 + lane % 32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) yl[row_t * kYS + wn * 64 + j * 32 + lane % 32] = f32_to_bf16(acc[i][j][r]);
-      }
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<u32x2_t*>(yl + row_t * kYS + wn * 64 + j * 32 + q * 8 + khalf * 4) =
+              u32x2_t{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                      pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+    }
     __syncthreads();
     const int seg = tid % 32;
     const int64_t col = static_cast<int64_t>(tm.nt) * kBN + seg * 8;
@@ -332,19 +343,22 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp4_kernel(
       }
     }
   } else {
+    // fp32 y straight from the registers, 16 bytes (4 adjacent columns) per lane
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      const int64_t grow = tm.row0 + wm * WROWS + i * 32 + lane % 32;
+      if (grow >= tm.row_end) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
-        const int64_t grow = tm.row0 + row_t;
-        if (grow >= tm.row_end) continue;
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int64_t col = static_cast<int64_t>(tm.nt) * kBN + wn * 64 + j * 32 + lane % 32;
-          if (col < N) static_cast<float*>(out)[grow * N + col] = acc[i][j][r];
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = static_cast<int64_t>(tm.nt) * kBN + wn * 64 + j * 32 + q * 8 + khalf * 4;
+          if (col < N) {  // N % 256 == 0
+            const f32x4_t w = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + grow * N + col) = w;
+          }
         }
-      }
+    }
   }
 }
 

@@ -352,8 +352,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
           for (int q = 0; q < NQ; ++q) {
             if (q < NL * FN) {
               const int i = q / FN, j = q % FN;
-              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[0][i], bfr[0][j], acc[i][j], 0, 0, 0,
-                                                                           sae[i], 0, sbe[j]);
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[0][j], af[0][i], acc[i][j], 0, 0, 0,
+                                                                           sbe[j], 0, sae[i]);
             }
             read_unit(kt, 1, 1, q);
             if (q >= NQ - B_ROUNDS && do_b) b_load(tb, q - (NQ - B_ROUNDS));
@@ -380,8 +380,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
           for (int q = 0; q < NQ; ++q) {
             if (q < NL * FN) {
               const int i = q / FN, j = q % FN;
-              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[1][i], bfr[1][j], acc[i][j], 0, 0, 0,
-                                                                           sae[i], 0, sbe[j]);
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[1][j], af[1][i], acc[i][j], 0, 0, 0,
+                                                                           sbe[j], 0, sae[i]);
             }
             read_unit(kt + 1, 0, 0, q);  // unconditional: a branch would make the compiler wait for it
             const int p = q - (NQ - NLD);  // the loads take the last NLD slots
@@ -404,25 +404,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
         for (int i = 0; i < NL; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            tmp[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[buf][i], bfr[buf][j],
+            tmp[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[buf][j], af[buf][i],
                                                                          first ? zero16 : tmp[i][j], 0, 0, 0, 127, 0,
                                                                          127);
       };
       // Scales of tile kt for the promotion at the end of its iteration, read before the next
-      // sub-step's fragments so that the promotion does not wait for those: per block i the row
-      // scales of this lane's 16 accumulator rows (4 runs of 4 consecutive rows), per block j the
-      // weight block's.
-      f32x4_t sa[NLA][4];
+      // sub-step's fragments so that the promotion does not wait for those: per block i the scale
+      // of this lane's accumulator row, per block j the weight block's.
+      float sa[NLA];
       float sb[FN];
       auto read_scales = [&](int kt) {
         const uint32_t sbase = scale_base(kt);
 #pragma unroll
         for (int i = 0; i < NL; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int row = wm * WROWS + i * 32 + q * 8 + khalf * 4;
-            sa[i][q] = *reinterpret_cast<const lds_f32x4_t*>(static_cast<uintptr_t>(sbase + row * 4));
-          }
+          sa[i] = *reinterpret_cast<const __attribute__((address_space(3))) float*>(
+              static_cast<uintptr_t>(sbase + (wm * WROWS + i * 32 + lane % 32) * 4));
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           sb[j] = *reinterpret_cast<const __attribute__((address_space(3))) float*>(
@@ -446,31 +442,39 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
 #pragma unroll
           for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(tmp[i][j][r], sa[i][r / 4][r % 4] * sb[j], acc[i][j][r]);
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(tmp[i][j][r], sa[i] * sb[j], acc[i][j][r]);
       }
     }
   };
   dispatch_live<FM>(nlive, run);
 
-  // ---- epilogue.  32x32 accumulator layout: slot r of lane l is
-  //      row (r / 4) * 8 + (l / 32) * 4 + (r % 4), column l % 32.
+  // ---- epilogue.  The MFMAs take the weight fragment as their first operand, so each computes a
+  //      transposed 32x32 block: slot r of lane l of acc[i][j] is the wave's row i * 32 + l % 32
+  //      and column j * 32 + (r / 4) * 8 + (l / 32) * 4 + (r % 4) of block j -- 4 adjacent
+  //      columns of one row per group of 4 slots, written to LDS or memory 16 (fp32) or 8 (bf16)
+  //      bytes at a time.
   if (SWIGLU) {
     // h = SiLU(gate) * up, staged through LDS as fp32 rows of the tile's 128 h columns (one 1 x 128
     // quantisation block per row).  Read back by 8 consecutive lanes per row, 16 columns each:
     // the block amax is a register max and 3 shuffles, and each lane stores 16 E4M3 codes at once.
-    constexpr int kHS = 136;  // row stride in floats: rows 4 apart (the two lane halves) start 32 banks apart
+    constexpr int kHS = 132;  // row stride in floats: 16 consecutive rows start 4 banks apart
     static_assert(BM * kHS * 4 <= C::S_RING, "h staging fits in the operand rings");
     const int F = ldb / 2;
     wait_lgkm0();
     __syncthreads();  // every wave is done with the operand ring
     float* hl = reinterpret_cast<float*>(smem);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      if (i * 32 >= nl_rows) continue;  // no row of this block is live (wave-uniform)
+      const int row_t = wm * WROWS + i * 32 + lane % 32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
-        hl[row_t * kHS + wn * 32 + lane % 32] = silu_fast(acc[i][0][r]) * acc[i][1][r];
+      for (int q = 0; q < 4; ++q) {
+        f32x4_t w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w[t] = silu_fast(acc[i][0][4 * q + t]) * acc[i][1][4 * q + t];
+        *reinterpret_cast<f32x4_t*>(hl + row_t * kHS + wn * 32 + q * 8 + khalf * 4) = w;
       }
+    }
     __syncthreads();
     uint8_t* hq = static_cast<uint8_t*>(out);
     const int seg = tid % 8;
@@ -509,20 +513,27 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
       }
     }
   } else if (!OUT_F32) {
-    // bf16 y staged through LDS as [BM][256] (+ padding) and stored 16 bytes (8 columns) per lane
-    constexpr int kYS = 264;  // row stride in bf16: rows 4 apart (the two lane halves) 16 banks apart
+    // bf16 y staged through LDS as [BM][256] (+ padding), 4 adjacent columns (8 bytes) per lane and
+    // LDS write, and stored 16 bytes (8 columns) per lane along whole tile rows
+    constexpr int kYS = 264;  // row stride in bf16: rows 16-byte aligned
     static_assert(BM * kYS * 2 <= C::S_RING, "y staging fits in the operand rings");
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
     wait_lgkm0();
     __syncthreads();  // every wave is done with the operand ring
     bf16_t* yl = reinterpret_cast<bf16_t*>(smem);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      if (i * 32 >= nl_rows) continue;  // no row of this block is live (wave-uniform)
+      const int row_t = wm * WROWS + i * 32 + lane % 32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) yl[row_t * kYS + wn * 64 + j * 32 + lane % 32] = f32_to_bf16(acc[i][j][r]);
-      }
+        for (int q = 0; q < 4; ++q) {
+          const u32x2_t w = {pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                             pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+          *reinterpret_cast<u32x2_t*>(yl + row_t * kYS + wn * 64 + j * 32 + q * 8 + khalf * 4) = w;
+        }
+    }
     __syncthreads();
     const int seg = tid % 32;  // 8 columns each, 32 lanes per row
     const int64_t col = static_cast<int64_t>(tm.nt) * kBN + seg * 8;
@@ -537,19 +548,22 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
       }
     }
   } else {
+    // fp32 y straight from the registers, 16 bytes (4 adjacent columns) per lane
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      const int64_t grow = tm.row0 + wm * WROWS + i * 32 + lane % 32;
+      if (grow >= tm.row_end) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row_t = wm * WROWS + i * 32 + (r / 4) * 8 + khalf * 4 + (r % 4);
-        const int64_t grow = tm.row0 + row_t;
-        if (grow >= tm.row_end) continue;
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int64_t col = static_cast<int64_t>(tm.nt) * kBN + wn * 64 + j * 32 + lane % 32;
-          if (col < ldb) static_cast<float*>(out)[grow * ldb + col] = acc[i][j][r];
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = static_cast<int64_t>(tm.nt) * kBN + wn * 64 + j * 32 + q * 8 + khalf * 4;
+          if (col < ldb) {  // ldb % 128 == 0: a 4-column group is wholly in or out
+            const f32x4_t w = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + grow * ldb + col) = w;
+          }
         }
-      }
+    }
   }
 }
 
