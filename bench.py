@@ -481,12 +481,12 @@ def bench_backward(args, cfg, d, layer, torch, moe_gpu, _lib, util):
     if mm_dtype == "bf16":
         # bf16 expert GEMMs run on the forward's grouped-GEMM kernel (operand mode: 0 weights [K, N],
         # 1 weights [N, K], 2 per-expert products); the weight-gradient stages include the transposes
-        bm = {"recompute_u": 256 if cfg.T * cfg.k >= 192 * cfg.E else 128,
-              "dgrad_h": 256 if cfg.T * cfg.k >= 192 * cfg.E else 128,
-              "dgrad_x": 256 if cfg.T * cfg.k >= 192 * cfg.E else 128,
+        grouped = bf16_tile_rows(cfg.T * cfg.k, cfg.E)
+        bm = {"recompute_u": grouped, "dgrad_h": grouped, "dgrad_x": grouped,
               "wgrad_w2": 256 if cfg.F >= 256 else 128, "wgrad_w1": 256 if cfg.H >= 256 else 128}[dom]
         mode = {"recompute_u": 0, "dgrad_h": 1, "dgrad_x": 1, "wgrad_w2": 2, "wgrad_w1": 2}[dom]
-        kname = f"gemm_bf16_kernel<{bm}, 2, false, true, 1, {mode}> ({dom}" + \
+        out_f32 = "false" if dom == "dgrad_x" else "true"  # dx_perm is written in bf16
+        kname = f"gemm_bf16_kernel<{bm}, 2, false, {out_f32}, 1, {mode}> ({dom}" + \
                 (", with its operand transpose)" if mode == 2 else ")")
     else:
         layout = {"recompute_u": "NN", "dgrad_h": "NT", "dgrad_x": "NT", "wgrad_w2": "TN", "wgrad_w1": "TN"}[dom]

@@ -712,37 +712,47 @@ hipError_t launch_dense_gemm_f32out(const void* A, const void* B, int64_t rows, 
                    : launch_bf16<128, false, true>(a, b, nullptr, rows, 1, K, N, nt, out, stream, 0, nullptr, ksplit);
 }
 
-hipError_t launch_grouped_gemm_f32out(const void* A, const void* B, const int32_t* offsets, int64_t rows, int E,
-                                      int K, int N, float* out, hipStream_t stream, const int32_t* gather) {
+// Tile height of the grouped bf16 GEMMs for `rows` rows over E experts (dense: one expert, no
+// offsets): 128-row tiles when experts average fewer than 192 rows; 320-row tiles when they average
+// 232 to 304 rows, so that an expert of up to 320 rows (most of them, with the spread of a balanced
+// router) streams each weight tile through LDS once instead of twice; else 256-row tiles (the last,
+// partial m-tile of an expert only computes its live 32-row blocks).  DeepSeek-V3-shaped routing
+// (211-304 rows per expert): forward GEMM1 4.31 -> 3.87 ms, GEMM2 2.42 -> 2.34 ms; with exactly 224
+// rows per expert (one tile either way) the 256-row tiles and their three B stages are 5% faster,
+// with exactly 288 rows the 320-row tiles 12%.
+int grouped_tile_rows(int64_t rows, int E, bool dense) {
+  const int64_t e = dense ? 1 : E;
+  if (rows < 192 * e) return 128;
+  return !dense && rows >= 232 * e && rows <= 304 * e ? 320 : 256;
+}
+
+template <bool OUT_F32, int MODE>
+hipError_t launch_grouped_plain(const void* A, const void* B, const int32_t* offsets, int64_t rows, int E, int K,
+                                int N, void* out, hipStream_t stream, const int32_t* gather) {
   if (rows <= 0) return hipSuccess;
-  const bool big = offsets == nullptr ? rows >= 192 : rows >= 192 * static_cast<int64_t>(E);
   const int nt = static_cast<int>(ceil_div(N, kBN));
   const bf16_t* a = static_cast<const bf16_t*>(A);
   const bf16_t* b = static_cast<const bf16_t*>(B);
-  return big ? launch_bf16<256, false, true>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather)
-             : launch_bf16<128, false, true>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather);
+  switch (grouped_tile_rows(rows, E, offsets == nullptr)) {
+    case 320: return launch_bf16<320, false, OUT_F32, 2, 1, MODE>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather);
+    case 256: return launch_bf16<256, false, OUT_F32, 2, 1, MODE>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather);
+    default: return launch_bf16<128, false, OUT_F32, 2, 1, MODE>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather);
+  }
+}
+
+hipError_t launch_grouped_gemm_f32out(const void* A, const void* B, const int32_t* offsets, int64_t rows, int E,
+                                      int K, int N, float* out, hipStream_t stream, const int32_t* gather) {
+  return launch_grouped_plain<true, kModeNN>(A, B, offsets, rows, E, K, N, out, stream, gather);
 }
 
 hipError_t launch_grouped_gemm_nt_f32out(const void* A, const void* B, const int32_t* offsets, int64_t rows, int E,
                                          int K, int N, float* out, hipStream_t stream, const int32_t* gather) {
-  if (rows <= 0) return hipSuccess;
-  const bool big = offsets == nullptr ? rows >= 192 : rows >= 192 * static_cast<int64_t>(E);
-  const int nt = static_cast<int>(ceil_div(N, kBN));
-  const bf16_t* a = static_cast<const bf16_t*>(A);
-  const bf16_t* b = static_cast<const bf16_t*>(B);
-  return big ? launch_bf16<256, false, true, 2, 1, kModeNT>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather)
-             : launch_bf16<128, false, true, 2, 1, kModeNT>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather);
+  return launch_grouped_plain<true, kModeNT>(A, B, offsets, rows, E, K, N, out, stream, gather);
 }
 
 hipError_t launch_grouped_gemm_nt_bf16out(const void* A, const void* B, const int32_t* offsets, int64_t rows, int E,
                                           int K, int N, void* out, hipStream_t stream, const int32_t* gather) {
-  if (rows <= 0) return hipSuccess;
-  const bool big = offsets == nullptr ? rows >= 192 : rows >= 192 * static_cast<int64_t>(E);
-  const int nt = static_cast<int>(ceil_div(N, kBN));
-  const bf16_t* a = static_cast<const bf16_t*>(A);
-  const bf16_t* b = static_cast<const bf16_t*>(B);
-  return big ? launch_bf16<256, false, false, 2, 1, kModeNT>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather)
-             : launch_bf16<128, false, false, 2, 1, kModeNT>(a, b, offsets, rows, E, K, N, nt, out, stream, 0, gather);
+  return launch_grouped_plain<false, kModeNT>(A, B, offsets, rows, E, K, N, out, stream, gather);
 }
 
 hipError_t launch_batched_gemm_f32out(const void* A, int64_t lda, const void* B, const int32_t* kinfo, int E, int M,
@@ -788,22 +798,17 @@ hipError_t launch_grouped_swiglu(const void* x_perm, const void* x_scales, int d
     return hipGetLastError();
   }
   if (dt == 1) {
-    // 128-row tiles when experts average < 192 rows; 320-row tiles when they average 232 to 304
-    // rows, so that an expert of up to 320 rows (most of them, with the spread of a balanced
-    // router) streams each weight tile through LDS once instead of twice; else 256-row tiles (the
-    // last, partial m-tile of an expert only computes its live 32-row blocks).  DeepSeek-V3-shaped
-    // routing (211-304 rows per expert): GEMM1 4.31 -> 3.87 ms, GEMM2 2.42 -> 2.34 ms; with exactly
-    // 224 rows per expert (one tile either way) the 256-row tiles and their three B stages are 5%
-    // faster, with exactly 288 rows the 320-row tiles 12%.
-    const int64_t e = offsets == nullptr ? 1 : E;
-    if (rows < 192 * e)
-      return launch_bf16_pair<128>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream,
-                                   between, gather, row_scale);
-    if (offsets != nullptr && rows >= 232 * e && rows <= 304 * e)
-      return launch_bf16_pair<320>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream,
-                                   between, gather, row_scale);
-    return launch_bf16_pair<256>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream,
-                                 between, gather, row_scale);
+    switch (grouped_tile_rows(rows, E, offsets == nullptr)) {
+      case 320:
+        return launch_bf16_pair<320>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream,
+                                     between, gather, row_scale);
+      case 256:
+        return launch_bf16_pair<256>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream,
+                                     between, gather, row_scale);
+      default:
+        return launch_bf16_pair<128>(x_perm, w1, w2, offsets, rows, E, H, F, y_perm, out_dt, scratch, stream,
+                                     between, gather, row_scale);
+    }
   }
   return hipErrorNotSupported;
 }

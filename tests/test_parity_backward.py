@@ -38,6 +38,9 @@ CASES = {
     "mixtral_small": _cfg("mixtral_8x7b", T=300, H=256, F=384),
     "qwen3_small": _cfg("qwen3_235b", T=333, H=320, E=16, k=4, F=256),
     "deepseek_small": _cfg("deepseek_v3", T=257, H=512, E=32, k=8, F=256, Fs=384),
+    # experts averaging 192-288 rows: the 320-row tiles in the recomputation and the data-gradient
+    # products (fp32 results staged 32 rows at a time; dx_perm in bf16); H = 384 leaves a half N tile
+    "deepseek_bm320": _cfg("deepseek_v3", T=520, H=384, E=8, k=4, F=256, Fs=256),
     # >= 128 rows per expert and H, 2F not multiples of 128: ragged M, N and K tiles everywhere
     "mixtral_ragged": _cfg("mixtral_8x7b", T=700, H=320, E=3, k=2, F=384),
     # most experts without rows: their weight gradients must be exactly zero
