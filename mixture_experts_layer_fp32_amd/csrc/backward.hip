@@ -742,6 +742,76 @@ __global__ __launch_bounds__(256) void bwd_gather_rows_kernel(const bf16_t* __re
   }
 }
 
+constexpr int kRouterPadRows = 64;  // zero rows after the last token of dW_r's B operand
+
+// The router's products of a bf16 layer on the bf16 MFMA kernel, as accurate as fp32: dlogits dl
+// (fp32) is split into three bf16 parts d1 + d2 + d3 (each the bf16 rounding, to nearest even, of
+// what the parts before it leave; the remainders are exact in fp32) and so is W_r (w1 + w2 + w3);
+// x is bf16 already.
+//   dx_r = dl W_r^T: the six products d_a w_b with a + b <= 4 -- the three left out are below
+//          2^-24 of the terms -- as one product over a 6E-deep contraction, the parts paired
+//          [d3 d2 d1 d2 d1 d1] . [w1 w2 w3 w1 w2 w1], the smallest first;
+//   dW_r = x^T dl = x^T d3 + x^T d2 + x^T d1: one per-slice product of x^T with [d3 d2 d1] over S
+//          row slices of the tokens, then summed over the slices and the parts.
+__device__ __forceinline__ void split_bf16x3(float v, bf16_t& p1, bf16_t& p2, bf16_t& p3) {
+  p1 = f32_to_bf16(v);
+  const float r1 = v - bf16_to_f32(p1);
+  p2 = f32_to_bf16(r1);
+  p3 = f32_to_bf16(r1 - bf16_to_f32(p2));
+}
+
+// a6 [T, 6E] = [d3 d2 d1 d2 d1 d1]; d3 [T + 64, 3E] = [d3 d2 d1], its last 64 rows zero.
+__global__ __launch_bounds__(256) void bwd_split_dl_kernel(const float* __restrict__ dl, int64_t T, int E,
+                                                           bf16_t* __restrict__ a6, bf16_t* __restrict__ d3) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= (T + kRouterPadRows) * E) return;
+  const int64_t t = i / E;
+  const int e = static_cast<int>(i % E);
+  bf16_t* d = d3 + t * 3 * E + e;
+  if (t >= T) {
+    d[0] = d[E] = d[2 * E] = 0;
+    return;
+  }
+  bf16_t p1, p2, p3;
+  split_bf16x3(dl[t * E + e], p1, p2, p3);
+  bf16_t* a = a6 + t * 6 * E + e;
+  a[0] = p3; a[E] = p2; a[2 * E] = p1; a[3 * E] = p2; a[4 * E] = p1; a[5 * E] = p1;
+  d[0] = p3; d[E] = p2; d[2 * E] = p1;
+}
+
+// b6 [H, 6E] = [w1 w2 w3 w1 w2 w1] of W_r [H, E] (row h of b6 is weight row h: the [N, K] operand).
+__global__ __launch_bounds__(256) void bwd_split_wr_kernel(const float* __restrict__ wr, int H, int E,
+                                                           bf16_t* __restrict__ b6) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(H) * E) return;
+  const int64_t h = i / E;
+  const int e = static_cast<int>(i % E);
+  bf16_t p1, p2, p3;
+  split_bf16x3(wr[i], p1, p2, p3);
+  bf16_t* b = b6 + h * 6 * E + e;
+  b[0] = p1; b[E] = p2; b[2 * E] = p3; b[3 * E] = p1; b[4 * E] = p2; b[5 * E] = p1;
+}
+
+// off[s] = T s / S, s = 0 .. S: the row slices of dW_r's contraction.
+__global__ void bwd_slice_offsets_kernel(int64_t T, int S, int32_t* __restrict__ off) {
+  const int s = static_cast<int>(threadIdx.x);
+  if (s <= S) off[s] = static_cast<int32_t>(T * s / S);
+}
+
+// dW_r[h][e] = sum over the parts d3, d2, d1 (the smallest first) and, inside each, the slices in
+// order of part[s][h][p E + e].
+__global__ __launch_bounds__(256) void bwd_router_dw_sum_kernel(const float* __restrict__ part, int S, int H, int E,
+                                                                float* __restrict__ dw) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(H) * E) return;
+  const int64_t h = i / E;
+  const int e = static_cast<int>(i % E);
+  float acc = 0.0f;
+  for (int p = 0; p < 3; ++p)
+    for (int sl = 0; sl < S; ++sl) acc += part[(static_cast<int64_t>(sl) * H + h) * 3 * E + p * E + e];
+  dw[i] = acc;
+}
+
 // Rows a per-expert product's B operand may read past the group's last row (its padding).
 constexpr int kPadRows = 64;
 
@@ -884,21 +954,55 @@ hipError_t layer_backward(const BackwardShape& sh, const BackwardIO& io, const B
     e = hipGetLastError();
   }
   // dx_router = dl W_r^T (W_r [H, E] read as [N = H, K = E]); dW_r = x^T dl
-  if (e == hipSuccess)
-    e = launch_bwd_gemm<kNT>(args(static_cast<const float*>(ws.dl), sh.E, static_cast<const int32_t*>(nullptr), T,
-                                  io.w_router, sh.E, 0, nullptr, 0, nullptr, T, 1, 0, sh.H, sh.E, ws.dxr, sh.H, 0),
-                             s);
-  const int S = router_slices(T, sh.H, sh.E);
-  if (e == hipSuccess)
-    e = launch_bwd_gemm<kTN>(args(x, sh.H, static_cast<const int32_t*>(nullptr), T, static_cast<const float*>(ws.dl),
-                                  sh.E, 0, static_cast<const int32_t*>(nullptr), T, nullptr, T, S, sh.H, sh.E, 0,
-                                  S > 1 ? ws.dwr_part : io.dw_router, sh.E, int64_t{sh.H} * sh.E),
-                             s);
-  if (e == hipSuccess && S > 1) {
-    const int64_t n = int64_t{sh.H} * sh.E;
-    hipLaunchKernelGGL(bwd_sum_slices_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, s,
-                       ws.dwr_part, S, n, io.dw_router);
-    e = hipGetLastError();
+  if constexpr (std::is_same<WT, bf16_t>::value) {
+    if (ws.ra6 != nullptr) {  // router_split: split bf16 products on the grouped-GEMM kernel
+      const int E = sh.E, H = sh.H, S = ws.rS;
+      const int64_t n = int64_t{H} * E;
+      if (e == hipSuccess) {
+        hipLaunchKernelGGL(bwd_split_dl_kernel, dim3(static_cast<unsigned>(ceil_div((T + kRouterPadRows) * E, 256))),
+                           dim3(256), 0, s, static_cast<const float*>(ws.dl), T, E, static_cast<bf16_t*>(ws.ra6),
+                           static_cast<bf16_t*>(ws.rd3));
+        e = hipGetLastError();
+      }
+      if (e == hipSuccess) {
+        hipLaunchKernelGGL(bwd_split_wr_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, s,
+                           io.w_router, H, E, static_cast<bf16_t*>(ws.rb6));
+        e = hipGetLastError();
+      }
+      if (e == hipSuccess)
+        e = launch_grouped_gemm_nt_f32out(ws.ra6, ws.rb6, nullptr, T, 1, 6 * E, H, ws.dxr, s, nullptr);
+      if (e == hipSuccess) {
+        hipLaunchKernelGGL(bwd_slice_offsets_kernel, dim3(1), dim3(64), 0, s, T, S, ws.roff);
+        e = hipGetLastError();
+      }
+      if (e == hipSuccess)
+        e = wgrad_bf16(x, nullptr, H, static_cast<const bf16_t*>(ws.rd3), 3 * E, ws.roff, T, S, ws.kinfo,
+                       static_cast<bf16_t*>(ws.xt), ws.ld_t, ws.rpart, s);
+      if (e == hipSuccess) {
+        hipLaunchKernelGGL(bwd_router_dw_sum_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, s,
+                           ws.rpart, S, H, E, io.dw_router);
+        e = hipGetLastError();
+      }
+    }
+  }
+  if (ws.ra6 == nullptr) {
+    if (e == hipSuccess)
+      e = launch_bwd_gemm<kNT>(args(static_cast<const float*>(ws.dl), sh.E, static_cast<const int32_t*>(nullptr), T,
+                                    io.w_router, sh.E, 0, nullptr, 0, nullptr, T, 1, 0, sh.H, sh.E, ws.dxr, sh.H, 0),
+                               s);
+    const int S = router_slices(T, sh.H, sh.E);
+    if (e == hipSuccess)
+      e = launch_bwd_gemm<kTN>(args(x, sh.H, static_cast<const int32_t*>(nullptr), T,
+                                    static_cast<const float*>(ws.dl), sh.E, 0, static_cast<const int32_t*>(nullptr), T,
+                                    nullptr, T, S, sh.H, sh.E, 0, S > 1 ? ws.dwr_part : io.dw_router, sh.E,
+                                    int64_t{sh.H} * sh.E),
+                               s);
+    if (e == hipSuccess && S > 1) {
+      const int64_t n = int64_t{sh.H} * sh.E;
+      hipLaunchKernelGGL(bwd_sum_slices_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, s,
+                         ws.dwr_part, S, n, io.dw_router);
+      e = hipGetLastError();
+    }
   }
   if (e == hipSuccess && T > 0) {
     hipLaunchKernelGGL(bwd_dx_kernel<WT>, dim3(static_cast<unsigned>(T)), dim3(256), 0, s,
@@ -912,6 +1016,14 @@ hipError_t layer_backward(const BackwardShape& sh, const BackwardIO& io, const B
 }
 
 }  // namespace
+
+bool router_split(const BackwardShape& sh, int dt) { return dt != 0 && sh.E % 32 == 0 && sh.H % 64 == 0 && sh.T > 0; }
+
+int router_split_slices(int64_t T) {
+  // about 1024 tokens per slice, at most 6 (the [H, 3E] product then has enough tiles)
+  const int64_t S = T / 1024;
+  return S < 1 ? 1 : (S > 6 ? 6 : static_cast<int>(S));
+}
 
 int router_slices(int64_t T, int H, int E) {
   // enough slices for ~512 workgroups, each of at least 64 rows, at most 32
@@ -933,8 +1045,18 @@ BackwardScratch carve_backward(const BackwardShape& sh, int dt, void* base, size
     return p;
   };
   BackwardScratch w{};
-  const int S = router_slices(T, sh.H, sh.E);
-  w.dwr_part = S > 1 ? static_cast<float*>(take(static_cast<size_t>(S) * sh.H * sh.E * 4)) : nullptr;
+  if (router_split(sh, dt)) {
+    const int64_t E = sh.E;
+    w.rS = router_split_slices(T);
+    w.ra6 = take(T * 6 * E * 2);
+    w.rb6 = take(int64_t{sh.H} * 6 * E * 2);
+    w.rd3 = take((T + kRouterPadRows) * 3 * E * 2);
+    w.rpart = static_cast<float*>(take(static_cast<size_t>(w.rS) * sh.H * 3 * E * 4));
+    w.roff = static_cast<int32_t*>(take(static_cast<size_t>(w.rS + 1) * 4));
+  } else {
+    const int S = router_slices(T, sh.H, sh.E);
+    w.dwr_part = S > 1 ? static_cast<float*>(take(static_cast<size_t>(S) * sh.H * sh.E * 4)) : nullptr;
+  }
   const bool bf16 = dt != 0;
   const int64_t pad = bf16 ? kPadRows : 0;  // zero rows after du and dy's row-order copy (bf16 weight gradients)
   w.u = static_cast<float*>(take(R * 2 * sh.F * 4));

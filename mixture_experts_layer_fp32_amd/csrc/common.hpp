@@ -273,9 +273,20 @@ struct BackwardScratch {
   int32_t *kinfo, *kinfo_s;
   void *xt, *dyp;
   int64_t ld_t;
+  // the router's products of a bf16 layer as bf16 products (router_split): dlogits split into
+  // three bf16 parts ([T, 6E] for dx, [T + 64, 3E] for dW_r), W_r split ([H, 6E]), the row slices of
+  // dW_r's contraction (offsets, S + 1 ints) and their partial products [S, H, 3E]
+  void *ra6, *rb6, *rd3;
+  int32_t* roff;
+  float* rpart;
+  int rS;
 };
 // Row slices of the router-weight gradient x^T dlogits (its [H, E] output has few tiles).
 int router_slices(int64_t T, int H, int E);
+// Whether a layer's router products run as split bf16 products (bf16 layers, E % 32 == 0,
+// H % 64 == 0), and the row slices of dW_r's contraction then.
+bool router_split(const BackwardShape& sh, int dt);
+int router_split_slices(int64_t T);
 // Carves the workspace from `base` (null: sizes only); *bytes receives the total.
 BackwardScratch carve_backward(const BackwardShape& sh, int dt, void* base, size_t* bytes);
 // dt: 0 = fp32, 1 = bf16 (activations, weights and dy alike).  events: null or 9 hipEvent_t

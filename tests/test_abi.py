@@ -211,6 +211,27 @@ def test_backward_workspace_size():
     assert L.moe_backward_workspace_size(ctypes.byref(_layer(k=9)), T) == 0
 
 
+def test_backward_workspace_size_split_router():
+    """bf16 layers with E % 32 == 0 and H % 64 == 0 take the router's products as split bf16 products:
+    dlogits in three bf16 parts [T, 6E] and [T + 64, 3E], W_r's parts [H, 6E], the partial products of
+    S = clamp(T // 1024, 1, 6) row slices [S, H, 3E] (fp32) and their offsets, in place of the fp32
+    slices; the rest as above."""
+    L = _lib.lib()
+    T, H, E, k, F = 2048, 256, 64, 2, 256
+    lay = _layer(E=E)
+    R = T * k
+    S = 2
+
+    def a(n):
+        return (n + 255) // 256 * 256
+    ld = (R + 64 * E + 63) // 64 * 64
+    want = (a(T * 6 * E * 2) + a(H * 6 * E * 2) + a((T + 64) * 3 * E * 2) + a(S * H * 3 * E * 4) + a((S + 1) * 4)
+            + a(R * 2 * F * 4) + a(R * F * 4) + a((R + 64) * 2 * F * 2) + a(R * F * 2) + a(R * 4) + a(R * H * 2)
+            + a(T * E * 4) + a(T * H * 4) + a(2 * (E + 1) * 4) + a(16) + a(max(H, F) * ld * 2)
+            + a((R + 64) * H * 2))
+    assert L.moe_backward_workspace_size(ctypes.byref(lay), T) == want
+
+
 @pytest.mark.parametrize("case,code", [
     ("fp8", UNSUP), ("no_grads", INVALID), ("no_dw1", INVALID), ("misaligned_dx", INVALID),
     ("no_routing", INVALID), ("no_offsets", INVALID), ("shared_without_dws", INVALID),

@@ -38,6 +38,9 @@ CASES = {
     "mixtral_small": _cfg("mixtral_8x7b", T=300, H=256, F=384),
     "qwen3_small": _cfg("qwen3_235b", T=333, H=320, E=16, k=4, F=256),
     "deepseek_small": _cfg("deepseek_v3", T=257, H=512, E=32, k=8, F=256, Fs=384),
+    # bf16 router products as split bf16 products (E % 32 == 0, H % 64 == 0) over 2 row slices of dW_r's
+    # contraction (T >= 2048), a slice boundary inside a 64-row block
+    "router_split_slices": _cfg("deepseek_v3", T=2100, H=256, E=32, k=2, F=128, Fs=128),
     # experts averaging 192-288 rows: the 320-row tiles in the recomputation and the data-gradient
     # products (fp32 results staged 32 rows at a time; dx_perm in bf16); H = 384 leaves a half N tile
     "deepseek_bm320": _cfg("deepseek_v3", T=520, H=384, E=8, k=4, F=256, Fs=256),
