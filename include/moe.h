@@ -268,7 +268,12 @@ moe_status moe_forward(const moe_layer* L, const void* x, int64_t T, void* y, co
  *            row slices of partial router-weight gradients [slices, H, E] fp32; for bf16
  *            also the weight gradients' operands: one activation transposed per expert with
  *            each expert's rows padded to a multiple of 64 ([max(H, F, Fs), T*k + 64 E] bf16),
- *            dy in expert-row order ([T*k + 64, H] bf16) and two small index tables.
+ *            dy in expert-row order ([T*k + 64, H] bf16) and two small index tables.  For bf16
+ *            with E a multiple of 32 and H of 64 the router's two products run as bf16 products
+ *            of split operands, as accurate as fp32 (dlogits and W_r each as three bf16 parts,
+ *            each the rounding of what the parts before it leave): in place of the fp32 row
+ *            slices, dlogits' parts [T, 6E] and [T + 64, 3E], W_r's parts [H, 6E] (bf16), and
+ *            up to 6 row slices of partial products [slices, H, 3E] fp32 with their offsets.
  * Accumulation is fp32 throughout (fp32 MFMA for fp32 operands, bf16 MFMA with fp32 accumulate
  * for bf16 ones); du and g h are rounded to x_dt before their GEMMs, and the per-row input
  * gradients dx_perm (and the shared expert's) to x_dt before dx sums them in fp32, as the forward
