@@ -35,29 +35,18 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) { return static_cast<bf16
 // SiLU(z) = z / (1 + e^-z)
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// OCP E4M3 ("e4m3fn") encode of an fp32 value already clamped to [-448, 448]: round to
-// nearest, ties to even, from the format definition (1-4-3 bits, bias 7, subnormals
-// m * 2^-9, largest finite 448).  Works on the bit pattern, no table.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;            // |v| bits
-  // |v| < 2^-6 (fp32 exponent < 121): subnormal range, quantum 2^-9.
-  if (a < (121u << 23)) {
-    // value / 2^-9 rounded to nearest even integer in [0, 8]; 2^-9 scaling is exact.
-    float q = __uint_as_float(a) * 512.0f;
-    float r = __builtin_rintf(q);          // round half to even (default rounding mode)
-    uint32_t m = static_cast<uint32_t>(r); // 0..8; 8 == smallest normal (code 0x08)
-    return m ? (sign | m) : 0u;            // a value that rounds to zero encodes as +0
-  }
-  // normal: keep 3 mantissa bits with round-to-nearest-even on the fp32 pattern
-  uint32_t lsb = (a >> 20) & 1u;
-  uint32_t rounded = a + 0x7FFFFu + lsb;   // round at bit 20
-  uint32_t e = (rounded >> 23) - 120u;     // e4m3 exponent field (fp32 bias 127, e4m3 bias 7)
-  uint32_t m = (rounded >> 20) & 7u;
-  uint32_t code = (e << 3) | m;
-  if (code > 0x7Eu) code = 0x7Eu;          // saturate (clamped input can only round to 448)
-  return sign | code;                      // code >= 8 here, never a signed zero
+// Four fp32 values already clamped to [-448, 448] -> four OCP E4M3 ("e4m3fn") codes, byte i for
+// value i, rounded to nearest with ties to even (the format: 1-4-3 bits, bias 7, subnormals m 2^-9,
+// largest finite 448): gfx950's v_cvt_pk_fp8_f32, two values per instruction, in the shader's
+// default rounding mode.  A negative value that rounds to zero is written as +0 (code 0x00), so a
+// zero is always the one code.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  const uint32_t u = static_cast<uint32_t>(w);
+  const uint32_t mag = u & 0x7F7F7F7Fu;
+  const uint32_t nz = (mag + 0x7F7F7F7Fu) & 0x80808080u;  // bit 7 of a byte: its magnitude is not 0
+  return mag | (u & nz);
 }
 
 // Scale of an e4m3 block with max magnitude amax: the smallest power of two 2^q with

@@ -502,11 +502,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp8_kernel(
         u32x4_t codes;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          uint32_t w = 0;
+          float r[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            w |= f32_to_e4m3(fminf(fmaxf(v[q][c] * inv, -448.0f), 448.0f)) << (8 * c);
-          codes[q] = w;
+          for (int c = 0; c < 4; ++c) r[c] = fminf(fmaxf(v[q][c] * inv, -448.0f), 448.0f);
+          codes[q] = pack_e4m3x4(r[0], r[1], r[2], r[3]);
         }
         *reinterpret_cast<u32x4_t*>(hq + grow * F + static_cast<int64_t>(tm.nt) * 128 + seg * 16) = codes;
         if (seg == 0) out_scales[grow * (F / 128) + tm.nt] = sc;

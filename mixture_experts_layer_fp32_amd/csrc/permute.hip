@@ -187,15 +187,11 @@ __device__ __forceinline__ uint2 quant_e4m3_x8(uint4 v, float& scale) {
   for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
   const float s = e4m3_block_scale(amax);  // a power of two
   const float inv = pow2_inverse(s);        // x * inv is x / s rounded once
-  uint32_t q[8];
+  float r[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float r = f[i] * inv;
-    r = fminf(fmaxf(r, -448.0f), 448.0f);
-    q[i] = f32_to_e4m3(r);
-  }
+  for (int i = 0; i < 8; ++i) r[i] = fminf(fmaxf(f[i] * inv, -448.0f), 448.0f);
   scale = s;
-  return make_uint2(q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24), q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24));
+  return make_uint2(pack_e4m3x4(r[0], r[1], r[2], r[3]), pack_e4m3x4(r[4], r[5], r[6], r[7]));
 }
 
 // bf16 -> e4m3 with one fp32 scale per 1x128 block (16 lanes x 8 values).
