@@ -76,13 +76,20 @@ __device__ __forceinline__ int e8m0_of(float s) { return static_cast<int>((__flo
 
 // ---- MXFP4: FP4 E2M1 elements (1 sign, 2 exponent bits with bias 1, 1 mantissa bit; magnitudes
 // 0, 0.5, 1, 1.5, 2, 3, 4, 6) with one E8M0 scale byte (2^(e - 127)) per 32 elements.
-// Code of a scaled value (|v| <= 6): the nearest magnitude, ties to the even-mantissa code; each
-// comparison adds one step, strict where the tie goes down, inclusive where it goes up.
-__device__ __forceinline__ uint32_t f32_to_fp4(float v) {
-  const float m = fabsf(v);
-  const uint32_t code = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) + (m >= 3.5f) +
-                        (m > 5.0f);
-  return (v < 0.0f && code != 0u) ? (code | 8u) : code;  // values rounding to 0 encode as +0
+// Codes of eight scaled values (|v| <= 6), nibble i for value i (low nibble first): the nearest
+// magnitude, ties to the even-mantissa code, on gfx950's v_cvt_scalef32_pk_fp4_f32 (two values per
+// instruction, scale 1, the shader's default rounding mode); a negative value that rounds to zero
+// is written as +0 (code 0), so a zero is always the one code.
+__device__ __forceinline__ uint32_t pack_fp4x8(float v0, float v1, float v2, float v3, float v4, float v5,
+                                               float v6, float v7) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v0, v1, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v2, v3, 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v4, v5, 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v6, v7, 1.0f, 3);
+  const uint32_t mag = w & 0x77777777u;
+  const uint32_t nz = (mag + 0x77777777u) & 0x88888888u;  // bit 3 of a nibble: its magnitude is not 0
+  return mag | (w & nz);
 }
 
 // E8M0 byte of the smallest power of two 2^q with 6 * 2^q >= amax, q in [-127, 127]; 127 (2^0) for

@@ -304,9 +304,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fp4_kernel(
       m = fmaxf(m, __shfl_xor(m, 1, kWave));
       const int e = fp4_block_e8m0(m);
       const float inv = e8m0_inverse(e);
-      uint32_t packed[2] = {0u, 0u};
+      uint32_t packed[2];
 #pragma unroll
-      for (int c = 0; c < 16; ++c) packed[c / 8] |= f32_to_fp4(v[c] * inv) << (4 * (c % 8));
+      for (int h = 0; h < 2; ++h) {
+        const float* p = v + 8 * h;
+        packed[h] = pack_fp4x8(p[0] * inv, p[1] * inv, p[2] * inv, p[3] * inv, p[4] * inv, p[5] * inv, p[6] * inv,
+                               p[7] * inv);
+      }
       if (grow < tm.row_end) {
         *reinterpret_cast<u32x2_t*>(hq + grow * (F / 2) + static_cast<int64_t>(tm.nt) * 64 + seg * 8) =
             u32x2_t{packed[0], packed[1]};

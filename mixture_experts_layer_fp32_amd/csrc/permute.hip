@@ -249,10 +249,7 @@ __device__ __forceinline__ uint32_t quant_fp4_x8(uint4 v, int& e8) {
   amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
   e8 = fp4_block_e8m0(amax);
   const float inv = e8m0_inverse(e8);  // f * inv is f / scale rounded once (exact: a power of two)
-  uint32_t q = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) q |= f32_to_fp4(f[i] * inv) << (4 * i);
-  return q;
+  return pack_fp4x8(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv, f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
 }
 
 // bf16 -> MXFP4 rows scattered to their permuted positions (codes [R, H / 2], scales [R, H / 32]).
