@@ -73,8 +73,20 @@ __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(int32_t* __rest
   const int64_t per = ceil_div(n, kScanThreads);
   const int64_t lo = tid * per;
   const int64_t hi = lo + per < n ? lo + per : n;
+  // runs of up to kRun entries (E ceil(T / 256) <= 16384: 256 experts and up to 16384 tokens) are
+  // loaded once, all at the same time, and kept in registers; longer runs take two passes over memory
+  constexpr int kRun = 16;
+  const bool in_regs = per <= kRun;
+  int32_t rv[kRun];
   int32_t s = 0;
-  for (int64_t i = lo; i < hi; ++i) s += base[i];
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) rv[i] = lo + i < hi ? base[lo + i] : 0;
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) s += rv[i];
+  } else {
+    for (int64_t i = lo; i < hi; ++i) s += base[i];
+  }
   // inclusive scan of the 1024 partial sums: within each wave by shuffles, then across the 16 wave
   // totals by wave 0, then each thread adds the totals of the waves before it
   const int lane = tid % kWave, wave = tid / kWave;
@@ -98,10 +110,18 @@ __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(int32_t* __rest
   }
   __syncthreads();
   int32_t run = v - s + (wave > 0 ? part[wave - 1] : 0);  // exclusive prefix of this thread's chunk
-  for (int64_t i = lo; i < hi; ++i) {
-    int32_t c = base[i];
-    base[i] = run;
-    run += c;
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+      if (lo + i < hi) base[lo + i] = run;
+      run += rv[i];
+    }
+  } else {
+    for (int64_t i = lo; i < hi; ++i) {
+      int32_t c = base[i];
+      base[i] = run;
+      run += c;
+    }
   }
   __syncthreads();
   const int32_t total = part[NW - 1];
