@@ -9,10 +9,19 @@ issue order for every K length and checks, at every wait, that
   * no load overwrites a stage before the barrier after which no wave reads its old tile
     (tile t is read between the barriers of iterations t - 1 and t).
 
-The issue orders restate the kernels' loops: a change there must be mirrored here.
+The issue orders restate the kernels' loops.  test_compiled_waits_match_the_model ties them to
+the code that runs: it compiles the GEMM sources to gfx950 assembly with the library's own flags
+and requires every instantiated kernel's set of `s_waitcnt vmcnt` counts to be exactly the set
+the model's replay waits with, so a change of ring depth, load rounds or wait counts in a kernel
+that is not made here as well fails.
 """
 
+import concurrent.futures
 import itertools
+import os
+import re
+import subprocess
+import tempfile
 
 import pytest
 
@@ -23,6 +32,7 @@ class Wave:
         self.issued = []          # (operand, tile) per load, in issue order
         self.last_barrier = -1    # iteration whose barrier was passed last (-1: the prologue's)
         self.needs = {"A", "B"} if loads_a else {"B"}  # operands this wave loads for every tile
+        self.waits = set()        # every vmcnt count the replay waited with
 
     def load(self, op, tile, count):
         ring = self.NA if op == "A" else self.NB
@@ -32,6 +42,7 @@ class Wave:
 
     def wait(self, n, tile):
         """s_waitcnt vmcnt(n): every load but the n newest has landed; `tile` must be complete."""
+        self.waits.add(n)
         done = len(self.issued) - n
         assert done >= 0
         ops = set()
@@ -121,9 +132,32 @@ def fp8_kernel(NA, NB, AR, BR, nk, scale_load, mx):
     return w
 
 
+def fp4_kernel(AR, BR, BSR, nk, scale_load):
+    """gemm_fp4_kernel: one ring of three stages, each holding a K stage of A, B and both operands'
+    scale bytes; the prologue issues stages 0 and 1; in iteration kt the wave waits for stage kt
+    (all but the next stage's loads landed), meets the barrier that publishes it, and issues stage
+    kt + 2 into the slot stage kt - 1 left.  Waves that gather A scales issue one more load per
+    stage."""
+    w = Wave(3, 3, nk)
+
+    def issue(kt):
+        if kt < nk:
+            w.load("A", kt, AR + scale_load)
+            w.load("B", kt, BR + BSR)
+
+    issue(0)
+    issue(1)
+    for kt in range(nk):
+        w.wait(AR + BR + BSR + scale_load if kt + 1 < nk else 0, kt)
+        w.last_barrier = kt - 1  # the barrier publishing stage kt frees stage kt - 1
+        issue(kt + 2)
+    return w
+
+
 # ring depths and loads per wave per tile of the instantiated kernels
 BF16 = {"BM 320": (2, 2, 5, 4, 2), "BM 256": (2, 3, 4, 4, 0), "BM 128": (3, 3, 2, 4, 0)}
 FP8 = {"MX, BM 192": (2, 3, 3, 4, True), "general, BM 128": (3, 3, 2, 4, False)}
+FP4 = {"BM 128": (2, 4, 1)}  # A rounds, B rounds, B scale rounds per wave per stage
 
 
 @pytest.mark.parametrize("name", list(BF16))
@@ -175,3 +209,82 @@ def test_model_catches_an_early_overwrite():
         w.load("A", 2, 1)  # the stage of A tile 0, before the barrier of iteration 0
     w.last_barrier = 0
     w.load("A", 2, 1)
+
+
+@pytest.mark.parametrize("name", list(FP4))
+def test_fp4_ring_protocol(name):
+    AR, BR, BSR = FP4[name]
+    for nk, scale_load in itertools.product(range(1, 80), (0, 1)):
+        fp4_kernel(AR, BR, BSR, nk, scale_load)
+
+
+# ---- the model against the compiled kernels
+
+def _model_waits():
+    """vmcnt counts of the model's replays, per kernel family and tile height (mangled BM)."""
+    out = {}
+    for name, (NA, NB, AR, BR, place) in BF16.items():
+        s = set()
+        for nk, dead in itertools.product(range(1, 80), range(AR + 1)):
+            s |= bf16_kernel(NA, NB, AR, BR, nk, dead, place).waits
+        out[("gemm_bf16_kernel", int(name.split()[-1]))] = s
+    for name, (NA, NB, AR, BR, mx) in FP8.items():
+        s = set()
+        for nk, scale_load in itertools.product(range(1, 80), (0, 1)):
+            s |= fp8_kernel(NA, NB, AR, BR, nk, scale_load, mx).waits
+        out[("gemm_fp8_kernel", int(name.split()[-1]))] = s
+    for name, (AR, BR, BSR) in FP4.items():
+        s = set()
+        for nk, scale_load in itertools.product(range(1, 80), (0, 1)):
+            s |= fp4_kernel(AR, BR, BSR, nk, scale_load).waits
+        out[("gemm_fp4_kernel", int(name.split()[-1]))] = s
+    return out
+
+
+@pytest.fixture(scope="module")
+def compiled_asm():
+    from mixture_experts_layer_fp32_amd import build
+    try:
+        cc = build.hipcc()
+    except RuntimeError as e:
+        pytest.skip(str(e))
+    srcs = ["gemm.hip", "gemm_fp8.hip", "gemm_fp4.hip"]
+    with tempfile.TemporaryDirectory() as d:
+        def one(src):
+            out = os.path.join(d, src + ".s")
+            cmd = [cc] + build._flags() + ["--cuda-device-only", "-S", os.path.join(build.CSRC, src), "-o", out]
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            assert res.returncode == 0, res.stderr[-2000:]
+            with open(out) as f:
+                return f.read()
+        with concurrent.futures.ThreadPoolExecutor(len(srcs)) as ex:
+            return "\n".join(ex.map(one, srcs))
+
+
+def test_compiled_waits_match_the_model(compiled_asm):
+    """Every instantiated GEMM kernel waits with exactly the vmcnt counts the model's replay of its
+    ring configuration uses (the kernels' only vmcnt waits are the protocol's)."""
+    model = _model_waits()
+    seen = set()
+    for m in re.finditer(r"^(_ZN\S*?(gemm_(?:bf16|fp8|fp4)_kernel)ILi(\d+)E\S*):\s*(?:;.*)?$", compiled_asm, re.M):
+        sym, fam, bm = m.group(1), m.group(2), int(m.group(3))
+        end = compiled_asm.find(".Lfunc_end", m.end())
+        waits = {int(v) for v in re.findall(r"s_waitcnt vmcnt\((\d+)\)", compiled_asm[m.end():end])}
+        assert (fam, bm) in model, f"{sym}: no model for this tile height"
+        assert waits == model[(fam, bm)], (sym, sorted(waits), sorted(model[(fam, bm)]))
+        seen.add((fam, bm))
+    assert seen == set(model), ("configurations modelled but not compiled", set(model) - seen)
+
+
+@pytest.mark.parametrize("fam,key,wrong", [
+    ("bf16", "BM 256", (2, 3, 3, 4, 0)),           # one A round fewer than the kernel loads
+    ("bf16", "BM 320", (2, 3, 5, 4, 0)),           # a third B stage the kernel does not have
+    ("fp8", "MX, BM 192", (2, 2, 3, 4, True)),     # a B ring one stage shallower
+    ("fp4", "BM 128", (2, 4, 2)),                  # twice the B scale loads
+])
+def test_compiled_check_detects_a_changed_ring(compiled_asm, monkeypatch, fam, key, wrong):
+    """The comparison is not vacuous: a model one step off the kernel's configuration fails it."""
+    table = {"bf16": BF16, "fp8": FP8, "fp4": FP4}[fam]
+    monkeypatch.setitem(table, key, wrong)
+    with pytest.raises(AssertionError):
+        test_compiled_waits_match_the_model(compiled_asm)
