@@ -3,7 +3,11 @@
 The index formulas of bwd_gemm_kernel are restated here and checked for coverage: every operand
 tile element is loaded and stored by exactly one thread, the LDS swizzle is a permutation of each
 row that keeps 16-byte chunks whole, and the XCD-contiguous order of the TN tiles visits every
-tile exactly once.  A change to those formulas in the kernel must be mirrored here.
+tile exactly once.  The restated formulas are this model's; the kernel itself is checked by the
+GPU parity of the fp32 backward (tests/test_parity_backward.py: the fp32 cases, among them
+fp32_multi_group with 9 and 10 m-tiles per weight gradient, run this kernel for every product),
+so a formula changed in the kernel but not here fails there, and this model covers the shapes
+those cases do not.
 """
 
 import itertools
